@@ -1,0 +1,59 @@
+"""Test-side packers: write known codes / scales into the byte formats.
+
+These are written independently of both the oracle (which only unpacks) and
+the GPU library.  The layouts they produce are the readings documented in
+the design doc (affine-4: low nibble first, 8 codes per little-endian 32-bit word;
+Q4_K: the public 144-byte GGUF block); the hand-packed pins in
+test_oracle_pins.py fix those layouts byte by byte.
+"""
+import numpy as np
+
+
+def pack_affine4_codes(q):
+    """q: int array [N, K] with values 0..15 -> uint32 [N, K/8]."""
+    q = np.asarray(q, dtype=np.uint64)
+    N, K = q.shape
+    assert K % 8 == 0
+    q = q.reshape(N, K // 8, 8)
+    words = np.zeros((N, K // 8), dtype=np.uint64)
+    for i in range(8):
+        words |= q[:, :, i] << np.uint64(4 * i)
+    return words.astype(np.uint32)
+
+
+def pack_q4k_scales(sc, m):
+    """sc, m: int arrays [..., 8] of 6-bit values -> uint8 [..., 12]."""
+    sc = np.asarray(sc, dtype=np.uint8)
+    m = np.asarray(m, dtype=np.uint8)
+    out = np.zeros(sc.shape[:-1] + (12,), dtype=np.uint8)
+    for j in range(4):
+        out[..., j] = (sc[..., j] & 63) | ((sc[..., j + 4] >> 4) << 6)
+        out[..., j + 4] = (m[..., j] & 63) | ((m[..., j + 4] >> 4) << 6)
+        out[..., j + 8] = (sc[..., j + 4] & 15) | ((m[..., j + 4] & 15) << 4)
+    return out
+
+
+def pack_q4k_codes(q):
+    """q: int array [..., 256] (codes of one block, in weight order) -> uint8 [..., 128]."""
+    q = np.asarray(q, dtype=np.uint8)
+    out = np.zeros(q.shape[:-1] + (128,), dtype=np.uint8)
+    for c in range(4):
+        lo = q[..., 64 * c: 64 * c + 32]
+        hi = q[..., 64 * c + 32: 64 * c + 64]
+        out[..., 32 * c: 32 * c + 32] = (lo & 15) | ((hi & 15) << 4)
+    return out
+
+
+def q4k_block(d_bits, dmin_bits, sc, m, q):
+    """Assemble Q4_K blocks. d_bits/dmin_bits: uint16 [...]; sc, m: [..., 8]; q: [..., 256]."""
+    d_bits = np.asarray(d_bits, dtype=np.uint16)
+    dmin_bits = np.asarray(dmin_bits, dtype=np.uint16)
+    shape = d_bits.shape
+    out = np.zeros(shape + (144,), dtype=np.uint8)
+    out[..., 0] = d_bits & 0xFF
+    out[..., 1] = d_bits >> 8
+    out[..., 2] = dmin_bits & 0xFF
+    out[..., 3] = dmin_bits >> 8
+    out[..., 4:16] = pack_q4k_scales(sc, m)
+    out[..., 16:144] = pack_q4k_codes(q)
+    return out
