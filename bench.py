@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the 4-bit quantized decode hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  1. 4B-class speculative verify MLP block, M = 8 rows:
+       rmsnorm_gateup_swiglu  X[8,2560] -> h[8,12800]   (gate+up 25600 x 2560, affine-4 g64)
+       qgemv_affine4          h[8,12800] -> Y[8,2560]   (down 2560 x 12800, affine-4 g64)
+  2. Q4_K MoE decode token:
+       moe_expert_qgemv       x[1,2048], 128 experts, top-8, gate/up 1536 x 2048, down 2048 x 768
+  3. Untied LM head with greedy verify, M = 8:
+       lmhead_argmax          X[8,1024] x W[151936,1024] affine-4 g64 -> ids[8], accepted
+Weights are resident in HBM; distinct copies are rotated (and the MoE router
+logits change every step) so that no step is served by the 256 MB Infinity
+Cache.  The same step at M = 1 gives the verify cost ratio t(M=8)/t(M=1).
+
+Prints ONE JSON line (see the "roofline" and "cpu_baseline" objects).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) for 4-bit qGEMV at M=1 and M=8; verify cost ratio"
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["bit_quantized_decode_group_amd/csrc/common.h", "bit_quantized_decode_group_amd/csrc/affine4.hip",
+                  "bit_quantized_decode_group_amd/csrc/q4k.hip", "bit_quantized_decode_group_amd/csrc/abi.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=5, help="weight copies rotated to defeat the Infinity Cache")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-m1", action="store_true", help="skip the M=1 step (verify ratio)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus N with N > 1 is not supported "
+              "(the projection has no multi-GPU path here)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_quantized_decode_group_amd import ops, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ops.lib()
+
+    def to_dev(a, kind):
+        a = np.ascontiguousarray(a)
+        if kind == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        if kind == "u32":
+            return torch.from_numpy(a.view(np.int32)).to(dev)
+        if kind == "u8":
+            return torch.from_numpy(a).to(dev)
+        if kind == "f32":
+            return torch.from_numpy(a.astype(np.float32)).to(dev)
+        if kind == "i32":
+            return torch.from_numpy(a.astype(np.int32)).to(dev)
+        raise ValueError(kind)
+
+    t0 = time.time()
+    vb = synth.verify_block()          # M=8, D=2560, I=12800, seed 1003
+    lm = synth.lm_head(M=8)            # V=151936, K=1024, seed 1005
+    n_logit_sets = 64
+    moe = synth.moe_token(n_logit_sets=n_logit_sets)  # E=128, D=2048, I=768, top-8, seed 1004
+    log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+
+    C = max(1, args.copies)
+    base = {
+        "codes_gu": to_dev(vb["codes_gu"], "u32"), "scales_gu": to_dev(vb["scales_gu"], "bf16"),
+        "biases_gu": to_dev(vb["biases_gu"], "bf16"), "codes_d": to_dev(vb["codes_d"], "u32"),
+        "scales_d": to_dev(vb["scales_d"], "bf16"), "biases_d": to_dev(vb["biases_d"], "bf16"),
+        "codes_lm": to_dev(lm["codes"], "u32"), "scales_lm": to_dev(lm["scales"], "bf16"),
+        "biases_lm": to_dev(lm["biases"], "bf16"),
+    }
+    copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(C - 1)]
+    moe_base = {"w_gu": to_dev(moe["w_gu"], "u8"), "w_down": to_dev(moe["w_down"], "u8")}
+    moe_stacks = [moe_base, {k: v.clone() for k, v in moe_base.items()}]
+    logits = to_dev(moe["logits"], "f32")
+    x8 = to_dev(vb["x"], "bf16")
+    gamma = to_dev(vb["gamma"], "bf16")
+    xm = to_dev(moe["x"], "bf16")
+    xl8 = to_dev(lm["x"], "bf16")
+    draft = to_dev(lm["draft"], "i32")
+    torch.cuda.synchronize()
+    log(f"[bench] {C} weight copies + 2 MoE stacks resident in HBM")
+
+    D, I, V, K5 = vb["D"], vb["I"], lm["V"], lm["K"]
+    E, Dm, Im, top_k = moe["E"], moe["D"], moe["I"], moe["top_k"]
+
+    def bufs(M):
+        return {
+            "x": x8[:M].contiguous(), "xl": xl8[:M].contiguous(),
+            "h": torch.empty((M, I), dtype=torch.bfloat16, device=dev),
+            "y": torch.empty((M, D), dtype=torch.bfloat16, device=dev),
+            "ym": torch.empty((1, Dm), dtype=torch.bfloat16, device=dev),
+            "mids": torch.empty(top_k, dtype=torch.int32, device=dev),
+            "mw": torch.empty(top_k, dtype=torch.float32, device=dev),
+            "ids": torch.empty(M, dtype=torch.int32, device=dev),
+            "acc": torch.empty(1, dtype=torch.int32, device=dev),
+        }
+
+    # Algorithmic bytes per step: every weight byte once (0.5625 B/weight), the
+    # activations read, the outputs written, and the two intermediates (h of
+    # the MLP block, the MoE expert activations) written once and read once.
+    def step_bytes(M):
+        w = {
+            "rmsnorm_gateup_swiglu": 2 * I * D // 2 + 2 * (2 * I * D // 64) * 2,
+            "qgemv_affine4": D * I // 2 + 2 * (D * I // 64) * 2,
+            "moe_expert_qgemv": top_k * (2 * Im * Dm // 256 * 144 + Dm * Im // 256 * 144),
+            "lmhead_argmax": V * K5 // 2 + 2 * (V * K5 // 64) * 2,
+        }
+        a = {
+            "rmsnorm_gateup_swiglu": M * D * 2 + D * 2 + M * I * 2,
+            "qgemv_affine4": M * I * 2 + M * D * 2,
+            "moe_expert_qgemv": Dm * 2 + E * 4 + 2 * top_k * Im * 4 + Dm * 2 + top_k * 8,
+            "lmhead_argmax": M * K5 * 2 + M * 4 * 2 + 4,
+        }
+        return {k: w[k] + a[k] for k in w}, w
+
+    names = ["rmsnorm_gateup_swiglu", "qgemv_affine4", "moe_expert_qgemv", "lmhead_argmax"]
+
+    def run_step(i, M, b, ev=None):
+        c = copies[i % C]
+        ms = moe_stacks[i % 2]
+        lg = logits[i % n_logit_sets]
+        if ev is not None:
+            ev[0].record()
+        ops.rmsnorm_gateup_swiglu(b["x"], gamma, vb["eps"], c["codes_gu"], c["scales_gu"], c["biases_gu"], h=b["h"])
+        if ev is not None:
+            ev[1].record()
+        ops.qgemv_affine4(b["h"], c["codes_d"], c["scales_d"], c["biases_d"], y=b["y"])
+        if ev is not None:
+            ev[2].record()
+        ops.moe_expert_qgemv(xm, lg, top_k, ms["w_gu"], ms["w_down"], y=b["ym"], out_ids=b["mids"], out_w=b["mw"])
+        if ev is not None:
+            ev[3].record()
+        ops.lmhead_argmax(b["xl"], c["codes_lm"], c["scales_lm"], c["biases_lm"], draft=draft[:M].contiguous()
+                          if M < 8 else draft, ids=b["ids"], accepted=b["acc"])
+        if ev is not None:
+            ev[4].record()
+
+    def timed(M, steps, warmup):
+        b = bufs(M)
+        for i in range(warmup):
+            run_step(i, M, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            run_step(warmup + i, M, b)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        ms_step = e0.elapsed_time(e1) / steps
+        # per-kernel durations: the same steps again with events around each launch
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        for i in range(steps):
+            run_step(warmup + steps + i, M, b, evs[i])
+        torch.cuda.synchronize()
+        per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)])) * 1e3
+               for j, n in enumerate(names)}
+        inst = float(np.mean([evs[i][0].elapsed_time(evs[i][4]) for i in range(steps)]))
+        return ms_step, wall, per, inst, b
+
+    log(f"[bench] timing M=8: warmup {args.warmup}, steps {args.steps}")
+    ms8, wall8, per8, inst8, b8 = timed(8, args.steps, args.warmup)
+    bytes8, wbytes = step_bytes(8)
+    total8 = sum(bytes8.values())
+    value = total8 / (ms8 * 1e-3) / 1e9
+    log(f"[bench] M=8: {ms8 * 1e3:.1f} us/step -> {value:.0f} GB/s; per kernel (us): "
+        + ", ".join(f"{n}={per8[n]:.1f}" for n in names))
+    accepted = int(b8["acc"].cpu()[0])
+
+    ms1 = per1 = None
+    if not args.no_m1:
+        s1 = max(20, args.steps // 2)
+        log(f"[bench] timing M=1: steps {s1}")
+        ms1, _, per1, _, _ = timed(1, s1, max(5, args.warmup // 2))
+        log(f"[bench] M=1: {ms1 * 1e3:.1f} us/step; ratio {ms8 / ms1:.3f}")
+
+    # practical streaming ceiling (context): torch's reduction over 2 GiB, read once
+    big = torch.empty(2 ** 30, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    for _ in range(2):
+        big.sum(dtype=torch.float32)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        big.sum(dtype=torch.float32)
+    e1.record()
+    torch.cuda.synchronize()
+    stream_gbs = 5 * big.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del big
+
+    kernels = {}
+    for n in names:
+        k = {"us_m8": round(per8[n], 2), "bytes_m8": bytes8[n], "gb_s_m8": round(bytes8[n] / (per8[n] * 1e-6) / 1e9, 1),
+             "frac_m8": round(bytes8[n] / (per8[n] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        if per1 is not None:
+            b1 = step_bytes(1)[0][n]
+            k.update({"us_m1": round(per1[n], 2), "gb_s_m1": round(b1 / (per1[n] * 1e-6) / 1e9, 1),
+                      "frac_m1": round(b1 / (per1[n] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                      "verify_ratio": round(per8[n] / per1[n], 3)})
+        kernels[n] = k
+
+    # dominant kernel = largest share of the step's time
+    dom = max(names, key=lambda n: per8[n])
+    dom_gbs = bytes8[dom] / (per8[dom] * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tf = json.load(open(TRAFFIC_FILE))
+            ent = tf.get("kernels", {}).get(dom)
+            if ent and tf.get("source_hash") == kernel_source_hash():
+                traffic = ent.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": bytes8[dom], "avg_launch_us": round(per8[dom], 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(vb, lm, moe, total8)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms8, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode verify step (M=8): 4B-class MLP block X[8,2560] RMSNorm->gate+up "
+                               "2560->2x12800->SwiGLU->down 12800->2560 (affine-4 g64) + Q4_K MoE token "
+                               "(128 experts, top-8, 2048<->768) + untied LM head X[8,1024] x W[151936,1024] "
+                               "(affine-4 g64) greedy verify",
+                   "M": 8, "weight_copies": C, "algorithmic_bytes_per_step": total8,
+                   "weight_bytes_per_step": sum(wbytes.values()), "accum": "fp32", "weights": "4-bit"},
+        "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+        "ms_per_step_m1": round(ms1, 5) if ms1 else None,
+        "verify_ratio": round(ms8 / ms1, 4) if ms1 else None,
+        "tokens_per_s_m8": round(8 / (ms8 * 1e-3), 1),
+        "tokens_per_s_m1": round(1 / (ms1 * 1e-3), 1) if ms1 else None,
+        "accepted_prefix": accepted,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stream_ceiling_gb_s": round(stream_gbs, 1),
+        "instrumented_ms_per_step": round(inst8, 5),
+        "wall_s_timed": round(wall8, 4),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(vb, lm, moe, step_bytes):
+    """The CPU oracle (plain single-threaded C, fp64) on the same step: the
+    full MLP block at M=8, the MoE token with the first logit set, and the LM
+    head at M=8 with its draft ids.  Reported in the same unit."""
+    import oracle
+    t = time.perf_counter()
+    oracle.mlp_block(vb["x"], vb["gamma"], vb["eps"], vb["codes_gu"], vb["scales_gu"], vb["biases_gu"],
+                     vb["codes_d"], vb["scales_d"], vb["biases_d"])
+    oracle.moe(moe["x"], moe["logits"][0], moe["top_k"], moe["w_gu"], moe["w_down"], moe["E"], moe["D"], moe["I"])
+    oracle.lmhead(lm["x"], lm["codes"], lm["scales"], lm["biases"], draft=lm["draft"], want_logits=False)
+    dt = time.perf_counter() - t
+    log(f"[bench] cpu oracle: one full step in {dt:.1f}s")
+    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "one full step (MLP block M=8, MoE token, LM head M=8), same seeded inputs",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

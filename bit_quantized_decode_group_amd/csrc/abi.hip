@@ -1,0 +1,489 @@
+// abi.hip -- the C ABI of libqgemv.so (declared in include/qgemv.h):
+// argument checks, the per-(device, stream) workspace, the work decomposition
+// (split-K, tiles per wave) and dispatch to the kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/qgemv.h"
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qg_status fail(qg_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_err() { g_err[0] = '\0'; }
+
+struct Buf {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+qg_status check_ptr(const Buf& b, size_t align, const char* fn) {
+  if (b.bytes == 0) return QG_OK;
+  if (!b.p) return fail(QG_EINVAL, "%s: %s is null", fn, b.name);
+  if (!aligned(b.p, align)) return fail(QG_EINVAL, "%s: %s must be %zu-byte aligned", fn, b.name, align);
+  return QG_OK;
+}
+
+bool overlaps(const Buf& a, const Buf& b) {
+  if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.bytes, b0 = (uintptr_t)b.p, b1 = b0 + b.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+qg_status check_alias(const Buf* outs, int nout, const Buf* ins, int nin, const char* fn) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(outs[i], ins[j]))
+        return fail(QG_EALIAS, "%s: output %s overlaps input %s", fn, outs[i].name, ins[j].name);
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(outs[i], outs[j]))
+        return fail(QG_EALIAS, "%s: output %s overlaps output %s", fn, outs[i].name, outs[j].name);
+  }
+  return QG_OK;
+}
+
+constexpr size_t kLdsBudget = 65536;       // bytes of LDS one workgroup may use
+constexpr int kWaves = 4;                  // waves per workgroup of the projection kernels
+constexpr int kTargetWaves = 2048;         // enough waves to cover HBM latency on 256 CUs
+constexpr int kMaxWavesInFlight = 4096;    // beyond this, waves stream several tiles
+constexpr size_t kCounterArea = 256 * 1024;  // zeroed area: argmax keys, done counter, tile counters
+constexpr size_t kKeysOff = 0, kDoneOff = 64, kTileCntOff = 1024;
+constexpr int kMaxTileCounters = (int)((kCounterArea - kTileCntOff) / 4);
+
+size_t affine_lds_per_chunk(int M) { return (size_t)256 * M + 64 + (size_t)8 * M; }
+size_t affine_lds_fixed() { return 32 + (size_t)kWaves * 64; }
+size_t q4k_lds_per_sb(int M) { return (size_t)512 * M + 256; }
+
+// Modes without split-K stage all of K: ceil(K/128) chunks must fit.
+bool fits_lds_unsplit(int M, int K) {
+  const size_t nchunks = ((size_t)K / 64 + 1) / 2;
+  return nchunks * affine_lds_per_chunk(M) + affine_lds_fixed() <= kLdsBudget;
+}
+
+struct Plan {
+  int S, cps, tpw, rgroups;
+};
+
+// Split-K and tiles-per-wave choice shared by the projection kernels.
+Plan plan_split(int ntiles, int nchunks, int cps_max, bool allow_split) {
+  Plan pl{};
+  const int s_min = (nchunks + cps_max - 1) / cps_max;
+  int S = s_min;
+  if (allow_split && (long long)ntiles * S < kTargetWaves) {
+    const int want = (kTargetWaves + ntiles - 1) / std::max(ntiles, 1);
+    S = std::max(s_min, std::min(want, std::max(1, nchunks / 2)));
+  }
+  if (!allow_split) S = 1;
+  pl.cps = (nchunks + S - 1) / S;
+  pl.S = (nchunks + pl.cps - 1) / pl.cps;
+  const long long waves = (long long)ntiles * pl.S;
+  pl.tpw = (int)std::min<long long>(8, std::max<long long>(1, waves / kMaxWavesInFlight));
+  pl.rgroups = (ntiles + kWaves * pl.tpw - 1) / (kWaves * pl.tpw);
+  return pl;
+}
+
+// ---------------------------------------------------------- workspace --
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+// Returns a zero-initialised-at-creation workspace of at least `need` bytes
+// beyond the counter area, for the current device and this stream.
+qg_status get_workspace(hipStream_t stream, size_t need, unsigned char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QG_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace& w = g_ws[{dev, stream}];
+  const size_t total = kCounterArea + need;
+  if (w.bytes < total) {
+    if (w.ptr) {
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return fail(QG_EHIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    size_t nb = std::max(total, (size_t)4 << 20);
+    void* p = nullptr;
+    e = hipMalloc(&p, nb);
+    if (e != hipSuccess) return fail(QG_ENOMEM, "workspace hipMalloc(%zu): %s", nb, hipGetErrorString(e));
+    e = hipMemsetAsync(p, 0, nb, stream);
+    if (e != hipSuccess) {
+      (void)hipFree(p);
+      return fail(QG_EHIP, "workspace hipMemsetAsync: %s", hipGetErrorString(e));
+    }
+    w.ptr = p;
+    w.bytes = nb;
+  }
+  *out = static_cast<unsigned char*>(w.ptr);
+  return QG_OK;
+}
+
+// The kernels are gfx950 code objects; refuse other devices by name.
+qg_status check_device() {
+  static std::mutex mu;
+  static int ok[64] = {0};  // 0 unknown, 1 ok, -1 not gfx950
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QG_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(QG_EUNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(QG_EHIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  if (ok[dev] < 0) return fail(QG_EUNSUPPORTED, "device %d is not gfx950 (MI355X); no kernels for it", dev);
+  return QG_OK;
+}
+
+qg_status launched(int err, const char* fn) {
+  if (err != 0) return fail(QG_EHIP, "%s: launch failed: %s", fn, hipGetErrorString((hipError_t)err));
+  clear_err();
+  return QG_OK;
+}
+
+// ------------------------------------------------------------ checks --
+qg_status check_affine_common(const char* fn, int M, int N, int K) {
+  if (M < 1 || M > 8) return fail(QG_EINVAL, "%s: M=%d must be in 1..8", fn, M);
+  if (N < 0) return fail(QG_EINVAL, "%s: N=%d must be >= 0", fn, N);
+  if (K <= 0 || K % 64 != 0) return fail(QG_EINVAL, "%s: K=%d must be a positive multiple of 64", fn, K);
+  if ((long long)N * 16 > 0x7FFFFFFFLL) return fail(QG_EINVAL, "%s: N=%d too large", fn, N);
+  return QG_OK;
+}
+
+qg_status do_check_qgemv_affine4(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                                 const uint16_t* biases, uint16_t* y, int M, int N, int K) {
+  const char* fn = "qgemv_affine4";
+  qg_status st = check_affine_common(fn, M, N, K);
+  if (st) return st;
+  const size_t n = (size_t)N, k = (size_t)K;
+  const Buf in[] = {{x, (size_t)M * k * 2, "x"},
+                    {codes, n * k / 2, "codes"},
+                    {scales, n * (k / 64) * 2, "scales"},
+                    {biases, n * (k / 64) * 2, "biases"}};
+  const Buf out[] = {{y, (size_t)M * n * 2, "y"}};
+  if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(in[2], 2, fn)) ||
+      (st = check_ptr(in[3], 2, fn)) || (st = check_ptr(out[0], 2, fn)))
+    return st;
+  return check_alias(out, 1, in, 4, fn);
+}
+
+qg_status do_check_qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K) {
+  const char* fn = "qgemv_q4k";
+  if (M < 1 || M > 8) return fail(QG_EINVAL, "%s: M=%d must be in 1..8", fn, M);
+  if (N < 0) return fail(QG_EINVAL, "%s: N=%d must be >= 0", fn, N);
+  if (K <= 0 || K % 256 != 0) return fail(QG_EINVAL, "%s: K=%d must be a positive multiple of 256", fn, K);
+  if ((long long)N * 16 > 0x7FFFFFFFLL) return fail(QG_EINVAL, "%s: N=%d too large", fn, N);
+  const size_t n = (size_t)N, k = (size_t)K;
+  const Buf in[] = {{x, (size_t)M * k * 2, "x"}, {blocks, n * (k / 256) * 144, "blocks"}};
+  const Buf out[] = {{y, (size_t)M * n * 2, "y"}};
+  qg_status st;
+  if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(out[0], 2, fn)))
+    return st;
+  return check_alias(out, 1, in, 2, fn);
+}
+
+qg_status do_check_gateup(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes,
+                          const uint16_t* scales, const uint16_t* biases, uint16_t* h, int M, int I, int K) {
+  const char* fn = "rmsnorm_gateup_swiglu";
+  qg_status st = check_affine_common(fn, M, I, K);
+  if (st) return st;
+  if (!(eps > 0.0f) || eps != eps || eps > 3.0e38f) return fail(QG_EINVAL, "%s: eps must be positive and finite", fn);
+  if (!fits_lds_unsplit(M, K))
+    return fail(QG_EUNSUPPORTED, "%s: M=%d rows of K=%d do not fit the staged-activation LDS budget", fn, M, K);
+  if ((long long)I * 2 * 16 > 0x7FFFFFFFLL) return fail(QG_EINVAL, "%s: I=%d too large", fn, I);
+  const size_t i2 = (size_t)2 * I, k = (size_t)K;
+  const Buf in[] = {{x, (size_t)M * k * 2, "x"},
+                    {gamma, k * 2, "gamma"},
+                    {codes, i2 * k / 2, "codes_gu"},
+                    {scales, i2 * (k / 64) * 2, "scales_gu"},
+                    {biases, i2 * (k / 64) * 2, "biases_gu"}};
+  const Buf out[] = {{h, (size_t)M * I * 2, "h"}};
+  if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(in[2], 16, fn)) ||
+      (st = check_ptr(in[3], 2, fn)) || (st = check_ptr(in[4], 2, fn)) || (st = check_ptr(out[0], 2, fn)))
+    return st;
+  return check_alias(out, 1, in, 5, fn);
+}
+
+qg_status do_check_moe(const uint16_t* x, const float* logits, int top_k, const uint8_t* w_gu,
+                       const uint8_t* w_down, uint16_t* y, int32_t* out_ids, float* out_w, int E, int D, int I) {
+  const char* fn = "moe_expert_qgemv";
+  if (E < 1 || E > 1024) return fail(QG_EINVAL, "%s: E=%d must be in 1..1024", fn, E);
+  if (top_k < 1 || top_k > E) return fail(QG_EINVAL, "%s: top_k=%d must be in 1..E", fn, top_k);
+  if (top_k > 64) return fail(QG_EUNSUPPORTED, "%s: top_k=%d above 64", fn, top_k);
+  if (D <= 0 || D % 256 != 0) return fail(QG_EINVAL, "%s: D=%d must be a positive multiple of 256", fn, D);
+  if (I <= 0 || I % 256 != 0) return fail(QG_EINVAL, "%s: I=%d must be a positive multiple of 256", fn, I);
+  if ((size_t)(D / 256) * 768 > kLdsBudget)
+    return fail(QG_EUNSUPPORTED, "%s: D=%d too large for the staged activation", fn, D);
+  if ((size_t)top_k * (I / 256) * 768 > kLdsBudget)
+    return fail(QG_EUNSUPPORTED, "%s: top_k*I/256=%d too large for the staged expert activations", fn,
+                top_k * (I / 256));
+  const size_t e = (size_t)E, d = (size_t)D, i = (size_t)I;
+  const Buf in[] = {{x, d * 2, "x"},
+                    {logits, e * 4, "router_logits"},
+                    {w_gu, e * 2 * i * (d / 256) * 144, "w_gu"},
+                    {w_down, e * d * (i / 256) * 144, "w_down"}};
+  const Buf out[] = {{y, d * 2, "y"}, {out_ids, out_ids ? (size_t)top_k * 4 : 0, "out_ids"},
+                     {out_w, out_w ? (size_t)top_k * 4 : 0, "out_w"}};
+  qg_status st;
+  if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 4, fn)) || (st = check_ptr(in[2], 16, fn)) ||
+      (st = check_ptr(in[3], 16, fn)) || (st = check_ptr(out[0], 2, fn)))
+    return st;
+  if (out_ids && (st = check_ptr(out[1], 4, fn))) return st;
+  if (out_w && (st = check_ptr(out[2], 4, fn))) return st;
+  return check_alias(out, 3, in, 4, fn);
+}
+
+qg_status do_check_lmhead(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                          float* logits, int32_t* ids, const int32_t* draft, int32_t* accepted, int M, int V,
+                          int K) {
+  const char* fn = "lmhead_argmax";
+  qg_status st = check_affine_common(fn, M, V, K);
+  if (st) return st;
+  if (V < 1) return fail(QG_EINVAL, "%s: V=%d must be >= 1", fn, V);
+  if (!fits_lds_unsplit(M, K))
+    return fail(QG_EUNSUPPORTED, "%s: M=%d rows of K=%d do not fit the staged-activation LDS budget", fn, M, K);
+  const size_t v = (size_t)V, k = (size_t)K;
+  const Buf in[] = {{x, (size_t)M * k * 2, "x"},
+                    {codes, v * k / 2, "codes"},
+                    {scales, v * (k / 64) * 2, "scales"},
+                    {biases, v * (k / 64) * 2, "biases"},
+                    {draft, draft ? (size_t)M * 4 : 0, "draft"}};
+  const Buf out[] = {{logits, logits ? (size_t)M * v * 4 : 0, "logits"},
+                     {ids, (size_t)M * 4, "ids"},
+                     {accepted, accepted ? (size_t)4 : (size_t)0, "accepted"}};
+  if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(in[2], 2, fn)) ||
+      (st = check_ptr(in[3], 2, fn)) || (st = check_ptr(out[1], 4, fn)))
+    return st;
+  if (draft && (st = check_ptr(in[4], 4, fn))) return st;
+  if (logits && (st = check_ptr(out[0], 4, fn))) return st;
+  if (accepted && (st = check_ptr(out[2], 4, fn))) return st;
+  return check_alias(out, 3, in, 5, fn);
+}
+
+// --------------------------------------------------------- dispatch --
+qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* fn) {
+  const int G = a.K / 64;
+  a.G = G;
+  a.nchunks = (G + 1) / 2;
+  a.ntiles = (a.N + 15) / 16;
+  a.waves = kWaves;
+  const size_t per = affine_lds_per_chunk(a.M);
+  const int cps_max = (int)std::min<size_t>((size_t)a.nchunks, (kLdsBudget - affine_lds_fixed()) / per);
+  const bool allow_split = (mode == QG_MODE_PLAIN) && a.ntiles <= kMaxTileCounters;
+  if (!allow_split && a.nchunks > cps_max)
+    return fail(QG_EUNSUPPORTED, "%s: K=%d needs a split of K this mode or size lacks", fn, a.K);
+  Plan pl = plan_split(a.ntiles, a.nchunks, std::max(cps_max, 1), allow_split);
+  a.S = pl.S;
+  a.cps = pl.cps;
+  a.tpw = pl.tpw;
+  a.rgroups = pl.rgroups;
+  unsigned char* ws = nullptr;
+  const size_t part_bytes = (a.S > 1) ? (size_t)a.S * a.M * a.N * 4 : 0;
+  qg_status st = get_workspace(stream, part_bytes, &ws);
+  if (st) return st;
+  a.keys = reinterpret_cast<unsigned long long*>(ws + kKeysOff);
+  a.done_cnt = reinterpret_cast<uint32_t*>(ws + kDoneOff);
+  a.tile_cnt = reinterpret_cast<uint32_t*>(ws + kTileCntOff);
+  a.part = reinterpret_cast<float*>(ws + kCounterArea);
+  const size_t lds = (size_t)a.cps * per + affine_lds_fixed();
+  return launched(qg_launch_affine(mode, a, lds, stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qg_status_string(qg_status s) {
+  switch (s) {
+    case QG_OK: return "ok";
+    case QG_EINVAL: return "invalid argument (shape, null pointer or alignment)";
+    case QG_EALIAS: return "an output overlaps an input or another output";
+    case QG_EUNSUPPORTED: return "valid request with no kernel instance";
+    case QG_EHIP: return "HIP runtime or launch error";
+    case QG_ENOMEM: return "workspace allocation failed";
+    default: return "unknown status";
+  }
+}
+
+const char* qg_last_error(void) { return g_err; }
+
+qg_status qg_check_qgemv_affine4(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                                 const uint16_t* biases, uint16_t* y, int M, int N, int K) {
+  clear_err();
+  return do_check_qgemv_affine4(x, codes, scales, biases, y, M, N, K);
+}
+
+qg_status qg_check_qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K) {
+  clear_err();
+  return do_check_qgemv_q4k(x, blocks, y, M, N, K);
+}
+
+qg_status qg_check_rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma, float eps,
+                                         const uint32_t* codes_gu, const uint16_t* scales_gu,
+                                         const uint16_t* biases_gu, uint16_t* h, int M, int I, int K) {
+  clear_err();
+  return do_check_gateup(x, gamma, eps, codes_gu, scales_gu, biases_gu, h, M, I, K);
+}
+
+qg_status qg_check_moe_expert_qgemv(const uint16_t* x, const float* router_logits, int top_k, const uint8_t* w_gu,
+                                    const uint8_t* w_down, uint16_t* y, int32_t* out_ids, float* out_w, int E, int D,
+                                    int I) {
+  clear_err();
+  return do_check_moe(x, router_logits, top_k, w_gu, w_down, y, out_ids, out_w, E, D, I);
+}
+
+qg_status qg_check_lmhead_argmax(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                                 const uint16_t* biases, float* logits, int32_t* ids, const int32_t* draft,
+                                 int32_t* accepted, int M, int V, int K) {
+  clear_err();
+  return do_check_lmhead(x, codes, scales, biases, logits, ids, draft, accepted, M, V, K);
+}
+
+qg_status qgemv_affine4(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                        uint16_t* y, int M, int N, int K, void* stream) {
+  clear_err();
+  qg_status st = do_check_qgemv_affine4(x, codes, scales, biases, y, M, N, K);
+  if (st) return st;
+  if (N == 0) return QG_OK;
+  if ((st = check_device())) return st;
+  QgAffineArgs a{};
+  a.x = x;
+  a.codes = codes;
+  a.scales = scales;
+  a.biases = biases;
+  a.y = y;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  return run_affine(QG_MODE_PLAIN, a, (hipStream_t)stream, "qgemv_affine4");
+}
+
+qg_status rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes_gu,
+                                const uint16_t* scales_gu, const uint16_t* biases_gu, uint16_t* h, int M, int I,
+                                int K, void* stream) {
+  clear_err();
+  qg_status st = do_check_gateup(x, gamma, eps, codes_gu, scales_gu, biases_gu, h, M, I, K);
+  if (st) return st;
+  if (I == 0) return QG_OK;
+  if ((st = check_device())) return st;
+  QgAffineArgs a{};
+  a.x = x;
+  a.gamma = gamma;
+  a.eps = eps;
+  a.codes = codes_gu;
+  a.scales = scales_gu;
+  a.biases = biases_gu;
+  a.y = h;
+  a.M = M;
+  a.N = I;
+  a.K = K;
+  return run_affine(QG_MODE_GATEUP, a, (hipStream_t)stream, "rmsnorm_gateup_swiglu");
+}
+
+qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                        float* logits, int32_t* ids, const int32_t* draft, int32_t* accepted, int M, int V, int K,
+                        void* stream) {
+  clear_err();
+  qg_status st = do_check_lmhead(x, codes, scales, biases, logits, ids, draft, accepted, M, V, K);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  QgAffineArgs a{};
+  a.x = x;
+  a.codes = codes;
+  a.scales = scales;
+  a.biases = biases;
+  a.logits = logits;
+  a.ids = ids;
+  a.draft = draft;
+  a.accepted = accepted;
+  a.M = M;
+  a.N = V;
+  a.K = K;
+  return run_affine(QG_MODE_LMHEAD, a, (hipStream_t)stream, "lmhead_argmax");
+}
+
+qg_status qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K, void* stream) {
+  clear_err();
+  qg_status st = do_check_qgemv_q4k(x, blocks, y, M, N, K);
+  if (st) return st;
+  if (N == 0) return QG_OK;
+  if ((st = check_device())) return st;
+  QgQ4kArgs a{};
+  a.x = x;
+  a.blocks = blocks;
+  a.y = y;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.nchunks = K / 256;
+  a.ntiles = (N + 15) / 16;
+  a.waves = kWaves;
+  const size_t per = q4k_lds_per_sb(M);
+  const int cps_max = (int)std::max<size_t>(1, std::min<size_t>((size_t)a.nchunks, kLdsBudget / per));
+  const bool allow_split = a.ntiles <= kMaxTileCounters;
+  Plan pl = plan_split(a.ntiles, a.nchunks, cps_max, allow_split);
+  if (pl.S > 1 && !allow_split) return fail(QG_EUNSUPPORTED, "qgemv_q4k: N=%d too large to split K=%d", N, K);
+  a.S = pl.S;
+  a.cps = pl.cps;
+  a.tpw = pl.tpw;
+  a.rgroups = pl.rgroups;
+  unsigned char* ws = nullptr;
+  const size_t part_bytes = (a.S > 1) ? (size_t)a.S * M * N * 4 : 0;
+  if ((st = get_workspace((hipStream_t)stream, part_bytes, &ws))) return st;
+  a.tile_cnt = reinterpret_cast<uint32_t*>(ws + kTileCntOff);
+  a.part = reinterpret_cast<float*>(ws + kCounterArea);
+  return launched(qg_launch_q4k(a, (size_t)a.cps * per, (hipStream_t)stream), "qgemv_q4k");
+}
+
+qg_status moe_expert_qgemv(const uint16_t* x, const float* router_logits, int top_k, const uint8_t* w_gu,
+                           const uint8_t* w_down, uint16_t* y, int32_t* out_ids, float* out_w, int E, int D, int I,
+                           void* stream) {
+  clear_err();
+  qg_status st = do_check_moe(x, router_logits, top_k, w_gu, w_down, y, out_ids, out_w, E, D, I);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  unsigned char* ws = nullptr;
+  if ((st = get_workspace((hipStream_t)stream, (size_t)top_k * I * 4, &ws))) return st;
+  QgMoeArgs a{};
+  a.x = x;
+  a.logits = router_logits;
+  a.top_k = top_k;
+  a.w_gu = w_gu;
+  a.w_down = w_down;
+  a.y = y;
+  a.out_ids = out_ids;
+  a.out_w = out_w;
+  a.h = reinterpret_cast<float*>(ws + kCounterArea);
+  a.E = E;
+  a.D = D;
+  a.I = I;
+  return launched(qg_launch_moe(a, (hipStream_t)stream), "moe_expert_qgemv");
+}
+
+}  // extern "C"

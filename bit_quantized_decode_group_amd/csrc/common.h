@@ -1,0 +1,143 @@
+// common.h -- device helpers and launch descriptors shared by the gfx950
+// kernels of libqgemv.so.  Internal to the library.
+//
+// Operand scheme used by every projection kernel
+// ----------------------------------------------
+// The reduction runs on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16):
+//   A (16 x 32)  = activation rows (one MFMA row per activation row m < M),
+//   B (32 x 16)  = 16 weight rows n of the current tile,
+//   C (16 x 16)  = fp32 partial sums.
+// Lane l of a wave holds A row l%16, B column l%16 and k-slots 8*(l/16)..+7 of
+// both operands; it receives C rows 4*(l/16)..+3 of column l%16.
+//
+// Exact operands: a 4-bit code q becomes the bf16 bit pattern 0x4300|q, which
+// is exactly 128+q, so no dequantised weight is ever rounded.  The activation
+// is bf16 already.  The offset and the per-group affine are applied to the
+// fp32 group sums afterwards:  sum_k x*(s*q+b) = s*D + (b-128*s)*sum_k x,
+// with D = sum_k x*(128+q) coming from the MFMA.
+//
+// Two scale groups per MFMA: decode activations have M <= 8 rows but the MFMA
+// has 16.  Rows 0..7 carry group g and rows 8..15 carry group g+1; the k-slots
+// of lanes 0..31 (l/16 in {0,1}) hold codes of group g and those of lanes
+// 32..63 codes of group g+1, and the activation row of the other group is zero
+// in those slots.  After the MFMAs of one "chunk" (two groups), lanes 0..31
+// hold group g's sums and lanes 32..63 group g+1's, so every lane applies one
+// scale and one bias; the two halves are added once per tile.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN, overflow -> inf.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Eight affine codes of one little-endian word (code i at bits 4i..4i+3) as
+// eight bf16 values 128+q.  Element 2j (low half of dword j) is code j and
+// element 2j+1 (high half) is code j+4, so MFMA k-slot s holds code
+// kAffineSlotCode[s].
+__device__ __forceinline__ uint4 unpack_affine_word(uint32_t w) {
+  const uint32_t m = 0x000F000Fu, one28 = 0x43004300u;
+  uint4 r;
+  r.x = (w & m) | one28;
+  r.y = ((w >> 4) & m) | one28;
+  r.z = ((w >> 8) & m) | one28;
+  r.w = ((w >> 12) & m) | one28;
+  return r;
+}
+
+// Eight Q4_K codes from eight consecutive code bytes (w0 = bytes 0..3, w1 =
+// bytes 4..7): the low nibbles when sh == 0, the high nibbles when sh == 4.
+// Slot s holds the code of byte kQ4kSlotByte[s].
+__device__ __forceinline__ uint4 unpack_q4k_bytes(uint32_t w0, uint32_t w1, uint32_t sh) {
+  const uint32_t m = 0x000F000Fu, one28 = 0x43004300u;
+  uint4 r;
+  r.x = ((w0 >> sh) & m) | one28;
+  r.y = ((w0 >> (sh + 8u)) & m) | one28;
+  r.z = ((w1 >> sh) & m) | one28;
+  r.w = ((w1 >> (sh + 8u)) & m) | one28;
+  return r;
+}
+
+// Order-preserving key of (logit, index) for a max-reduction: a larger value
+// wins, then a lower index; any NaN beats every number (the first NaN wins);
+// -0 and +0 compare equal.
+__device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t fk;
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) fk = 0xFFFFFFFFu;
+  else if ((u & 0x7FFFFFFFu) == 0u) fk = 0x80000000u;
+  else fk = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)fk << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
+}
+
+}  // namespace qg
+
+// ----------------------------------------------------------- host side ---
+// Launch descriptors filled by the ABI layer (abi.hip) and consumed by the
+// launchers in affine4.hip / q4k.hip.
+
+enum QgAffineMode { QG_MODE_PLAIN = 0, QG_MODE_GATEUP = 1, QG_MODE_LMHEAD = 2 };
+
+struct QgAffineArgs {
+  const uint16_t* x;
+  const uint16_t* gamma;
+  float eps;
+  const uint32_t* codes;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  uint16_t* y;  // PLAIN: Y [M][N]; GATEUP: h [M][N] with N = I
+  float* logits;
+  int32_t* ids;
+  const int32_t* draft;
+  int32_t* accepted;
+  float* part;                // [S][M][N] split-K partials
+  uint32_t* tile_cnt;         // [ntiles] split-K arrival counters (zero between calls)
+  unsigned long long* keys;   // [8] argmax keys (zero between calls)
+  uint32_t* done_cnt;         // [1] finished-workgroup counter (zero between calls)
+  int M, N, K, G;
+  int nchunks, S, cps, ntiles, tpw, rgroups, waves;
+};
+
+struct QgQ4kArgs {
+  const uint16_t* x;
+  const uint8_t* blocks;
+  uint16_t* y;
+  float* part;
+  uint32_t* tile_cnt;
+  int M, N, K;
+  int nchunks, S, cps, ntiles, tpw, rgroups, waves;
+};
+
+struct QgMoeArgs {
+  const uint16_t* x;
+  const float* logits;
+  int top_k;
+  const uint8_t* w_gu;
+  const uint8_t* w_down;
+  uint16_t* y;
+  int32_t* out_ids;
+  float* out_w;
+  float* h;  // [top_k][I] fp32 workspace
+  int E, D, I;
+};
+
+// Launchers return a hipError_t value (0 on success).
+int qg_launch_affine(int mode, const QgAffineArgs& a, size_t lds_bytes, hipStream_t stream);
+int qg_launch_q4k(const QgQ4kArgs& a, size_t lds_bytes, hipStream_t stream);
+int qg_launch_moe(const QgMoeArgs& a, hipStream_t stream);

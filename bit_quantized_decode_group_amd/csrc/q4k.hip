@@ -1,0 +1,429 @@
+// q4k.hip -- gfx950 kernels for GGUF Q4_K weights (256-weight superblocks,
+// eight 32-weight sub-blocks with 6-bit scales and mins, fp16 d and dmin),
+// consumed as stored (runNburn page, section "GGUF를 그대로 진실의 원본으로 둡니다").
+//
+//   k_q4k          Y = X . dequant(W)^T                          (qgemv_q4k)
+//   k_moe_gateup   route, then h_e = silu(G_e x) * (U_e x) for every selected
+//                  expert e, into an fp32 workspace
+//   k_moe_down     route, then y = sum_e p_e Down_e h_e over the selected
+//                  experts in ascending expert order
+//   (uzu page: MixtureOfExperts with a routing function; runNburn page: the
+//   engine never alters routing or quantisation semantics -- the selected set
+//   and weights are the plain top-k / softmax of the given logits.)
+//
+// Operand mapping (see common.h for the MFMA scheme).  A Q4_K "chunk" is 64
+// consecutive weights = 32 code bytes = sub-blocks 2c (low nibbles) and 2c+1
+// (high nibbles).  Lane l (row l%16, kb = l/16) loads code bytes 8kb..8kb+7
+// of the chunk.  MFMA t (t = 0, 1) of the chunk uses the low nibbles in lanes
+// with (kb/2) ^ t == 0 and the high nibbles in the others, so C rows 0..7 sum
+// sub-block 2c and rows 8..15 sub-block 2c+1, and lane l's C values belong to
+// sub-block 2c + l/32.  Slot s of a lane holds code byte
+// {0,2,1,3,4,6,5,7}[s] of its eight bytes.
+#include "common.h"
+
+namespace qg {
+
+constexpr int kSbBatch = 2;  // superblocks whose loads are issued together
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Stage activation rows [M][K-slice of nsb superblocks starting at sb0] into
+// LDS in operand order.  Entry ((cc*2 + t)*4 + kb)*M + m holds the eight
+// activations at k = 64cc + 32pk + 8kb + byte(s), pk = (kb/2) ^ t, for chunk
+// cc of the slice; sx[jl*8 + m] is the fp32 sum of sub-block jl's 32 staged
+// values.  Source rows are bf16 (T = uint16_t) or fp32 rounded to bf16
+// (T = float, the SwiGLU output of the gate/up kernel).
+template <int M, typename T>
+__device__ __forceinline__ void stage_q4k_x(const T* src, size_t ld, int K, uint4* xs, float* sx, int sb0,
+                                            int nsb, int tid, int nthr) {
+  const int nj = 8 * nsb;
+  for (int pi = tid; pi < M * nj; pi += nthr) {
+    const int m = pi / nj;
+    const int jl = pi - m * nj;
+    const size_t k0 = (size_t)(sb0 * 8 + jl) * 32;
+    uint32_t v[16];  // 32 bf16 values, pairs
+    float sum = 0.f;
+    if (k0 < (size_t)K) {
+      if constexpr (sizeof(T) == 2) {
+        const uint4* s4 = reinterpret_cast<const uint4*>(src + (size_t)m * ld + k0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 t = s4[i];
+          v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+        }
+      } else {
+        const float4* s4 = reinterpret_cast<const float4*>(src + (size_t)m * ld + k0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 t = s4[i];
+          v[2 * i] = (uint32_t)f32_to_bf16_bits(t.x) | ((uint32_t)f32_to_bf16_bits(t.y) << 16);
+          v[2 * i + 1] = (uint32_t)f32_to_bf16_bits(t.z) | ((uint32_t)f32_to_bf16_bits(t.w) << 16);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sum += bf16_bits_to_f32(v[i] & 0xFFFFu);
+        sum += bf16_bits_to_f32(v[i] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = 0u;
+    }
+    const int cc = jl >> 1, pk = jl & 1;
+    constexpr int kByte[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int t = pk ^ (kb >> 1);
+      uint32_t e[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int klo = 8 * kb + kByte[2 * j], khi = 8 * kb + kByte[2 * j + 1];
+        const uint32_t lo = (klo & 1) ? (v[klo >> 1] >> 16) : (v[klo >> 1] & 0xFFFFu);
+        const uint32_t hi = (khi & 1) ? (v[khi >> 1] >> 16) : (v[khi >> 1] & 0xFFFFu);
+        e[j] = lo | (hi << 16);
+      }
+      xs[((cc * 2 + t) * 4 + kb) * M + m] = make_uint4(e[0], e[1], e[2], e[3]);
+    }
+    sx[jl * 8 + m] = sum;
+  }
+  if (M < 8) {
+    for (int pi = tid; pi < nj * (8 - M); pi += nthr) sx[(pi / (8 - M)) * 8 + M + pi % (8 - M)] = 0.f;
+  }
+}
+
+// Accumulate one lane's share of a 16-row tile over nsb superblocks of K into
+// acc[b] for NB tiles whose (row, superblock 0) blocks start at blk[b].
+// xs / sx are this slice's staged activations.
+template <int M, int NB>
+__device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* const (&blk)[NB], bool row_ok,
+                                         int nsb, const uint4* xs, const float* sx, int lane) {
+  const int kb = lane >> 4;
+  const int half = lane >> 5;
+  const int rho = lane & 15;
+  const bool act0 = ((rho >> 3) == ((kb >> 1) ^ 0)) && ((rho & 7) < M);
+  const bool act1 = ((rho >> 3) == ((kb >> 1) ^ 1)) && ((rho & 7) < M);
+  const uint32_t sh0 = 4u * (uint32_t)((kb >> 1) ^ 0), sh1 = 4u * (uint32_t)((kb >> 1) ^ 1);
+  const uint4* a_base = xs + kb * M + (rho & 7);
+  const float* sx_base = sx + half * 8 + 4 * (kb & 1);
+
+  for (int sb = 0; sb < nsb; sb += kSbBatch) {
+    uint4 hdr[NB][kSbBatch];
+    uint2 cq[NB][kSbBatch][4];
+#pragma unroll
+    for (int u = 0; u < kSbBatch; ++u) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        hdr[b][u] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) cq[b][u][c] = make_uint2(0u, 0u);
+        if (row_ok && sb + u < nsb) {
+          const uint8_t* bp = blk[b] + (size_t)(sb + u) * 144;
+          hdr[b][u] = *reinterpret_cast<const uint4*>(bp);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) cq[b][u][c] = *reinterpret_cast<const uint2*>(bp + 16 + 32 * c + 8 * kb);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSbBatch; ++u) {
+      const int sbl = sb + u;
+      if (sbl >= nsb) break;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const uint4 h = hdr[b][u];
+        const float d = f16_bits_to_f32(h.x & 0xFFFFu);
+        const float dmin = f16_bits_to_f32(h.x >> 16);
+        const uint32_t Y = h.y >> (8 * half), Z = h.z >> (8 * half), Wd = h.w >> (8 * half);
+        // six-bit scale / min of sub-block j = 2c + half (public Q4_K packing)
+        const uint32_t sc[4] = {Y & 63u, (Y >> 16) & 63u, (Wd & 15u) | ((Y >> 2) & 0x30u),
+                                ((Wd >> 16) & 15u) | ((Y >> 18) & 0x30u)};
+        const uint32_t mn[4] = {Z & 63u, (Z >> 16) & 63u, ((Wd >> 4) & 15u) | ((Z >> 2) & 0x30u),
+                                ((Wd >> 20) & 15u) | ((Z >> 18) & 0x30u)};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int cc = sbl * 4 + c;
+          const uint4* ap = a_base + (size_t)cc * 8 * M;
+          const uint4 a0 = act0 ? ap[0] : make_uint4(0u, 0u, 0u, 0u);
+          const uint4 a1 = act1 ? ap[4 * M] : make_uint4(0u, 0u, 0u, 0u);
+          f32x4_t C = {0.f, 0.f, 0.f, 0.f};
+          C = mfma_bf16(a0, unpack_q4k_bytes(cq[b][u][c].x, cq[b][u][c].y, sh0), C);
+          C = mfma_bf16(a1, unpack_q4k_bytes(cq[b][u][c].x, cq[b][u][c].y, sh1), C);
+          const float4 sxv = *reinterpret_cast<const float4*>(sx_base + cc * 16);
+          const float a = d * (float)sc[c];                 // exact in fp32
+          const float bt = fmaf(dmin, (float)mn[c], 128.0f * a);
+          acc[b][0] = fmaf(a, C[0], fmaf(-bt, sxv.x, acc[b][0]));
+          acc[b][1] = fmaf(a, C[1], fmaf(-bt, sxv.y, acc[b][1]));
+          acc[b][2] = fmaf(a, C[2], fmaf(-bt, sxv.z, acc[b][2]));
+          acc[b][3] = fmaf(a, C[3], fmaf(-bt, sxv.w, acc[b][3]));
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ qgemv_q4k --
+template <int M>
+__global__ void __launch_bounds__(256) k_q4k(QgQ4kArgs p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int slice = blockIdx.x % p.S, rg = blockIdx.x / p.S;
+  const int sb0 = slice * p.cps;
+  const int nsb = min(p.cps, p.nchunks - sb0);  // here a "chunk" of the split is one superblock
+  uint4* xs = reinterpret_cast<uint4*>(smem);
+  float* sx = reinterpret_cast<float*>(xs + nsb * 32 * M);
+  stage_q4k_x<M, uint16_t>(p.x, (size_t)p.K, p.K, xs, sx, sb0, nsb, threadIdx.x, blockDim.x);
+  __syncthreads();
+
+  const int nb_row = p.K / 256;
+  for (int it = 0; it < p.tpw; ++it) {
+    const int tile = (rg * W) * p.tpw + wave + it * W;
+    if (tile >= p.ntiles) break;
+    const int row = tile * 16 + (lane & 15);
+    const bool row_ok = row < p.N;
+    const uint8_t* blk[1] = {p.blocks + ((size_t)(row_ok ? row : 0) * nb_row + sb0) * 144};
+    f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    q4k_tile<M, 1>(acc, blk, row_ok, nsb, xs, sx, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[0][r] += __shfl_xor(acc[0][r], 32);
+    const bool out_lane = (lane < 32) && row_ok;
+    const int mbase = 4 * (lane >> 4);
+    if (p.S == 1) {
+      if (out_lane) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (mbase + r < M) p.y[(size_t)(mbase + r) * p.N + row] = f32_to_bf16_bits(acc[0][r]);
+      }
+    } else {
+      if (out_lane) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (mbase + r < M) p.part[((size_t)slice * M + mbase + r) * p.N + row] = acc[0][r];
+      }
+      __threadfence();
+      uint32_t prev = 0u;
+      if (lane == 0) prev = atomicAdd(&p.tile_cnt[tile], 1u);
+      prev = (uint32_t)__shfl((int)prev, 0);
+      if (prev == (uint32_t)(p.S - 1)) {
+        __threadfence();
+        if (out_lane) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (mbase + r < M) {
+              float t = 0.f;
+              for (int s2 = 0; s2 < p.S; ++s2) t += p.part[((size_t)s2 * M + mbase + r) * p.N + row];
+              p.y[(size_t)(mbase + r) * p.N + row] = f32_to_bf16_bits(t);
+            }
+          }
+        }
+        if (lane == 0) atomicExch(&p.tile_cnt[tile], 0u);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- routing --
+// Wave 0 of the workgroup selects the top_k largest logits (larger first,
+// equal values -> lower index) and their softmax weights over the selected
+// set.  Results in LDS: sel[] / pw[] in selection order, asc[] / pasc[] sorted
+// by expert index.  Every workgroup runs the same code on the same logits and
+// gets the same bytes.
+__device__ void route_topk(const float* logits, int E, int top_k, int* sel, float* pw, int* asc, float* pasc) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    float v[16];
+    uint32_t taken = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = (e < E) ? logits[e] : 0.f;
+    }
+    for (int s = 0; s < top_k; ++s) {
+      float bv = 0.f;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && !((taken >> i) & 1u)) {
+          if (bi == 0x7FFFFFFF || v[i] > bv || (v[i] == bv && e < bi)) {
+            bv = v[i];
+            bi = e;
+          }
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi))) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (lane == 0) sel[s] = bi;
+    }
+    if (lane == 0) {
+      const float lmax = logits[sel[0]];
+      float z = 0.f;
+      for (int s = 0; s < top_k; ++s) {
+        pw[s] = expf(logits[sel[s]] - lmax);
+        z += pw[s];
+      }
+      for (int s = 0; s < top_k; ++s) pw[s] = pw[s] / z;
+      for (int s = 0; s < top_k; ++s) {  // insertion sort by expert index
+        int e = sel[s];
+        float w = pw[s];
+        int j = s - 1;
+        while (j >= 0 && asc[j] > e) {
+          asc[j + 1] = asc[j];
+          pasc[j + 1] = pasc[j];
+          --j;
+        }
+        asc[j + 1] = e;
+        pasc[j + 1] = w;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------- MoE gate/up --
+// One workgroup per (selected expert slot, 16-row tile of I); its four waves
+// split the D/256 superblocks and add their partial sums in wave order.
+constexpr int kMoeWaves = 4;
+
+__global__ void __launch_bounds__(256) k_moe_gateup(QgMoeArgs p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int sel[64], asc[64];
+  __shared__ float pw[64], pasc[64];
+  __shared__ f32x4_t red[kMoeWaves][2][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tiles = (p.I + 15) / 16;
+  const int slot = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  const int nsb = p.D / 256;
+  uint4* xs = reinterpret_cast<uint4*>(smem);
+  float* sx = reinterpret_cast<float*>(xs + nsb * 32);
+
+  route_topk(p.logits, p.E, p.top_k, sel, pw, asc, pasc);
+  stage_q4k_x<1, uint16_t>(p.x, (size_t)p.D, p.D, xs, sx, 0, nsb, threadIdx.x, blockDim.x);
+  __syncthreads();
+
+  const int e = asc[slot];
+  const int row = tile * 16 + (lane & 15);
+  const bool row_ok = row < p.I;
+  // this wave's superblocks: [sb_lo, sb_hi)
+  const int per = (nsb + kMoeWaves - 1) / kMoeWaves;
+  const int sb_lo = min(nsb, wave * per), sb_hi = min(nsb, sb_lo + per);
+  const size_t expert_bytes = (size_t)2 * p.I * nsb * 144;
+  const uint8_t* base = p.w_gu + (size_t)e * expert_bytes;
+  const int r0 = row_ok ? row : 0;
+  const uint8_t* blk[2] = {base + ((size_t)r0 * nsb + sb_lo) * 144, base + ((size_t)(p.I + r0) * nsb + sb_lo) * 144};
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  if (sb_hi > sb_lo)
+    q4k_tile<1, 2>(acc, blk, row_ok, sb_hi - sb_lo, xs + (size_t)sb_lo * 32, sx + sb_lo * 64, lane);
+  red[wave][0][lane] = acc[0];
+  red[wave][1][lane] = acc[1];
+  __syncthreads();
+  if (wave == 0) {
+    f32x4_t g = red[0][0][lane], u = red[0][1][lane];
+    for (int w = 1; w < kMoeWaves; ++w) {
+      g += red[w][0][lane];
+      u += red[w][1][lane];
+    }
+    const float gv = g[0] + __shfl_xor(g[0], 32);  // M = 1: row 0 lives in element 0 of lanes 0..15
+    const float uv = u[0] + __shfl_xor(u[0], 32);
+    if (lane < 16 && row_ok) p.h[(size_t)slot * p.I + row] = gv / (1.0f + __expf(-gv)) * uv;
+  }
+}
+
+// ------------------------------------------------------------- MoE down --
+// One workgroup per 16-row tile of D.  Wave w handles the selected experts
+// w, w+W, ... (ascending expert order); each expert's sum is scaled by its
+// routing weight; the waves' totals are added in wave order.
+constexpr int kMoeDownWaves = 8;
+
+__global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int sel[64], asc[64];
+  __shared__ float pw[64], pasc[64];
+  __shared__ f32x4_t red[kMoeDownWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
+  const int tile = blockIdx.x;
+  const int nsb = p.I / 256;
+  const size_t xs_per = (size_t)nsb * 32;  // uint4 entries per expert (M = 1)
+  uint4* xs = reinterpret_cast<uint4*>(smem);
+  float* sx = reinterpret_cast<float*>(xs + xs_per * p.top_k);
+
+  route_topk(p.logits, p.E, p.top_k, sel, pw, asc, pasc);
+  for (int s = 0; s < p.top_k; ++s)
+    stage_q4k_x<1, float>(p.h + (size_t)s * p.I, (size_t)p.I, p.I, xs + xs_per * s, sx + (size_t)s * nsb * 64, 0,
+                          nsb, threadIdx.x, blockDim.x);
+  __syncthreads();
+
+  const int row = tile * 16 + (lane & 15);
+  const bool row_ok = row < p.D;
+  const int r0 = row_ok ? row : 0;
+  const size_t expert_bytes = (size_t)p.D * nsb * 144;
+  f32x4_t tot = {0.f, 0.f, 0.f, 0.f};
+  for (int s = wave; s < p.top_k; s += W) {
+    const int e = asc[s];
+    const uint8_t* blk[1] = {p.w_down + (size_t)e * expert_bytes + (size_t)r0 * nsb * 144};
+    f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    q4k_tile<1, 1>(acc, blk, row_ok, nsb, xs + xs_per * s, sx + (size_t)s * nsb * 64, lane);
+    const float pe = pasc[s];
+    tot[0] = fmaf(pe, acc[0][0], tot[0]);
+    tot[1] = fmaf(pe, acc[0][1], tot[1]);
+    tot[2] = fmaf(pe, acc[0][2], tot[2]);
+    tot[3] = fmaf(pe, acc[0][3], tot[3]);
+  }
+  red[wave][lane] = tot;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4_t t = red[0][lane];
+    for (int w = 1; w < W; ++w) t += red[w][lane];
+    const float yv = t[0] + __shfl_xor(t[0], 32);
+    if (lane < 16 && row_ok) p.y[row] = f32_to_bf16_bits(yv);
+    if (blockIdx.x == 0 && lane < p.top_k) {
+      if (p.out_ids) p.out_ids[lane] = sel[lane];
+      if (p.out_w) p.out_w[lane] = pw[lane];
+    }
+  }
+}
+
+template <int M>
+static int launch_q4k_m(const QgQ4kArgs& a, size_t lds, hipStream_t st) {
+  hipLaunchKernelGGL((k_q4k<M>), dim3((unsigned)(a.S * a.rgroups)), dim3((unsigned)(64 * a.waves)), lds, st, a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace qg
+
+int qg_launch_q4k(const QgQ4kArgs& a, size_t lds, hipStream_t st) {
+  switch (a.M) {
+    case 1: return qg::launch_q4k_m<1>(a, lds, st);
+    case 2: return qg::launch_q4k_m<2>(a, lds, st);
+    case 3: return qg::launch_q4k_m<3>(a, lds, st);
+    case 4: return qg::launch_q4k_m<4>(a, lds, st);
+    case 5: return qg::launch_q4k_m<5>(a, lds, st);
+    case 6: return qg::launch_q4k_m<6>(a, lds, st);
+    case 7: return qg::launch_q4k_m<7>(a, lds, st);
+    case 8: return qg::launch_q4k_m<8>(a, lds, st);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+int qg_launch_moe(const QgMoeArgs& a, hipStream_t st) {
+  const int nsb_d = a.D / 256, nsb_i = a.I / 256;
+  const size_t lds_gu = (size_t)nsb_d * 32 * 16 + (size_t)nsb_d * 64 * 4;
+  const int tiles_i = (a.I + 15) / 16;
+  hipLaunchKernelGGL(qg::k_moe_gateup, dim3((unsigned)(a.top_k * tiles_i)), dim3(64 * qg::kMoeWaves), lds_gu, st,
+                     a);
+  int err = (int)hipGetLastError();
+  if (err) return err;
+  const size_t lds_dn = (size_t)a.top_k * ((size_t)nsb_i * 32 * 16 + (size_t)nsb_i * 64 * 4);
+  const int waves = a.top_k < qg::kMoeDownWaves ? a.top_k : qg::kMoeDownWaves;
+  hipLaunchKernelGGL(qg::k_moe_down, dim3((unsigned)((a.D + 15) / 16)), dim3(64 * waves), lds_dn, st, a);
+  return (int)hipGetLastError();
+}

@@ -1,0 +1,210 @@
+"""Thin Python binding over libqgemv.so (declared in include/qgemv.h).
+
+Argument marshalling only: every function takes torch CUDA tensors, checks
+that their dtypes / element sizes / contiguity match what the C ABI expects,
+allocates outputs that were not passed in, and hands raw device pointers and
+torch's current HIP stream to the library.  All arithmetic runs in the HIP
+kernels.  There is no fallback: if the library was not built, the first call
+raises.
+
+Tensor conventions (bit patterns are what the ABI sees):
+  bf16 data   torch.bfloat16 (or int16/uint16 holding bf16 bits)
+  affine4     codes int32/uint32 [N, K/8]; scales, biases bf16 [N, K/64]
+  Q4_K        uint8 [..., K/256, 144] (any leading shape; row-major blocks)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemv.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "qgemv.h")
+
+QG_OK, QG_EINVAL, QG_EALIAS, QG_EUNSUPPORTED, QG_EHIP, QG_ENOMEM = 0, -1, -2, -3, -4, -5
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SIGS = {
+    "qgemv_affine4": [_P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "qgemv_q4k": [_P, _P, _P, _I, _I, _I, _P],
+    "rmsnorm_gateup_swiglu": [_P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P],
+    "moe_expert_qgemv": [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "lmhead_argmax": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "qg_check_qgemv_affine4": [_P, _P, _P, _P, _P, _I, _I, _I],
+    "qg_check_qgemv_q4k": [_P, _P, _P, _I, _I, _I],
+    "qg_check_rmsnorm_gateup_swiglu": [_P, _P, _F, _P, _P, _P, _P, _I, _I, _I],
+    "qg_check_moe_expert_qgemv": [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I],
+    "qg_check_lmhead_argmax": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I],
+}
+
+
+class QgError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+def lib():
+    """Load libqgemv.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m bit_quantized_decode_group_amd.build` "
+                "(there is no CPU fallback)")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(l, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int32
+        l.qg_status_string.argtypes = [ctypes.c_int32]
+        l.qg_status_string.restype = ctypes.c_char_p
+        l.qg_last_error.argtypes = []
+        l.qg_last_error.restype = ctypes.c_char_p
+        _lib = l
+    return _lib
+
+
+def _raise_on(status: int, where: str):
+    if status != QG_OK:
+        l = lib()
+        detail = l.qg_last_error().decode() or l.qg_status_string(status).decode()
+        raise QgError(status, where, detail)
+
+
+def _ptr(t):
+    return None if t is None else _P(t.data_ptr())
+
+
+def _stream():
+    return _P(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, esize, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.element_size() != esize:
+        raise TypeError(f"{name}: element size {t.element_size()} != {esize}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _dims2(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    return t.shape[0], t.shape[1]
+
+
+def qgemv_affine4(x, codes, scales, biases, y=None):
+    """Y[M,N] (bf16) = X[M,K] . dequant(W)[N,K]^T for affine-4 weights."""
+    M, K = _dims2(x, "x")
+    N = codes.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    for t, n, e in ((x, "x", 2), (codes, "codes", 4), (scales, "scales", 2), (biases, "biases", 2), (y, "y", 2)):
+        _need(t, n, e, x.device)
+    with torch.cuda.device(x.device):
+        _raise_on(lib().qgemv_affine4(_ptr(x), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(y), M, N, K, _stream()),
+                  "qgemv_affine4")
+    return y
+
+
+def qgemv_q4k(x, blocks, y=None):
+    """Y[M,N] (bf16) = X[M,K] . dequant(W)[N,K]^T for Q4_K blocks [N, K/256, 144]."""
+    M, K = _dims2(x, "x")
+    N = blocks.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    for t, n, e in ((x, "x", 2), (blocks, "blocks", 1), (y, "y", 2)):
+        _need(t, n, e, x.device)
+    if blocks.numel() != N * (K // 256) * 144:
+        raise ValueError("blocks must hold N * K/256 * 144 bytes")
+    with torch.cuda.device(x.device):
+        _raise_on(lib().qgemv_q4k(_ptr(x), _ptr(blocks), _ptr(y), M, N, K, _stream()), "qgemv_q4k")
+    return y
+
+
+def rmsnorm_gateup_swiglu(x, gamma, eps, codes_gu, scales_gu, biases_gu, h=None):
+    """h[M,I] (bf16) = silu(xn.Wg^T) * (xn.Wu^T), xn = RMSNorm(x; gamma, eps)."""
+    M, K = _dims2(x, "x")
+    I = codes_gu.shape[0] // 2
+    if h is None:
+        h = torch.empty((M, I), dtype=torch.bfloat16, device=x.device)
+    for t, n, e in ((x, "x", 2), (gamma, "gamma", 2), (codes_gu, "codes_gu", 4), (scales_gu, "scales_gu", 2),
+                    (biases_gu, "biases_gu", 2), (h, "h", 2)):
+        _need(t, n, e, x.device)
+    with torch.cuda.device(x.device):
+        _raise_on(lib().rmsnorm_gateup_swiglu(_ptr(x), _ptr(gamma), float(eps), _ptr(codes_gu), _ptr(scales_gu),
+                                              _ptr(biases_gu), _ptr(h), M, I, K, _stream()),
+                  "rmsnorm_gateup_swiglu")
+    return h
+
+
+def moe_expert_qgemv(x, router_logits, top_k, w_gu, w_down, y=None, out_ids=None, out_w=None):
+    """One token through the top-k routed Q4_K SwiGLU experts.  Returns (y, ids, w)."""
+    D = x.numel()
+    E = router_logits.numel()
+    I = w_down.numel() // (E * D * 144) * 256
+    if y is None:
+        y = torch.empty((1, D), dtype=torch.bfloat16, device=x.device)
+    if out_ids is None:
+        out_ids = torch.empty(top_k, dtype=torch.int32, device=x.device)
+    if out_w is None:
+        out_w = torch.empty(top_k, dtype=torch.float32, device=x.device)
+    for t, n, e in ((x, "x", 2), (router_logits, "router_logits", 4), (w_gu, "w_gu", 1), (w_down, "w_down", 1),
+                    (y, "y", 2), (out_ids, "out_ids", 4), (out_w, "out_w", 4)):
+        _need(t, n, e, x.device)
+    with torch.cuda.device(x.device):
+        _raise_on(lib().moe_expert_qgemv(_ptr(x), _ptr(router_logits), int(top_k), _ptr(w_gu), _ptr(w_down), _ptr(y),
+                                         _ptr(out_ids), _ptr(out_w), E, D, I, _stream()), "moe_expert_qgemv")
+    return y, out_ids, out_w
+
+
+def lmhead_argmax(x, codes, scales, biases, draft=None, logits=None, want_logits=False, ids=None, accepted=None):
+    """Greedy readout.  Returns (ids int32 [M], accepted int32 [1], logits fp32 [M,V] or None)."""
+    M, K = _dims2(x, "x")
+    V = codes.shape[0]
+    if logits is None and want_logits:
+        logits = torch.empty((M, V), dtype=torch.float32, device=x.device)
+    if ids is None:
+        ids = torch.empty(M, dtype=torch.int32, device=x.device)
+    if accepted is None:
+        accepted = torch.empty(1, dtype=torch.int32, device=x.device)
+    for t, n, e in ((x, "x", 2), (codes, "codes", 4), (scales, "scales", 2), (biases, "biases", 2),
+                    (logits, "logits", 4), (ids, "ids", 4), (draft, "draft", 4), (accepted, "accepted", 4)):
+        _need(t, n, e, x.device)
+    if draft is not None and draft.numel() < M:
+        raise ValueError("draft must hold at least M ids")
+    with torch.cuda.device(x.device):
+        _raise_on(lib().lmhead_argmax(_ptr(x), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(logits), _ptr(ids),
+                                      _ptr(draft), _ptr(accepted), M, V, K, _stream()), "lmhead_argmax")
+    return ids, accepted, logits
+
+
+# ------------------------------------------------------------- host checks --
+# The qg_check_* twins run the entry points' argument checks on the host only
+# (no GPU, no launch); they take raw addresses so tests can probe the rules.
+
+def check(name: str, *args) -> int:
+    """Call qg_check_<name>(*args) with integer addresses; returns the status."""
+    fn = getattr(lib(), "qg_check_" + name)
+    conv = []
+    for a, ty in zip(args, fn.argtypes):
+        conv.append(_P(a) if ty is _P else a)
+    return int(fn(*conv))
+
+
+def last_error() -> str:
+    return lib().qg_last_error().decode()

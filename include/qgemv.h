@@ -1,0 +1,182 @@
+/*
+ * qgemv.h -- C ABI of libqgemv.so: 4-bit quantized decode projections on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the weight projection of one LLM decode step,
+ *     Y[M][N] = X[M][K] . dequant(W)[N][K]^T,
+ * with M = 1 for a plain decode step and M <= 8 for a speculative verify block
+ * that scores the current token and up to seven drafted tokens in one read of
+ * the weights (Husky page "Husky - MLX보다 최대 4.5배 빠른 추론 엔진", sections
+ * "일반 글쓰기의 한계와 편집 가속 원리" (an 8-token block verified per step) and
+ * "8행 투영 커널 개선..." (the 8-row projection kernel)).
+ *
+ * Weight formats
+ *   affine4  MLX-style 4-bit weights with one bf16 scale and one bf16 bias per
+ *            group of 64 consecutive weights along K (uzu deep-dive page,
+ *            section "내부 동작 1", weight_matrix row: MLX 4/8-bit; TensorFold
+ *            deep-dive page, box-measurement table: "4-bit group 64").
+ *            codes  : uint32 [N][K/8]; code of weight k of row n is bits
+ *                     4*(k%8) .. 4*(k%8)+3 of word k/8 (low nibble first).
+ *            scales : bf16 [N][K/64];  biases : bf16 [N][K/64].
+ *            w[n][k] = scale[n][k/64] * code + bias[n][k/64].
+ *   q4k      GGUF Q4_K superblocks, consumed as stored (runNburn page, section
+ *            "GGUF를 그대로 진실의 원본으로 둡니다").  blocks: uint8 [N][K/256][144]:
+ *            fp16 d, fp16 dmin, 12 bytes of eight 6-bit scales sc_j and eight
+ *            6-bit mins m_j, then 128 bytes of codes; weight o of a block is in
+ *            sub-block j = o/32 and equals d*sc_j*q - dmin*m_j.  The byte layout
+ *            is the public GGUF one (the pages only name the format).
+ *
+ * Common conventions
+ *   * bf16 and fp16 values are passed as uint16_t bit patterns.
+ *   * Every pointer is caller-owned device memory (hipMalloc / torch CUDA
+ *     tensors).  X, codes and Q4_K blocks must be 16-byte aligned; float and
+ *     int32 buffers 4-byte aligned; other bf16 buffers 2-byte aligned.
+ *   * `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work and return; results are ready when the stream is synchronised.
+ *   * Every argument is checked before anything is launched; a call that fails
+ *     its checks writes nothing (the refuse-before-touching-weights and
+ *     explicit-error conventions of the TensorFold and runNburn pages).
+ *     Outputs may not overlap any input or each other (QG_EALIAS).
+ *   * The library keeps one scratch workspace per (device, stream), allocated
+ *     on first use and zero-initialised (split-K partials, tile counters and
+ *     argmax keys; counters are restored to zero by the kernels).  Two calls
+ *     on the same stream are ordered by the stream; calls on different streams
+ *     use different workspaces.  A call that must grow the workspace
+ *     synchronises that stream once.
+ *   * Floating point: fp32 accumulation; bf16 outputs rounded to nearest even.
+ *     Results are deterministic: the same inputs give the same bytes on every
+ *     call (fixed reduction order, no floating-point atomics).
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t qg_status;
+#define QG_OK 0
+#define QG_EINVAL (-1)        /* bad shape, null pointer or misalignment        */
+#define QG_EALIAS (-2)        /* an output overlaps an input or another output  */
+#define QG_EUNSUPPORTED (-3)  /* valid request with no kernel instance          */
+#define QG_EHIP (-4)          /* HIP runtime or launch error                    */
+#define QG_ENOMEM (-5)        /* workspace allocation failed                    */
+
+/* Static description of a status code. */
+const char* qg_status_string(qg_status status);
+/* Detail of the most recent failure on the calling thread ("" if none). */
+const char* qg_last_error(void);
+
+/*
+ * qgemv_affine4 -- Y = X . dequant(W)^T for affine4 weights.
+ *   x      bf16 [M][K]           activations
+ *   codes  uint32 [N][K/8]; scales, biases bf16 [N][K/64]
+ *   y      bf16 [M][N]           output
+ *   1 <= M <= 8; N >= 0 (N = 0 does nothing); K > 0, K % 64 == 0.
+ */
+qg_status qgemv_affine4(const uint16_t* x, const uint32_t* codes,
+                        const uint16_t* scales, const uint16_t* biases,
+                        uint16_t* y, int M, int N, int K, void* stream);
+
+/*
+ * qgemv_q4k -- Y = X . dequant(W)^T for Q4_K weights.
+ *   x bf16 [M][K]; blocks uint8 [N][K/256][144]; y bf16 [M][N].
+ *   1 <= M <= 8; N >= 0; K > 0, K % 256 == 0.
+ */
+qg_status qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y,
+                    int M, int N, int K, void* stream);
+
+/*
+ * rmsnorm_gateup_swiglu -- the front half of a dense SwiGLU MLP with the norm
+ * fused into the projection and gate and up computed together (Husky page,
+ * section "MSI의 네 가지 구현 요소"):
+ *   xn[m][k] = x[m][k] * gamma[k] / sqrt(mean_k x[m][k]^2 + eps)
+ *   g = xn . Wg^T, u = xn . Wu^T, h[m][i] = silu(g[m][i]) * u[m][i]
+ *   x bf16 [M][K]; gamma bf16 [K]; eps > 0 (finite)
+ *   codes_gu uint32 [2I][K/8], scales_gu / biases_gu bf16 [2I][K/64]:
+ *     rows 0..I-1 are the gate projection, rows I..2I-1 the up projection.
+ *   h bf16 [M][I].   1 <= M <= 8; I >= 0; K % 64 == 0.  All of x is staged
+ *   on chip: ceil(K/128) * (264*M + 64) + 288 <= 65536 bytes (M = 8: K <= 3712;
+ *   M = 1: K <= 25344), else QG_EUNSUPPORTED.
+ */
+qg_status rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma,
+                                float eps, const uint32_t* codes_gu,
+                                const uint16_t* scales_gu,
+                                const uint16_t* biases_gu, uint16_t* h, int M,
+                                int I, int K, void* stream);
+
+/*
+ * moe_expert_qgemv -- one decode token through a routed-expert SwiGLU MLP
+ * stored in Q4_K (uzu page: MixtureOfExperts with a routing function; runNburn
+ * page: routing and quantisation semantics are never altered):
+ *   S = the top_k largest router logits (ties -> lower expert index),
+ *   p_e = softmax over the selected logits only,
+ *   y = sum_{e in S} p_e * Down_e . swiglu(GU_e . x), summed in ascending e.
+ *   x bf16 [D]; router_logits fp32 [E];
+ *   w_gu   uint8 [E][2I][D/256][144]  (rows 0..I-1 gate, I..2I-1 up)
+ *   w_down uint8 [E][D][I/256][144]
+ *   y bf16 [D]; out_ids int32 [top_k] (nullable; selected experts, largest
+ *   logit first); out_w fp32 [top_k] (nullable; their weights, same order).
+ *   1 <= top_k <= E <= 1024, top_k <= 64; D, I > 0 and multiples of 256.
+ *   NaN router logits are not supported.
+ */
+qg_status moe_expert_qgemv(const uint16_t* x, const float* router_logits,
+                           int top_k, const uint8_t* w_gu,
+                           const uint8_t* w_down, uint16_t* y,
+                           int32_t* out_ids, float* out_w, int E, int D, int I,
+                           void* stream);
+
+/*
+ * lmhead_argmax -- untied LM-head readout with greedy verify (uzu page,
+ * linear row: untied_readout; DFlash + Weaver section: the target scores the
+ * proposal and keeps the longest accepted path; Husky page: the next token is
+ * handed over on the GPU):
+ *   logits[m][v] = x[m] . dequant(W)[v]      (fp32; stored only if non-null)
+ *   ids[m]       = lowest v with the largest logit (a NaN logit counts as the
+ *                  largest; the first NaN wins)
+ *   accepted     = number of leading rows m with ids[m] == draft[m]
+ *                  (written only if non-null; 0 if draft is null)
+ *   x bf16 [M][K]; codes uint32 [V][K/8]; scales, biases bf16 [V][K/64];
+ *   logits fp32 [M][V] (nullable); ids int32 [M]; draft int32 [M] (nullable);
+ *   accepted int32 [1] (nullable).   1 <= M <= 8; V >= 1; K % 64 == 0, and
+ *   the same on-chip staging limit on M and K as rmsnorm_gateup_swiglu.
+ */
+qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes,
+                        const uint16_t* scales, const uint16_t* biases,
+                        float* logits, int32_t* ids, const int32_t* draft,
+                        int32_t* accepted, int M, int V, int K, void* stream);
+
+/*
+ * Host-only twins of the entry points above: the same argument checks, no
+ * GPU access, no launch.  They return what the entry point would return
+ * before launching anything.
+ */
+qg_status qg_check_qgemv_affine4(const uint16_t* x, const uint32_t* codes,
+                                 const uint16_t* scales, const uint16_t* biases,
+                                 uint16_t* y, int M, int N, int K);
+qg_status qg_check_qgemv_q4k(const uint16_t* x, const uint8_t* blocks,
+                             uint16_t* y, int M, int N, int K);
+qg_status qg_check_rmsnorm_gateup_swiglu(const uint16_t* x,
+                                         const uint16_t* gamma, float eps,
+                                         const uint32_t* codes_gu,
+                                         const uint16_t* scales_gu,
+                                         const uint16_t* biases_gu, uint16_t* h,
+                                         int M, int I, int K);
+qg_status qg_check_moe_expert_qgemv(const uint16_t* x,
+                                    const float* router_logits, int top_k,
+                                    const uint8_t* w_gu, const uint8_t* w_down,
+                                    uint16_t* y, int32_t* out_ids, float* out_w,
+                                    int E, int D, int I);
+qg_status qg_check_lmhead_argmax(const uint16_t* x, const uint32_t* codes,
+                                 const uint16_t* scales, const uint16_t* biases,
+                                 float* logits, int32_t* ids,
+                                 const int32_t* draft, int32_t* accepted, int M,
+                                 int V, int K);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QGEMV_H */

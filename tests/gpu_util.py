@@ -1,0 +1,81 @@
+"""Helpers for the GPU parity tests: host<->device copies of bit-pattern
+arrays and the comparison rules.
+
+Pass bar (the same for every floating-point output):
+  * |y_gpu - y_oracle| <= 2e-2 * rms(y_oracle) + 2^-8 * |y_oracle| for every
+    output, rms over all outputs of the call: the stated tolerance for bf16
+    outputs with fp32 accumulation, with the output's own bf16 rounding (at most
+    half an ulp, 2^-8 |y|) not counted against it -- for heavy-tailed outputs
+    (max/rms above 5, e.g. silu(g)*u) that one rounding alone exceeds 2e-2*rms;
+  * and, as a tighter check, |err| <= 2^-8 * |y_oracle| + slack * rms: one bf16
+    rounding of the output plus fp32 accumulation.  slack is 1e-3 for a
+    projection; the MLP block's bf16 intermediate h (part of its definition
+    here) gets 8e-3, the MoE's bf16 expert activations likewise.
+Argmax ids: equal to the oracle's wherever the oracle's top-2 gap is > 1e-2;
+elsewhere the chosen id's oracle logit is within 1e-2 of the maximum.
+"""
+import math
+
+import numpy as np
+import torch
+
+
+def dev_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def dev_u32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint32).view(np.int32)).cuda()
+
+
+def dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def host_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bits_to_f64(b):
+    return (np.asarray(b, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def host_bf16_f64(t):
+    return bits_to_f64(host_bits(t))
+
+
+def assert_close(y_gpu_f64, ref, slack=1e-3, what=""):
+    y = np.asarray(y_gpu_f64, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert y.shape == ref.shape, (what, y.shape, ref.shape)
+    if ref.size == 0:
+        return 0.0
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    err = np.abs(y - ref)
+    mx = float(err.max())
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    over = err - (2.0 ** -8) * np.abs(ref)
+    assert float(over.max()) <= 2e-2 * rms, (f"{what}: max(|err| - 2^-8|y|) {float(over.max()):.4g} > 2e-2*rms "
+                                            f"({rms:.4g}); max|err| {mx:.4g}")
+    bad = err > (2.0 ** -8) * np.abs(ref) + slack * rms
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements outside 2^-8|y|+{slack}*rms; worst at "
+                           f"{np.unravel_index(int(np.argmax(err - (2.0 ** -8) * np.abs(ref))), ref.shape)}")
+    return mx / rms if rms > 0 else 0.0
+
+
+def assert_ids(ids_gpu, ids_ref, gap_ref, logits_ref, what=""):
+    ids_gpu = np.asarray(ids_gpu).reshape(-1)
+    for m in range(len(ids_ref)):
+        if gap_ref[m] > 1e-2:
+            assert ids_gpu[m] == ids_ref[m], f"{what}: row {m} id {ids_gpu[m]} != {ids_ref[m]} (gap {gap_ref[m]:.3g})"
+        else:
+            mx = logits_ref[m].max()
+            assert logits_ref[m, ids_gpu[m]] >= mx - 1e-2, f"{what}: row {m} id {ids_gpu[m]} not within 1e-2 of max"

@@ -1,0 +1,164 @@
+"""Host-side tests of libqgemv.so (no GPU needed): it loads, it exports every
+function include/qgemv.h declares, and every entry point checks its arguments
+before touching the GPU (the host-only qg_check_* twins and the entry points
+themselves return the same status for rejected arguments)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from bit_quantized_decode_group_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        from bit_quantized_decode_group_amd import build
+        build.build()
+    return ops.lib()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "qgemv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:qg_status|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for n in ["qgemv_affine4", "qgemv_q4k", "rmsnorm_gateup_swiglu", "moe_expert_qgemv", "lmhead_argmax",
+              "qg_status_string", "qg_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = {l.split()[-1] for l in out.stdout.splitlines() if " T " in l}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.qg_status_string(st).decode()
+    assert lib.qg_status_string(42).decode() == "unknown status"
+
+
+# Distinct, 16-byte aligned fake device addresses far apart from each other.
+A = [0x10_0000_0000 * (i + 1) for i in range(12)]
+
+
+def affine_args(M=2, N=32, K=128):
+    return [A[0], A[1], A[2], A[3], A[4], M, N, K]
+
+
+def test_qgemv_affine4_checks(lib):
+    c = lambda *a: ops.check("qgemv_affine4", *a)
+    assert c(*affine_args()) == ops.QG_OK
+    for M in (0, 9, -1):
+        assert c(*affine_args(M=M)) == ops.QG_EINVAL
+    for K in (0, 63, 100, -64):
+        assert c(*affine_args(K=K)) == ops.QG_EINVAL
+    assert c(*affine_args(N=-1)) == ops.QG_EINVAL
+    assert c(*affine_args(N=0)) == ops.QG_OK
+    args = affine_args()
+    args[0] = 0
+    assert c(*args) == ops.QG_EINVAL and "x is null" in ops.last_error()
+    args = affine_args()
+    args[1] = A[1] + 4  # codes must be 16-byte aligned
+    assert c(*args) == ops.QG_EINVAL and "aligned" in ops.last_error()
+    for i in range(4):  # y overlapping each input
+        args = affine_args()
+        args[4] = args[i]
+        assert c(*args) == ops.QG_EALIAS, i
+    # y right after x is fine; one byte into x is not
+    args = affine_args(M=2, N=32, K=128)
+    args[4] = A[0] + 2 * 128 * 2
+    assert c(*args) == ops.QG_OK
+    args[4] = A[0] + 2 * 128 * 2 - 2
+    assert c(*args) == ops.QG_EALIAS
+
+
+def test_entry_points_refuse_before_launch(lib):
+    """The real entry points return the check status without any GPU work."""
+    P = ops._P
+    assert lib.qgemv_affine4(P(A[0]), P(A[1]), P(A[2]), P(A[3]), P(A[4]), 9, 16, 64, None) == ops.QG_EINVAL
+    assert lib.qgemv_q4k(P(A[0]), P(A[1]), P(A[2]), 1, 16, 100, None) == ops.QG_EINVAL
+    assert lib.rmsnorm_gateup_swiglu(P(A[0]), P(A[1]), 0.0, P(A[2]), P(A[3]), P(A[4]), P(A[5]), 1, 16, 64,
+                                     None) == ops.QG_EINVAL
+    assert lib.moe_expert_qgemv(P(A[0]), P(A[1]), 9, P(A[2]), P(A[3]), P(A[4]), None, None, 8, 256, 256,
+                                None) == ops.QG_EINVAL
+    assert lib.lmhead_argmax(P(A[0]), P(A[1]), P(A[2]), P(A[3]), None, P(A[4]), None, None, 1, 0, 64,
+                             None) == ops.QG_EINVAL
+    assert lib.qgemv_affine4(P(A[0]), P(A[1]), P(A[2]), P(A[3]), P(A[0]), 1, 16, 64, None) == ops.QG_EALIAS
+
+
+def test_qgemv_q4k_checks(lib):
+    c = lambda *a: ops.check("qgemv_q4k", *a)
+    assert c(A[0], A[1], A[2], 8, 17, 768) == ops.QG_OK
+    assert c(A[0], A[1], A[2], 8, 17, 64) == ops.QG_EINVAL  # K must be a multiple of 256
+    assert c(A[0], A[1] + 8, A[2], 1, 17, 256) == ops.QG_EINVAL
+    assert c(A[0], A[1], A[1], 1, 17, 256) == ops.QG_EALIAS
+
+
+def test_gateup_checks(lib):
+    c = lambda *a: ops.check("rmsnorm_gateup_swiglu", *a)
+    ok = [A[0], A[1], 1e-6, A[2], A[3], A[4], A[5], 8, 64, 1024]
+    assert c(*ok) == ops.QG_OK
+    for eps in (0.0, -1.0, float("nan"), float("inf")):
+        bad = list(ok)
+        bad[2] = eps
+        assert c(*bad) == ops.QG_EINVAL
+    big = list(ok)
+    big[9] = 8192  # M*K above the staged-activation limit
+    assert c(*big) == ops.QG_EUNSUPPORTED
+    big[7] = 1  # one row of K = 8192 fits
+    assert c(*big) == ops.QG_OK
+    alias = list(ok)
+    alias[6] = A[1]  # h over gamma
+    assert c(*alias) == ops.QG_EALIAS
+
+
+def test_moe_checks(lib):
+    c = lambda *a: ops.check("moe_expert_qgemv", *a)
+    ok = [A[0], A[1], 8, A[2], A[3], A[4], A[5], A[6], 128, 2048, 768]
+    assert c(*ok) == ops.QG_OK
+    for idx, val, st in [(2, 0, ops.QG_EINVAL), (2, 129, ops.QG_EINVAL), (8, 2000, ops.QG_EINVAL),
+                         (9, 2000, ops.QG_EINVAL), (10, 700, ops.QG_EINVAL), (2, 65, ops.QG_EUNSUPPORTED)]:
+        bad = list(ok)
+        bad[idx] = val
+        assert c(*bad) == st, (idx, val)
+    opt = list(ok)
+    opt[6] = 0
+    opt[7] = 0  # out_ids / out_w are optional
+    assert c(*opt) == ops.QG_OK
+    alias = list(ok)
+    alias[6] = A[4]  # out_ids inside y
+    assert c(*alias) == ops.QG_EALIAS
+
+
+def test_lmhead_checks(lib):
+    c = lambda *a: ops.check("lmhead_argmax", *a)
+    ok = [A[0], A[1], A[2], A[3], A[4], A[5], A[6], A[7], 8, 151936, 1024]
+    assert c(*ok) == ops.QG_OK
+    opt = list(ok)
+    opt[4] = 0
+    opt[6] = 0
+    opt[7] = 0
+    assert c(*opt) == ops.QG_OK
+    bad = list(ok)
+    bad[9] = 0
+    assert c(*bad) == ops.QG_EINVAL
+    bad = list(ok)
+    bad[5] = 0  # ids required
+    assert c(*bad) == ops.QG_EINVAL
+    bad = list(ok)
+    bad[7] = A[5]  # accepted over ids
+    assert c(*bad) == ops.QG_EALIAS
+    bad = list(ok)
+    bad[10] = 8192
+    assert c(*bad) == ops.QG_EUNSUPPORTED

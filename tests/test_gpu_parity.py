@@ -1,0 +1,340 @@
+"""GPU parity: every entry point of libqgemv.so, called through the C ABI
+(via the thin binding), against the CPU oracle on the same seeded inputs.
+
+Small shapes span several 16-row tiles, ragged row tails, odd group counts
+and the split-K path; the full-size workloads are the five decode
+configurations, compared on every output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_quantized_decode_group_amd import ops, synth
+from tests import packers
+from tests.gpu_util import (assert_close, assert_ids, bits_to_f64, dev_bf16, dev_f32, dev_i32, dev_u8, dev_u32,
+                            host_bf16_f64, host_bits)
+from tests.test_oracle_pins import HAND_BIASES, HAND_CODES, HAND_SCALES, HAND_VALUES, Q4K_HAND, Q4K_HAND_VALUES
+
+pytestmark = pytest.mark.gpu
+
+
+def _affine_dev(d):
+    return dev_u32(d["codes"]), dev_bf16(d["scales"]), dev_bf16(d["biases"])
+
+
+# ------------------------------------------------------------ qgemv_affine4 --
+
+@pytest.mark.parametrize("K", [64, 192, 1024, 12800])
+@pytest.mark.parametrize("N", [1, 16, 17, 40])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_qgemv_affine4_small(M, N, K):
+    d = synth.single_projection(M=M, N=N, K=K, seed=3000 + 97 * M + 7 * N + K)
+    ref = oracle.qgemv_affine4(d["x"], d["codes"], d["scales"], d["biases"])
+    y = ops.qgemv_affine4(dev_bf16(d["x"]), *_affine_dev(d))
+    torch.cuda.synchronize()
+    assert_close(host_bf16_f64(y), ref, what=f"affine4 M{M} N{N} K{K}")
+
+
+def test_qgemv_affine4_hand_packed_exact():
+    ks = [0, 7, 8, 63, 64, 100, 127, 1]
+    x = np.zeros((8, 128), dtype=np.uint16)
+    for m, k in enumerate(ks):
+        x[m, k] = 0x3F80
+    y = host_bits(ops.qgemv_affine4(dev_bf16(x), dev_u32(HAND_CODES), dev_bf16(HAND_SCALES), dev_bf16(HAND_BIASES)))
+    for m, k in enumerate(ks):
+        for n in range(2):
+            if (n, k) in HAND_VALUES:
+                assert y[m, n] == oracle.f64_to_bf16_rne(HAND_VALUES[(n, k)]), (m, n, k)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 33, 1024), (8, 50, 1024), (5, 17, 448), (8, 3, 4096)])
+def test_qgemv_affine4_exact_integers(M, N, K):
+    """Integer activations, scales, biases: every fp32 partial sum is exact, so the
+    bf16 output must equal the exact sum rounded once."""
+    g = np.random.default_rng(40 + M + N)
+    q = g.integers(0, 16, (N, K))
+    s = g.choice([0.5, 1.0, 2.0], size=(N, K // 64))
+    b = g.integers(-4, 5, (N, K // 64)).astype(np.float64)
+    x = g.integers(-8, 9, (M, K)).astype(np.float64)
+    xb = synth.to_bf16_bits(x)
+    sb = synth.to_bf16_bits(s)
+    bb = synth.to_bf16_bits(b)
+    codes = packers.pack_affine4_codes(q)
+    exact = x @ (s.repeat(64, axis=1) * q + b.repeat(64, axis=1)).T
+    y = host_bits(ops.qgemv_affine4(dev_bf16(xb), dev_u32(codes), dev_bf16(sb), dev_bf16(bb)))
+    want = np.array([oracle.f64_to_bf16_rne(v) for v in exact.reshape(-1)], np.uint16).reshape(exact.shape)
+    assert np.array_equal(y, want)
+    assert np.array_equal(want, np.array([oracle.f64_to_bf16_rne(v) for v in
+                                          oracle.qgemv_affine4(xb, codes, sb, bb).reshape(-1)],
+                                         np.uint16).reshape(exact.shape))
+
+
+def test_qgemv_affine4_empty_and_guard_bytes():
+    d = synth.single_projection(M=3, N=37, K=320, seed=51)
+    codes, scales, biases = _affine_dev(d)
+    x = dev_bf16(d["x"])
+    # N = 0: a no-op
+    y0 = torch.full((3, 0), 0, dtype=torch.bfloat16, device="cuda")
+    ops.qgemv_affine4(x, codes[:0], scales[:0], biases[:0], y=y0)
+    # guard bytes around the output stay intact
+    buf = torch.full((3 * 37 + 64,), -7.0, dtype=torch.bfloat16, device="cuda")
+    y = buf[32:32 + 3 * 37].view(3, 37)
+    ops.qgemv_affine4(x, codes, scales, biases, y=y)
+    torch.cuda.synchronize()
+    b = buf.float().cpu().numpy()
+    assert np.all(b[:32] == -7.0) and np.all(b[32 + 3 * 37:] == -7.0)
+    ref = oracle.qgemv_affine4(d["x"], d["codes"], d["scales"], d["biases"])
+    assert_close(host_bf16_f64(y), ref, what="guarded")
+
+
+def test_qgemv_affine4_rejects_alias_and_bad_shapes():
+    d = synth.single_projection(M=2, N=16, K=128, seed=52)
+    codes, scales, biases = _affine_dev(d)
+    x = dev_bf16(d["x"])
+    with pytest.raises(ops.QgError) as e:
+        ops.qgemv_affine4(x, codes, scales, biases, y=x.view(-1)[:32].view(2, 16))
+    assert e.value.status == ops.QG_EALIAS
+    x9 = torch.zeros((9, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ops.QgError) as e:
+        ops.qgemv_affine4(x9, codes, scales, biases)
+    assert e.value.status == ops.QG_EINVAL
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 2560, 12800), (1, 40, 1024), (8, 7000, 1024)])
+def test_qgemv_affine4_deterministic(M, N, K):
+    d = synth.single_projection(M=M, N=N, K=K, seed=53)
+    args = (dev_bf16(d["x"]), *_affine_dev(d))
+    outs = [host_bits(ops.qgemv_affine4(*args)) for _ in range(5)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+# --------------------------------------------------------------- qgemv_q4k --
+
+@pytest.mark.parametrize("K", [256, 768, 2048, 5120])
+@pytest.mark.parametrize("N", [1, 16, 17, 50])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_qgemv_q4k_small(M, N, K):
+    g = synth.rng(4000 + 31 * M + N + K)
+    x = synth.normal_bf16(g, (M, K))
+    blocks = synth.q4k_matrix(g, N, K)
+    ref = oracle.qgemv_q4k(x, blocks)
+    y = ops.qgemv_q4k(dev_bf16(x), dev_u8(blocks))
+    assert_close(host_bf16_f64(y), ref, what=f"q4k M{M} N{N} K{K}")
+
+
+def test_qgemv_q4k_hand_packed_exact():
+    ks = [0, 32, 100, 130, 170, 200, 240, 255]
+    x = np.zeros((8, 256), dtype=np.uint16)
+    for m, k in enumerate(ks):
+        x[m, k] = 0x3F80
+    y = host_bits(ops.qgemv_q4k(dev_bf16(x), dev_u8(np.tile(Q4K_HAND, (3, 1)).reshape(3, 1, 144))))
+    for m, k in enumerate(ks):
+        for n in range(3):
+            assert y[m, n] == oracle.f64_to_bf16_rne(Q4K_HAND_VALUES[k]), (m, k)
+
+
+def test_qgemv_q4k_exact_integers():
+    g = np.random.default_rng(61)
+    N, nb, M = 21, 4, 6
+    sc = g.integers(0, 64, (N, nb, 8))
+    mn = g.integers(0, 64, (N, nb, 8))
+    q = g.integers(0, 16, (N, nb, 256))
+    blocks = packers.q4k_block(np.full((N, nb), 0x3C00, np.uint16), np.full((N, nb), 0x3C00, np.uint16), sc, mn, q)
+    x = g.integers(-4, 5, (M, nb * 256)).astype(np.float64)
+    w = (sc.repeat(32, axis=2) * q - mn.repeat(32, axis=2)).reshape(N, nb * 256)
+    exact = x @ w.T
+    y = host_bits(ops.qgemv_q4k(dev_bf16(synth.to_bf16_bits(x)), dev_u8(blocks)))
+    want = np.array([oracle.f64_to_bf16_rne(v) for v in exact.reshape(-1)], np.uint16).reshape(exact.shape)
+    assert np.array_equal(y, want)
+
+
+# ---------------------------------------------------- rmsnorm_gateup_swiglu --
+
+@pytest.mark.parametrize("K", [64, 192, 1024, 3648])
+@pytest.mark.parametrize("I", [16, 33, 100])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_gateup_small(M, I, K):
+    g = synth.rng(5000 + 11 * M + I + K)
+    gu = synth.affine4_matrix(g, 2 * I, K)
+    d = {"x": synth.normal_bf16(g, (M, K)), "gamma": synth.uniform_bf16(g, 0.8, 1.2, (K,)), "eps": 1e-6,
+         "codes_gu": gu["codes"], "scales_gu": gu["scales"], "biases_gu": gu["biases"]}
+    ref = oracle.rmsnorm_gateup_swiglu(d["x"], d["gamma"], d["eps"], d["codes_gu"], d["scales_gu"], d["biases_gu"])
+    h = ops.rmsnorm_gateup_swiglu(dev_bf16(d["x"]), dev_bf16(d["gamma"]), d["eps"], dev_u32(d["codes_gu"]),
+                                  dev_bf16(d["scales_gu"]), dev_bf16(d["biases_gu"]))
+    assert_close(host_bf16_f64(h), ref, slack=5e-3, what=f"gateup M{M} I{I} K{K}")
+
+
+def test_gateup_unit_gamma_matches_plain_projection():
+    """gamma = 1 and a large eps-free row: the norm is a per-row scale, so
+    g and u equal the plain projection of x scaled by 1/rms(x)."""
+    g0 = synth.rng(71)
+    gu0 = synth.affine4_matrix(g0, 96, 256)
+    d = {"x": synth.normal_bf16(g0, (2, 256)), "codes_gu": gu0["codes"], "scales_gu": gu0["scales"],
+         "biases_gu": gu0["biases"]}
+    gamma = np.full(256, 0x3F80, np.uint16)
+    h = host_bf16_f64(ops.rmsnorm_gateup_swiglu(dev_bf16(d["x"]), dev_bf16(gamma), 1e-6, dev_u32(d["codes_gu"]),
+                                                dev_bf16(d["scales_gu"]), dev_bf16(d["biases_gu"])))
+    gu = oracle.qgemv_affine4(d["x"], d["codes_gu"], d["scales_gu"], d["biases_gu"])
+    x = bits_to_f64(d["x"])
+    r = 1.0 / np.sqrt((x ** 2).mean(axis=1, keepdims=True) + 1e-6)
+    g, u = gu[:, :48] * r, gu[:, 48:] * r
+    assert_close(h, g / (1 + np.exp(-g)) * u, slack=1e-3, what="unit gamma")
+
+
+# ---------------------------------------------------------- lmhead_argmax --
+
+@pytest.mark.parametrize("K", [64, 1024])
+@pytest.mark.parametrize("V", [1, 17, 1000, 5000])
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_lmhead_small(M, V, K):
+    d = synth.lm_head(M=M, V=V, K=K, seed=6000 + M + V + K)
+    logits, ids, gap, _ = oracle.lmhead(d["x"], d["codes"], d["scales"], d["biases"])
+    gi, acc, gl = ops.lmhead_argmax(dev_bf16(d["x"]), *_affine_dev(d), want_logits=True)
+    gl = gl.cpu().numpy().astype(np.float64)
+    assert_close(gl, logits, slack=1e-4, what=f"logits M{M} V{V} K{K}")
+    assert_ids(gi.cpu().numpy(), ids, gap, logits, what=f"lmhead M{M} V{V} K{K}")
+    assert int(acc.cpu()[0]) == 0  # no draft given
+
+
+def _bias_rows(V, K, bias_bits):
+    codes = np.zeros((V, K // 8), np.uint32)
+    scales = np.full((V, K // 64), 0x3F80, np.uint16)
+    biases = np.repeat(np.asarray(bias_bits, np.uint16).reshape(V, 1), K // 64, axis=1)
+    return dev_u32(codes), dev_bf16(scales), dev_bf16(biases)
+
+
+def test_lmhead_ties_nan_and_planted():
+    V, K = 3000, 128
+    x = dev_bf16(np.full((2, K), 0x3F80, np.uint16))
+    bias = np.full(V, 0x3F00, np.uint16)
+    bias[2222] = 0x3F80
+    ids, _, _ = ops.lmhead_argmax(x, *_bias_rows(V, K, bias))
+    assert list(ids.cpu().numpy()) == [2222, 2222]
+    bias[17] = 0x3F80  # equal maximum at a lower index wins
+    ids, _, _ = ops.lmhead_argmax(x, *_bias_rows(V, K, bias))
+    assert list(ids.cpu().numpy()) == [17, 17]
+    bias[2500] = 0x7FC0  # NaN logits: the first NaN wins
+    bias[2900] = 0x7FC0
+    ids, _, _ = ops.lmhead_argmax(x, *_bias_rows(V, K, bias))
+    assert list(ids.cpu().numpy()) == [2500, 2500]
+
+
+def test_lmhead_accepted_prefix_and_repeat_calls():
+    d = synth.lm_head(M=8, V=4000, K=256, seed=81)
+    _, ids_ref, gap, logits = oracle.lmhead(d["x"], d["codes"], d["scales"], d["biases"])
+    assert (gap > 1e-2).all()
+    x, args = dev_bf16(d["x"]), _affine_dev(d)
+    for k in range(9):
+        draft = ids_ref.copy()
+        if k < 8:
+            draft[k] = (draft[k] + 1) % 4000
+        ids, acc, _ = ops.lmhead_argmax(x, *args, draft=dev_i32(draft))
+        assert list(ids.cpu().numpy()) == list(ids_ref)
+        assert int(acc.cpu()[0]) == k
+    ids, acc, _ = ops.lmhead_argmax(x, *args, draft=dev_i32(d["draft"]))
+    lead = 0
+    while lead < 8 and d["draft"][lead] == ids_ref[lead]:
+        lead += 1
+    assert int(acc.cpu()[0]) == lead
+
+
+# -------------------------------------------------------- moe_expert_qgemv --
+
+@pytest.mark.parametrize("E,D,I,top_k", [(8, 256, 256, 1), (8, 256, 512, 8), (16, 512, 256, 2), (32, 768, 512, 8),
+                                         (128, 256, 256, 64)])
+def test_moe_small(E, D, I, top_k):
+    d = synth.moe_token(E=E, D=D, I=I, top_k=top_k, seed=7000 + E + D + I + top_k, n_logit_sets=2)
+    for s in range(2):
+        lg = d["logits"][s]
+        y_ref, ids_ref, p_ref = oracle.moe(d["x"], lg, top_k, d["w_gu"], d["w_down"], E, D, I)
+        y, ids, w = ops.moe_expert_qgemv(dev_bf16(d["x"]), dev_f32(lg), top_k, dev_u8(d["w_gu"]), dev_u8(d["w_down"]))
+        assert list(ids.cpu().numpy()) == list(ids_ref)
+        assert np.allclose(w.cpu().numpy(), p_ref, rtol=1e-5, atol=1e-7)
+        assert_close(host_bf16_f64(y)[0], y_ref, slack=8e-3, what=f"moe E{E} D{D} I{I} k{top_k} set{s}")
+
+
+def test_moe_tie_order():
+    d = synth.moe_token(E=8, D=256, I=256, top_k=3, seed=91)
+    lg = np.array([0.5, 2.0, 2.0, -1.0, 0.0, 2.0, 1.0, 3.0], np.float32)
+    _, ids, _ = ops.moe_expert_qgemv(dev_bf16(d["x"]), dev_f32(lg), 3, dev_u8(d["w_gu"]), dev_u8(d["w_down"]))
+    assert list(ids.cpu().numpy()) == [7, 1, 2]
+
+
+# ------------------------------------------------------- full-size configs --
+
+def test_config_single_projection_m1_and_m8():
+    for M in (1, 8):
+        d = synth.single_projection(M=M)
+        ref = oracle.qgemv_affine4(d["x"], d["codes"], d["scales"], d["biases"])
+        y = ops.qgemv_affine4(dev_bf16(d["x"]), *_affine_dev(d))
+        assert_close(host_bf16_f64(y), ref, what=f"single projection M{M}")
+
+
+def _block(d):
+    x = dev_bf16(d["x"])
+    h = ops.rmsnorm_gateup_swiglu(x, dev_bf16(d["gamma"]), d["eps"], dev_u32(d["codes_gu"]), dev_bf16(d["scales_gu"]),
+                                  dev_bf16(d["biases_gu"]))
+    y = ops.qgemv_affine4(h, dev_u32(d["codes_d"]), dev_bf16(d["scales_d"]), dev_bf16(d["biases_d"]))
+    return h, y
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_config_mlp_block_06b(M):
+    d = synth.mlp_block(M=M)
+    h, y = _block(d)
+    h_ref = oracle.rmsnorm_gateup_swiglu(d["x"], d["gamma"], d["eps"], d["codes_gu"], d["scales_gu"], d["biases_gu"])
+    y_ref = oracle.mlp_block(d["x"], d["gamma"], d["eps"], d["codes_gu"], d["scales_gu"], d["biases_gu"],
+                             d["codes_d"], d["scales_d"], d["biases_d"])
+    assert_close(host_bf16_f64(h), h_ref, slack=5e-3, what="0.6B h")
+    assert_close(host_bf16_f64(y), y_ref, slack=8e-3, what="0.6B block")
+
+
+@pytest.mark.parametrize("M", [8, 1])
+def test_config_verify_block_4b(M):
+    d = synth.verify_block()
+    if M == 1:
+        d = dict(d, x=d["x"][:1].copy())
+    h, y = _block(d)
+    h_ref = oracle.rmsnorm_gateup_swiglu(d["x"], d["gamma"], d["eps"], d["codes_gu"], d["scales_gu"], d["biases_gu"])
+    # the down projection checked on the GPU's own h (a bf16 input), and the block end to end
+    y_ref_h = oracle.qgemv_affine4(host_bits(h), d["codes_d"], d["scales_d"], d["biases_d"])
+    y_ref = oracle.qgemv_affine4_f64x(h_ref, d["codes_d"], d["scales_d"], d["biases_d"])
+    assert_close(host_bf16_f64(h), h_ref, slack=5e-3, what="4B h")
+    assert_close(host_bf16_f64(y), y_ref_h, what="4B down on gpu h")
+    assert_close(host_bf16_f64(y), y_ref, slack=8e-3, what="4B block")
+
+
+def test_config_moe_q4k():
+    d = synth.moe_token(n_logit_sets=3)
+    E, D, I, k = d["E"], d["D"], d["I"], d["top_k"]
+    x, wgu, wdn = dev_bf16(d["x"]), dev_u8(d["w_gu"]), dev_u8(d["w_down"])
+    for s in range(3):
+        y_ref, ids_ref, p_ref = oracle.moe(d["x"], d["logits"][s], k, d["w_gu"], d["w_down"], E, D, I)
+        y, ids, w = ops.moe_expert_qgemv(x, dev_f32(d["logits"][s]), k, wgu, wdn)
+        assert list(ids.cpu().numpy()) == list(ids_ref)
+        assert np.allclose(w.cpu().numpy(), p_ref, rtol=1e-5, atol=1e-7)
+        assert_close(host_bf16_f64(y)[0], y_ref, slack=8e-3, what=f"moe config set {s}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_config_lm_head(M):
+    d = synth.lm_head(M=8)
+    xm = d["x"][:M].copy()
+    logits, ids_ref, gap, _ = oracle.lmhead(xm, d["codes"], d["scales"], d["biases"])
+    x, args = dev_bf16(xm), _affine_dev(d)
+    gi, acc, gl = ops.lmhead_argmax(x, *args, want_logits=True)
+    assert_close(gl.cpu().numpy().astype(np.float64), logits, slack=1e-4, what=f"lm head logits M{M}")
+    assert_ids(gi.cpu().numpy(), ids_ref, gap, logits, what=f"lm head M{M}")
+    # ids-only path (no logits stored) gives the same ids; planted draft prefix
+    k = M // 2
+    draft = ids_ref.copy()
+    if k < M:
+        draft[k] = (draft[k] + 1) % d["V"]
+    gi2, acc2, _ = ops.lmhead_argmax(x, *args, draft=dev_i32(draft))
+    assert np.array_equal(gi2.cpu().numpy(), gi.cpu().numpy())
+    exp_acc = 0
+    while exp_acc < M and gi.cpu().numpy()[exp_acc] == draft[exp_acc]:
+        exp_acc += 1
+    assert int(acc2.cpu()[0]) == exp_acc
