@@ -65,18 +65,18 @@ constexpr size_t kLdsBudget = 65536;       // bytes of LDS one workgroup may use
 constexpr int kWaves = 4;                  // waves per workgroup of the projection kernels
 constexpr int kTargetWaves = 2048;         // enough waves to cover HBM latency on 256 CUs
 constexpr int kMaxWavesInFlight = 4096;    // beyond this, waves stream several tiles
-constexpr size_t kCounterArea = 256 * 1024;  // zeroed area: argmax keys, done counter, tile counters
-constexpr size_t kKeysOff = 0, kDoneOff = 64, kTileCntOff = 1024;
-constexpr int kMaxTileCounters = (int)((kCounterArea - kTileCntOff) / 4);
 
-size_t affine_lds_per_chunk(int M) { return (size_t)256 * M + 64 + (size_t)8 * M; }
-size_t affine_lds_fixed() { return 32 + (size_t)kWaves * 64; }
+// LDS of the affine kernels per 128-k chunk of the staged slice (operand
+// entries for PL activation planes, group sums, GATEUP sums of x^2) and fixed
+// (zero entry, 1/rms values, per-wave argmax keys).
+size_t affine_lds_per_chunk(int M, int PL) { return (size_t)256 * M * PL + 64 + (size_t)8 * M; }
+size_t affine_lds_fixed() { return 16 + 32 + (size_t)kWaves * 64; }
 size_t q4k_lds_per_sb(int M) { return (size_t)512 * M + 256; }
 
-// Modes without split-K stage all of K: ceil(K/128) chunks must fit.
+// The LM-head mode stages all of K (no split): ceil(K/128) chunks must fit.
 bool fits_lds_unsplit(int M, int K) {
   const size_t nchunks = ((size_t)K / 64 + 1) / 2;
-  return nchunks * affine_lds_per_chunk(M) + affine_lds_fixed() <= kLdsBudget;
+  return nchunks * affine_lds_per_chunk(M, 1) + affine_lds_fixed() <= kLdsBudget;
 }
 
 struct Plan {
@@ -109,15 +109,16 @@ struct Workspace {
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-// Returns a zero-initialised-at-creation workspace of at least `need` bytes
-// beyond the counter area, for the current device and this stream.
+// Returns the workspace of the current device and this stream, grown to at
+// least `need` bytes.  Its contents carry nothing between calls (every kernel
+// writes what it later reads), so it needs no initialisation.
 qg_status get_workspace(hipStream_t stream, size_t need, unsigned char** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(QG_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
   std::lock_guard<std::mutex> lk(g_ws_mu);
   Workspace& w = g_ws[{dev, stream}];
-  const size_t total = kCounterArea + need;
+  const size_t total = std::max(need, (size_t)256);
   if (w.bytes < total) {
     if (w.ptr) {
       e = hipStreamSynchronize(stream);
@@ -130,11 +131,6 @@ qg_status get_workspace(hipStream_t stream, size_t need, unsigned char** out) {
     void* p = nullptr;
     e = hipMalloc(&p, nb);
     if (e != hipSuccess) return fail(QG_ENOMEM, "workspace hipMalloc(%zu): %s", nb, hipGetErrorString(e));
-    e = hipMemsetAsync(p, 0, nb, stream);
-    if (e != hipSuccess) {
-      (void)hipFree(p);
-      return fail(QG_EHIP, "workspace hipMemsetAsync: %s", hipGetErrorString(e));
-    }
     w.ptr = p;
     w.bytes = nb;
   }
@@ -214,8 +210,6 @@ qg_status do_check_gateup(const uint16_t* x, const uint16_t* gamma, float eps, c
   qg_status st = check_affine_common(fn, M, I, K);
   if (st) return st;
   if (!(eps > 0.0f) || eps != eps || eps > 3.0e38f) return fail(QG_EINVAL, "%s: eps must be positive and finite", fn);
-  if (!fits_lds_unsplit(M, K))
-    return fail(QG_EUNSUPPORTED, "%s: M=%d rows of K=%d do not fit the staged-activation LDS budget", fn, M, K);
   if ((long long)I * 2 * 16 > 0x7FFFFFFFLL) return fail(QG_EINVAL, "%s: I=%d too large", fn, I);
   const size_t i2 = (size_t)2 * I, k = (size_t)K;
   const Buf in[] = {{x, (size_t)M * k * 2, "x"},
@@ -238,9 +232,9 @@ qg_status do_check_moe(const uint16_t* x, const float* logits, int top_k, const 
   if (top_k > 64) return fail(QG_EUNSUPPORTED, "%s: top_k=%d above 64", fn, top_k);
   if (D <= 0 || D % 256 != 0) return fail(QG_EINVAL, "%s: D=%d must be a positive multiple of 256", fn, D);
   if (I <= 0 || I % 256 != 0) return fail(QG_EINVAL, "%s: I=%d must be a positive multiple of 256", fn, I);
-  if ((size_t)(D / 256) * 768 > kLdsBudget)
+  if (16 + (size_t)(D / 256) * 768 > kLdsBudget)
     return fail(QG_EUNSUPPORTED, "%s: D=%d too large for the staged activation", fn, D);
-  if ((size_t)top_k * (I / 256) * 768 > kLdsBudget)
+  if (16 + (size_t)top_k * (I / 256) * 768 > kLdsBudget)
     return fail(QG_EUNSUPPORTED, "%s: top_k*I/256=%d too large for the staged expert activations", fn,
                 top_k * (I / 256));
   const size_t e = (size_t)E, d = (size_t)D, i = (size_t)I;
@@ -293,9 +287,10 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
   a.nchunks = (G + 1) / 2;
   a.ntiles = (a.N + 15) / 16;
   a.waves = kWaves;
-  const size_t per = affine_lds_per_chunk(a.M);
+  const int PL = (mode == QG_MODE_GATEUP) ? 2 : 1, NB = PL;
+  const size_t per = affine_lds_per_chunk(a.M, PL);
   const int cps_max = (int)std::min<size_t>((size_t)a.nchunks, (kLdsBudget - affine_lds_fixed()) / per);
-  const bool allow_split = (mode == QG_MODE_PLAIN) && a.ntiles <= kMaxTileCounters;
+  const bool allow_split = (mode != QG_MODE_LMHEAD);
   if (!allow_split && a.nchunks > cps_max)
     return fail(QG_EUNSUPPORTED, "%s: K=%d needs a split of K this mode or size lacks", fn, a.K);
   Plan pl = plan_split(a.ntiles, a.nchunks, std::max(cps_max, 1), allow_split);
@@ -304,13 +299,14 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
   a.tpw = pl.tpw;
   a.rgroups = pl.rgroups;
   unsigned char* ws = nullptr;
-  const size_t part_bytes = (a.S > 1) ? (size_t)a.S * a.M * a.N * 4 : 0;
-  qg_status st = get_workspace(stream, part_bytes, &ws);
+  const size_t part_bytes = (a.S > 1) ? (size_t)a.S * NB * a.M * a.N * 4 : 0;
+  const size_t ssq_bytes = (a.S > 1) ? (size_t)a.S * 8 * 4 : 0;
+  const size_t key_bytes = (mode == QG_MODE_LMHEAD) ? (size_t)a.S * a.rgroups * 8 * 8 : 0;
+  qg_status st = get_workspace(stream, part_bytes + ssq_bytes + key_bytes, &ws);
   if (st) return st;
-  a.keys = reinterpret_cast<unsigned long long*>(ws + kKeysOff);
-  a.done_cnt = reinterpret_cast<uint32_t*>(ws + kDoneOff);
-  a.tile_cnt = reinterpret_cast<uint32_t*>(ws + kTileCntOff);
-  a.part = reinterpret_cast<float*>(ws + kCounterArea);
+  a.part = reinterpret_cast<float*>(ws);
+  a.ssq_part = reinterpret_cast<float*>(ws + part_bytes);
+  a.keys = reinterpret_cast<unsigned long long*>(ws + part_bytes + ssq_bytes);
   const size_t lds = (size_t)a.cps * per + affine_lds_fixed();
   return launched(qg_launch_affine(mode, a, lds, stream), fn);
 }
@@ -445,10 +441,8 @@ qg_status qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M
   a.ntiles = (N + 15) / 16;
   a.waves = kWaves;
   const size_t per = q4k_lds_per_sb(M);
-  const int cps_max = (int)std::max<size_t>(1, std::min<size_t>((size_t)a.nchunks, kLdsBudget / per));
-  const bool allow_split = a.ntiles <= kMaxTileCounters;
-  Plan pl = plan_split(a.ntiles, a.nchunks, cps_max, allow_split);
-  if (pl.S > 1 && !allow_split) return fail(QG_EUNSUPPORTED, "qgemv_q4k: N=%d too large to split K=%d", N, K);
+  const int cps_max = (int)std::max<size_t>(1, std::min<size_t>((size_t)a.nchunks, (kLdsBudget - 16) / per));
+  Plan pl = plan_split(a.ntiles, a.nchunks, cps_max, true);
   a.S = pl.S;
   a.cps = pl.cps;
   a.tpw = pl.tpw;
@@ -456,9 +450,8 @@ qg_status qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M
   unsigned char* ws = nullptr;
   const size_t part_bytes = (a.S > 1) ? (size_t)a.S * M * N * 4 : 0;
   if ((st = get_workspace((hipStream_t)stream, part_bytes, &ws))) return st;
-  a.tile_cnt = reinterpret_cast<uint32_t*>(ws + kTileCntOff);
-  a.part = reinterpret_cast<float*>(ws + kCounterArea);
-  return launched(qg_launch_q4k(a, (size_t)a.cps * per, (hipStream_t)stream), "qgemv_q4k");
+  a.part = reinterpret_cast<float*>(ws);
+  return launched(qg_launch_q4k(a, 16 + (size_t)a.cps * per, (hipStream_t)stream), "qgemv_q4k");
 }
 
 qg_status moe_expert_qgemv(const uint16_t* x, const float* router_logits, int top_k, const uint8_t* w_gu,
@@ -479,7 +472,7 @@ qg_status moe_expert_qgemv(const uint16_t* x, const float* router_logits, int to
   a.y = y;
   a.out_ids = out_ids;
   a.out_w = out_w;
-  a.h = reinterpret_cast<float*>(ws + kCounterArea);
+  a.h = reinterpret_cast<float*>(ws);
   a.E = E;
   a.D = D;
   a.I = I;

@@ -12,94 +12,117 @@
 //                   readout; Husky page: next token handed over on the GPU)
 //
 // Work decomposition
-//   * A "tile" is 16 consecutive weight rows (one MFMA B operand width).
+//   * A "tile" is 16 consecutive weight rows (one MFMA B operand width); in
+//     GATEUP a unit is the gate tile rows n.. and the up tile rows I+n.. .
 //   * A "chunk" is 128 consecutive k (two scale groups): per lane one 16-byte
 //     load of codes (4 words = 32 codes) and one scale+bias per lane.
 //   * The K axis is cut into S slices of `cps` chunks (split-K across
-//     workgroups, used when there are few tiles); each workgroup owns one
-//     slice and a run of tiles, stages its slice of X once in LDS, and its
-//     waves stream whole tiles.  With S > 1 the last workgroup to finish a
-//     tile (per-tile arrival counter) adds the S fp32 partials in slice order,
-//     so the result does not depend on timing.
+//     workgroups, used when there are few tiles or when the staged activations
+//     would not fit); each workgroup owns one slice and a run of tiles, stages
+//     its slice of X once in LDS, and its waves stream whole tiles.  With
+//     S > 1 every slice stores fp32 partial sums and k_split_reduce, launched
+//     next on the same stream, adds them in slice order and applies the
+//     epilogue: no atomics, no cross-workgroup fences, and the result does not
+//     depend on timing.
+//   * The LM head stores one (logit, index) key per row and workgroup;
+//     k_lmhead_finalize takes the maximum over workgroups and writes the ids
+//     and the accepted count.
 //   * Weight bytes are read exactly once; X is read once per workgroup.
 //
 // Per chunk and lane: codes word t (t = 0..3) of lane l covers
 //   k = 128*c + 32*(l/16) + 8*t + i, i = 0..7,
 // lanes 0..31 therefore carry group 2c and lanes 32..63 group 2c+1, which is
 // exactly the split of C rows described in common.h.
+//
+// GATEUP operands stay exact: x*gamma of two bf16 values is exact in fp32 and
+// has at most 16 significant bits, so it is the sum of hi = bf16(x*gamma) and
+// lo = x*gamma - hi, both exact bf16 values.  Each MFMA step runs on the hi
+// plane and then the lo plane with the same unpacked weights.
 #include "common.h"
 
 namespace qg {
 
-constexpr int kAffineChunkK = 128;
-constexpr int kBatch = 8;  // chunks whose loads are issued together
+__device__ __forceinline__ uint32_t half_of(const uint32_t* v, int k) {
+  return (k & 1) ? (v[k >> 1] >> 16) : (v[k >> 1] & 0xFFFFu);
+}
 
 // Activation staging: X[:, slice] -> LDS in MFMA operand order.
-// LDS entry ((c*4 + t)*4 + kb)*M + m holds, for activation row m, the eight
-// values at k = 128c + 32kb + 8t + nib(s), s = 0..7 with nib(s) = s/2 + 4*(s%2)
-// (the code order unpack_affine_word produces).  sx[(2c + par)*8 + m] holds
-// the fp32 sum of the 64 staged values of group 2c+par (the value the offset
-// and bias are folded against).  GATEUP stages bf16(x*gamma) and keeps the
-// per-(row, group) sum of x^2 for the RMS.
+// xs[0] is a zero entry (read by lanes whose operand slots are empty); entry
+// 1 + (((c*4 + t)*4 + kb)*PL + plane)*M + m holds, for activation row m,
+// the eight values at k = 128c + 32kb + 8t + nib(s), s = 0..7 with
+// nib(s) = s/2 + 4*(s%2) (the code order unpack_affine_word produces).
+// sx[(2c + par)*8 + m] holds the fp32 sum of the 64 staged values (all planes)
+// of group 2c+par, the value the offset and the bias are folded against.
+// GATEUP keeps the per-(row, group) sum of x^2 in ssq for the RMS.
 template <int M, int MODE>
 __device__ __forceinline__ void stage_affine_x(const QgAffineArgs& p, uint4* xs, float* sx, float* ssq,
                                                int c0, int nc) {
+  constexpr int PL = (MODE == QG_MODE_GATEUP) ? 2 : 1;
   const int ngl = 2 * nc;
   for (int pi = threadIdx.x; pi < M * ngl; pi += blockDim.x) {
     const int m = pi / ngl;
     const int gl = pi - m * ngl;
     const int g = 2 * c0 + gl;
-    uint32_t v[32];
-    float sum = 0.f, sq = 0.f;
-    if (g < p.G) {
-      const uint4* src = reinterpret_cast<const uint4*>(p.x + (size_t)m * p.K + (size_t)g * 64);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint4 t = src[i];
-        v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
-      }
-      if (MODE == QG_MODE_GATEUP) {
-        const uint4* gsrc = reinterpret_cast<const uint4*>(p.gamma + (size_t)g * 64);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint4 t = gsrc[i];
-          const uint32_t gg[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t xv = v[4 * i + j];
-            const float x0 = bf16_bits_to_f32(xv & 0xFFFFu), x1 = bf16_bits_to_f32(xv >> 16);
-            const float g0 = bf16_bits_to_f32(gg[j] & 0xFFFFu), g1 = bf16_bits_to_f32(gg[j] >> 16);
-            sq = fmaf(x0, x0, sq);
-            sq = fmaf(x1, x1, sq);
-            // x*gamma of two bf16 values is exact in fp32; one rounding to bf16
-            v[4 * i + j] = (uint32_t)f32_to_bf16_bits(x0 * g0) | ((uint32_t)f32_to_bf16_bits(x1 * g1) << 16);
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        sum += bf16_bits_to_f32(v[i] & 0xFFFFu);
-        sum += bf16_bits_to_f32(v[i] >> 16);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = 0u;
-    }
+    const bool live = g < p.G;
     const int c = gl >> 1, par = gl & 1;
+    float sum = 0.f, sq = 0.f;
+    // the group's 64 values in two halves of 32 (lanes kb = 2*par and 2*par+1)
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
+      uint32_t v[PL][16];
+      if (live) {
+        const uint4* src = reinterpret_cast<const uint4*>(p.x + (size_t)m * p.K + (size_t)g * 64 + 32 * kb2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 t = src[i];
+          v[0][4 * i] = t.x; v[0][4 * i + 1] = t.y; v[0][4 * i + 2] = t.z; v[0][4 * i + 3] = t.w;
+        }
+        if constexpr (MODE == QG_MODE_GATEUP) {
+          const uint4* gsrc = reinterpret_cast<const uint4*>(p.gamma + (size_t)g * 64 + 32 * kb2);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint4 t = gsrc[i];
+            const uint32_t gg[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t xv = v[0][4 * i + j];
+              const float x0 = bf16_bits_to_f32(xv & 0xFFFFu), x1 = bf16_bits_to_f32(xv >> 16);
+              sq = fmaf(x0, x0, sq);
+              sq = fmaf(x1, x1, sq);
+              const float p0 = x0 * bf16_bits_to_f32(gg[j] & 0xFFFFu);  // exact in fp32
+              const float p1 = x1 * bf16_bits_to_f32(gg[j] >> 16);
+              const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
+              const uint32_t l0 = f32_to_bf16_bits(p0 - bf16_bits_to_f32(h0));  // exact remainder
+              const uint32_t l1 = f32_to_bf16_bits(p1 - bf16_bits_to_f32(h1));
+              v[0][4 * i + j] = h0 | (h1 << 16);
+              v[PL - 1][4 * i + j] = l0 | (l1 << 16);
+            }
+          }
+        }
+#pragma unroll
+        for (int pl = 0; pl < PL; ++pl)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            sum += bf16_bits_to_f32(v[pl][i] & 0xFFFFu);
+            sum += bf16_bits_to_f32(v[pl][i] >> 16);
+          }
+      } else {
+#pragma unroll
+        for (int pl = 0; pl < PL; ++pl)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[pl][i] = 0u;
+      }
+      const int kb = 2 * par + kb2;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int base = 32 * kb2 + 8 * t;  // k within the group, even
-        uint32_t e[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int klo = base + j, khi = base + j + 4;
-          const uint32_t lo = (klo & 1) ? (v[klo >> 1] >> 16) : (v[klo >> 1] & 0xFFFFu);
-          const uint32_t hi = (khi & 1) ? (v[khi >> 1] >> 16) : (v[khi >> 1] & 0xFFFFu);
-          e[j] = lo | (hi << 16);
+        for (int pl = 0; pl < PL; ++pl) {
+          uint32_t e[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            e[j] = half_of(v[pl], 8 * t + j) | (half_of(v[pl], 8 * t + j + 4) << 16);
+          xs[1 + (((c * 4 + t) * 4 + kb) * PL + pl) * M + m] = make_uint4(e[0], e[1], e[2], e[3]);
         }
-        xs[((c * 4 + t) * 4 + (2 * par + kb2)) * M + m] = make_uint4(e[0], e[1], e[2], e[3]);
       }
     }
     sx[gl * 8 + m] = sum;
@@ -119,10 +142,14 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   return ((unsigned long long)hi2 << 32) | lo2;
 }
 
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
 template <int M, int MODE>
-__global__ void __launch_bounds__(256) k_affine(QgAffineArgs p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) k_affine(QgAffineArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NB = (MODE == QG_MODE_GATEUP) ? 2 : 1;  // weight tiles per unit (gate, up)
+  constexpr int PL = (MODE == QG_MODE_GATEUP) ? 2 : 1;  // activation planes (hi, lo)
+  constexpr int BATCH = (MODE == QG_MODE_GATEUP) ? 2 : 4;  // chunks whose loads are issued together
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
@@ -132,13 +159,11 @@ __global__ void __launch_bounds__(256) k_affine(QgAffineArgs p) {
   const int nc = min(p.cps, p.nchunks - c0);
 
   uint4* xs = reinterpret_cast<uint4*>(smem);
-  float* sx = reinterpret_cast<float*>(xs + nc * 16 * M);
+  float* sx = reinterpret_cast<float*>(xs + 1 + nc * 16 * M * PL);
   float* ssq = sx + nc * 16;       // GATEUP: [M][2nc]
   float* rinv = ssq + M * 2 * nc;  // GATEUP: [8]
   unsigned long long* wkeys = reinterpret_cast<unsigned long long*>(rinv + 8);  // LMHEAD: [W][8]
-  __shared__ int s_last;
-  __shared__ int s_ids[8];
-
+  if (threadIdx.x == 0) xs[0] = make_uint4(0u, 0u, 0u, 0u);
   if (MODE == QG_MODE_LMHEAD) {
     for (int i = threadIdx.x; i < W * 8; i += blockDim.x) wkeys[i] = 0ull;
   }
@@ -148,7 +173,11 @@ __global__ void __launch_bounds__(256) k_affine(QgAffineArgs p) {
     if (threadIdx.x < M) {
       float t = 0.f;
       for (int gl = 0; gl < 2 * nc; ++gl) t += ssq[threadIdx.x * 2 * nc + gl];
-      rinv[threadIdx.x] = 1.0f / sqrtf(t / (float)p.K + p.eps);
+      if (p.S == 1) {
+        rinv[threadIdx.x] = 1.0f / sqrtf(t / (float)p.K + p.eps);
+      } else if (rg == 0) {
+        p.ssq_part[(size_t)slice * 8 + threadIdx.x] = t;  // this slice's sum of x^2, for k_split_reduce
+      }
     }
     __syncthreads();
   }
@@ -158,9 +187,14 @@ __global__ void __launch_bounds__(256) k_affine(QgAffineArgs p) {
   const int half = lane >> 5;  // scale group parity of this lane (B and C layouts agree)
   const int rho = lane & 15;
   const bool a_act = ((rho >> 3) == (kb >> 1)) && ((rho & 7) < M);
-  const uint4* a_base = xs + kb * M + (rho & 7);
+  // operand entry of this lane for (chunk cl, step t, plane pl): 1 + a_lane + (cl*16 + t*4)*PL*M + pl*M,
+  // or the zero entry for lanes whose slots carry the other group / a padding row
+  const uint32_t a_lane = 1u + (uint32_t)(kb * PL * M + (rho & 7));
+  const uint32_t a_mask = a_act ? 0xFFFFFFFFu : 0u;
   const float* sx_base = sx + half * 8 + 4 * (kb & 1);
   const size_t wrow_words = (size_t)p.K / 8;
+  const uint32_t wmax = (uint32_t)(wrow_words - 4);  // last in-row 16-byte load
+  const int mbase = 4 * (lane >> 4);  // activation row of C element 0 (lanes < 32)
 
   unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
 
@@ -169,53 +203,67 @@ __global__ void __launch_bounds__(256) k_affine(QgAffineArgs p) {
     if (tile >= p.ntiles) break;
     const int row = tile * 16 + nl;
     const bool row_ok = row < p.N;
+    const size_t row_c = (size_t)(row_ok ? row : p.N - 1);  // loads stay in bounds; results unused
     f32x4_t acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int cb = 0; cb < nc; cb += kBatch) {
-      uint4 q[NB][kBatch];
-      uint32_t sb[NB][kBatch];
+    for (int cb = 0; cb < nc; cb += BATCH) {
+      // all loads of the batch first, unconditionally, at clamped in-bounds addresses
+      uint4 q[NB][BATCH];
+      uint32_t sv[NB][BATCH], bv[NB][BATCH];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int cl = cb + u;
+      for (int u = 0; u < BATCH; ++u) {
+        const int cl = min(cb + u, nc - 1);
         const int cg = c0 + cl;
-        const int g = 2 * cg + half;
-        const bool ok = row_ok && (cl < nc) && (g < p.G);
+        const uint32_t wo = min((uint32_t)(cg * 16 + kb * 4), wmax);
+        const int g = min(2 * cg + half, p.G - 1);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          const size_t r = (size_t)row + (size_t)b * p.N;  // up rows follow the I gate rows
-          q[b][u] = make_uint4(0u, 0u, 0u, 0u);
-          sb[b][u] = 0u;
-          if (ok) {
-            q[b][u] = *reinterpret_cast<const uint4*>(p.codes + r * wrow_words + (size_t)cg * 16 + kb * 4);
-            sb[b][u] = (uint32_t)p.scales[r * p.G + g] | ((uint32_t)p.biases[r * p.G + g] << 16);
+          const size_t r = row_c + (size_t)b * p.N;  // up rows follow the I gate rows
+          q[b][u] = *reinterpret_cast<const uint4*>(p.codes + r * wrow_words + wo);
+          sv[b][u] = p.scales[r * p.G + g];
+          bv[b][u] = p.biases[r * p.G + g];
+        }
+      }
+      // group sums of the batch's chunks: independent MFMA chains, interleaved
+      f32x4_t C[NB][BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) C[b][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          if (cb + u < nc) {
+            uint4 a[PL];
+#pragma unroll
+            for (int pl = 0; pl < PL; ++pl)
+              a[pl] = xs[(a_lane + (uint32_t)(((cb + u) * 16 + t * 4) * PL * M + pl * M)) & a_mask];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const uint32_t w = t == 0 ? q[b][u].x : t == 1 ? q[b][u].y : t == 2 ? q[b][u].z : q[b][u].w;
+              const uint4 bw = unpack_affine_word(w);
+#pragma unroll
+              for (int pl = 0; pl < PL; ++pl) C[b][u] = mfma_bf16(a[pl], bw, C[b][u]);
+            }
           }
         }
       }
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int cl = cb + u;
-        if (cl >= nc) break;
-        uint4 a[4];
-        const uint4* ap = a_base + (size_t)cl * 16 * M;
+      for (int u = 0; u < BATCH; ++u) {
+        if (cb + u < nc) {
+          const float4 sxv = *reinterpret_cast<const float4*>(sx_base + (cb + u) * 16);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) a[t] = a_act ? ap[t * 4 * M] : make_uint4(0u, 0u, 0u, 0u);
-        const float4 sxv = *reinterpret_cast<const float4*>(sx_base + cl * 16);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          f32x4_t C = {0.f, 0.f, 0.f, 0.f};
-          C = mfma_bf16(a[0], unpack_affine_word(q[b][u].x), C);
-          C = mfma_bf16(a[1], unpack_affine_word(q[b][u].y), C);
-          C = mfma_bf16(a[2], unpack_affine_word(q[b][u].z), C);
-          C = mfma_bf16(a[3], unpack_affine_word(q[b][u].w), C);
-          const float sv = bf16_bits_to_f32(sb[b][u] & 0xFFFFu);
-          const float bv = bf16_bits_to_f32(sb[b][u] >> 16);
-          const float cbias = fmaf(-128.0f, sv, bv);
-          acc[b][0] = fmaf(sv, C[0], fmaf(cbias, sxv.x, acc[b][0]));
-          acc[b][1] = fmaf(sv, C[1], fmaf(cbias, sxv.y, acc[b][1]));
-          acc[b][2] = fmaf(sv, C[2], fmaf(cbias, sxv.z, acc[b][2]));
-          acc[b][3] = fmaf(sv, C[3], fmaf(cbias, sxv.w, acc[b][3]));
+          for (int b = 0; b < NB; ++b) {
+            const float s = bf16_bits_to_f32(sv[b][u]);
+            const float cbias = fmaf(-128.0f, s, bf16_bits_to_f32(bv[b][u]));
+            acc[b][0] = fmaf(s, C[b][u][0], fmaf(cbias, sxv.x, acc[b][0]));
+            acc[b][1] = fmaf(s, C[b][u][1], fmaf(cbias, sxv.y, acc[b][1]));
+            acc[b][2] = fmaf(s, C[b][u][2], fmaf(cbias, sxv.z, acc[b][2]));
+            acc[b][3] = fmaf(s, C[b][u][3], fmaf(cbias, sxv.w, acc[b][3]));
+          }
         }
       }
     }
@@ -226,67 +274,41 @@ __global__ void __launch_bounds__(256) k_affine(QgAffineArgs p) {
       for (int r = 0; r < 4; ++r) acc[b][r] += __shfl_xor(acc[b][r], 32);
 
     const bool out_lane = (lane < 32) && row_ok;
-    const int mbase = 4 * (lane >> 4);  // valid for lanes < 32
+    if (!out_lane) continue;
+    if (p.S > 1) {
+      // split-K: this slice's sums; k_split_reduce finishes the tile
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (mbase + r < M) p.part[(((size_t)slice * NB + b) * M + mbase + r) * p.N + row] = acc[b][r];
+      continue;
+    }
 
     if (MODE == QG_MODE_GATEUP) {
-      if (out_lane) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mbase + r;
-          if (m < M) {
-            const float gv = acc[0][r] * rinv[m];
-            const float uv = acc[NB - 1][r] * rinv[m];
-            const float h = gv / (1.0f + __expf(-gv)) * uv;
-            p.y[(size_t)m * p.N + row] = f32_to_bf16_bits(h);
-          }
+      for (int r = 0; r < 4; ++r) {
+        const int m = mbase + r;
+        if (m < M) {
+          const float ri = rinv[m];
+          p.y[(size_t)m * p.N + row] = f32_to_bf16_bits(silu_mul(acc[0][r] * ri, acc[NB - 1][r] * ri));
         }
       }
     } else if (MODE == QG_MODE_LMHEAD) {
-      if (out_lane) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mbase + r;
-          if (m < M) {
-            if (p.logits) p.logits[(size_t)m * p.N + row] = acc[0][r];
-            const unsigned long long key = argmax_key(acc[0][r], (uint32_t)row);
-            best[r] = key > best[r] ? key : best[r];
-          }
-        }
-      }
-    } else if (p.S == 1) {
-      if (out_lane) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mbase + r;
-          if (m < M) p.y[(size_t)m * p.N + row] = f32_to_bf16_bits(acc[0][r]);
+      for (int r = 0; r < 4; ++r) {
+        const int m = mbase + r;
+        if (m < M) {
+          if (p.logits) p.logits[(size_t)m * p.N + row] = acc[0][r];
+          const unsigned long long key = argmax_key(acc[0][r], (uint32_t)row);
+          best[r] = key > best[r] ? key : best[r];
         }
       }
     } else {
-      if (out_lane) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mbase + r;
-          if (m < M) p.part[((size_t)slice * M + m) * p.N + row] = acc[0][r];
-        }
-      }
-      __threadfence();  // release this slice's partials (device scope)
-      uint32_t prev = 0u;
-      if (lane == 0) prev = atomicAdd(&p.tile_cnt[tile], 1u);
-      prev = (uint32_t)__shfl((int)prev, 0);
-      if (prev == (uint32_t)(p.S - 1)) {
-        __threadfence();  // acquire the other slices' partials
-        if (out_lane) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = mbase + r;
-            if (m < M) {
-              float t = 0.f;
-              for (int s2 = 0; s2 < p.S; ++s2) t += p.part[((size_t)s2 * M + m) * p.N + row];
-              p.y[(size_t)m * p.N + row] = f32_to_bf16_bits(t);
-            }
-          }
-        }
-        if (lane == 0) atomicExch(&p.tile_cnt[tile], 0u);  // leave the counter at zero
+      for (int r = 0; r < 4; ++r) {
+        const int m = mbase + r;
+        if (m < M) p.y[(size_t)m * p.N + row] = f32_to_bf16_bits(acc[0][r]);
       }
     }
   }
@@ -311,32 +333,67 @@ __global__ void __launch_bounds__(256) k_affine(QgAffineArgs p) {
     if (threadIdx.x < M) {
       unsigned long long v = 0ull;
       for (int w = 0; w < W; ++w) v = wkeys[w * 8 + threadIdx.x] > v ? wkeys[w * 8 + threadIdx.x] : v;
-      if (v) atomicMax(&p.keys[threadIdx.x], v);
+      p.keys[(size_t)blockIdx.x * 8 + threadIdx.x] = v;  // this workgroup's best (logit, index) of row m
     }
-    __threadfence();
+  }
+}
+
+// Split-K epilogue: one thread per output (m, n); the S slices' partial sums are
+// added in slice order, then the mode's epilogue (bf16 store, or RMS scaling and
+// SwiGLU for gate/up).
+template <int MODE>
+__global__ void __launch_bounds__(256) k_split_reduce(QgAffineArgs p) {
+  constexpr int NB = (MODE == QG_MODE_GATEUP) ? 2 : 1;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t total = (size_t)p.M * p.N;
+  if (idx >= total) return;
+  const int m = (int)(idx / (size_t)p.N);
+  float t[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    t[b] = 0.f;
+    for (int s2 = 0; s2 < p.S; ++s2) t[b] += p.part[((size_t)s2 * NB + b) * total + idx];
+  }
+  if (MODE == QG_MODE_GATEUP) {
+    float ss = 0.f;
+    for (int s2 = 0; s2 < p.S; ++s2) ss += p.ssq_part[(size_t)s2 * 8 + m];
+    const float ri = 1.0f / sqrtf(ss / (float)p.K + p.eps);
+    p.y[idx] = f32_to_bf16_bits(silu_mul(t[0] * ri, t[NB - 1] * ri));
+  } else {
+    p.y[idx] = f32_to_bf16_bits(t[0]);
+  }
+}
+
+// Greedy verify: maximum key over all workgroups per row (order-independent),
+// then the ids and the number of leading rows that match the draft.
+__global__ void __launch_bounds__(256) k_lmhead_finalize(QgAffineArgs p, int nwg) {
+  __shared__ unsigned long long red[256];
+  __shared__ int s_ids[8];
+  for (int m = 0; m < p.M; ++m) {
+    unsigned long long v = 0ull;
+    for (int w = threadIdx.x; w < nwg; w += blockDim.x) {
+      const unsigned long long k = p.keys[(size_t)w * 8 + m];
+      v = k > v ? k : v;
+    }
+    red[threadIdx.x] = v;
     __syncthreads();
-    if (threadIdx.x == 0) s_last = (atomicAdd(p.done_cnt, 1u) == gridDim.x - 1) ? 1 : 0;
-    __syncthreads();
-    if (s_last) {
-      __threadfence();
-      if (threadIdx.x < M) {
-        const unsigned long long k = atomicMax(&p.keys[threadIdx.x], 0ull);  // read
-        const int id = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
-        p.ids[threadIdx.x] = id;
-        s_ids[threadIdx.x] = id;
-        atomicExch(&p.keys[threadIdx.x], 0ull);
-      }
+    for (int off = blockDim.x / 2; off > 0; off >>= 1) {
+      if ((int)threadIdx.x < off) red[threadIdx.x] = red[threadIdx.x + off] > red[threadIdx.x] ? red[threadIdx.x + off]
+                                                                                            : red[threadIdx.x];
       __syncthreads();
-      if (threadIdx.x == 0) {
-        if (p.accepted) {
-          int a = 0;
-          if (p.draft)
-            while (a < M && s_ids[a] == p.draft[a]) ++a;
-          *p.accepted = a;
-        }
-        atomicExch(p.done_cnt, 0u);
-      }
     }
+    if (threadIdx.x == 0) {
+      const int id = (int)(0xFFFFFFFFu - (uint32_t)(red[0] & 0xFFFFFFFFull));
+      p.ids[m] = id;
+      s_ids[m] = id;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && p.accepted) {
+    int a = 0;
+    if (p.draft)
+      while (a < p.M && s_ids[a] == p.draft[a]) ++a;
+    *p.accepted = a;
   }
 }
 
@@ -353,6 +410,17 @@ static int launch_affine_m(int mode, const QgAffineArgs& a, size_t lds, hipStrea
     default:
       hipLaunchKernelGGL((k_affine<M, QG_MODE_LMHEAD>), grid, block, lds, st, a);
       break;
+  }
+  int err = (int)hipGetLastError();
+  if (err) return err;
+  if (mode == QG_MODE_LMHEAD) {
+    hipLaunchKernelGGL(k_lmhead_finalize, dim3(1), dim3(256), 0, st, a, (int)grid.x);
+  } else if (a.S > 1) {
+    const unsigned nblk = (unsigned)(((size_t)a.M * a.N + 255) / 256);
+    if (mode == QG_MODE_GATEUP)
+      hipLaunchKernelGGL(k_split_reduce<QG_MODE_GATEUP>, dim3(nblk), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_split_reduce<QG_MODE_PLAIN>, dim3(nblk), dim3(256), 0, st, a);
   }
   return (int)hipGetLastError();
 }

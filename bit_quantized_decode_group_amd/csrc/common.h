@@ -50,7 +50,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // Eight affine codes of one little-endian word (code i at bits 4i..4i+3) as
 // eight bf16 values 128+q.  Element 2j (low half of dword j) is code j and
 // element 2j+1 (high half) is code j+4, so MFMA k-slot s holds code
-// kAffineSlotCode[s].
+// s/2 + 4*(s%2).
 __device__ __forceinline__ uint4 unpack_affine_word(uint32_t w) {
   const uint32_t m = 0x000F000Fu, one28 = 0x43004300u;
   uint4 r;
@@ -63,7 +63,7 @@ __device__ __forceinline__ uint4 unpack_affine_word(uint32_t w) {
 
 // Eight Q4_K codes from eight consecutive code bytes (w0 = bytes 0..3, w1 =
 // bytes 4..7): the low nibbles when sh == 0, the high nibbles when sh == 4.
-// Slot s holds the code of byte kQ4kSlotByte[s].
+// Slot s holds the code of byte {0,2,1,3,4,6,5,7}[s].
 __device__ __forceinline__ uint4 unpack_q4k_bytes(uint32_t w0, uint32_t w1, uint32_t sh) {
   const uint32_t m = 0x000F000Fu, one28 = 0x43004300u;
   uint4 r;
@@ -106,10 +106,9 @@ struct QgAffineArgs {
   int32_t* ids;
   const int32_t* draft;
   int32_t* accepted;
-  float* part;                // [S][M][N] split-K partials
-  uint32_t* tile_cnt;         // [ntiles] split-K arrival counters (zero between calls)
-  unsigned long long* keys;   // [8] argmax keys (zero between calls)
-  uint32_t* done_cnt;         // [1] finished-workgroup counter (zero between calls)
+  float* part;                // [S][NB][M][N] split-K partials (NB = 2 for gate and up)
+  float* ssq_part;            // [S][8] per-slice sums of x^2 (GATEUP with S > 1)
+  unsigned long long* keys;   // [workgroups][8] per-workgroup argmax keys (LM head)
   int M, N, K, G;
   int nchunks, S, cps, ntiles, tpw, rgroups, waves;
 };
@@ -118,8 +117,7 @@ struct QgQ4kArgs {
   const uint16_t* x;
   const uint8_t* blocks;
   uint16_t* y;
-  float* part;
-  uint32_t* tile_cnt;
+  float* part;  // [S][M][N] split-K partials
   int M, N, K;
   int nchunks, S, cps, ntiles, tpw, rgroups, waves;
 };

@@ -96,34 +96,35 @@ __device__ __forceinline__ void stage_q4k_x(const T* src, size_t ld, int K, uint
 // Accumulate one lane's share of a 16-row tile over nsb superblocks of K into
 // acc[b] for NB tiles whose (row, superblock 0) blocks start at blk[b].
 // xs / sx are this slice's staged activations.
+// Operands are read from lds[region + entry]; lds[0] is a zero entry that
+// lanes whose slots carry the other sub-block (or a padding row) read instead.
 template <int M, int NB>
 __device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* const (&blk)[NB], bool row_ok,
-                                         int nsb, const uint4* xs, const float* sx, int lane) {
+                                         int nsb, const uint4* lds, uint32_t region, const float* sx,
+                                         int lane) {
+  (void)row_ok;  // rows past the end are clamped by the caller; their sums are not stored
   const int kb = lane >> 4;
   const int half = lane >> 5;
   const int rho = lane & 15;
-  const bool act0 = ((rho >> 3) == ((kb >> 1) ^ 0)) && ((rho & 7) < M);
-  const bool act1 = ((rho >> 3) == ((kb >> 1) ^ 1)) && ((rho & 7) < M);
+  const uint32_t mask0 = (((rho >> 3) == ((kb >> 1) ^ 0)) && ((rho & 7) < M)) ? 0xFFFFFFFFu : 0u;
+  const uint32_t mask1 = (((rho >> 3) == ((kb >> 1) ^ 1)) && ((rho & 7) < M)) ? 0xFFFFFFFFu : 0u;
   const uint32_t sh0 = 4u * (uint32_t)((kb >> 1) ^ 0), sh1 = 4u * (uint32_t)((kb >> 1) ^ 1);
-  const uint4* a_base = xs + kb * M + (rho & 7);
+  const uint32_t a_lane = region + (uint32_t)(kb * M + (rho & 7));
   const float* sx_base = sx + half * 8 + 4 * (kb & 1);
 
   for (int sb = 0; sb < nsb; sb += kSbBatch) {
+    // all loads of the batch first, unconditionally, at in-bounds addresses (the
+    // callers clamp the row; the superblock index is clamped here)
     uint4 hdr[NB][kSbBatch];
     uint2 cq[NB][kSbBatch][4];
 #pragma unroll
     for (int u = 0; u < kSbBatch; ++u) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        hdr[b][u] = make_uint4(0u, 0u, 0u, 0u);
+        const uint8_t* bp = blk[b] + (size_t)min(sb + u, nsb - 1) * 144;
+        hdr[b][u] = *reinterpret_cast<const uint4*>(bp);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) cq[b][u][c] = make_uint2(0u, 0u);
-        if (row_ok && sb + u < nsb) {
-          const uint8_t* bp = blk[b] + (size_t)(sb + u) * 144;
-          hdr[b][u] = *reinterpret_cast<const uint4*>(bp);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) cq[b][u][c] = *reinterpret_cast<const uint2*>(bp + 16 + 32 * c + 8 * kb);
-        }
+        for (int c = 0; c < 4; ++c) cq[b][u][c] = *reinterpret_cast<const uint2*>(bp + 16 + 32 * c + 8 * kb);
       }
     }
 #pragma unroll
@@ -144,9 +145,9 @@ __device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* cons
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int cc = sbl * 4 + c;
-          const uint4* ap = a_base + (size_t)cc * 8 * M;
-          const uint4 a0 = act0 ? ap[0] : make_uint4(0u, 0u, 0u, 0u);
-          const uint4 a1 = act1 ? ap[4 * M] : make_uint4(0u, 0u, 0u, 0u);
+          const uint32_t ai = a_lane + (uint32_t)(cc * 8 * M);
+          const uint4 a0 = lds[ai & mask0];
+          const uint4 a1 = lds[(ai + 4 * M) & mask1];
           f32x4_t C = {0.f, 0.f, 0.f, 0.f};
           C = mfma_bf16(a0, unpack_q4k_bytes(cq[b][u][c].x, cq[b][u][c].y, sh0), C);
           C = mfma_bf16(a1, unpack_q4k_bytes(cq[b][u][c].x, cq[b][u][c].y, sh1), C);
@@ -171,9 +172,10 @@ __global__ void __launch_bounds__(256) k_q4k(QgQ4kArgs p) {
   const int slice = blockIdx.x % p.S, rg = blockIdx.x / p.S;
   const int sb0 = slice * p.cps;
   const int nsb = min(p.cps, p.nchunks - sb0);  // here a "chunk" of the split is one superblock
-  uint4* xs = reinterpret_cast<uint4*>(smem);
-  float* sx = reinterpret_cast<float*>(xs + nsb * 32 * M);
-  stage_q4k_x<M, uint16_t>(p.x, (size_t)p.K, p.K, xs, sx, sb0, nsb, threadIdx.x, blockDim.x);
+  uint4* lds = reinterpret_cast<uint4*>(smem);  // [0] zero entry, then the staged slice
+  float* sx = reinterpret_cast<float*>(lds + 1 + nsb * 32 * M);
+  if (threadIdx.x == 0) lds[0] = make_uint4(0u, 0u, 0u, 0u);
+  stage_q4k_x<M, uint16_t>(p.x, (size_t)p.K, p.K, lds + 1, sx, sb0, nsb, threadIdx.x, blockDim.x);
   __syncthreads();
 
   const int nb_row = p.K / 256;
@@ -184,43 +186,32 @@ __global__ void __launch_bounds__(256) k_q4k(QgQ4kArgs p) {
     const bool row_ok = row < p.N;
     const uint8_t* blk[1] = {p.blocks + ((size_t)(row_ok ? row : 0) * nb_row + sb0) * 144};
     f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    q4k_tile<M, 1>(acc, blk, row_ok, nsb, xs, sx, lane);
+    q4k_tile<M, 1>(acc, blk, row_ok, nsb, lds, 1u, sx, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[0][r] += __shfl_xor(acc[0][r], 32);
     const bool out_lane = (lane < 32) && row_ok;
     const int mbase = 4 * (lane >> 4);
-    if (p.S == 1) {
-      if (out_lane) {
+    if (!out_lane) continue;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (mbase + r < M) p.y[(size_t)(mbase + r) * p.N + row] = f32_to_bf16_bits(acc[0][r]);
-      }
-    } else {
-      if (out_lane) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (mbase + r < M) p.part[((size_t)slice * M + mbase + r) * p.N + row] = acc[0][r];
-      }
-      __threadfence();
-      uint32_t prev = 0u;
-      if (lane == 0) prev = atomicAdd(&p.tile_cnt[tile], 1u);
-      prev = (uint32_t)__shfl((int)prev, 0);
-      if (prev == (uint32_t)(p.S - 1)) {
-        __threadfence();
-        if (out_lane) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (mbase + r < M) {
-              float t = 0.f;
-              for (int s2 = 0; s2 < p.S; ++s2) t += p.part[((size_t)s2 * M + mbase + r) * p.N + row];
-              p.y[(size_t)(mbase + r) * p.N + row] = f32_to_bf16_bits(t);
-            }
-          }
-        }
-        if (lane == 0) atomicExch(&p.tile_cnt[tile], 0u);
+    for (int r = 0; r < 4; ++r) {
+      if (mbase + r < M) {
+        if (p.S == 1)
+          p.y[(size_t)(mbase + r) * p.N + row] = f32_to_bf16_bits(acc[0][r]);
+        else  // this slice's sums; k_q4k_reduce adds the slices in order
+          p.part[((size_t)slice * M + mbase + r) * p.N + row] = acc[0][r];
       }
     }
   }
+}
+
+// Split-K epilogue: one thread per output, slices added in slice order.
+__global__ void __launch_bounds__(256) k_q4k_reduce(QgQ4kArgs p) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t total = (size_t)p.M * p.N;
+  if (idx >= total) return;
+  float t = 0.f;
+  for (int s2 = 0; s2 < p.S; ++s2) t += p.part[(size_t)s2 * total + idx];
+  p.y[idx] = f32_to_bf16_bits(t);
 }
 
 // ---------------------------------------------------------------- routing --
@@ -302,11 +293,12 @@ __global__ void __launch_bounds__(256) k_moe_gateup(QgMoeArgs p) {
   const int tiles = (p.I + 15) / 16;
   const int slot = blockIdx.x / tiles, tile = blockIdx.x % tiles;
   const int nsb = p.D / 256;
-  uint4* xs = reinterpret_cast<uint4*>(smem);
-  float* sx = reinterpret_cast<float*>(xs + nsb * 32);
+  uint4* lds = reinterpret_cast<uint4*>(smem);  // [0] zero entry, then the staged token
+  float* sx = reinterpret_cast<float*>(lds + 1 + nsb * 32);
 
+  if (threadIdx.x == 0) lds[0] = make_uint4(0u, 0u, 0u, 0u);
   route_topk(p.logits, p.E, p.top_k, sel, pw, asc, pasc);
-  stage_q4k_x<1, uint16_t>(p.x, (size_t)p.D, p.D, xs, sx, 0, nsb, threadIdx.x, blockDim.x);
+  stage_q4k_x<1, uint16_t>(p.x, (size_t)p.D, p.D, lds + 1, sx, 0, nsb, threadIdx.x, blockDim.x);
   __syncthreads();
 
   const int e = asc[slot];
@@ -321,7 +313,7 @@ __global__ void __launch_bounds__(256) k_moe_gateup(QgMoeArgs p) {
   const uint8_t* blk[2] = {base + ((size_t)r0 * nsb + sb_lo) * 144, base + ((size_t)(p.I + r0) * nsb + sb_lo) * 144};
   f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
   if (sb_hi > sb_lo)
-    q4k_tile<1, 2>(acc, blk, row_ok, sb_hi - sb_lo, xs + (size_t)sb_lo * 32, sx + sb_lo * 64, lane);
+    q4k_tile<1, 2>(acc, blk, row_ok, sb_hi - sb_lo, lds, 1u + (uint32_t)sb_lo * 32u, sx + sb_lo * 64, lane);
   red[wave][0][lane] = acc[0];
   red[wave][1][lane] = acc[1];
   __syncthreads();
@@ -353,13 +345,14 @@ __global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
   const int tile = blockIdx.x;
   const int nsb = p.I / 256;
   const size_t xs_per = (size_t)nsb * 32;  // uint4 entries per expert (M = 1)
-  uint4* xs = reinterpret_cast<uint4*>(smem);
-  float* sx = reinterpret_cast<float*>(xs + xs_per * p.top_k);
+  uint4* lds = reinterpret_cast<uint4*>(smem);  // [0] zero entry, then one staged region per expert
+  float* sx = reinterpret_cast<float*>(lds + 1 + xs_per * p.top_k);
 
+  if (threadIdx.x == 0) lds[0] = make_uint4(0u, 0u, 0u, 0u);
   route_topk(p.logits, p.E, p.top_k, sel, pw, asc, pasc);
   for (int s = 0; s < p.top_k; ++s)
-    stage_q4k_x<1, float>(p.h + (size_t)s * p.I, (size_t)p.I, p.I, xs + xs_per * s, sx + (size_t)s * nsb * 64, 0,
-                          nsb, threadIdx.x, blockDim.x);
+    stage_q4k_x<1, float>(p.h + (size_t)s * p.I, (size_t)p.I, p.I, lds + 1 + xs_per * s, sx + (size_t)s * nsb * 64,
+                          0, nsb, threadIdx.x, blockDim.x);
   __syncthreads();
 
   const int row = tile * 16 + (lane & 15);
@@ -371,7 +364,7 @@ __global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
     const int e = asc[s];
     const uint8_t* blk[1] = {p.w_down + (size_t)e * expert_bytes + (size_t)r0 * nsb * 144};
     f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    q4k_tile<1, 1>(acc, blk, row_ok, nsb, xs + xs_per * s, sx + (size_t)s * nsb * 64, lane);
+    q4k_tile<1, 1>(acc, blk, row_ok, nsb, lds, 1u + (uint32_t)(xs_per * s), sx + (size_t)s * nsb * 64, lane);
     const float pe = pasc[s];
     tot[0] = fmaf(pe, acc[0][0], tot[0]);
     tot[1] = fmaf(pe, acc[0][1], tot[1]);
@@ -395,6 +388,9 @@ __global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
 template <int M>
 static int launch_q4k_m(const QgQ4kArgs& a, size_t lds, hipStream_t st) {
   hipLaunchKernelGGL((k_q4k<M>), dim3((unsigned)(a.S * a.rgroups)), dim3((unsigned)(64 * a.waves)), lds, st, a);
+  int err = (int)hipGetLastError();
+  if (err || a.S == 1) return err;
+  hipLaunchKernelGGL(k_q4k_reduce, dim3((unsigned)(((size_t)a.M * a.N + 255) / 256)), dim3(256), 0, st, a);
   return (int)hipGetLastError();
 }
 
@@ -416,13 +412,13 @@ int qg_launch_q4k(const QgQ4kArgs& a, size_t lds, hipStream_t st) {
 
 int qg_launch_moe(const QgMoeArgs& a, hipStream_t st) {
   const int nsb_d = a.D / 256, nsb_i = a.I / 256;
-  const size_t lds_gu = (size_t)nsb_d * 32 * 16 + (size_t)nsb_d * 64 * 4;
+  const size_t lds_gu = 16 + (size_t)nsb_d * 32 * 16 + (size_t)nsb_d * 64 * 4;
   const int tiles_i = (a.I + 15) / 16;
   hipLaunchKernelGGL(qg::k_moe_gateup, dim3((unsigned)(a.top_k * tiles_i)), dim3(64 * qg::kMoeWaves), lds_gu, st,
                      a);
   int err = (int)hipGetLastError();
   if (err) return err;
-  const size_t lds_dn = (size_t)a.top_k * ((size_t)nsb_i * 32 * 16 + (size_t)nsb_i * 64 * 4);
+  const size_t lds_dn = 16 + (size_t)a.top_k * ((size_t)nsb_i * 32 * 16 + (size_t)nsb_i * 64 * 4);
   const int waves = a.top_k < qg::kMoeDownWaves ? a.top_k : qg::kMoeDownWaves;
   hipLaunchKernelGGL(qg::k_moe_down, dim3((unsigned)((a.D + 15) / 16)), dim3(64 * waves), lds_dn, st, a);
   return (int)hipGetLastError();

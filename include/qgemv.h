@@ -38,14 +38,15 @@
  *     explicit-error conventions of the TensorFold and runNburn pages).
  *     Outputs may not overlap any input or each other (QG_EALIAS).
  *   * The library keeps one scratch workspace per (device, stream), allocated
- *     on first use and zero-initialised (split-K partials, tile counters and
- *     argmax keys; counters are restored to zero by the kernels).  Two calls
- *     on the same stream are ordered by the stream; calls on different streams
- *     use different workspaces.  A call that must grow the workspace
- *     synchronises that stream once.
+ *     on first use (split-K partial sums, per-workgroup argmax keys, MoE expert
+ *     activations).  Two calls on the same stream are ordered by the stream;
+ *     calls on different streams use different workspaces.  A call that must
+ *     grow the workspace synchronises that stream once.  A call may enqueue
+ *     more than one kernel (a split-K or argmax reduction follows its main
+ *     kernel on the same stream).
  *   * Floating point: fp32 accumulation; bf16 outputs rounded to nearest even.
  *     Results are deterministic: the same inputs give the same bytes on every
- *     call (fixed reduction order, no floating-point atomics).
+ *     call (fixed reduction order, no atomics).
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -98,9 +99,7 @@ qg_status qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y,
  *   x bf16 [M][K]; gamma bf16 [K]; eps > 0 (finite)
  *   codes_gu uint32 [2I][K/8], scales_gu / biases_gu bf16 [2I][K/64]:
  *     rows 0..I-1 are the gate projection, rows I..2I-1 the up projection.
- *   h bf16 [M][I].   1 <= M <= 8; I >= 0; K % 64 == 0.  All of x is staged
- *   on chip: ceil(K/128) * (264*M + 64) + 288 <= 65536 bytes (M = 8: K <= 3712;
- *   M = 1: K <= 25344), else QG_EUNSUPPORTED.
+ *   h bf16 [M][I].   1 <= M <= 8; I >= 0; K > 0, K % 64 == 0.
  */
 qg_status rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma,
                                 float eps, const uint32_t* codes_gu,
@@ -141,8 +140,9 @@ qg_status moe_expert_qgemv(const uint16_t* x, const float* router_logits,
  *                  (written only if non-null; 0 if draft is null)
  *   x bf16 [M][K]; codes uint32 [V][K/8]; scales, biases bf16 [V][K/64];
  *   logits fp32 [M][V] (nullable); ids int32 [M]; draft int32 [M] (nullable);
- *   accepted int32 [1] (nullable).   1 <= M <= 8; V >= 1; K % 64 == 0, and
- *   the same on-chip staging limit on M and K as rmsnorm_gateup_swiglu.
+ *   accepted int32 [1] (nullable).   1 <= M <= 8; V >= 1; K % 64 == 0.  All
+ *   of x is staged on chip: ceil(K/128) * (264*M + 64) + 304 <= 65536 bytes
+ *   (M = 8: K <= 3712; M = 1: K <= 25344), else QG_EUNSUPPORTED.
  */
 qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes,
                         const uint16_t* scales, const uint16_t* biases,
