@@ -138,6 +138,8 @@ qg_status get_workspace(hipStream_t stream, size_t need, unsigned char** out) {
   return QG_OK;
 }
 
+int g_cus[64] = {0};  // compute units per device, filled by check_device
+
 // The kernels are gfx950 code objects; refuse other devices by name.
 qg_status check_device() {
   static std::mutex mu;
@@ -152,9 +154,29 @@ qg_status check_device() {
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return fail(QG_EHIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
     ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_cus[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   }
   if (ok[dev] < 0) return fail(QG_EUNSUPPORTED, "device %d is not gfx950 (MI355X); no kernels for it", dev);
   return QG_OK;
+}
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || g_cus[dev] <= 0) return 256;
+  return g_cus[dev];
+}
+
+// Workgroups per K slice for the persistent affine kernel: fill every
+// resident workgroup slot of the device once (4 waves per workgroup, at most
+// 16 waves per CU, fewer if the staged slice limits LDS occupancy), and give
+// every wave at least one tile.
+int affine_rgroups(int ntiles, int S, size_t lds, int max_occ) {
+  const size_t lds_cu = 160 * 1024;
+  const int occ = (int)std::max<size_t>(1, std::min<size_t>((size_t)max_occ, lds_cu / std::max<size_t>(lds, 1)));
+  const long long slots = (long long)device_cus() * occ;
+  const long long per_slice = std::max<long long>(1, slots / S);
+  const long long max_r = std::max<long long>(1, (ntiles + kWaves - 1) / kWaves);
+  return (int)std::min(per_slice, max_r);
 }
 
 qg_status launched(int err, const char* fn) {
@@ -294,10 +316,25 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
   if (!allow_split && a.nchunks > cps_max)
     return fail(QG_EUNSUPPORTED, "%s: K=%d needs a split of K this mode or size lacks", fn, a.K);
   Plan pl = plan_split(a.ntiles, a.nchunks, std::max(cps_max, 1), allow_split);
+  // slices start on a batch boundary (4 chunks, 2 for gate/up) when that keeps them within LDS
+  const int batch = (mode == QG_MODE_GATEUP) ? 2 : 4;
+  if (pl.S > 1) {
+    const int cps_b = (pl.cps + batch - 1) / batch * batch;
+    if (cps_b <= cps_max) {
+      pl.cps = cps_b;
+      pl.S = (a.nchunks + pl.cps - 1) / pl.cps;
+    }
+  }
   a.S = pl.S;
   a.cps = pl.cps;
-  a.tpw = pl.tpw;
-  a.rgroups = pl.rgroups;
+  {
+    const size_t vec = (size_t)2 * batch * 2;  // bytes of one batch's scales of one row
+    a.wide = (a.G % (2 * batch) == 0) && (a.S == 1 || a.cps % batch == 0) &&
+             ((uintptr_t)a.scales % vec == 0) && ((uintptr_t)a.biases % vec == 0);
+  }
+  const size_t lds = (size_t)a.cps * per + affine_lds_fixed();
+  // gate/up keeps 168 registers per lane (3 waves per SIMD), the others 128 (4)
+  a.rgroups = affine_rgroups(a.ntiles, a.S, lds, mode == QG_MODE_GATEUP ? 3 : 4);
   unsigned char* ws = nullptr;
   const size_t part_bytes = (a.S > 1) ? (size_t)a.S * NB * a.M * a.N * 4 : 0;
   const size_t ssq_bytes = (a.S > 1) ? (size_t)a.S * 8 * 4 : 0;
@@ -307,7 +344,6 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
   a.part = reinterpret_cast<float*>(ws);
   a.ssq_part = reinterpret_cast<float*>(ws + part_bytes);
   a.keys = reinterpret_cast<unsigned long long*>(ws + part_bytes + ssq_bytes);
-  const size_t lds = (size_t)a.cps * per + affine_lds_fixed();
   return launched(qg_launch_affine(mode, a, lds, stream), fn);
 }
 

@@ -110,7 +110,10 @@ struct QgAffineArgs {
   float* ssq_part;            // [S][8] per-slice sums of x^2 (GATEUP with S > 1)
   unsigned long long* keys;   // [workgroups][8] per-workgroup argmax keys (LM head)
   int M, N, K, G;
-  int nchunks, S, cps, ntiles, tpw, rgroups, waves;
+  int nchunks, S, cps, ntiles;
+  int rgroups;  // workgroups per K slice; workgroup r owns tiles [r*ntiles/rgroups, (r+1)*ntiles/rgroups)
+  int waves;    // waves per workgroup
+  int wide;     // scales/biases of a whole batch can be loaded as one aligned vector per row
 };
 
 struct QgQ4kArgs {

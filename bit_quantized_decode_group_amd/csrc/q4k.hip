@@ -37,24 +37,30 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
 // (T = float, the SwiGLU output of the gate/up kernel).
 template <int M, typename T>
 __device__ __forceinline__ void stage_q4k_x(const T* src, size_t ld, int K, uint4* xs, float* sx, int sb0,
-                                            int nsb, int tid, int nthr) {
+                                            int nsb, int tid, int nthr, int regions = 1) {
+  // `regions` > 1 stages that many independent M-row activations (source rows
+  // r*M.., region r at xs + r*nsb*32*M and sx + r*nsb*64)
   const int nj = 8 * nsb;
-  for (int pi = tid; pi < M * nj; pi += nthr) {
-    const int m = pi / nj;
-    const int jl = pi - m * nj;
+  for (int pi = tid; pi < regions * M * nj; pi += nthr) {
+    const int reg = pi / (M * nj);
+    const int m = (pi - reg * M * nj) / nj;
+    const int jl = pi - reg * M * nj - m * nj;
     const size_t k0 = (size_t)(sb0 * 8 + jl) * 32;
+    const size_t srow = (size_t)reg * M + m;
+    uint4* rxs = xs + (size_t)reg * nsb * 32 * M;
+    float* rsx = sx + (size_t)reg * nsb * 64;
     uint32_t v[16];  // 32 bf16 values, pairs
     float sum = 0.f;
     if (k0 < (size_t)K) {
       if constexpr (sizeof(T) == 2) {
-        const uint4* s4 = reinterpret_cast<const uint4*>(src + (size_t)m * ld + k0);
+        const uint4* s4 = reinterpret_cast<const uint4*>(src + srow * ld + k0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint4 t = s4[i];
           v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
         }
       } else {
-        const float4* s4 = reinterpret_cast<const float4*>(src + (size_t)m * ld + k0);
+        const float4* s4 = reinterpret_cast<const float4*>(src + srow * ld + k0);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float4 t = s4[i];
@@ -84,12 +90,13 @@ __device__ __forceinline__ void stage_q4k_x(const T* src, size_t ld, int K, uint
         const uint32_t hi = (khi & 1) ? (v[khi >> 1] >> 16) : (v[khi >> 1] & 0xFFFFu);
         e[j] = lo | (hi << 16);
       }
-      xs[((cc * 2 + t) * 4 + kb) * M + m] = make_uint4(e[0], e[1], e[2], e[3]);
+      rxs[((cc * 2 + t) * 4 + kb) * M + m] = make_uint4(e[0], e[1], e[2], e[3]);
     }
-    sx[jl * 8 + m] = sum;
+    rsx[jl * 8 + m] = sum;
   }
   if (M < 8) {
-    for (int pi = tid; pi < nj * (8 - M); pi += nthr) sx[(pi / (8 - M)) * 8 + M + pi % (8 - M)] = 0.f;
+    for (int pi = tid; pi < regions * nj * (8 - M); pi += nthr)
+      sx[(pi / (8 - M)) * 8 + M + pi % (8 - M)] = 0.f;
   }
 }
 
@@ -215,68 +222,46 @@ __global__ void __launch_bounds__(256) k_q4k_reduce(QgQ4kArgs p) {
 }
 
 // ---------------------------------------------------------------- routing --
-// Wave 0 of the workgroup selects the top_k largest logits (larger first,
-// equal values -> lower index) and their softmax weights over the selected
-// set.  Results in LDS: sel[] / pw[] in selection order, asc[] / pasc[] sorted
-// by expert index.  Every workgroup runs the same code on the same logits and
-// gets the same bytes.
-__device__ void route_topk(const float* logits, int E, int top_k, int* sel, float* pw, int* asc, float* pasc) {
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x < 64) {
-    float v[16];
-    uint32_t taken = 0u;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = lane + 64 * i;
-      v[i] = (e < E) ? logits[e] : 0.f;
+// All threads of the workgroup select the top_k largest logits by rank: the
+// rank of expert e is the number of experts with a larger logit or an equal
+// logit and a lower index, so ranks are unique and expert e is selected iff
+// its rank < top_k (larger first, ties -> lower index).  lg[] is E floats of
+// LDS.  Results in LDS: sel[] / pw[] in rank order with the softmax weights
+// over the selected logits, asc[] / pasc[] the same sorted by expert index.
+// Every workgroup runs the same code on the same logits and gets the same
+// bytes.  Ends with a barrier.
+__device__ void route_topk(const float* logits, int E, int top_k, float* lg, int* sel, float* pw, int* asc,
+                           float* pasc) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) lg[e] = logits[e];
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const float v = lg[e];
+    int rank = 0;
+    for (int j = 0; j < E; ++j) {
+      const float w = lg[j];
+      rank += (w > v || (w == v && j < e)) ? 1 : 0;
     }
-    for (int s = 0; s < top_k; ++s) {
-      float bv = 0.f;
-      int bi = 0x7FFFFFFF;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && !((taken >> i) & 1u)) {
-          if (bi == 0x7FFFFFFF || v[i] > bv || (v[i] == bv && e < bi)) {
-            bv = v[i];
-            bi = e;
-          }
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi))) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == 0) sel[s] = bi;
-    }
-    if (lane == 0) {
-      const float lmax = logits[sel[0]];
-      float z = 0.f;
-      for (int s = 0; s < top_k; ++s) {
-        pw[s] = expf(logits[sel[s]] - lmax);
-        z += pw[s];
-      }
-      for (int s = 0; s < top_k; ++s) pw[s] = pw[s] / z;
-      for (int s = 0; s < top_k; ++s) {  // insertion sort by expert index
-        int e = sel[s];
-        float w = pw[s];
-        int j = s - 1;
-        while (j >= 0 && asc[j] > e) {
-          asc[j + 1] = asc[j];
-          pasc[j + 1] = pasc[j];
-          --j;
-        }
-        asc[j + 1] = e;
-        pasc[j + 1] = w;
-      }
-    }
+    if (rank < top_k) sel[rank] = e;
   }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float lmax = lg[sel[0]];
+    float z = 0.f;
+    for (int s = 0; s < top_k; ++s) {
+      pw[s] = expf(lg[sel[s]] - lmax);
+      z += pw[s];
+    }
+    for (int s = 0; s < top_k; ++s) pw[s] = pw[s] / z;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < top_k) {  // position of sel[t] among the selected, by expert index
+    const int e = sel[threadIdx.x];
+    int pos = 0;
+    for (int s = 0; s < top_k; ++s) pos += (sel[s] < e) ? 1 : 0;
+    asc[pos] = e;
+    pasc[pos] = pw[threadIdx.x];
+  }
+  __syncthreads();
 }
 
 // ----------------------------------------------------------- MoE gate/up --
@@ -287,7 +272,7 @@ constexpr int kMoeWaves = 4;
 __global__ void __launch_bounds__(256) k_moe_gateup(QgMoeArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int sel[64], asc[64];
-  __shared__ float pw[64], pasc[64];
+  __shared__ float pw[64], pasc[64], lg[1024];
   __shared__ f32x4_t red[kMoeWaves][2][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tiles = (p.I + 15) / 16;
@@ -297,9 +282,8 @@ __global__ void __launch_bounds__(256) k_moe_gateup(QgMoeArgs p) {
   float* sx = reinterpret_cast<float*>(lds + 1 + nsb * 32);
 
   if (threadIdx.x == 0) lds[0] = make_uint4(0u, 0u, 0u, 0u);
-  route_topk(p.logits, p.E, p.top_k, sel, pw, asc, pasc);
   stage_q4k_x<1, uint16_t>(p.x, (size_t)p.D, p.D, lds + 1, sx, 0, nsb, threadIdx.x, blockDim.x);
-  __syncthreads();
+  route_topk(p.logits, p.E, p.top_k, lg, sel, pw, asc, pasc);
 
   const int e = asc[slot];
   const int row = tile * 16 + (lane & 15);
@@ -338,7 +322,7 @@ constexpr int kMoeDownWaves = 8;
 __global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int sel[64], asc[64];
-  __shared__ float pw[64], pasc[64];
+  __shared__ float pw[64], pasc[64], lg[1024];
   __shared__ f32x4_t red[kMoeDownWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
@@ -349,11 +333,9 @@ __global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
   float* sx = reinterpret_cast<float*>(lds + 1 + xs_per * p.top_k);
 
   if (threadIdx.x == 0) lds[0] = make_uint4(0u, 0u, 0u, 0u);
-  route_topk(p.logits, p.E, p.top_k, sel, pw, asc, pasc);
-  for (int s = 0; s < p.top_k; ++s)
-    stage_q4k_x<1, float>(p.h + (size_t)s * p.I, (size_t)p.I, p.I, lds + 1 + xs_per * s, sx + (size_t)s * nsb * 64,
-                          0, nsb, threadIdx.x, blockDim.x);
-  __syncthreads();
+  // the selected experts' activations, one row per expert slot, staged in one pass
+  stage_q4k_x<1, float>(p.h, (size_t)p.I, p.I, lds + 1, sx, 0, nsb, threadIdx.x, blockDim.x, p.top_k);
+  route_topk(p.logits, p.E, p.top_k, lg, sel, pw, asc, pasc);
 
   const int row = tile * 16 + (lane & 15);
   const bool row_ok = row < p.D;

@@ -338,3 +338,22 @@ def test_config_lm_head(M):
     while exp_acc < M and gi.cpu().numpy()[exp_acc] == draft[exp_acc]:
         exp_acc += 1
     assert int(acc2.cpu()[0]) == exp_acc
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 300, 1024), (3, 70, 12800), (1, 33, 2560)])
+def test_qgemv_affine4_scale_load_paths_agree(M, N, K):
+    """Scales and biases that start one element past a 16-byte boundary take the
+    per-chunk load path; the result must be bit-identical to the vector path."""
+    d = synth.single_projection(M=M, N=N, K=K, seed=900 + M + N)
+    x, codes, scales, biases = dev_bf16(d["x"]), *_affine_dev(d)
+    y1 = host_bits(ops.qgemv_affine4(x, codes, scales, biases))
+    sbuf = torch.empty(scales.numel() + 1, dtype=torch.bfloat16, device="cuda")
+    bbuf = torch.empty(biases.numel() + 1, dtype=torch.bfloat16, device="cuda")
+    sbuf[1:].copy_(scales.view(-1))
+    bbuf[1:].copy_(biases.view(-1))
+    s2, b2 = sbuf[1:].view(scales.shape), bbuf[1:].view(biases.shape)
+    assert s2.data_ptr() % 16 != 0
+    y2 = host_bits(ops.qgemv_affine4(x, codes, s2, b2))
+    assert np.array_equal(y1, y2)
+    ref = oracle.qgemv_affine4(d["x"], d["codes"], d["scales"], d["biases"])
+    assert_close(bits_to_f64(y1), ref, what=f"vector path M{M} N{N} K{K}")
