@@ -61,16 +61,17 @@ qg_status check_alias(const Buf* outs, int nout, const Buf* ins, int nin, const 
   return QG_OK;
 }
 
-constexpr size_t kLdsBudget = 65536;       // bytes of LDS one workgroup may use
+constexpr size_t kLdsBudget = 163840;      // bytes of LDS one workgroup may use (all of a gfx950 CU's)
+constexpr size_t kQ4kLdsBudget = 65536;    // staged-slice bound of the Q4_K projection (keeps 2+ workgroups per CU)
 constexpr int kWaves = 4;                  // waves per workgroup of the projection kernels
-constexpr int kTargetWaves = 2048;         // enough waves to cover HBM latency on 256 CUs
+constexpr int kTargetWaves = 2048;         // enough (tile, slice) pieces to cover HBM latency on 256 CUs
 constexpr int kMaxWavesInFlight = 4096;    // beyond this, waves stream several tiles
 
 // LDS of the affine kernels per 128-k chunk of the staged slice (operand
-// entries for PL activation planes, group sums, GATEUP sums of x^2) and fixed
-// (zero entry, 1/rms values, per-wave argmax keys).
+// entries for PL activation planes, group sums, sums of x^2) and fixed (zero
+// entry, per-wave argmax keys).
 size_t affine_lds_per_chunk(int M, int PL) { return (size_t)256 * M * PL + 64 + (size_t)8 * M; }
-size_t affine_lds_fixed() { return 16 + 32 + (size_t)kWaves * 64; }
+size_t affine_lds_fixed() { return 16 + (size_t)kWaves * 64; }
 size_t q4k_lds_per_sb(int M) { return (size_t)512 * M + 256; }
 
 // The LM-head mode stages all of K (no split): ceil(K/128) chunks must fit.
@@ -84,12 +85,12 @@ struct Plan {
 };
 
 // Split-K and tiles-per-wave choice shared by the projection kernels.
-Plan plan_split(int ntiles, int nchunks, int cps_max, bool allow_split) {
+Plan plan_split(int ntiles, int nchunks, int cps_max, bool allow_split, int target = kTargetWaves) {
   Plan pl{};
   const int s_min = (nchunks + cps_max - 1) / cps_max;
   int S = s_min;
-  if (allow_split && (long long)ntiles * S < kTargetWaves) {
-    const int want = (kTargetWaves + ntiles - 1) / std::max(ntiles, 1);
+  if (allow_split && (long long)ntiles * S < target) {
+    const int want = (target + ntiles - 1) / std::max(ntiles, 1);
     S = std::max(s_min, std::min(want, std::max(1, nchunks / 2)));
   }
   if (!allow_split) S = 1;
@@ -166,14 +167,14 @@ int device_cus() {
   return g_cus[dev];
 }
 
-// Workgroups per K slice for the persistent affine kernel: fill every
-// resident workgroup slot of the device once (4 waves per workgroup, at most
-// 16 waves per CU, fewer if the staged slice limits LDS occupancy), and give
-// every wave at least one tile.
-int affine_rgroups(int ntiles, int S, size_t lds, int max_occ) {
+// Workgroups per K slice for the persistent affine kernel: `fill_pct` percent
+// of the device's resident workgroup slots (4 waves per workgroup, at most
+// max_occ workgroups per CU, fewer if the staged slice limits LDS occupancy),
+// and no more workgroups than it takes to give every wave a tile.
+int affine_rgroups(int ntiles, int S, size_t lds, int max_occ, int fill_pct) {
   const size_t lds_cu = 160 * 1024;
   const int occ = (int)std::max<size_t>(1, std::min<size_t>((size_t)max_occ, lds_cu / std::max<size_t>(lds, 1)));
-  const long long slots = (long long)device_cus() * occ;
+  const long long slots = (long long)device_cus() * occ * fill_pct / 100;
   const long long per_slice = std::max<long long>(1, slots / S);
   const long long max_r = std::max<long long>(1, (ntiles + kWaves - 1) / kWaves);
   return (int)std::min(per_slice, max_r);
@@ -309,15 +310,21 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
   a.nchunks = (G + 1) / 2;
   a.ntiles = (a.N + 15) / 16;
   a.waves = kWaves;
-  const int PL = (mode == QG_MODE_GATEUP) ? 2 : 1, NB = PL;
+  const int PL = (mode == QG_MODE_GATEUP) ? 2 : 1;
   const size_t per = affine_lds_per_chunk(a.M, PL);
   const int cps_max = (int)std::min<size_t>((size_t)a.nchunks, (kLdsBudget - affine_lds_fixed()) / per);
   const bool allow_split = (mode != QG_MODE_LMHEAD);
   if (!allow_split && a.nchunks > cps_max)
     return fail(QG_EUNSUPPORTED, "%s: K=%d needs a split of K this mode or size lacks", fn, a.K);
-  Plan pl = plan_split(a.ntiles, a.nchunks, std::max(cps_max, 1), allow_split);
-  // slices start on a batch boundary (4 chunks, 2 for gate/up) when that keeps them within LDS
-  const int batch = (mode == QG_MODE_GATEUP) ? 2 : 4;
+  // Pieces to aim for and share of the resident workgroup slots to fill, per
+  // mode (measured on the decode shapes): gate/up, whose staging is the
+  // costliest, prefers many short slices on every slot; the weight-streaming
+  // modes run best with half the slots and two or more tiles per wave.
+  const int target = (mode == QG_MODE_GATEUP) ? 4 * kTargetWaves : 2 * kTargetWaves;
+  const int fill_pct = (mode == QG_MODE_GATEUP) ? 100 : 50;
+  Plan pl = plan_split(a.ntiles, a.nchunks, std::max(cps_max, 1), allow_split, target);
+  // slices start on a batch boundary (4 chunks) when that keeps them within LDS
+  const int batch = 4;
   if (pl.S > 1) {
     const int cps_b = (pl.cps + batch - 1) / batch * batch;
     if (cps_b <= cps_max) {
@@ -334,10 +341,11 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
   }
   const size_t lds = (size_t)a.cps * per + affine_lds_fixed();
   // gate/up keeps 168 registers per lane (3 waves per SIMD), the others 128 (4)
-  a.rgroups = affine_rgroups(a.ntiles, a.S, lds, mode == QG_MODE_GATEUP ? 3 : 4);
+  a.rgroups = affine_rgroups(a.ntiles, a.S, lds, mode == QG_MODE_GATEUP ? 3 : 4, fill_pct);
   unsigned char* ws = nullptr;
-  const size_t part_bytes = (a.S > 1) ? (size_t)a.S * NB * a.M * a.N * 4 : 0;
-  const size_t ssq_bytes = (a.S > 1) ? (size_t)a.S * 8 * 4 : 0;
+  const bool partials = a.S > 1 || mode == QG_MODE_GATEUP;
+  const size_t part_bytes = partials ? (size_t)a.S * a.M * a.N * 4 : 0;
+  const size_t ssq_bytes = (mode == QG_MODE_GATEUP) ? (size_t)a.S * 8 * 4 : 0;
   const size_t key_bytes = (mode == QG_MODE_LMHEAD) ? (size_t)a.S * a.rgroups * 8 * 8 : 0;
   qg_status st = get_workspace(stream, part_bytes + ssq_bytes + key_bytes, &ws);
   if (st) return st;
@@ -433,7 +441,7 @@ qg_status rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma, float 
   a.biases = biases_gu;
   a.y = h;
   a.M = M;
-  a.N = I;
+  a.N = 2 * I;  // gate rows then up rows, one matrix for the projection kernel
   a.K = K;
   return run_affine(QG_MODE_GATEUP, a, (hipStream_t)stream, "rmsnorm_gateup_swiglu");
 }
@@ -477,7 +485,7 @@ qg_status qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M
   a.ntiles = (N + 15) / 16;
   a.waves = kWaves;
   const size_t per = q4k_lds_per_sb(M);
-  const int cps_max = (int)std::max<size_t>(1, std::min<size_t>((size_t)a.nchunks, (kLdsBudget - 16) / per));
+  const int cps_max = (int)std::max<size_t>(1, std::min<size_t>((size_t)a.nchunks, (kQ4kLdsBudget - 16) / per));
   Plan pl = plan_split(a.ntiles, a.nchunks, cps_max, true);
   a.S = pl.S;
   a.cps = pl.cps;

@@ -12,18 +12,20 @@
 //                   readout; Husky page: next token handed over on the GPU)
 //
 // Work decomposition
-//   * A "tile" is 16 consecutive weight rows (one MFMA B operand width); in
-//     GATEUP a unit is the gate tile rows n.. and the up tile rows I+n.. .
+//   * A "tile" is 16 consecutive weight rows (one MFMA B operand width).  In
+//     GATEUP the 2I rows of the gate and up projections form one matrix; its
+//     tiles are independent and k_split_reduce pairs gate row n with up row
+//     I+n.
 //   * A "chunk" is 128 consecutive k (two scale groups): per lane one 16-byte
 //     load of codes (4 words = 32 codes) and one scale+bias per lane.
 //   * The K axis is cut into S slices of `cps` chunks (split-K across
 //     workgroups, used when there are few tiles or when the staged activations
-//     would not fit); each workgroup owns one slice and a run of tiles, stages
+//     would not fit); each workgroup owns one slice and a share of its tiles, stages
 //     its slice of X once in LDS, and its waves stream whole tiles.  With
-//     S > 1 every slice stores fp32 partial sums and k_split_reduce, launched
-//     next on the same stream, adds them in slice order and applies the
-//     epilogue: no atomics, no cross-workgroup fences, and the result does not
-//     depend on timing.
+//     S > 1 (and always in GATEUP) every slice stores fp32 partial sums and
+//     k_split_reduce, launched next on the same stream, adds them in slice
+//     order and applies the epilogue: no atomics, no cross-workgroup fences,
+//     and the result does not depend on timing.
 //   * The LM head stores one (logit, index) key per row and workgroup;
 //     k_lmhead_finalize takes the maximum over workgroups and writes the ids
 //     and the accepted count.
@@ -42,96 +44,103 @@
 
 namespace qg {
 
-__device__ __forceinline__ uint32_t half_of(const uint32_t* v, int k) {
-  return (k & 1) ? (v[k >> 1] >> 16) : (v[k >> 1] & 0xFFFFu);
-}
-
 // Activation staging: X[:, slice] -> LDS in MFMA operand order.
 // xs[0] is a zero entry (read by lanes whose operand slots are empty); entry
 // 1 + (((c*4 + t)*4 + kb)*PL + plane)*M + m holds, for activation row m,
 // the eight values at k = 128c + 32kb + 8t + nib(s), s = 0..7 with
 // nib(s) = s/2 + 4*(s%2) (the code order unpack_affine_word produces).
 // sx[(2c + par)*8 + m] holds the fp32 sum of the 64 staged values (all planes)
-// of group 2c+par, the value the offset and the bias are folded against.
-// GATEUP keeps the per-(row, group) sum of x^2 in ssq for the RMS.
+// of group 2c+par, the value the offset and the bias are folded against
+// (zero for rows m >= M).  GATEUP keeps the per-(row, group) sum of x^2 in ssq
+// for the RMS.
+//
+// One wave stages one scale group at a time: lane (m, h, t) = (lane & 7,
+// (lane >> 3) & 1, lane >> 4) takes the eight values of row m at
+// k = 64g + 32h + 8t, so the eight lanes of a row write consecutive entries
+// and the group sum is a butterfly over the lanes of that row.  A round
+// gives each wave kStageGroups groups; all of a round's loads are issued
+// before any is used.
+constexpr int kStageGroups = 4;
+
+template <int MODE>
+struct StageIn {
+  uint4 x[kStageGroups];
+  uint4 gm[MODE == QG_MODE_GATEUP ? kStageGroups : 1];
+};
+
 template <int M, int MODE>
-__device__ __forceinline__ void stage_affine_x(const QgAffineArgs& p, uint4* xs, float* sx, float* ssq,
-                                               int c0, int nc) {
-  constexpr int PL = (MODE == QG_MODE_GATEUP) ? 2 : 1;
-  const int ngl = 2 * nc;
-  for (int pi = threadIdx.x; pi < M * ngl; pi += blockDim.x) {
-    const int m = pi / ngl;
-    const int gl = pi - m * ngl;
-    const int g = 2 * c0 + gl;
-    const bool live = g < p.G;
-    const int c = gl >> 1, par = gl & 1;
-    float sum = 0.f, sq = 0.f;
-    // the group's 64 values in two halves of 32 (lanes kb = 2*par and 2*par+1)
+__device__ __forceinline__ void stage_load(const QgAffineArgs& p, int c0, int nc, int round, StageIn<MODE>& in) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int m = min(lane & 7, M - 1), h = (lane >> 3) & 1, t = lane >> 4;
+  const int glmax = 2 * nc - 1;
+  constexpr int SG = kStageGroups;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      uint32_t v[PL][16];
-      if (live) {
-        const uint4* src = reinterpret_cast<const uint4*>(p.x + (size_t)m * p.K + (size_t)g * 64 + 32 * kb2);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 t = src[i];
-          v[0][4 * i] = t.x; v[0][4 * i + 1] = t.y; v[0][4 * i + 2] = t.z; v[0][4 * i + 3] = t.w;
-        }
-        if constexpr (MODE == QG_MODE_GATEUP) {
-          const uint4* gsrc = reinterpret_cast<const uint4*>(p.gamma + (size_t)g * 64 + 32 * kb2);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint4 t = gsrc[i];
-            const uint32_t gg[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t xv = v[0][4 * i + j];
-              const float x0 = bf16_bits_to_f32(xv & 0xFFFFu), x1 = bf16_bits_to_f32(xv >> 16);
-              sq = fmaf(x0, x0, sq);
-              sq = fmaf(x1, x1, sq);
-              const float p0 = x0 * bf16_bits_to_f32(gg[j] & 0xFFFFu);  // exact in fp32
-              const float p1 = x1 * bf16_bits_to_f32(gg[j] >> 16);
-              const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
-              const uint32_t l0 = f32_to_bf16_bits(p0 - bf16_bits_to_f32(h0));  // exact remainder
-              const uint32_t l1 = f32_to_bf16_bits(p1 - bf16_bits_to_f32(h1));
-              v[0][4 * i + j] = h0 | (h1 << 16);
-              v[PL - 1][4 * i + j] = l0 | (l1 << 16);
-            }
-          }
-        }
-#pragma unroll
-        for (int pl = 0; pl < PL; ++pl)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            sum += bf16_bits_to_f32(v[pl][i] & 0xFFFFu);
-            sum += bf16_bits_to_f32(v[pl][i] >> 16);
-          }
-      } else {
-#pragma unroll
-        for (int pl = 0; pl < PL; ++pl)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) v[pl][i] = 0u;
-      }
-      const int kb = 2 * par + kb2;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int pl = 0; pl < PL; ++pl) {
-          uint32_t e[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            e[j] = half_of(v[pl], 8 * t + j) | (half_of(v[pl], 8 * t + j + 4) << 16);
-          xs[1 + (((c * 4 + t) * 4 + kb) * PL + pl) * M + m] = make_uint4(e[0], e[1], e[2], e[3]);
-        }
-      }
-    }
-    sx[gl * 8 + m] = sum;
-    if (MODE == QG_MODE_GATEUP) ssq[m * ngl + gl] = sq;
+  for (int j = 0; j < SG; ++j) {
+    // clamped in-bounds addresses; stage_store discards what it does not need
+    const int gl = min((round * SG + j) * W + wave, glmax);
+    const int g = min(2 * c0 + gl, p.G - 1);
+    const size_t k0 = (size_t)g * 64 + 32 * h + 8 * t;
+    in.x[j] = *reinterpret_cast<const uint4*>(p.x + (size_t)m * p.K + k0);
+    if constexpr (MODE == QG_MODE_GATEUP) in.gm[j] = *reinterpret_cast<const uint4*>(p.gamma + k0);
   }
-  if (M < 8) {
-    for (int pi = threadIdx.x; pi < ngl * (8 - M); pi += blockDim.x) {
-      const int gl = pi / (8 - M), m = M + pi % (8 - M);
-      sx[gl * 8 + m] = 0.f;
+}
+
+template <int M, int MODE>
+__device__ __forceinline__ void stage_store(const QgAffineArgs& p, uint4* xs, float* sx, float* ssq, int c0, int nc,
+                                            int round, const StageIn<MODE>& in) {
+  constexpr int PL = (MODE == QG_MODE_GATEUP) ? 2 : 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int m = lane & 7, h = (lane >> 3) & 1, t = lane >> 4;
+  const int ngl = 2 * nc;
+  constexpr int SG = kStageGroups;
+#pragma unroll
+  for (int j = 0; j < SG; ++j) {
+    const int gl = (round * SG + j) * W + wave;
+    if (gl >= ngl) break;  // uniform across the wave
+    const int g = 2 * c0 + gl;
+    const bool live = (m < M) && (g < p.G);
+    const uint32_t raw[4] = {live ? in.x[j].x : 0u, live ? in.x[j].y : 0u, live ? in.x[j].z : 0u,
+                             live ? in.x[j].w : 0u};
+    uint32_t v[PL][4];  // value i of the eight at dword i/2, half i%2
+    float sum = 0.f, sq = 0.f;
+    if constexpr (MODE == QG_MODE_GATEUP) {
+      const uint32_t gg[4] = {in.gm[j].x, in.gm[j].y, in.gm[j].z, in.gm[j].w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float x0 = bf16_bits_to_f32(raw[d] & 0xFFFFu), x1 = bf16_bits_to_f32(raw[d] >> 16);
+        sq = fmaf(x0, x0, sq);
+        sq = fmaf(x1, x1, sq);
+        const float p0 = x0 * bf16_bits_to_f32(gg[d] & 0xFFFFu);  // exact in fp32
+        const float p1 = x1 * bf16_bits_to_f32(gg[d] >> 16);
+        const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
+        const uint32_t l0 = f32_to_bf16_bits(p0 - bf16_bits_to_f32(h0));  // exact remainder
+        const uint32_t l1 = f32_to_bf16_bits(p1 - bf16_bits_to_f32(h1));
+        v[0][d] = h0 | (h1 << 16);
+        v[PL - 1][d] = l0 | (l1 << 16);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) v[0][d] = raw[d];
+    }
+    const int c = gl >> 1, kb = 2 * (gl & 1) + h;
+#pragma unroll
+    for (int pl = 0; pl < PL; ++pl) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) sum += bf16_bits_to_f32(v[pl][d] & 0xFFFFu) + bf16_bits_to_f32(v[pl][d] >> 16);
+      // operand dword e holds values e and e + 4
+      const uint4 e = make_uint4((v[pl][0] & 0xFFFFu) | (v[pl][2] << 16), (v[pl][0] >> 16) | (v[pl][2] & 0xFFFF0000u),
+                                 (v[pl][1] & 0xFFFFu) | (v[pl][3] << 16), (v[pl][1] >> 16) | (v[pl][3] & 0xFFFF0000u));
+      if (m < M) xs[1 + (((c * 4 + t) * 4 + kb) * PL + pl) * M + m] = e;
+    }
+    // sum over the eight lanes of row m (every lane ends with the same value)
+#pragma unroll
+    for (int off = 8; off <= 32; off <<= 1) {
+      sum += __shfl_xor(sum, off);
+      if constexpr (MODE == QG_MODE_GATEUP) sq += __shfl_xor(sq, off);
+    }
+    if (lane < 8) {
+      sx[gl * 8 + m] = sum;
+      if (MODE == QG_MODE_GATEUP && m < M) ssq[m * ngl + gl] = sq;
     }
   }
 }
@@ -147,15 +156,19 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // WIDE: every batch of every slice lies inside the row and the scale/bias rows
 // are aligned for one vector load per batch (the host checks G, the slice
 // length and the pointers); the loop body then has no data-dependent branch
-// around its loads, so the loads of the next step stay in flight while the
-// current one is computed.
+// around its loads.
+//
+// Each wave keeps a ring of R steps of weight loads in flight: the loads of
+// step st + R are issued as soon as step st has been computed.  Gate/up, with
+// two activation planes, gets 168 registers per lane (3 waves per SIMD), the
+// other modes 128 (4 waves per SIMD).
 template <int M, int MODE, bool WIDE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == QG_MODE_GATEUP ? 3 : 4, 8)))
 k_affine(QgAffineArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int NB = (MODE == QG_MODE_GATEUP) ? 2 : 1;     // weight tiles per unit (gate, up)
-  constexpr int PL = (MODE == QG_MODE_GATEUP) ? 2 : 1;     // activation planes (hi, lo)
-  constexpr int BATCH = (MODE == QG_MODE_GATEUP) ? 2 : 4;  // chunks whose loads are issued together
+  constexpr int PL = (MODE == QG_MODE_GATEUP) ? 2 : 1;  // activation planes (hi, lo)
+  constexpr int BATCH = 4;                              // chunks whose loads are issued together
+  constexpr int R = 2;                                  // steps of weight loads in flight per wave
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
@@ -163,18 +176,17 @@ k_affine(QgAffineArgs p) {
   const int rg = blockIdx.x / p.S;
   const int c0 = slice * p.cps;
   const int nc = min(p.cps, p.nchunks - c0);
-  // this workgroup's tiles [t_begin, t_end); wave w takes t_begin + w, t_begin + w + W, ...
-  const int t_begin = (int)(((long long)rg * p.ntiles) / p.rgroups);
-  const int t_end = (int)(((long long)(rg + 1) * p.ntiles) / p.rgroups);
-  const int ntw = (t_end - t_begin > wave) ? (t_end - t_begin - wave + W - 1) / W : 0;
+  // the slice's tiles are dealt round-robin to its rgroups*W waves: wave gw
+  // takes tiles gw, gw + nw, ... (neighbouring waves read neighbouring tiles)
+  const int gw = rg * W + wave, nw = p.rgroups * W;
+  const int ntw = gw < p.ntiles ? (p.ntiles - gw + nw - 1) / nw : 0;
   const int nbt = (nc + BATCH - 1) / BATCH;  // batches per tile
   const int nsteps = ntw * nbt;              // this wave's (tile, batch) steps
 
   uint4* xs = reinterpret_cast<uint4*>(smem);
   float* sx = reinterpret_cast<float*>(xs + 1 + nc * 16 * M * PL);
-  float* ssq = sx + nc * 16;       // GATEUP: [M][2nc]
-  float* rinv = ssq + M * 2 * nc;  // GATEUP: [8]
-  unsigned long long* wkeys = reinterpret_cast<unsigned long long*>(rinv + 8);  // LMHEAD: [W][8]
+  float* ssq = sx + nc * 16;  // GATEUP: [M][2nc]
+  unsigned long long* wkeys = reinterpret_cast<unsigned long long*>(ssq + M * 2 * nc);  // LMHEAD: [W][8]
 
   const int nl = lane & 15;
   const int kb = lane >> 4;
@@ -192,94 +204,60 @@ k_affine(QgAffineArgs p) {
 
   // ---- loads of one (tile, batch) step: unconditional, at clamped in-bounds addresses.
   // sw / bw dword u holds the bf16 scales / biases of groups 2(c0+cb+u) (low half) and
-  // 2(c0+cb+u)+1 (high half); lane l uses the half of its group parity.  A batch
-  // whose 2*BATCH groups are all inside the row loads them as one vector per row.
+  // 2(c0+cb+u)+1 (high half); lane l uses the half of its group parity.
   struct Buf {
-    uint4 q[NB][BATCH];
-    uint32_t sw[NB][BATCH], bw[NB][BATCH];
+    uint4 q[BATCH];
+    uint32_t sw[BATCH], bw[BATCH];
   };
   auto load_step = [&](Buf& bf, int st) {
     const int ti = st / nbt;
     const int cb = (st - ti * nbt) * BATCH;
-    const int row = (t_begin + wave + ti * W) * 16 + nl;
+    const int row = (gw + ti * nw) * 16 + nl;
     const size_t row_c = (size_t)min(row, p.N - 1);
     const int gb = 2 * (c0 + cb);  // first scale group of the batch
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int cg = WIDE ? c0 + cb + u : c0 + min(cb + u, nc - 1);
       const uint32_t wo = min((uint32_t)(cg * 16 + kb * 4), wmax);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const size_t r = row_c + (size_t)b * p.N;  // up rows follow the I gate rows
-        bf.q[b][u] = *reinterpret_cast<const uint4*>(p.codes + r * wrow_words + wo);
-      }
+      bf.q[u] = *reinterpret_cast<const uint4*>(p.codes + row_c * wrow_words + wo);
     }
     if constexpr (WIDE) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const size_t off = (row_c + (size_t)b * p.N) * p.G + gb;
-        if constexpr (BATCH == 4) {
-          const uint4 sv = *reinterpret_cast<const uint4*>(p.scales + off);
-          const uint4 bv = *reinterpret_cast<const uint4*>(p.biases + off);
-          bf.sw[b][0] = sv.x; bf.sw[b][1] = sv.y; bf.sw[b][2] = sv.z; bf.sw[b][3] = sv.w;
-          bf.bw[b][0] = bv.x; bf.bw[b][1] = bv.y; bf.bw[b][2] = bv.z; bf.bw[b][3] = bv.w;
-        } else {
-          const uint2 sv = *reinterpret_cast<const uint2*>(p.scales + off);
-          const uint2 bv = *reinterpret_cast<const uint2*>(p.biases + off);
-          bf.sw[b][0] = sv.x; bf.sw[b][1] = sv.y;
-          bf.bw[b][0] = bv.x; bf.bw[b][1] = bv.y;
-        }
-      }
+      const size_t off = row_c * p.G + gb;
+      const uint4 sv = *reinterpret_cast<const uint4*>(p.scales + off);
+      const uint4 bv = *reinterpret_cast<const uint4*>(p.biases + off);
+      bf.sw[0] = sv.x; bf.sw[1] = sv.y; bf.sw[2] = sv.z; bf.sw[3] = sv.w;
+      bf.bw[0] = bv.x; bf.bw[1] = bv.y; bf.bw[2] = bv.z; bf.bw[3] = bv.w;
     } else {
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
         const int g = min(gb + 2 * u + half, p.G - 1);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const size_t r = row_c + (size_t)b * p.N;
-          bf.sw[b][u] = (uint32_t)p.scales[r * p.G + g] << (16 * half);
-          bf.bw[b][u] = (uint32_t)p.biases[r * p.G + g] << (16 * half);
-        }
+        bf.sw[u] = (uint32_t)p.scales[row_c * p.G + g] << (16 * half);
+        bf.bw[u] = (uint32_t)p.biases[row_c * p.G + g] << (16 * half);
       }
     }
   };
 
-  f32x4_t acc[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
 
   // ---- end of a tile: add the two group halves, then store / publish
   auto finish_tile = [&](int tile) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[b][r] += __shfl_xor(acc[b][r], 32);
+    for (int r = 0; r < 4; ++r) acc[r] += __shfl_xor(acc[r], 32);
     const int row = tile * 16 + nl;
     if ((lane < 32) && row < p.N) {
-      if (p.S > 1) {
-        // split-K: this slice's sums; k_split_reduce finishes the tile
+      if (MODE == QG_MODE_GATEUP || p.S > 1) {
+        // this slice's sums; k_split_reduce finishes the row (and pairs gate with up)
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (mbase + r < M) p.part[(((size_t)slice * NB + b) * M + mbase + r) * p.N + row] = acc[b][r];
-      } else if (MODE == QG_MODE_GATEUP) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mbase + r;
-          if (m < M) {
-            const float ri = rinv[m];
-            p.y[(size_t)m * p.N + row] = f32_to_bf16_bits(silu_mul(acc[0][r] * ri, acc[NB - 1][r] * ri));
-          }
-        }
+        for (int r = 0; r < 4; ++r)
+          if (mbase + r < M) p.part[((size_t)slice * M + mbase + r) * p.N + row] = acc[r];
       } else if (MODE == QG_MODE_LMHEAD) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = mbase + r;
           if (m < M) {
-            if (p.logits) p.logits[(size_t)m * p.N + row] = acc[0][r];
-            const unsigned long long key = argmax_key(acc[0][r], (uint32_t)row);
+            if (p.logits) p.logits[(size_t)m * p.N + row] = acc[r];
+            const unsigned long long key = argmax_key(acc[r], (uint32_t)row);
             best[r] = key > best[r] ? key : best[r];
           }
         }
@@ -287,12 +265,11 @@ k_affine(QgAffineArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = mbase + r;
-          if (m < M) p.y[(size_t)m * p.N + row] = f32_to_bf16_bits(acc[0][r]);
+          if (m < M) p.y[(size_t)m * p.N + row] = f32_to_bf16_bits(acc[r]);
         }
       }
     }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   };
 
   // ---- compute one (tile, batch) step: independent MFMA chains per chunk, then the group epilogues
@@ -300,26 +277,20 @@ k_affine(QgAffineArgs p) {
     const int ti = st / nbt;
     const int bi = st - ti * nbt;
     const int cb = bi * BATCH;
-    f32x4_t C[NB][BATCH];
+    f32x4_t C[BATCH];
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) C[b][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < BATCH; ++u) C[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
         if (WIDE || cb + u < nc) {
-          uint4 a[PL];
+          const uint32_t w = t == 0 ? bf.q[u].x : t == 1 ? bf.q[u].y : t == 2 ? bf.q[u].z : bf.q[u].w;
+          const uint4 bw = unpack_affine_word(w);
 #pragma unroll
-          for (int pl = 0; pl < PL; ++pl)
-            a[pl] = xs[(a_lane + (uint32_t)(((cb + u) * 16 + t * 4) * PL * M + pl * M)) & a_mask];
-#pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            const uint32_t w = t == 0 ? bf.q[b][u].x : t == 1 ? bf.q[b][u].y : t == 2 ? bf.q[b][u].z : bf.q[b][u].w;
-            const uint4 bw = unpack_affine_word(w);
-#pragma unroll
-            for (int pl = 0; pl < PL; ++pl) C[b][u] = mfma_bf16(a[pl], bw, C[b][u]);
+          for (int pl = 0; pl < PL; ++pl) {
+            const uint4 a = xs[(a_lane + (uint32_t)(((cb + u) * 16 + t * 4) * PL * M + pl * M)) & a_mask];
+            C[u] = mfma_bf16(a, bw, C[u]);
           }
         }
       }
@@ -328,55 +299,56 @@ k_affine(QgAffineArgs p) {
     for (int u = 0; u < BATCH; ++u) {
       if (WIDE || cb + u < nc) {
         const float4 sxv = *reinterpret_cast<const float4*>(sx_base + (cb + u) * 16);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float sc = __uint_as_float((bf.sw[b][u] >> (16 * half)) << 16);
-          const float cbias = fmaf(-128.0f, sc, __uint_as_float((bf.bw[b][u] >> (16 * half)) << 16));
-          acc[b][0] = fmaf(sc, C[b][u][0], fmaf(cbias, sxv.x, acc[b][0]));
-          acc[b][1] = fmaf(sc, C[b][u][1], fmaf(cbias, sxv.y, acc[b][1]));
-          acc[b][2] = fmaf(sc, C[b][u][2], fmaf(cbias, sxv.z, acc[b][2]));
-          acc[b][3] = fmaf(sc, C[b][u][3], fmaf(cbias, sxv.w, acc[b][3]));
-        }
+        const float sc = __uint_as_float((bf.sw[u] >> (16 * half)) << 16);
+        const float cbias = fmaf(-128.0f, sc, __uint_as_float((bf.bw[u] >> (16 * half)) << 16));
+        acc[0] = fmaf(sc, C[u][0], fmaf(cbias, sxv.x, acc[0]));
+        acc[1] = fmaf(sc, C[u][1], fmaf(cbias, sxv.y, acc[1]));
+        acc[2] = fmaf(sc, C[u][2], fmaf(cbias, sxv.z, acc[2]));
+        acc[3] = fmaf(sc, C[u][3], fmaf(cbias, sxv.w, acc[3]));
       }
     }
-    if (bi == nbt - 1) finish_tile(t_begin + wave + ti * W);
+    if (bi == nbt - 1) finish_tile(gw + ti * nw);
   };
 
-  // ---- prologue: first weight loads in flight while the activations are staged
-  // every load_step takes a step index clamped to [0, last]: a wave without
-  // work, or the odd step after the last one, reloads an in-bounds step
+  // ---- prologue: the activation loads go out first and the first R weight
+  // steps right after them, so staging waits only for the former.  Every
+  // load_step takes a step index clamped to [0, last]: a wave without work,
+  // or the steps past its last one, reload an in-bounds step.
   const int last = max(nsteps - 1, 0);
-  Buf bufA, bufB;
-  load_step(bufA, 0);
+  Buf ring[R];
+  StageIn<MODE> sin;
+  stage_load<M, MODE>(p, c0, nc, 0, sin);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < R; ++r) load_step(ring[r], min(r, last));
+  __builtin_amdgcn_sched_barrier(0);
   if (threadIdx.x == 0) xs[0] = make_uint4(0u, 0u, 0u, 0u);
   if (MODE == QG_MODE_LMHEAD) {
     for (int i = threadIdx.x; i < W * 8; i += blockDim.x) wkeys[i] = 0ull;
   }
-  stage_affine_x<M, MODE>(p, xs, sx, ssq, c0, nc);
+  stage_store<M, MODE>(p, xs, sx, ssq, c0, nc, 0, sin);
+  const int rounds = (2 * nc + kStageGroups * W - 1) / (kStageGroups * W);
+  for (int r = 1; r < rounds; ++r) {
+    stage_load<M, MODE>(p, c0, nc, r, sin);
+    stage_store<M, MODE>(p, xs, sx, ssq, c0, nc, r, sin);
+  }
   __syncthreads();
-  if (MODE == QG_MODE_GATEUP) {
-    if (threadIdx.x < M) {
-      float t = 0.f;
-      for (int gl = 0; gl < 2 * nc; ++gl) t += ssq[threadIdx.x * 2 * nc + gl];
-      if (p.S == 1) {
-        rinv[threadIdx.x] = 1.0f / sqrtf(t / (float)p.K + p.eps);
-      } else if (rg == 0) {
-        p.ssq_part[(size_t)slice * 8 + threadIdx.x] = t;  // this slice's sum of x^2, for k_split_reduce
-      }
-    }
-    __syncthreads();
+  if (MODE == QG_MODE_GATEUP && rg == 0 && threadIdx.x < M) {
+    float t = 0.f;
+    for (int gl = 0; gl < 2 * nc; ++gl) t += ssq[threadIdx.x * 2 * nc + gl];
+    p.ssq_part[(size_t)slice * 8 + threadIdx.x] = t;  // this slice's sum of x^2, for k_split_reduce
   }
 
-  // ---- main loop: two steps per iteration, loads of the next step ahead of the compute
-  // (the scheduling barriers keep the compiler from sinking the loads below
-  // the computation that waits for the previous step's data)
-  for (int st = 0; st < nsteps; st += 2) {
-    load_step(bufB, min(st + 1, last));
-    __builtin_amdgcn_sched_barrier(0);
-    compute_step(bufA, st);
-    load_step(bufA, min(st + 2, last));
-    __builtin_amdgcn_sched_barrier(0);
-    if (st + 1 < nsteps) compute_step(bufB, st + 1);
+  // ---- main loop: compute step st from ring slot st % R, then refill the
+  // slot with step st + R (the scheduling barriers keep the compiler from
+  // moving loads across the computation that waits for older ones)
+  for (int st = 0; st < nsteps; st += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (st + r < nsteps) compute_step(ring[r], st + r);
+      load_step(ring[r], min(st + r + R, last));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   if (MODE == QG_MODE_LMHEAD) {
@@ -404,16 +376,21 @@ k_affine(QgAffineArgs p) {
   }
 }
 
-// Split-K epilogue: one thread per output (m, n); the S slices' partial sums are
-// added in slice order, then the mode's epilogue (bf16 store, or RMS scaling and
-// SwiGLU for gate/up).  Loads are issued eight slices at a time.
+// Split-K epilogue: one thread per output (m, n); the S slices' partial sums
+// ([S][M][N] fp32) are added in slice order, then the mode's epilogue: a bf16
+// store, or for gate/up (N = 2I: gate rows 0..I-1, up rows I..2I-1) the RMS
+// scaling and SwiGLU of the gate and up sums of row n.  Loads are issued eight
+// slices at a time.
 template <int MODE>
 __global__ void __launch_bounds__(256) k_split_reduce(QgAffineArgs p) {
   constexpr int NB = (MODE == QG_MODE_GATEUP) ? 2 : 1;
+  const int NO = p.N / NB;  // outputs per row
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t total = (size_t)p.M * p.N;
-  if (idx >= total) return;
-  const int m = (int)(idx / (size_t)p.N);
+  if (idx >= (size_t)p.M * NO) return;
+  const int m = (int)(idx / (size_t)NO);
+  const int n = (int)(idx - (size_t)m * NO);
+  const size_t stride = (size_t)p.M * p.N;  // one slice
+  const size_t base = (size_t)m * p.N + n;
   float t[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -421,7 +398,7 @@ __global__ void __launch_bounds__(256) k_split_reduce(QgAffineArgs p) {
     for (int s0 = 0; s0 < p.S; s0 += 8) {
       float v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = p.part[((size_t)min(s0 + j, p.S - 1) * NB + b) * total + idx];
+      for (int j = 0; j < 8; ++j) v[j] = p.part[(size_t)min(s0 + j, p.S - 1) * stride + base + (size_t)b * NO];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         if (s0 + j < p.S) t[b] += v[j];
@@ -512,8 +489,9 @@ static int launch_affine_m(int mode, const QgAffineArgs& a, size_t lds, hipStrea
   if (err) return err;
   if (mode == QG_MODE_LMHEAD) {
     hipLaunchKernelGGL(k_lmhead_finalize, dim3(1), dim3(256), 0, st, a, (int)grid.x);
-  } else if (a.S > 1) {
-    const unsigned nblk = (unsigned)(((size_t)a.M * a.N + 255) / 256);
+  } else if (a.S > 1 || mode == QG_MODE_GATEUP) {
+    const size_t outs = (size_t)a.M * (mode == QG_MODE_GATEUP ? a.N / 2 : a.N);
+    const unsigned nblk = (unsigned)((outs + 255) / 256);
     if (mode == QG_MODE_GATEUP)
       hipLaunchKernelGGL(k_split_reduce<QG_MODE_GATEUP>, dim3(nblk), dim3(256), 0, st, a);
     else
