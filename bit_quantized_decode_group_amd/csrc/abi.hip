@@ -506,7 +506,7 @@ qg_status moe_expert_qgemv(const uint16_t* x, const float* router_logits, int to
   if (st) return st;
   if ((st = check_device())) return st;
   unsigned char* ws = nullptr;
-  if ((st = get_workspace((hipStream_t)stream, (size_t)top_k * I * 4, &ws))) return st;
+  if ((st = get_workspace((hipStream_t)stream, 512 + (size_t)top_k * I * 2, &ws))) return st;
   QgMoeArgs a{};
   a.x = x;
   a.logits = router_logits;
@@ -516,7 +516,9 @@ qg_status moe_expert_qgemv(const uint16_t* x, const float* router_logits, int to
   a.y = y;
   a.out_ids = out_ids;
   a.out_w = out_w;
-  a.h = reinterpret_cast<float*>(ws);
+  a.route_ids = reinterpret_cast<int32_t*>(ws);      // 64 entries
+  a.route_w = reinterpret_cast<float*>(ws + 256);     // 64 entries
+  a.h = reinterpret_cast<uint16_t*>(ws + 512);
   a.E = E;
   a.D = D;
   a.I = I;

@@ -134,7 +134,9 @@ struct QgMoeArgs {
   uint16_t* y;
   int32_t* out_ids;
   float* out_w;
-  float* h;  // [top_k][I] fp32 workspace
+  int32_t* route_ids;  // [top_k] workspace: selected experts in ascending order
+  float* route_w;      // [top_k] workspace: their routing weights
+  uint16_t* h;         // [top_k][I] bf16 workspace
   int E, D, I;
 };
 

@@ -4,9 +4,9 @@
 //
 //   k_q4k          Y = X . dequant(W)^T                          (qgemv_q4k)
 //   k_moe_gateup   route, then h_e = silu(G_e x) * (U_e x) for every selected
-//                  expert e, into an fp32 workspace
-//   k_moe_down     route, then y = sum_e p_e Down_e h_e over the selected
-//                  experts in ascending expert order
+//                  expert e, into a bf16 workspace (with the routing)
+//   k_moe_down     y = sum_e p_e Down_e h_e over the selected experts in
+//                  ascending expert order
 //   (uzu page: MixtureOfExperts with a routing function; runNburn page: the
 //   engine never alters routing or quantisation semantics -- the selected set
 //   and weights are the plain top-k / softmax of the given logits.)
@@ -34,7 +34,7 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
 // activations at k = 64cc + 32pk + 8kb + byte(s), pk = (kb/2) ^ t, for chunk
 // cc of the slice; sx[jl*8 + m] is the fp32 sum of sub-block jl's 32 staged
 // values.  Source rows are bf16 (T = uint16_t) or fp32 rounded to bf16
-// (T = float, the SwiGLU output of the gate/up kernel).
+// (T = float).
 template <int M, typename T>
 __device__ __forceinline__ void stage_q4k_x(const T* src, size_t ld, int K, uint4* xs, float* sx, int sb0,
                                             int nsb, int tid, int nthr, int regions = 1) {
@@ -100,16 +100,41 @@ __device__ __forceinline__ void stage_q4k_x(const T* src, size_t ld, int K, uint
   }
 }
 
+// Loads of one batch of kSbBatch superblocks for NB tiles: each block's
+// 16-byte header and this lane's eight code bytes of each of its four chunks.
+template <int NB>
+struct Q4kBuf {
+  uint4 hdr[NB][kSbBatch];
+  uint2 cq[NB][kSbBatch][4];
+};
+
+// Issues the loads of the batch starting at superblock sb (clamped to the
+// last of nsb, so every address is in bounds; the caller clamps the row).
+template <int NB>
+__device__ __forceinline__ void q4k_load(Q4kBuf<NB>& bf, const uint8_t* const (&blk)[NB], int sb, int nsb, int kb) {
+#pragma unroll
+  for (int u = 0; u < kSbBatch; ++u) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const uint8_t* bp = blk[b] + (size_t)min(sb + u, nsb - 1) * 144;
+      bf.hdr[b][u] = *reinterpret_cast<const uint4*>(bp);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bf.cq[b][u][c] = *reinterpret_cast<const uint2*>(bp + 16 + 32 * c + 8 * kb);
+    }
+  }
+}
+
 // Accumulate one lane's share of a 16-row tile over nsb superblocks of K into
-// acc[b] for NB tiles whose (row, superblock 0) blocks start at blk[b].
-// xs / sx are this slice's staged activations.
-// Operands are read from lds[region + entry]; lds[0] is a zero entry that
-// lanes whose slots carry the other sub-block (or a padding row) read instead.
+// acc[b] for NB tiles whose (row, superblock 0) blocks start at blk[b].  `cur`
+// holds the loads of the first batch (issued by the caller, so they can be in
+// flight while the activations are staged); each batch's successor, if any,
+// is loaded before the batch is used.  xs / sx are this slice's staged activations,
+// read from lds[region + entry]; lds[0] is a zero entry that lanes whose
+// slots carry the other sub-block (or a padding row) read instead.
 template <int M, int NB>
-__device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* const (&blk)[NB], bool row_ok,
-                                         int nsb, const uint4* lds, uint32_t region, const float* sx,
-                                         int lane) {
-  (void)row_ok;  // rows past the end are clamped by the caller; their sums are not stored
+__device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* const (&blk)[NB], int nsb,
+                                         const uint4* lds, uint32_t region, const float* sx, int lane,
+                                         Q4kBuf<NB> cur) {
   const int kb = lane >> 4;
   const int half = lane >> 5;
   const int rho = lane & 15;
@@ -119,28 +144,14 @@ __device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* cons
   const uint32_t a_lane = region + (uint32_t)(kb * M + (rho & 7));
   const float* sx_base = sx + half * 8 + 4 * (kb & 1);
 
-  for (int sb = 0; sb < nsb; sb += kSbBatch) {
-    // all loads of the batch first, unconditionally, at in-bounds addresses (the
-    // callers clamp the row; the superblock index is clamped here)
-    uint4 hdr[NB][kSbBatch];
-    uint2 cq[NB][kSbBatch][4];
-#pragma unroll
-    for (int u = 0; u < kSbBatch; ++u) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const uint8_t* bp = blk[b] + (size_t)min(sb + u, nsb - 1) * 144;
-        hdr[b][u] = *reinterpret_cast<const uint4*>(bp);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) cq[b][u][c] = *reinterpret_cast<const uint2*>(bp + 16 + 32 * c + 8 * kb);
-      }
-    }
+  auto compute = [&](const Q4kBuf<NB>& cur, int sb) {
 #pragma unroll
     for (int u = 0; u < kSbBatch; ++u) {
       const int sbl = sb + u;
       if (sbl >= nsb) break;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const uint4 h = hdr[b][u];
+        const uint4 h = cur.hdr[b][u];
         const float d = f16_bits_to_f32(h.x & 0xFFFFu);
         const float dmin = f16_bits_to_f32(h.x >> 16);
         const uint32_t Y = h.y >> (8 * half), Z = h.z >> (8 * half), Wd = h.w >> (8 * half);
@@ -156,8 +167,8 @@ __device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* cons
           const uint4 a0 = lds[ai & mask0];
           const uint4 a1 = lds[(ai + 4 * M) & mask1];
           f32x4_t C = {0.f, 0.f, 0.f, 0.f};
-          C = mfma_bf16(a0, unpack_q4k_bytes(cq[b][u][c].x, cq[b][u][c].y, sh0), C);
-          C = mfma_bf16(a1, unpack_q4k_bytes(cq[b][u][c].x, cq[b][u][c].y, sh1), C);
+          C = mfma_bf16(a0, unpack_q4k_bytes(cur.cq[b][u][c].x, cur.cq[b][u][c].y, sh0), C);
+          C = mfma_bf16(a1, unpack_q4k_bytes(cur.cq[b][u][c].x, cur.cq[b][u][c].y, sh1), C);
           const float4 sxv = *reinterpret_cast<const float4*>(sx_base + cc * 16);
           const float a = d * (float)sc[c];                 // exact in fp32
           const float bt = fmaf(dmin, (float)mn[c], 128.0f * a);
@@ -168,7 +179,18 @@ __device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* cons
         }
       }
     }
+  };
+  // every batch but the last has a successor to load first; the loop body has
+  // no branch around its loads
+  int sb = 0;
+  for (; sb + kSbBatch < nsb; sb += kSbBatch) {
+    Q4kBuf<NB> nxt;
+    q4k_load<NB>(nxt, blk, sb + kSbBatch, nsb, kb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, sb);
+    cur = nxt;
   }
+  compute(cur, sb);
 }
 
 // ------------------------------------------------------------ qgemv_q4k --
@@ -181,19 +203,33 @@ __global__ void __launch_bounds__(256) k_q4k(QgQ4kArgs p) {
   const int nsb = min(p.cps, p.nchunks - sb0);  // here a "chunk" of the split is one superblock
   uint4* lds = reinterpret_cast<uint4*>(smem);  // [0] zero entry, then the staged slice
   float* sx = reinterpret_cast<float*>(lds + 1 + nsb * 32 * M);
+  const int nb_row = p.K / 256;
+  auto tile_blocks = [&](int it, bool& row_ok) {
+    const int tile = min((rg * W) * p.tpw + wave + it * W, p.ntiles - 1);
+    const int row = tile * 16 + (lane & 15);
+    row_ok = row < p.N;
+    return p.blocks + ((size_t)(row_ok ? row : 0) * nb_row + sb0) * 144;
+  };
+  // the first tile's first weight batch is in flight while the slice is staged
+  bool ok0;
+  const uint8_t* blk0[1] = {tile_blocks(0, ok0)};
+  (void)ok0;
+  Q4kBuf<1> first;
+  q4k_load<1>(first, blk0, 0, nsb, lane >> 4);
+  __builtin_amdgcn_sched_barrier(0);
   if (threadIdx.x == 0) lds[0] = make_uint4(0u, 0u, 0u, 0u);
   stage_q4k_x<M, uint16_t>(p.x, (size_t)p.K, p.K, lds + 1, sx, sb0, nsb, threadIdx.x, blockDim.x);
   __syncthreads();
 
-  const int nb_row = p.K / 256;
   for (int it = 0; it < p.tpw; ++it) {
     const int tile = (rg * W) * p.tpw + wave + it * W;
     if (tile >= p.ntiles) break;
     const int row = tile * 16 + (lane & 15);
-    const bool row_ok = row < p.N;
-    const uint8_t* blk[1] = {p.blocks + ((size_t)(row_ok ? row : 0) * nb_row + sb0) * 144};
+    bool row_ok;
+    const uint8_t* blk[1] = {tile_blocks(it, row_ok)};
+    if (it > 0) q4k_load<1>(first, blk, 0, nsb, lane >> 4);
     f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    q4k_tile<M, 1>(acc, blk, row_ok, nsb, lds, 1u, sx, lane);
+    q4k_tile<M, 1>(acc, blk, nsb, lds, 1u, sx, lane, first);
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[0][r] += __shfl_xor(acc[0][r], 32);
     const bool out_lane = (lane < 32) && row_ok;
@@ -222,44 +258,70 @@ __global__ void __launch_bounds__(256) k_q4k_reduce(QgQ4kArgs p) {
 }
 
 // ---------------------------------------------------------------- routing --
-// All threads of the workgroup select the top_k largest logits by rank: the
-// rank of expert e is the number of experts with a larger logit or an equal
-// logit and a lower index, so ranks are unique and expert e is selected iff
-// its rank < top_k (larger first, ties -> lower index).  lg[] is E floats of
-// LDS.  Results in LDS: sel[] / pw[] in rank order with the softmax weights
-// over the selected logits, asc[] / pasc[] the same sorted by expert index.
-// Every workgroup runs the same code on the same logits and gets the same
-// bytes.  Ends with a barrier.
-__device__ void route_topk(const float* logits, int E, int top_k, float* lg, int* sel, float* pw, int* asc,
-                           float* pasc) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) lg[e] = logits[e];
+// All threads of the workgroup select the top_k largest logits by rank.  Each
+// expert gets the 64-bit key argmax_key(logit, e) (larger logit first, then
+// lower index; keys are unique), and the rank of expert e is the number of
+// keys above its own, so expert e is selected iff its rank < top_k.  Results
+// in LDS: sel[] / pw[] in rank order with the softmax weights over the
+// selected logits, asc[] / pasc[] the same sorted by expert index.  Every
+// workgroup runs the same code on the same logits and gets the same bytes.
+// (NaN logits are unsupported; they still give a valid permutation.)
+//
+// route_load reads the logits into registers (up to four per thread, so
+// E <= 4 * blockDim; other loads can be issued while they are in flight),
+// route_store puts them and their keys into LDS (keys[] has two zero entries
+// past E), route_rank starts with a barrier, ranks and ends with a barrier.
+struct RouteIn {
+  float v[4];
+};
+
+__device__ __forceinline__ void route_load(const float* logits, int E, RouteIn& in) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) in.v[i] = logits[min((int)(threadIdx.x + i * blockDim.x), E - 1)];
+}
+
+__device__ __forceinline__ void route_store(const RouteIn& in, int E, float* lg, unsigned long long* keys) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = threadIdx.x + i * blockDim.x;
+    if (e < E) {
+      lg[e] = in.v[i];
+      keys[e] = argmax_key(in.v[i], (uint32_t)e);
+    }
+  }
+  if (threadIdx.x < 2) keys[E + threadIdx.x] = 0ull;  // below every key
+}
+
+__device__ void route_rank(int E, int top_k, const float* lg, const unsigned long long* keys, int* sel, float* pw,
+                           int* asc, float* pasc) {
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const float v = lg[e];
+    const unsigned long long ke = keys[e];
     int rank = 0;
-    for (int j = 0; j < E; ++j) {
-      const float w = lg[j];
-      rank += (w > v || (w == v && j < e)) ? 1 : 0;
+#pragma unroll 8
+    for (int j = 0; j < E; j += 2) {
+      const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(keys + j);
+      rank += (kk.x > ke ? 1 : 0) + (kk.y > ke ? 1 : 0);
     }
     if (rank < top_k) sel[rank] = e;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {  // one wave: softmax over the selected logits, then the ascending order
+    const int t = threadIdx.x;
     const float lmax = lg[sel[0]];
-    float z = 0.f;
-    for (int s = 0; s < top_k; ++s) {
-      pw[s] = expf(lg[sel[s]] - lmax);
-      z += pw[s];
+    const float ex = t < top_k ? expf(lg[sel[t]] - lmax) : 0.f;
+    float z = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+    if (t < top_k) {
+      const float w = ex / z;
+      pw[t] = w;
+      const int e = sel[t];
+      int pos = 0;  // position of expert e among the selected, by expert index
+      for (int s2 = 0; s2 < top_k; ++s2) pos += (sel[s2] < e) ? 1 : 0;
+      asc[pos] = e;
+      pasc[pos] = w;
     }
-    for (int s = 0; s < top_k; ++s) pw[s] = pw[s] / z;
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < top_k) {  // position of sel[t] among the selected, by expert index
-    const int e = sel[threadIdx.x];
-    int pos = 0;
-    for (int s = 0; s < top_k; ++s) pos += (sel[s] < e) ? 1 : 0;
-    asc[pos] = e;
-    pasc[pos] = pw[threadIdx.x];
   }
   __syncthreads();
 }
@@ -267,12 +329,17 @@ __device__ void route_topk(const float* logits, int E, int top_k, float* lg, int
 // ----------------------------------------------------------- MoE gate/up --
 // One workgroup per (selected expert slot, 16-row tile of I); its four waves
 // split the D/256 superblocks and add their partial sums in wave order.
+// Workgroup 0 also hands the routing to k_moe_down (workspace) and to the
+// caller (out_ids / out_w).  h is stored in bf16, the precision k_moe_down
+// consumes it in.
 constexpr int kMoeWaves = 4;
 
 __global__ void __launch_bounds__(256) k_moe_gateup(QgMoeArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int sel[64], asc[64];
-  __shared__ float pw[64], pasc[64], lg[1024];
+  __shared__ float pw[64], pasc[64];
+  __shared__ float lg[1024];
+  __shared__ __align__(16) unsigned long long keys[1026];
   __shared__ f32x4_t red[kMoeWaves][2][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tiles = (p.I + 15) / 16;
@@ -281,11 +348,20 @@ __global__ void __launch_bounds__(256) k_moe_gateup(QgMoeArgs p) {
   uint4* lds = reinterpret_cast<uint4*>(smem);  // [0] zero entry, then the staged token
   float* sx = reinterpret_cast<float*>(lds + 1 + nsb * 32);
 
+  RouteIn rin;
+  route_load(p.logits, p.E, rin);
   if (threadIdx.x == 0) lds[0] = make_uint4(0u, 0u, 0u, 0u);
   stage_q4k_x<1, uint16_t>(p.x, (size_t)p.D, p.D, lds + 1, sx, 0, nsb, threadIdx.x, blockDim.x);
-  route_topk(p.logits, p.E, p.top_k, lg, sel, pw, asc, pasc);
+  route_store(rin, p.E, lg, keys);
+  route_rank(p.E, p.top_k, lg, keys, sel, pw, asc, pasc);
+  if (blockIdx.x == 0 && (int)threadIdx.x < p.top_k) {
+    p.route_ids[threadIdx.x] = asc[threadIdx.x];
+    p.route_w[threadIdx.x] = pasc[threadIdx.x];
+    if (p.out_ids) p.out_ids[threadIdx.x] = sel[threadIdx.x];
+    if (p.out_w) p.out_w[threadIdx.x] = pw[threadIdx.x];
+  }
 
-  const int e = asc[slot];
+  const int e = min(max(asc[slot], 0), p.E - 1);  // always in range; clamped for memory safety
   const int row = tile * 16 + (lane & 15);
   const bool row_ok = row < p.I;
   // this wave's superblocks: [sb_lo, sb_hi)
@@ -294,10 +370,14 @@ __global__ void __launch_bounds__(256) k_moe_gateup(QgMoeArgs p) {
   const size_t expert_bytes = (size_t)2 * p.I * nsb * 144;
   const uint8_t* base = p.w_gu + (size_t)e * expert_bytes;
   const int r0 = row_ok ? row : 0;
-  const uint8_t* blk[2] = {base + ((size_t)r0 * nsb + sb_lo) * 144, base + ((size_t)(p.I + r0) * nsb + sb_lo) * 144};
+  const int sbc = min(sb_lo, nsb - 1);  // in-bounds base for a wave without superblocks
+  const uint8_t* blk[2] = {base + ((size_t)r0 * nsb + sbc) * 144, base + ((size_t)(p.I + r0) * nsb + sbc) * 144};
   f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  if (sb_hi > sb_lo)
-    q4k_tile<1, 2>(acc, blk, row_ok, sb_hi - sb_lo, lds, 1u + (uint32_t)sb_lo * 32u, sx + sb_lo * 64, lane);
+  if (sb_hi > sb_lo) {
+    Q4kBuf<2> first;
+    q4k_load<2>(first, blk, 0, sb_hi - sb_lo, lane >> 4);
+    q4k_tile<1, 2>(acc, blk, sb_hi - sb_lo, lds, 1u + (uint32_t)sb_lo * 32u, sx + sb_lo * 64, lane, first);
+  }
   red[wave][0][lane] = acc[0];
   red[wave][1][lane] = acc[1];
   __syncthreads();
@@ -309,20 +389,20 @@ __global__ void __launch_bounds__(256) k_moe_gateup(QgMoeArgs p) {
     }
     const float gv = g[0] + __shfl_xor(g[0], 32);  // M = 1: row 0 lives in element 0 of lanes 0..15
     const float uv = u[0] + __shfl_xor(u[0], 32);
-    if (lane < 16 && row_ok) p.h[(size_t)slot * p.I + row] = gv / (1.0f + __expf(-gv)) * uv;
+    if (lane < 16 && row_ok) p.h[(size_t)slot * p.I + row] = f32_to_bf16_bits(gv / (1.0f + __expf(-gv)) * uv);
   }
 }
 
 // ------------------------------------------------------------- MoE down --
 // One workgroup per 16-row tile of D.  Wave w handles the selected experts
-// w, w+W, ... (ascending expert order); each expert's sum is scaled by its
-// routing weight; the waves' totals are added in wave order.
+// w, w+W, ... (ascending expert order, as handed over by k_moe_gateup); each
+// expert's sum is scaled by its routing weight; the waves' totals are added
+// in wave order.  Each wave's first weight batch is in flight while the
+// experts' activations are staged.
 constexpr int kMoeDownWaves = 8;
 
 __global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int sel[64], asc[64];
-  __shared__ float pw[64], pasc[64], lg[1024];
   __shared__ f32x4_t red[kMoeDownWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
@@ -332,22 +412,32 @@ __global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
   uint4* lds = reinterpret_cast<uint4*>(smem);  // [0] zero entry, then one staged region per expert
   float* sx = reinterpret_cast<float*>(lds + 1 + xs_per * p.top_k);
 
-  if (threadIdx.x == 0) lds[0] = make_uint4(0u, 0u, 0u, 0u);
-  // the selected experts' activations, one row per expert slot, staged in one pass
-  stage_q4k_x<1, float>(p.h, (size_t)p.I, p.I, lds + 1, sx, 0, nsb, threadIdx.x, blockDim.x, p.top_k);
-  route_topk(p.logits, p.E, p.top_k, lg, sel, pw, asc, pasc);
-
   const int row = tile * 16 + (lane & 15);
   const bool row_ok = row < p.D;
   const int r0 = row_ok ? row : 0;
   const size_t expert_bytes = (size_t)p.D * nsb * 144;
+  auto expert_blocks = [&](int s) {
+    const int e = min(max(p.route_ids[s], 0), p.E - 1);
+    return p.w_down + (size_t)e * expert_bytes + (size_t)r0 * nsb * 144;
+  };
+  const int s0 = min(wave, p.top_k - 1);
+  const uint8_t* blk0[1] = {expert_blocks(s0)};
+  Q4kBuf<1> first;
+  q4k_load<1>(first, blk0, 0, nsb, lane >> 4);
+  __builtin_amdgcn_sched_barrier(0);
+
+  if (threadIdx.x == 0) lds[0] = make_uint4(0u, 0u, 0u, 0u);
+  // the selected experts' activations, one row per expert slot, staged in one pass
+  stage_q4k_x<1, uint16_t>(p.h, (size_t)p.I, p.I, lds + 1, sx, 0, nsb, threadIdx.x, blockDim.x, p.top_k);
+  __syncthreads();
+
   f32x4_t tot = {0.f, 0.f, 0.f, 0.f};
   for (int s = wave; s < p.top_k; s += W) {
-    const int e = asc[s];
-    const uint8_t* blk[1] = {p.w_down + (size_t)e * expert_bytes + (size_t)r0 * nsb * 144};
+    const uint8_t* blk[1] = {expert_blocks(s)};
+    if (s != wave) q4k_load<1>(first, blk, 0, nsb, lane >> 4);
     f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    q4k_tile<1, 1>(acc, blk, row_ok, nsb, lds, 1u + (uint32_t)(xs_per * s), sx + (size_t)s * nsb * 64, lane);
-    const float pe = pasc[s];
+    q4k_tile<1, 1>(acc, blk, nsb, lds, 1u + (uint32_t)(xs_per * s), sx + (size_t)s * nsb * 64, lane, first);
+    const float pe = p.route_w[s];
     tot[0] = fmaf(pe, acc[0][0], tot[0]);
     tot[1] = fmaf(pe, acc[0][1], tot[1]);
     tot[2] = fmaf(pe, acc[0][2], tot[2]);
@@ -360,10 +450,6 @@ __global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
     for (int w = 1; w < W; ++w) t += red[w][lane];
     const float yv = t[0] + __shfl_xor(t[0], 32);
     if (lane < 16 && row_ok) p.y[row] = f32_to_bf16_bits(yv);
-    if (blockIdx.x == 0 && lane < p.top_k) {
-      if (p.out_ids) p.out_ids[lane] = sel[lane];
-      if (p.out_w) p.out_w[lane] = pw[lane];
-    }
   }
 }
 
