@@ -34,6 +34,14 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["bit_quantized_decode_group_amd/csrc/common.h", "bit_quantized_decode_group_amd/csrc/affine4.hip",
                   "bit_quantized_decode_group_amd/csrc/q4k.hip", "bit_quantized_decode_group_amd/csrc/abi.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CALIB_BYTES = 384 << 20  # bytes read and written by the kernel that calibrates the HBM byte counters
+# kernels launched by each entry point (once per call) at M = 8
+ENTRY_KERNELS = {
+    "rmsnorm_gateup_swiglu": ["qg::k_affine<8, 1,", "qg::k_split_reduce<1>"],
+    "qgemv_affine4": ["qg::k_affine<8, 0,", "qg::k_split_reduce<0>"],
+    "moe_expert_qgemv": ["qg::k_moe_gateup", "qg::k_moe_down"],
+    "lmhead_argmax": ["qg::k_affine<8, 2,", "qg::k_lmhead_finalize"],
+}
 
 
 def log(*a):
@@ -56,11 +64,64 @@ def parse():
     ap.add_argument("--copies", type=int, default=5, help="weight copies rotated to defeat the Infinity Cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m1", action="store_true", help="skip the M=1 step (verify ratio)")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="short run for a rocprofv3 --pmc pass: a copy of CALIB_BYTES (counter calibration), "
+                         "then --steps M=8 steps; prints one JSON line")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn the counter CSVs of a FETCH_SIZE and a WRITE_SIZE --pmc pass into "
+                         "profiles/traffic.json (no GPU needed)")
     return ap.parse_args()
+
+
+def traffic_from_counters(fetch_csv, write_csv):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every kernel, each
+    scaled by the factor that makes the calibration copy read and write
+    CALIB_BYTES, summed over the kernels of each entry point."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {"source_hash": kernel_source_hash(), "calib_bytes": CALIB_BYTES, "kernels": {}}
+    avgs = {}
+    for which, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        vals = per_kernel(path, counter)
+        copies = [v * 1024 for n, l in vals.items() if "bitwise_not" in n for v in l]
+        if not copies:
+            raise SystemExit(f"bench.py --traffic: no calibration copy found in {path}")
+        factor = CALIB_BYTES / float(np.mean(copies))
+        out[f"{which}_factor"] = round(factor, 4)
+        avgs[which] = {n: float(np.mean(l)) * 1024 * factor for n, l in vals.items()}
+    for entry, kernels in ENTRY_KERNELS.items():
+        ent = {"kernels": {}}
+        total = 0.0
+        for pat in kernels:
+            names_ = [n for n in avgs["fetch"] if pat in n]
+            if not names_:
+                continue
+            n = names_[0]
+            f, w = avgs["fetch"].get(n, 0.0), avgs["write"].get(n, 0.0)
+            ent["kernels"][n] = {"fetch_bytes": round(f), "write_bytes": round(w)}
+            total += f + w
+        ent["bytes_per_launch"] = round(total)
+        out["kernels"][entry] = ent
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def main():
     args = parse()
+    if args.traffic:
+        traffic_from_counters(*args.traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus N with N > 1 is not supported "
               "(the projection has no multi-GPU path here)", file=sys.stderr)
@@ -145,7 +206,7 @@ def main():
         a = {
             "rmsnorm_gateup_swiglu": M * D * 2 + D * 2 + M * I * 2,
             "qgemv_affine4": M * I * 2 + M * D * 2,
-            "moe_expert_qgemv": Dm * 2 + E * 4 + 2 * top_k * Im * 4 + Dm * 2 + top_k * 8,
+            "moe_expert_qgemv": Dm * 2 + E * 4 + 2 * top_k * Im * 2 + Dm * 2 + top_k * 8,
             "lmhead_argmax": M * K5 * 2 + M * 4 * 2 + 4,
         }
         return {k: w[k] + a[k] for k in w}, w
@@ -196,6 +257,22 @@ def main():
         inst = float(np.mean([evs[i][0].elapsed_time(evs[i][4]) for i in range(steps)]))
         return ms_step, wall, per, inst, b
 
+    if args.pmc_pass:
+        # an elementwise kernel that reads and writes CALIB_BYTES (a plain
+        # device copy may go to the DMA engine and never show up as a kernel)
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        b = bufs(8)
+        for i in range(args.warmup + args.steps):
+            run_step(i, 8, b)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_pass": True, "calib_bytes": CALIB_BYTES, "steps": args.warmup + args.steps}), flush=True)
+        return
+
     log(f"[bench] timing M=8: warmup {args.warmup}, steps {args.steps}")
     ms8, wall8, per8, inst8, b8 = timed(8, args.steps, args.warmup)
     bytes8, wbytes = step_bytes(8)
@@ -212,19 +289,20 @@ def main():
         ms1, _, per1, _, _ = timed(1, s1, max(5, args.warmup // 2))
         log(f"[bench] M=1: {ms1 * 1e3:.1f} us/step; ratio {ms8 / ms1:.3f}")
 
-    # practical streaming ceiling (context): torch's reduction over 2 GiB, read once
-    big = torch.empty(2 ** 30, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    # context: the runtime's device-to-device copy of 1 GiB (bytes read + written)
+    src = torch.empty(2 ** 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
     for _ in range(2):
-        big.sum(dtype=torch.float32)
+        dst.copy_(src)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(5):
-        big.sum(dtype=torch.float32)
+        dst.copy_(src)
     e1.record()
     torch.cuda.synchronize()
-    stream_gbs = 5 * big.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del big
+    copy_gbs = 5 * 2 * src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
 
     kernels = {}
     for n in names:
@@ -276,7 +354,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "stream_ceiling_gb_s": round(stream_gbs, 1),
+        "d2d_copy_gb_s": round(copy_gbs, 1),
         "instrumented_ms_per_step": round(inst8, 5),
         "wall_s_timed": round(wall8, 4),
         "kernel_source_hash": kernel_source_hash(),
