@@ -340,8 +340,7 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
              ((uintptr_t)a.scales % vec == 0) && ((uintptr_t)a.biases % vec == 0);
   }
   const size_t lds = (size_t)a.cps * per + affine_lds_fixed();
-  // gate/up keeps 168 registers per lane (3 waves per SIMD), the others 128 (4)
-  a.rgroups = affine_rgroups(a.ntiles, a.S, lds, mode == QG_MODE_GATEUP ? 3 : 4, fill_pct);
+  a.rgroups = affine_rgroups(a.ntiles, a.S, lds, 4, fill_pct);  // 128 registers per lane: 4 waves per SIMD
   unsigned char* ws = nullptr;
   const bool partials = a.S > 1 || mode == QG_MODE_GATEUP;
   const size_t part_bytes = partials ? (size_t)a.S * a.M * a.N * 4 : 0;

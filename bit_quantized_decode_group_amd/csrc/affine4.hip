@@ -58,14 +58,16 @@ namespace qg {
 // (lane >> 3) & 1, lane >> 4) takes the eight values of row m at
 // k = 64g + 32h + 8t, so the eight lanes of a row write consecutive entries
 // and the group sum is a butterfly over the lanes of that row.  A round
-// gives each wave kStageGroups groups; all of a round's loads are issued
-// before any is used.
-constexpr int kStageGroups = 4;
+// gives each wave stage_groups(MODE) groups; all of a round's loads are
+// issued before any is used.  Gate/up also loads gamma, and its short K
+// slices need one round of two groups per wave, which keeps it within 128
+// registers per lane.
+__host__ __device__ constexpr int stage_groups(int mode) { return mode == QG_MODE_GATEUP ? 2 : 4; }
 
 template <int MODE>
 struct StageIn {
-  uint4 x[kStageGroups];
-  uint4 gm[MODE == QG_MODE_GATEUP ? kStageGroups : 1];
+  uint4 x[stage_groups(MODE)];
+  uint4 gm[MODE == QG_MODE_GATEUP ? stage_groups(MODE) : 1];
 };
 
 template <int M, int MODE>
@@ -73,7 +75,7 @@ __device__ __forceinline__ void stage_load(const QgAffineArgs& p, int c0, int nc
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
   const int m = min(lane & 7, M - 1), h = (lane >> 3) & 1, t = lane >> 4;
   const int glmax = 2 * nc - 1;
-  constexpr int SG = kStageGroups;
+  constexpr int SG = stage_groups(MODE);
 #pragma unroll
   for (int j = 0; j < SG; ++j) {
     // clamped in-bounds addresses; stage_store discards what it does not need
@@ -92,7 +94,7 @@ __device__ __forceinline__ void stage_store(const QgAffineArgs& p, uint4* xs, fl
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
   const int m = lane & 7, h = (lane >> 3) & 1, t = lane >> 4;
   const int ngl = 2 * nc;
-  constexpr int SG = kStageGroups;
+  constexpr int SG = stage_groups(MODE);
 #pragma unroll
   for (int j = 0; j < SG; ++j) {
     const int gl = (round * SG + j) * W + wave;
@@ -159,16 +161,17 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // around its loads.
 //
 // Each wave keeps a ring of R steps of weight loads in flight: the loads of
-// step st + R are issued as soon as step st has been computed.  Gate/up, with
-// two activation planes, gets 168 registers per lane (3 waves per SIMD), the
-// other modes 128 (4 waves per SIMD).
+// step st + R are issued as soon as step st has been computed.  The LM head's
+// waves stream several tiles each and keep two steps in flight; the split
+// projections' waves live for a few steps and run best with one (measured:
+// the extra registers and waits cost more than the overlap gains there).
+// Every mode keeps within 128 registers per lane (4 waves per SIMD).
 template <int M, int MODE, bool WIDE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == QG_MODE_GATEUP ? 3 : 4, 8)))
-k_affine(QgAffineArgs p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) k_affine(QgAffineArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int PL = (MODE == QG_MODE_GATEUP) ? 2 : 1;  // activation planes (hi, lo)
   constexpr int BATCH = 4;                              // chunks whose loads are issued together
-  constexpr int R = 2;                                  // steps of weight loads in flight per wave
+  constexpr int R = (MODE == QG_MODE_LMHEAD) ? 2 : 1;   // steps of weight loads in flight per wave
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
@@ -327,7 +330,7 @@ k_affine(QgAffineArgs p) {
     for (int i = threadIdx.x; i < W * 8; i += blockDim.x) wkeys[i] = 0ull;
   }
   stage_store<M, MODE>(p, xs, sx, ssq, c0, nc, 0, sin);
-  const int rounds = (2 * nc + kStageGroups * W - 1) / (kStageGroups * W);
+  const int rounds = (2 * nc + stage_groups(MODE) * W - 1) / (stage_groups(MODE) * W);
   for (int r = 1; r < rounds; ++r) {
     stage_load<M, MODE>(p, c0, nc, r, sin);
     stage_store<M, MODE>(p, xs, sx, ssq, c0, nc, r, sin);
@@ -406,7 +409,14 @@ __global__ void __launch_bounds__(256) k_split_reduce(QgAffineArgs p) {
   }
   if (MODE == QG_MODE_GATEUP) {
     float ss = 0.f;
-    for (int s2 = 0; s2 < p.S; ++s2) ss += p.ssq_part[(size_t)s2 * 8 + m];
+    for (int s0 = 0; s0 < p.S; s0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = p.ssq_part[(size_t)min(s0 + j, p.S - 1) * 8 + m];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < p.S) ss += v[j];
+    }
     const float ri = 1.0f / sqrtf(ss / (float)p.K + p.eps);
     p.y[idx] = f32_to_bf16_bits(silu_mul(t[0] * ri, t[NB - 1] * ri));
   } else {
@@ -419,8 +429,10 @@ __global__ void __launch_bounds__(256) k_split_reduce(QgAffineArgs p) {
 // workgroup; each thread reads whole 64-byte key records of several workgroups.
 __global__ void __launch_bounds__(256) k_lmhead_finalize(QgAffineArgs p, int nwg) {
   __shared__ unsigned long long red[4][8];
-  __shared__ int s_ids[8];
+  __shared__ int s_ids[8], s_draft[8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the draft ids are read up front, in parallel with the keys
+  if ((int)threadIdx.x < p.M) s_draft[threadIdx.x] = p.draft ? p.draft[threadIdx.x] : -1;
   unsigned long long v[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) v[m] = 0ull;
@@ -458,7 +470,7 @@ __global__ void __launch_bounds__(256) k_lmhead_finalize(QgAffineArgs p, int nwg
   if (threadIdx.x == 0 && p.accepted) {
     int a = 0;
     if (p.draft)
-      while (a < p.M && s_ids[a] == p.draft[a]) ++a;
+      while (a < p.M && s_ids[a] == s_draft[a]) ++a;
     *p.accepted = a;
   }
 }
