@@ -68,16 +68,17 @@ constexpr int kTargetWaves = 2048;         // enough (tile, slice) pieces to cov
 constexpr int kMaxWavesInFlight = 4096;    // beyond this, waves stream several tiles
 
 // LDS of the affine kernels per 128-k chunk of the staged slice (operand
-// entries for PL activation planes, group sums, sums of x^2) and fixed (zero
-// entry, per-wave argmax keys).
+// entries for PL activation planes, group sums, sums of x^2) and fixed (the
+// zero region read by empty operand slots, 64*PL*M entries of 16 bytes, and
+// the per-wave argmax keys).
 size_t affine_lds_per_chunk(int M, int PL) { return (size_t)256 * M * PL + 64 + (size_t)8 * M; }
-size_t affine_lds_fixed() { return 16 + (size_t)kWaves * 64; }
+size_t affine_lds_fixed(int M, int PL) { return (size_t)1024 * PL * M + (size_t)kWaves * 64; }
 size_t q4k_lds_per_sb(int M) { return (size_t)512 * M + 256; }
 
 // The LM-head mode stages all of K (no split): ceil(K/128) chunks must fit.
 bool fits_lds_unsplit(int M, int K) {
   const size_t nchunks = ((size_t)K / 64 + 1) / 2;
-  return nchunks * affine_lds_per_chunk(M, 1) + affine_lds_fixed() <= kLdsBudget;
+  return nchunks * affine_lds_per_chunk(M, 1) + affine_lds_fixed(M, 1) <= kLdsBudget;
 }
 
 struct Plan {
@@ -312,7 +313,7 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
   a.waves = kWaves;
   const int PL = (mode == QG_MODE_GATEUP) ? 2 : 1;
   const size_t per = affine_lds_per_chunk(a.M, PL);
-  const int cps_max = (int)std::min<size_t>((size_t)a.nchunks, (kLdsBudget - affine_lds_fixed()) / per);
+  const int cps_max = (int)std::min<size_t>((size_t)a.nchunks, (kLdsBudget - affine_lds_fixed(a.M, PL)) / per);
   const bool allow_split = (mode != QG_MODE_LMHEAD);
   if (!allow_split && a.nchunks > cps_max)
     return fail(QG_EUNSUPPORTED, "%s: K=%d needs a split of K this mode or size lacks", fn, a.K);
@@ -339,7 +340,7 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
     a.wide = (a.G % (2 * batch) == 0) && (a.S == 1 || a.cps % batch == 0) &&
              ((uintptr_t)a.scales % vec == 0) && ((uintptr_t)a.biases % vec == 0);
   }
-  const size_t lds = (size_t)a.cps * per + affine_lds_fixed();
+  const size_t lds = (size_t)a.cps * per + affine_lds_fixed(a.M, PL);
   a.rgroups = affine_rgroups(a.ntiles, a.S, lds, 4, fill_pct);  // 128 registers per lane: 4 waves per SIMD
   unsigned char* ws = nullptr;
   const bool partials = a.S > 1 || mode == QG_MODE_GATEUP;

@@ -44,9 +44,8 @@
 
 namespace qg {
 
-// Activation staging: X[:, slice] -> LDS in MFMA operand order.
-// xs[0] is a zero entry (read by lanes whose operand slots are empty); entry
-// 1 + (((c*4 + t)*4 + kb)*PL + plane)*M + m holds, for activation row m,
+// Activation staging: X[:, slice] -> LDS in MFMA operand order.  Entry
+// (((c*4 + t)*4 + kb)*PL + plane)*M + m of xs holds, for activation row m,
 // the eight values at k = 128c + 32kb + 8t + nib(s), s = 0..7 with
 // nib(s) = s/2 + 4*(s%2) (the code order unpack_affine_word produces).
 // sx[(2c + par)*8 + m] holds the fp32 sum of the 64 staged values (all planes)
@@ -132,7 +131,7 @@ __device__ __forceinline__ void stage_store(const QgAffineArgs& p, uint4* xs, fl
       // operand dword e holds values e and e + 4
       const uint4 e = make_uint4((v[pl][0] & 0xFFFFu) | (v[pl][2] << 16), (v[pl][0] >> 16) | (v[pl][2] & 0xFFFF0000u),
                                  (v[pl][1] & 0xFFFFu) | (v[pl][3] << 16), (v[pl][1] >> 16) | (v[pl][3] & 0xFFFF0000u));
-      if (m < M) xs[1 + (((c * 4 + t) * 4 + kb) * PL + pl) * M + m] = e;
+      if (m < M) xs[(((c * 4 + t) * 4 + kb) * PL + pl) * M + m] = e;
     }
     // sum over the eight lanes of row m (every lane ends with the same value)
 #pragma unroll
@@ -186,8 +185,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   const int nbt = (nc + BATCH - 1) / BATCH;  // batches per tile
   const int nsteps = ntw * nbt;              // this wave's (tile, batch) steps
 
-  uint4* xs = reinterpret_cast<uint4*>(smem);
-  float* sx = reinterpret_cast<float*>(xs + 1 + nc * 16 * M * PL);
+  // LDS: a zero region of ZR entries, then the staged slice (xs), its group
+  // sums (sx), sums of squares (ssq) and the LM head's per-wave keys.  Lanes
+  // whose operand slots carry the other scale group (or a padding row) read
+  // the zero region: one select per step instead of a mask per read, and
+  // every read of a step is an immediate offset from one base.
+  constexpr int ZR = 64 * PL * M;  // spans the operand offsets of one step
+  uint4* zr = reinterpret_cast<uint4*>(smem);
+  uint4* xs = zr + ZR;
+  float* sx = reinterpret_cast<float*>(xs + nc * 16 * M * PL);
   float* ssq = sx + nc * 16;  // GATEUP: [M][2nc]
   unsigned long long* wkeys = reinterpret_cast<unsigned long long*>(ssq + M * 2 * nc);  // LMHEAD: [W][8]
 
@@ -196,14 +202,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   const int half = lane >> 5;  // scale group parity of this lane (B and C layouts agree)
   const int rho = lane & 15;
   const bool a_act = ((rho >> 3) == (kb >> 1)) && ((rho & 7) < M);
-  // operand entry of this lane for (chunk cl, step t, plane pl): 1 + a_lane + (cl*16 + t*4)*PL*M + pl*M,
-  // or the zero entry for lanes whose slots carry the other group / a padding row
-  const uint32_t a_lane = 1u + (uint32_t)(kb * PL * M + (rho & 7));
-  const uint32_t a_mask = a_act ? 0xFFFFFFFFu : 0u;
+  // operand entry of this lane for (chunk cl, step t, plane pl): a_lane + (cl*16 + t*4)*PL*M + pl*M of xs
+  const uint32_t a_lane = (uint32_t)(ZR + kb * PL * M + (rho & 7));
   const float* sx_base = sx + half * 8 + 4 * (kb & 1);
   const size_t wrow_words = (size_t)p.K / 8;
   const uint32_t wmax = (uint32_t)(wrow_words - 4);  // last in-row 16-byte load
   const int mbase = 4 * (lane >> 4);                 // activation row of C element 0 (lanes < 32)
+  const UnpackK uk = unpack_constants();
 
   // ---- loads of one (tile, batch) step: unconditional, at clamped in-bounds addresses.
   // sw / bw dword u holds the bf16 scales / biases of groups 2(c0+cb+u) (low half) and
@@ -280,6 +285,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     const int ti = st / nbt;
     const int bi = st - ti * nbt;
     const int cb = bi * BATCH;
+    const uint32_t a_base = a_act ? a_lane + (uint32_t)(cb * 16 * PL * M) : 0u;  // entry in zr[]
     f32x4_t C[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) C[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -289,10 +295,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
       for (int u = 0; u < BATCH; ++u) {
         if (WIDE || cb + u < nc) {
           const uint32_t w = t == 0 ? bf.q[u].x : t == 1 ? bf.q[u].y : t == 2 ? bf.q[u].z : bf.q[u].w;
-          const uint4 bw = unpack_affine_word(w);
+          const uint4 bw = unpack_affine_word(w, uk);
 #pragma unroll
           for (int pl = 0; pl < PL; ++pl) {
-            const uint4 a = xs[(a_lane + (uint32_t)(((cb + u) * 16 + t * 4) * PL * M + pl * M)) & a_mask];
+            const uint4 a = zr[a_base + (uint32_t)((u * 16 + t * 4) * PL * M + pl * M)];
             C[u] = mfma_bf16(a, bw, C[u]);
           }
         }
@@ -325,7 +331,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
   for (int r = 0; r < R; ++r) load_step(ring[r], min(r, last));
   __builtin_amdgcn_sched_barrier(0);
-  if (threadIdx.x == 0) xs[0] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = threadIdx.x; i < ZR; i += blockDim.x) zr[i] = make_uint4(0u, 0u, 0u, 0u);
   if (MODE == QG_MODE_LMHEAD) {
     for (int i = threadIdx.x; i < W * 8; i += blockDim.x) wkeys[i] = 0ull;
   }

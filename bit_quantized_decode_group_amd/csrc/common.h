@@ -47,25 +47,39 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// The unpack constants, materialised once in vector registers: an and-or of
+// three vector operands is one instruction (v_and_or_b32), while with both
+// constants as literals or scalars it splits into two (a VOP3 instruction
+// reads at most one scalar or literal operand).  Non-volatile, so the
+// compiler hoists it.
+struct UnpackK {
+  uint32_t mask, one28;
+};
+__device__ __forceinline__ UnpackK unpack_constants() {
+  UnpackK k;
+  asm("v_mov_b32 %0, %1" : "=v"(k.mask) : "i"(0x000F000F));
+  asm("v_mov_b32 %0, %1" : "=v"(k.one28) : "i"(0x43004300));
+  return k;
+}
+
 // Eight affine codes of one little-endian word (code i at bits 4i..4i+3) as
-// eight bf16 values 128+q.  Element 2j (low half of dword j) is code j and
-// element 2j+1 (high half) is code j+4, so MFMA k-slot s holds code
-// s/2 + 4*(s%2).
-__device__ __forceinline__ uint4 unpack_affine_word(uint32_t w) {
-  const uint32_t m = 0x000F000Fu, one28 = 0x43004300u;
+// eight bf16 values 128+q (0x4300 | q).  Element 2j (low half of dword j) is
+// code j and element 2j+1 (high half) is code j+4, so MFMA k-slot s holds
+// code s/2 + 4*(s%2).
+__device__ __forceinline__ uint4 unpack_affine_word(uint32_t w, const UnpackK& k) {
   uint4 r;
-  r.x = (w & m) | one28;
-  r.y = ((w >> 4) & m) | one28;
-  r.z = ((w >> 8) & m) | one28;
-  r.w = ((w >> 12) & m) | one28;
+  r.x = (w & k.mask) | k.one28;
+  r.y = ((w >> 4) & k.mask) | k.one28;
+  r.z = ((w >> 8) & k.mask) | k.one28;
+  r.w = ((w >> 12) & k.mask) | k.one28;
   return r;
 }
 
 // Eight Q4_K codes from eight consecutive code bytes (w0 = bytes 0..3, w1 =
 // bytes 4..7): the low nibbles when sh == 0, the high nibbles when sh == 4.
 // Slot s holds the code of byte {0,2,1,3,4,6,5,7}[s].
-__device__ __forceinline__ uint4 unpack_q4k_bytes(uint32_t w0, uint32_t w1, uint32_t sh) {
-  const uint32_t m = 0x000F000Fu, one28 = 0x43004300u;
+__device__ __forceinline__ uint4 unpack_q4k_bytes(uint32_t w0, uint32_t w1, uint32_t sh, const UnpackK& k) {
+  const uint32_t m = k.mask, one28 = k.one28;
   uint4 r;
   r.x = ((w0 >> sh) & m) | one28;
   r.y = ((w0 >> (sh + 8u)) & m) | one28;

@@ -143,6 +143,7 @@ __device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* cons
   const uint32_t sh0 = 4u * (uint32_t)((kb >> 1) ^ 0), sh1 = 4u * (uint32_t)((kb >> 1) ^ 1);
   const uint32_t a_lane = region + (uint32_t)(kb * M + (rho & 7));
   const float* sx_base = sx + half * 8 + 4 * (kb & 1);
+  const UnpackK uk = unpack_constants();
 
   auto compute = [&](const Q4kBuf<NB>& cur, int sb) {
 #pragma unroll
@@ -167,8 +168,8 @@ __device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* cons
           const uint4 a0 = lds[ai & mask0];
           const uint4 a1 = lds[(ai + 4 * M) & mask1];
           f32x4_t C = {0.f, 0.f, 0.f, 0.f};
-          C = mfma_bf16(a0, unpack_q4k_bytes(cur.cq[b][u][c].x, cur.cq[b][u][c].y, sh0), C);
-          C = mfma_bf16(a1, unpack_q4k_bytes(cur.cq[b][u][c].x, cur.cq[b][u][c].y, sh1), C);
+          C = mfma_bf16(a0, unpack_q4k_bytes(cur.cq[b][u][c].x, cur.cq[b][u][c].y, sh0, uk), C);
+          C = mfma_bf16(a1, unpack_q4k_bytes(cur.cq[b][u][c].x, cur.cq[b][u][c].y, sh1, uk), C);
           const float4 sxv = *reinterpret_cast<const float4*>(sx_base + cc * 16);
           const float a = d * (float)sc[c];                 // exact in fp32
           const float bt = fmaf(dmin, (float)mn[c], 128.0f * a);

@@ -141,8 +141,8 @@ qg_status moe_expert_qgemv(const uint16_t* x, const float* router_logits,
  *   x bf16 [M][K]; codes uint32 [V][K/8]; scales, biases bf16 [V][K/64];
  *   logits fp32 [M][V] (nullable); ids int32 [M]; draft int32 [M] (nullable);
  *   accepted int32 [1] (nullable).   1 <= M <= 8; V >= 1; K % 64 == 0.  All
- *   of x is staged on chip: ceil(K/128) * (264*M + 64) + 272 <= 163840 bytes
- *   (M = 8: K <= 9600; M = 1: K <= 63744), else QG_EUNSUPPORTED.
+ *   of x is staged on chip: ceil(K/128) * (264*M + 64) + 1024*M + 256 <= 163840
+ *   bytes (M = 8: K <= 9088; M = 1: K <= 63360), else QG_EUNSUPPORTED.
  */
 qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes,
                         const uint16_t* scales, const uint16_t* biases,

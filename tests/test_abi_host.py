@@ -158,7 +158,7 @@ def test_lmhead_checks(lib):
     bad[7] = A[5]  # accepted over ids
     assert c(*bad) == ops.QG_EALIAS
     bad = list(ok)
-    bad[10] = 9600  # largest K whose 8 staged rows fit in 160 KB of LDS
+    bad[10] = 9088  # largest K whose 8 staged rows fit in 160 KB of LDS
     assert c(*bad) == ops.QG_OK
-    bad[10] = 9664
+    bad[10] = 9152
     assert c(*bad) == ops.QG_EUNSUPPORTED
