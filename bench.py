@@ -64,6 +64,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=5, help="weight copies rotated to defeat the Infinity Cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m1", action="store_true", help="skip the M=1 step (verify ratio)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration context timings")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="short run for a rocprofv3 --pmc pass: a copy of CALIB_BYTES (counter calibration), "
                          "then --steps M=8 steps; prints one JSON line")
@@ -233,20 +234,30 @@ def main():
         if ev is not None:
             ev[4].record()
 
+    spread = {}
+
     def timed(M, steps, warmup):
         b = bufs(M)
         for i in range(warmup):
             run_step(i, M, b)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # K steps timed start to end; events at five sub-batch boundaries (no
+        # synchronisation between them) give the spread of the per-step time
+        nsub = 5 if steps >= 5 else 1
+        cut = [round(steps * j / nsub) for j in range(nsub + 1)]
+        evb = [torch.cuda.Event(enable_timing=True) for _ in range(nsub + 1)]
         w0 = time.perf_counter()
-        e0.record()
-        for i in range(steps):
-            run_step(warmup + i, M, b)
-        e1.record()
+        evb[0].record()
+        for j in range(nsub):
+            for i in range(cut[j], cut[j + 1]):
+                run_step(warmup + i, M, b)
+            evb[j + 1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
-        ms_step = e0.elapsed_time(e1) / steps
+        ms_step = evb[0].elapsed_time(evb[nsub]) / steps
+        sub = [evb[j].elapsed_time(evb[j + 1]) / (cut[j + 1] - cut[j]) for j in range(nsub)]
+        spread[M] = {"median_ms": round(float(np.median(sub)), 5), "p10_ms": round(float(np.percentile(sub, 10)), 5),
+                     "p90_ms": round(float(np.percentile(sub, 90)), 5), "sub_batches": nsub}
         # per-kernel durations: the same steps again with events around each launch
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
         for i in range(steps):
@@ -304,6 +315,8 @@ def main():
     copy_gbs = 5 * 2 * src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
 
+    cfg = None if args.no_configs else config_timings(torch, ops, synth, to_dev, dev)
+
     kernels = {}
     for n in names:
         k = {"us_m8": round(per8[n], 2), "bytes_m8": bytes8[n], "gb_s_m8": round(bytes8[n] / (per8[n] * 1e-6) / 1e9, 1),
@@ -355,11 +368,97 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "d2d_copy_gb_s": round(copy_gbs, 1),
+        "step_spread": {f"M{m}": v for m, v in spread.items()},
+        "configs_context": cfg,
         "instrumented_ms_per_step": round(inst8, 5),
         "wall_s_timed": round(wall8, 4),
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(out), flush=True)
+
+
+def config_timings(torch, ops, synth, to_dev, dev):
+    """Context (not the bench value): per-call times of the smaller workloads
+    and variants, each rotating enough weight copies (>= 512 MB) that the
+    Infinity Cache cannot serve a call; HIP events around R back-to-back calls."""
+    def per_call(fn, n_copies, reps):
+        for i in range(min(reps, 20)):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    out = {}
+    # single projection X[M,1024] x W[3072,1024] affine-4 (M = 1 and 8)
+    sp = synth.single_projection(M=8)
+    w = {k: to_dev(sp[k], "u32" if k == "codes" else "bf16") for k in ("codes", "scales", "biases")}
+    nb = int(sp["codes"].nbytes + sp["scales"].nbytes + sp["biases"].nbytes)
+    n = max(2, (512 << 20) // nb + 1)
+    cps = [w] + [{k: v.clone() for k, v in w.items()} for _ in range(n - 1)]
+    x8 = to_dev(sp["x"], "bf16")
+    res = {}
+    for M in (1, 8):
+        xm = x8[:M].contiguous()
+        ym = torch.empty((M, sp["N"]), dtype=torch.bfloat16, device=dev)
+        us = per_call(lambda i: ops.qgemv_affine4(xm, cps[i % n]["codes"], cps[i % n]["scales"], cps[i % n]["biases"],
+                                                  y=ym), n, 3 * n)
+        b = nb + M * sp["K"] * 2 + M * sp["N"] * 2
+        res[f"M{M}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
+    res["ratio_m8_m1"] = round(res["M8"]["us"] / res["M1"]["us"], 3)
+    out["projection_3072x1024"] = res
+    del cps
+    # MLP block D=1024, I=3072 (RMSNorm -> gate/up -> SwiGLU -> down), M = 1 and 8
+    mb = synth.mlp_block(M=8)
+    keys = {"codes_gu": "u32", "scales_gu": "bf16", "biases_gu": "bf16", "codes_d": "u32", "scales_d": "bf16",
+            "biases_d": "bf16"}
+    w = {k: to_dev(mb[k], t) for k, t in keys.items()}
+    nb = int(sum(mb[k].nbytes for k in keys))
+    n = max(2, (512 << 20) // nb + 1)
+    cps = [w] + [{k: v.clone() for k, v in w.items()} for _ in range(n - 1)]
+    x8, gam = to_dev(mb["x"], "bf16"), to_dev(mb["gamma"], "bf16")
+    res = {}
+    for M in (1, 8):
+        xm = x8[:M].contiguous()
+        hm = torch.empty((M, mb["I"]), dtype=torch.bfloat16, device=dev)
+        ym = torch.empty((M, mb["D"]), dtype=torch.bfloat16, device=dev)
+
+        def blk(i):
+            c = cps[i % n]
+            ops.rmsnorm_gateup_swiglu(xm, gam, mb["eps"], c["codes_gu"], c["scales_gu"], c["biases_gu"], h=hm)
+            ops.qgemv_affine4(hm, c["codes_d"], c["scales_d"], c["biases_d"], y=ym)
+        us = per_call(blk, n, 3 * n)
+        b = nb + M * mb["D"] * 2 * 2 + 2 * M * mb["I"] * 2 + mb["D"] * 2
+        res[f"M{M}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
+    res["ratio_m8_m1"] = round(res["M8"]["us"] / res["M1"]["us"], 3)
+    out["mlp_block_1024x3072"] = res
+    del cps
+    # LM head variants: M = 4, and M = 8 with the fp32 logits stored
+    lm = synth.lm_head(M=8)
+    w = {k: to_dev(lm[k], "u32" if k == "codes" else "bf16") for k in ("codes", "scales", "biases")}
+    nb = int(lm["codes"].nbytes + lm["scales"].nbytes + lm["biases"].nbytes)
+    n = max(2, (512 << 20) // nb + 1)
+    cps = [w] + [{k: v.clone() for k, v in w.items()} for _ in range(n - 1)]
+    x8, draft = to_dev(lm["x"], "bf16"), to_dev(lm["draft"], "i32")
+    ids = torch.empty(8, dtype=torch.int32, device=dev)
+    acc = torch.empty(1, dtype=torch.int32, device=dev)
+    logits = torch.empty((8, lm["V"]), dtype=torch.float32, device=dev)
+    res = {}
+    for M, keep in ((4, False), (8, True)):
+        xm = x8[:M].contiguous()
+        us = per_call(lambda i: ops.lmhead_argmax(xm, cps[i % n]["codes"], cps[i % n]["scales"], cps[i % n]["biases"],
+                                                  draft=draft[:M].contiguous(), ids=ids[:M], accepted=acc,
+                                                  logits=logits[:M] if keep else None), n, 6 * n)
+        b = nb + M * lm["K"] * 2 + M * 8 + (M * lm["V"] * 4 if keep else 0)
+        res[f"M{M}" + ("_with_logits" if keep else "")] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
+    out["lm_head_151936x1024"] = res
+    del cps
+    log("[bench] context: " + json.dumps(out))
+    return out
 
 
 def cpu_baseline(vb, lm, moe, step_bytes):
