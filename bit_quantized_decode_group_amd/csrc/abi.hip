@@ -66,6 +66,7 @@ constexpr size_t kQ4kLdsBudget = 65536;    // staged-slice bound of the Q4_K pro
 constexpr int kWaves = 4;                  // waves per workgroup of the projection kernels
 constexpr int kTargetWaves = 2048;         // enough (tile, slice) pieces to cover HBM latency on 256 CUs
 constexpr int kMaxWavesInFlight = 4096;    // beyond this, waves stream several tiles
+constexpr int kMaxUnsplitSteps = 4;        // batches of loads per tile a plain projection takes unsplit
 
 // LDS of the affine kernels per 128-k chunk of the staged slice (operand
 // entries for PL activation planes, group sums, sums of x^2) and fixed (the
@@ -314,9 +315,16 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
   const int PL = (mode == QG_MODE_GATEUP) ? 2 : 1;
   const size_t per = affine_lds_per_chunk(a.M, PL);
   const int cps_max = (int)std::min<size_t>((size_t)a.nchunks, (kLdsBudget - affine_lds_fixed(a.M, PL)) / per);
-  const bool allow_split = (mode != QG_MODE_LMHEAD);
-  if (!allow_split && a.nchunks > cps_max)
+  const bool split_ok = (mode != QG_MODE_LMHEAD);
+  if (!split_ok && a.nchunks > cps_max)
     return fail(QG_EUNSUPPORTED, "%s: K=%d needs a split of K this mode or size lacks", fn, a.K);
+  // A split costs a follow-up kernel (a few microseconds); a plain projection
+  // is split only when a tile has more than kMaxUnsplitSteps batches of
+  // loads (or the slice would not fit on chip).  Gate/up always ends in the
+  // pairing reduce, so it may always split.
+  const int steps_per_tile = (a.nchunks + 3) / 4;
+  const bool allow_split = split_ok && (mode == QG_MODE_GATEUP || steps_per_tile > kMaxUnsplitSteps ||
+                                        a.nchunks > cps_max);
   // Pieces to aim for and share of the resident workgroup slots to fill, per
   // mode (measured on the decode shapes): gate/up, whose staging is the
   // costliest, prefers many short slices on every slot; the weight-streaming
