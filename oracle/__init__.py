@@ -66,10 +66,11 @@ def _load():
         lib.oracle_mlp_block.argtypes = [P, P, D, P, P, P, P, P, P, I, I64, I64, P]
         lib.oracle_moe.argtypes = [P, P, I, P, P, I, I64, I64, P, P, P]
         lib.oracle_lmhead.argtypes = [P, P, P, P, I, I64, I64, P, P, P, P, P]
+        lib.oracle_lmhead_topk.argtypes = [P, P, P, P, I, I64, I64, I, P, P]
         for name in ("oracle_dequant_affine4", "oracle_dequant_q4k", "oracle_qgemv_affine4",
                      "oracle_qgemv_affine4_f64x", "oracle_qgemv_q4k", "oracle_rmsnorm",
                      "oracle_rmsnorm_gateup_swiglu", "oracle_mlp_block", "oracle_moe",
-                     "oracle_lmhead"):
+                     "oracle_lmhead", "oracle_lmhead_topk"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -253,3 +254,20 @@ def lmhead(x, codes, scales, biases, draft=None, want_logits=True):
                                  ids.ctypes.data_as(ctypes.c_void_p), gap.ctypes.data_as(ctypes.c_void_p),
                                  pd, acc.ctypes.data_as(ctypes.c_void_p)), "lmhead")
     return logits, ids, gap, int(acc[0])
+
+
+# -------------------------------------------------------------------- O9 --
+def lmhead_topk(x, codes, scales, biases, k):
+    """Returns (ids int32 [M,k], vals fp64 [M,k]): the k largest logits of each
+    row, larger first, equal logits by lower index, NaN above every number."""
+    x, px = _c(x, np.uint16)
+    codes, pc = _c(codes, np.uint32)
+    _, ps = _c(scales, np.uint16)
+    _, pb = _c(biases, np.uint16)
+    M, K = x.shape
+    V = codes.shape[0]
+    ids = np.empty((M, k), dtype=np.int32)
+    vals = np.empty((M, k), dtype=np.float64)
+    _check(_load().oracle_lmhead_topk(px, pc, ps, pb, M, V, K, int(k), ids.ctypes.data_as(ctypes.c_void_p),
+                                      vals.ctypes.data_as(ctypes.c_void_p)), "lmhead_topk")
+    return ids, vals

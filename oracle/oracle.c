@@ -404,3 +404,54 @@ int oracle_lmhead(const uint16_t* x, const uint32_t* codes,
   free(isnan_best);
   return rc;
 }
+
+/* O9: all logits of the row in fp64 (O8's dot product), then k rounds of
+ * "the best not yet chosen" under the order stated in oracle.h. */
+static int topk_beats(double a, int64_t ia, double b, int64_t ib) {
+  /* does (a, ia) come before (b, ib)? */
+  const int na = isnan(a), nb = isnan(b);
+  if (na || nb) {
+    if (na && nb) return ia < ib;
+    return na;
+  }
+  if (a != b) return a > b;
+  return ia < ib;
+}
+
+int oracle_lmhead_topk(const uint16_t* x, const uint32_t* codes,
+                       const uint16_t* scales, const uint16_t* biases, int M,
+                       int64_t V, int64_t K, int k, int32_t* ids,
+                       double* vals) {
+  if (!x || !codes || !scales || !biases || !ids || M < 1 || V < 1 || K <= 0 ||
+      k < 1 || k > V)
+    return -1;
+  double* xd = decode_bf16_rows(x, M, K);
+  double* wrow = (double*)malloc(sizeof(double) * (size_t)K);
+  double* L = (double*)malloc(sizeof(double) * (size_t)M * (size_t)V);
+  char* taken = (char*)malloc((size_t)V);
+  int rc = (xd && wrow && L && taken) ? 0 : -1;
+  for (int64_t v = 0; v < V && rc == 0; ++v) {
+    rc = oracle_dequant_affine4(codes, scales, biases, V, K, v, 1, wrow);
+    if (rc) break;
+    for (int m = 0; m < M; ++m) L[(int64_t)m * V + v] = dot_asc(xd + (int64_t)m * K, wrow, K);
+  }
+  for (int m = 0; m < M && rc == 0; ++m) {
+    const double* row = L + (int64_t)m * V;
+    memset(taken, 0, (size_t)V);
+    for (int j = 0; j < k; ++j) {
+      int64_t best = -1;
+      for (int64_t v = 0; v < V; ++v) {
+        if (taken[v]) continue;
+        if (best < 0 || topk_beats(row[v], v, row[best], best)) best = v;
+      }
+      taken[best] = 1;
+      ids[(int64_t)m * k + j] = (int32_t)best;
+      if (vals) vals[(int64_t)m * k + j] = row[best];
+    }
+  }
+  free(xd);
+  free(wrow);
+  free(L);
+  free(taken);
+  return rc;
+}

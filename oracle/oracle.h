@@ -118,6 +118,17 @@ int oracle_lmhead(const uint16_t* x, const uint32_t* codes,
                   int64_t V, int64_t K, double* logits, int32_t* ids,
                   double* gap, const int32_t* draft, int32_t* accepted);
 
+/* O9: top-k readout (uzu page, "내부 동작 3: DFlash + Weaver 트리형 투기
+ * 디코딩": every preview row yields a candidate pool of its top tokens).
+ * For each row m, ids[m][0..k-1] are the indices of the k largest logits
+ * x[m] . w[v] in order: larger logit first, equal logits by lower index, a
+ * NaN logit above every number (NaNs by lower index).  vals[m][j]
+ * (nullable) is the logit of ids[m][j].  1 <= k <= V. */
+int oracle_lmhead_topk(const uint16_t* x, const uint32_t* codes,
+                       const uint16_t* scales, const uint16_t* biases, int M,
+                       int64_t V, int64_t K, int k, int32_t* ids,
+                       double* vals);
+
 #ifdef __cplusplus
 }
 #endif

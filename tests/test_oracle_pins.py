@@ -499,6 +499,42 @@ def test_lmhead_accepted_prefix():
     assert np.array_equal(logits, oracle.qgemv_affine4(d["x"], d["codes"], d["scales"], d["biases"]))
 
 
+def test_lmhead_topk_planted_order_ties_nan_and_signed_zero():
+    V, K = 64, 64
+    x = np.full((1, K), 0x3F80, np.uint16)  # ones: logit = 64 * bias
+    bias = np.full(V, 0x3F00, np.uint16)  # 0.5
+    bias[40] = bias[10] = 0x3F80  # 1.0, tied
+    bias[3] = bias[60] = 0x3F40  # 0.75, tied
+    bias[20] = 0x3F20  # 0.625
+    ids, vals = oracle.lmhead_topk(x, *_lm_bias_rows(V, K, bias), k=6)
+    assert ids[0].tolist() == [10, 40, 3, 60, 20, 0]
+    assert vals[0].tolist() == [64.0, 64.0, 48.0, 48.0, 40.0, 32.0]
+    bias[55] = bias[50] = 0x7FC0  # NaN logits come first, by index
+    ids, _ = oracle.lmhead_topk(x, *_lm_bias_rows(V, K, bias), k=3)
+    assert ids[0].tolist() == [50, 55, 10]
+    neg = np.full(V, 0xBF00, np.uint16)  # -0.5 everywhere ...
+    neg[5] = 0x8000  # ... except -0 at 5 and +0 at 2: equal logits, lower index first
+    neg[2] = 0x0000
+    ids, vals = oracle.lmhead_topk(x, *_lm_bias_rows(V, K, neg), k=3)
+    assert ids[0].tolist() == [2, 5, 0] and vals[0, 0] == 0.0 and vals[0, 2] == -32.0
+
+
+def test_lmhead_topk_matches_a_full_sort():
+    d = synth.lm_head(M=3, V=300, K=128, seed=91)
+    w = oracle.dequant_affine4(d["codes"], d["scales"], d["biases"])
+    xf = torch.from_numpy(d["x"].astype(np.int16)).view(torch.bfloat16).double().numpy()
+    logits = xf @ w.T  # numpy's product, not the oracle's ascending-k sum
+    for k in (1, 7, 300):
+        ids, vals = oracle.lmhead_topk(d["x"], d["codes"], d["scales"], d["biases"], k=k)
+        for m in range(3):
+            order = np.lexsort((np.arange(300), -logits[m]))[:k]  # larger first, then lower index
+            assert ids[m].tolist() == order.tolist()
+            np.testing.assert_allclose(vals[m], logits[m, order], rtol=1e-12, atol=1e-12)
+    _, am, _, _ = oracle.lmhead(d["x"], d["codes"], d["scales"], d["biases"])
+    ids1, _ = oracle.lmhead_topk(d["x"], d["codes"], d["scales"], d["biases"], k=1)
+    assert np.array_equal(ids1[:, 0], am)
+
+
 def test_oracle_rejects_bad_shapes():
     with pytest.raises(ValueError):
         oracle.dequant_affine4(np.zeros((2, 3), np.uint32), np.zeros((2, 1), np.uint16), np.zeros((2, 1), np.uint16))
