@@ -32,22 +32,25 @@ FLAGS = [
 ]
 
 
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(CSRC, src.replace(".hip", ".o"))
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs, flush=True)
+    return obj
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libqgemv.so (always rebuilds)."""
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(CSRC, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                         if "packed-fp32-ops" not in l)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{msgs}")
-        if verbose and msgs.strip():
-            print(msgs, flush=True)
-        objs.append(obj)
+    """Compile every HIP source (in parallel) and link libqgemv.so (always rebuilds)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
