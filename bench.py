@@ -32,7 +32,8 @@ sys.path.insert(0, ROOT)
 METRIC = "achieved HBM GB/s (% of peak) for 4-bit qGEMV at M=1 and M=8; verify cost ratio"
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["bit_quantized_decode_group_amd/csrc/common.h", "bit_quantized_decode_group_amd/csrc/affine4.hip",
-                  "bit_quantized_decode_group_amd/csrc/q4k.hip", "bit_quantized_decode_group_amd/csrc/abi.hip"]
+                  "bit_quantized_decode_group_amd/csrc/q4k.hip", "bit_quantized_decode_group_amd/csrc/abi.hip",
+                  "bit_quantized_decode_group_amd/csrc/topk.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CALIB_BYTES = 384 << 20  # bytes read and written by the kernel that calibrates the HBM byte counters
 # kernels launched by each entry point (once per call) at M = 8
@@ -455,6 +456,15 @@ def config_timings(torch, ops, synth, to_dev, dev):
                                                   logits=logits[:M] if keep else None), n, 6 * n)
         b = nb + M * lm["K"] * 2 + M * 8 + (M * lm["V"] * 4 if keep else 0)
         res[f"M{M}" + ("_with_logits" if keep else "")] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
+    # top-k readout (candidate pools), M = 8: projection + logits + selection
+    tids = torch.empty((8, 64), dtype=torch.int32, device=dev)
+    tvals = torch.empty((8, 64), dtype=torch.float32, device=dev)
+    for k in (8, 64):
+        us = per_call(lambda i: ops.lmhead_topk(x8, cps[i % n]["codes"], cps[i % n]["scales"], cps[i % n]["biases"], k,
+                                                ids=tids[:, :k].contiguous() if k < 64 else tids,
+                                                vals=tvals[:, :k].contiguous() if k < 64 else tvals), n, 6 * n)
+        b = nb + 8 * lm["K"] * 2 + 8 * k * 8
+        res[f"M8_top{k}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
     out["lm_head_151936x1024"] = res
     del cps
     log("[bench] context: " + json.dumps(out))

@@ -305,6 +305,36 @@ qg_status do_check_lmhead(const uint16_t* x, const uint32_t* codes, const uint16
   return check_alias(out, 3, in, 5, fn);
 }
 
+qg_status do_check_lmhead_topk(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                               const uint16_t* biases, float* logits, int32_t* ids, float* vals, int M, int V, int K,
+                               int k) {
+  const char* fn = "lmhead_topk";
+  qg_status st = check_affine_common(fn, M, V, K);
+  if (st) return st;
+  if (V < 1) return fail(QG_EINVAL, "%s: V=%d must be >= 1", fn, V);
+  if (k < 1 || k > V) return fail(QG_EINVAL, "%s: k=%d must be in 1..V", fn, k);
+  if (k > kTopkMax) return fail(QG_EUNSUPPORTED, "%s: k=%d above %d", fn, k, kTopkMax);
+  if ((long long)((V + kTopkBlock - 1) / kTopkBlock) * k > kTopkMergeMax)
+    return fail(QG_EUNSUPPORTED, "%s: V=%d with k=%d exceeds the on-chip merge (%d candidates)", fn, V, k,
+                kTopkMergeMax);
+  if (!fits_lds_unsplit(M, K))
+    return fail(QG_EUNSUPPORTED, "%s: M=%d rows of K=%d do not fit the staged-activation LDS budget", fn, M, K);
+  const size_t v = (size_t)V, kk = (size_t)K;
+  const Buf in[] = {{x, (size_t)M * kk * 2, "x"},
+                    {codes, v * kk / 2, "codes"},
+                    {scales, v * (kk / 64) * 2, "scales"},
+                    {biases, v * (kk / 64) * 2, "biases"}};
+  const Buf out[] = {{logits, logits ? (size_t)M * v * 4 : 0, "logits"},
+                     {ids, (size_t)M * k * 4, "ids"},
+                     {vals, vals ? (size_t)M * k * 4 : (size_t)0, "vals"}};
+  if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(in[2], 2, fn)) ||
+      (st = check_ptr(in[3], 2, fn)) || (st = check_ptr(out[1], 4, fn)))
+    return st;
+  if (logits && (st = check_ptr(out[0], 4, fn))) return st;
+  if (vals && (st = check_ptr(out[2], 4, fn))) return st;
+  return check_alias(out, 3, in, 4, fn);
+}
+
 // --------------------------------------------------------- dispatch --
 qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* fn) {
   const int G = a.K / 64;
@@ -355,11 +385,16 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
   const size_t part_bytes = partials ? (size_t)a.S * a.M * a.N * 4 : 0;
   const size_t ssq_bytes = (mode == QG_MODE_GATEUP) ? (size_t)a.S * 8 * 4 : 0;
   const size_t key_bytes = (mode == QG_MODE_LMHEAD) ? (size_t)a.S * a.rgroups * 8 * 8 : 0;
-  qg_status st = get_workspace(stream, part_bytes + ssq_bytes + key_bytes, &ws);
+  // top-k: the blocks' candidates, and the logits when the caller keeps none
+  const size_t cand_bytes = a.topk > 0 ? (size_t)a.M * ((a.N + kTopkBlock - 1) / kTopkBlock) * a.topk * 8 : 0;
+  const size_t lg_bytes = (a.topk > 0 && !a.logits) ? (size_t)a.M * a.N * 4 : 0;
+  qg_status st = get_workspace(stream, part_bytes + ssq_bytes + key_bytes + cand_bytes + lg_bytes, &ws);
   if (st) return st;
   a.part = reinterpret_cast<float*>(ws);
   a.ssq_part = reinterpret_cast<float*>(ws + part_bytes);
   a.keys = reinterpret_cast<unsigned long long*>(ws + part_bytes + ssq_bytes);
+  a.cand = reinterpret_cast<unsigned long long*>(ws + part_bytes + ssq_bytes + key_bytes);
+  if (lg_bytes) a.logits = reinterpret_cast<float*>(ws + part_bytes + ssq_bytes + key_bytes + cand_bytes);
   return launched(qg_launch_affine(mode, a, lds, stream), fn);
 }
 
@@ -474,6 +509,34 @@ qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes, const uint16_t
   a.N = V;
   a.K = K;
   return run_affine(QG_MODE_LMHEAD, a, (hipStream_t)stream, "lmhead_argmax");
+}
+
+qg_status qg_check_lmhead_topk(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                               const uint16_t* biases, float* logits, int32_t* ids, float* vals, int M, int V, int K,
+                               int k) {
+  clear_err();
+  return do_check_lmhead_topk(x, codes, scales, biases, logits, ids, vals, M, V, K, k);
+}
+
+qg_status lmhead_topk(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                      float* logits, int32_t* ids, float* vals, int M, int V, int K, int k, void* stream) {
+  clear_err();
+  qg_status st = do_check_lmhead_topk(x, codes, scales, biases, logits, ids, vals, M, V, K, k);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  QgAffineArgs a{};
+  a.x = x;
+  a.codes = codes;
+  a.scales = scales;
+  a.biases = biases;
+  a.logits = logits;
+  a.ids = ids;
+  a.topk = k;
+  a.topk_vals = vals;
+  a.M = M;
+  a.N = V;
+  a.K = K;
+  return run_affine(QG_MODE_LMHEAD, a, (hipStream_t)stream, "lmhead_topk");
 }
 
 qg_status qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K, void* stream) {

@@ -505,7 +505,9 @@ static int launch_affine_m(int mode, const QgAffineArgs& a, size_t lds, hipStrea
     launch_main<M, false>(mode, a, grid, block, lds, st);
   int err = (int)hipGetLastError();
   if (err) return err;
-  if (mode == QG_MODE_LMHEAD) {
+  if (mode == QG_MODE_LMHEAD && a.topk > 0) {
+    return qg_launch_topk(a, st);
+  } else if (mode == QG_MODE_LMHEAD) {
     hipLaunchKernelGGL(k_lmhead_finalize, dim3(1), dim3(256), 0, st, a, (int)grid.x);
   } else if (a.S > 1 || mode == QG_MODE_GATEUP) {
     const size_t outs = (size_t)a.M * (mode == QG_MODE_GATEUP ? a.N / 2 : a.N);

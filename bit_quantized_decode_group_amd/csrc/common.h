@@ -128,6 +128,11 @@ struct QgAffineArgs {
   int rgroups;  // workgroups per K slice; workgroup r owns tiles [r*ntiles/rgroups, (r+1)*ntiles/rgroups)
   int waves;    // waves per workgroup
   int wide;     // scales/biases of a whole batch can be loaded as one aligned vector per row
+  // top-k readout (LM head mode with topk > 0): logits must be set; ids is
+  // [M][topk]; the selection runs after the projection instead of the argmax
+  int topk;
+  float* topk_vals;              // [M][topk] (nullable)
+  unsigned long long* cand;      // [M][topk_blocks][topk] per-block candidates
 };
 
 struct QgQ4kArgs {
@@ -158,3 +163,8 @@ struct QgMoeArgs {
 int qg_launch_affine(int mode, const QgAffineArgs& a, size_t lds_bytes, hipStream_t stream);
 int qg_launch_q4k(const QgQ4kArgs& a, size_t lds_bytes, hipStream_t stream);
 int qg_launch_moe(const QgMoeArgs& a, hipStream_t stream);
+// Top-k selection over stored fp32 logits [M][V] (after the LM-head projection).
+constexpr int kTopkBlock = 2048;     // logits per first-stage selection block
+constexpr int kTopkMax = 64;         // largest k
+constexpr int kTopkMergeMax = 16384; // candidates one row's merge can sort on chip
+int qg_launch_topk(const QgAffineArgs& a, hipStream_t stream);

@@ -36,11 +36,13 @@ _SIGS = {
     "rmsnorm_gateup_swiglu": [_P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P],
     "moe_expert_qgemv": [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "lmhead_argmax": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "lmhead_topk": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P],
     "qg_check_qgemv_affine4": [_P, _P, _P, _P, _P, _I, _I, _I],
     "qg_check_qgemv_q4k": [_P, _P, _P, _I, _I, _I],
     "qg_check_rmsnorm_gateup_swiglu": [_P, _P, _F, _P, _P, _P, _P, _I, _I, _I],
     "qg_check_moe_expert_qgemv": [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I],
     "qg_check_lmhead_argmax": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I],
+    "qg_check_lmhead_topk": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I],
 }
 
 
@@ -191,6 +193,25 @@ def lmhead_argmax(x, codes, scales, biases, draft=None, logits=None, want_logits
         _raise_on(lib().lmhead_argmax(_ptr(x), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(logits), _ptr(ids),
                                       _ptr(draft), _ptr(accepted), M, V, K, _stream()), "lmhead_argmax")
     return ids, accepted, logits
+
+
+def lmhead_topk(x, codes, scales, biases, k, logits=None, want_logits=False, ids=None, vals=None, want_vals=True):
+    """Top-k readout.  Returns (ids int32 [M,k], vals fp32 [M,k] or None, logits fp32 [M,V] or None)."""
+    M, K = _dims2(x, "x")
+    V = codes.shape[0]
+    if logits is None and want_logits:
+        logits = torch.empty((M, V), dtype=torch.float32, device=x.device)
+    if ids is None:
+        ids = torch.empty((M, k), dtype=torch.int32, device=x.device)
+    if vals is None and want_vals:
+        vals = torch.empty((M, k), dtype=torch.float32, device=x.device)
+    for t, n, e in ((x, "x", 2), (codes, "codes", 4), (scales, "scales", 2), (biases, "biases", 2),
+                    (logits, "logits", 4), (ids, "ids", 4), (vals, "vals", 4)):
+        _need(t, n, e, x.device)
+    with torch.cuda.device(x.device):
+        _raise_on(lib().lmhead_topk(_ptr(x), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(logits), _ptr(ids),
+                                    _ptr(vals), M, V, K, int(k), _stream()), "lmhead_topk")
+    return ids, vals, logits
 
 
 # ------------------------------------------------------------- host checks --

@@ -150,6 +150,27 @@ qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes,
                         int32_t* accepted, int M, int V, int K, void* stream);
 
 /*
+ * lmhead_topk -- top-k readout of the untied LM head (uzu page, section
+ * "내부 동작 3: DFlash + Weaver": the target's readout of each draft position
+ * yields a pool of its best candidate tokens):
+ *   logits[m][v] = x[m] . dequant(W)[v]           (fp32)
+ *   ids[m][0..k-1] = indices of the k largest logits of row m, larger logit
+ *                    first, equal logits by lower index, a NaN logit above
+ *                    every number (NaNs by lower index)
+ *   vals[m][j]     = logits[m][ids[m][j]]           (written only if non-null)
+ *   x bf16 [M][K]; codes uint32 [V][K/8]; scales, biases bf16 [V][K/64];
+ *   logits fp32 [M][V] (nullable: if null the library keeps them in its
+ *   workspace); ids int32 [M][k]; vals fp32 [M][k] (nullable).
+ *   1 <= M <= 8; 1 <= k <= min(64, V); ceil(V/2048)*k <= 16384; K as for
+ *   lmhead_argmax (all of x staged on chip).
+ *   A call enqueues the projection and two selection kernels.
+ */
+qg_status lmhead_topk(const uint16_t* x, const uint32_t* codes,
+                      const uint16_t* scales, const uint16_t* biases,
+                      float* logits, int32_t* ids, float* vals, int M, int V,
+                      int K, int k, void* stream);
+
+/*
  * Host-only twins of the entry points above: the same argument checks, no
  * GPU access, no launch.  They return what the entry point would return
  * before launching anything.
@@ -175,6 +196,10 @@ qg_status qg_check_lmhead_argmax(const uint16_t* x, const uint32_t* codes,
                                  float* logits, int32_t* ids,
                                  const int32_t* draft, int32_t* accepted, int M,
                                  int V, int K);
+qg_status qg_check_lmhead_topk(const uint16_t* x, const uint32_t* codes,
+                               const uint16_t* scales, const uint16_t* biases,
+                               float* logits, int32_t* ids, float* vals, int M,
+                               int V, int K, int k);
 
 #ifdef __cplusplus
 }

@@ -27,10 +27,10 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:qg_status|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["qgemv_affine4", "qgemv_q4k", "rmsnorm_gateup_swiglu", "moe_expert_qgemv", "lmhead_argmax",
-              "qg_status_string", "qg_last_error"]:
+              "lmhead_topk", "qg_status_string", "qg_last_error"]:
         assert n in names
 
 
@@ -162,3 +162,40 @@ def test_lmhead_checks(lib):
     assert c(*bad) == ops.QG_OK
     bad[10] = 9152
     assert c(*bad) == ops.QG_EUNSUPPORTED
+
+
+def test_lmhead_topk_checks(lib):
+    c = lambda *a: ops.check("lmhead_topk", *a)
+    ok = [A[0], A[1], A[2], A[3], A[4], A[5], A[6], 8, 151936, 1024, 64]
+    assert c(*ok) == ops.QG_OK
+    opt = list(ok)
+    opt[4] = 0  # logits and vals are optional
+    opt[6] = 0
+    assert c(*opt) == ops.QG_OK
+    for idx, val, st in [(10, 0, ops.QG_EINVAL), (10, 65, ops.QG_EUNSUPPORTED), (7, 9, ops.QG_EINVAL),
+                         (8, 0, ops.QG_EINVAL), (9, 100, ops.QG_EINVAL)]:
+        bad = list(ok)
+        bad[idx] = val
+        assert c(*bad) == st, (idx, val)
+    small = list(ok)
+    small[8], small[10] = 5, 6  # k > V
+    assert c(*small) == ops.QG_EINVAL
+    small[10] = 5
+    assert c(*small) == ops.QG_OK
+    big = list(ok)
+    big[8] = 2048 * 256 + 1  # 257 blocks x 64 candidates exceed the on-chip merge
+    assert c(*big) == ops.QG_EUNSUPPORTED
+    big[10] = 32
+    assert c(*big) == ops.QG_OK
+    bad = list(ok)
+    bad[5] = 0  # ids required
+    assert c(*bad) == ops.QG_EINVAL
+    bad = list(ok)
+    bad[6] = A[5]  # vals over ids
+    assert c(*bad) == ops.QG_EALIAS
+    bad = list(ok)
+    bad[4] = A[1]  # logits over codes
+    assert c(*bad) == ops.QG_EALIAS
+    P = ops._P
+    assert lib.lmhead_topk(P(A[0]), P(A[1]), P(A[2]), P(A[3]), None, P(A[5]), None, 1, 16, 64, 0,
+                           None) == ops.QG_EINVAL

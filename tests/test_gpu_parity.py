@@ -357,3 +357,81 @@ def test_qgemv_affine4_scale_load_paths_agree(M, N, K):
     assert np.array_equal(y1, y2)
     ref = oracle.qgemv_affine4(d["x"], d["codes"], d["scales"], d["biases"])
     assert_close(bits_to_f64(y1), ref, what=f"vector path M{M} N{N} K{K}")
+
+
+# ------------------------------------------------------------ lmhead_topk --
+
+def _assert_topk(ids_gpu, vals_gpu, d, k, what):
+    """GPU top-k against the oracle: the j-th id's oracle logit is within 1e-2
+    of the oracle's j-th largest, ids are distinct, and where the oracle's
+    ranked logits are separated by more than 1e-2 on both sides of rank j the
+    id is exactly the oracle's (the argmax rule applied at every rank)."""
+    logits, _, _, _ = oracle.lmhead(d["x"], d["codes"], d["scales"], d["biases"])
+    V = logits.shape[1]
+    kk = min(k + 1, V)
+    ids_ref, vals_ref = oracle.lmhead_topk(d["x"], d["codes"], d["scales"], d["biases"], k=kk)
+    rms = float(np.sqrt(np.mean(logits ** 2)))
+    for m in range(ids_gpu.shape[0]):
+        g = ids_gpu[m]
+        assert len(set(g.tolist())) == k and g.min() >= 0 and g.max() < V, (what, m)
+        assert np.all(np.abs(logits[m, g] - vals_ref[m, :k]) <= 1e-2), (what, m)
+        for j in range(k):
+            left = j == 0 or vals_ref[m, j - 1] - vals_ref[m, j] > 1e-2
+            right = j + 1 >= kk or vals_ref[m, j] - vals_ref[m, j + 1] > 1e-2
+            if left and right:
+                assert g[j] == ids_ref[m, j], (what, m, j)
+        if vals_gpu is not None:
+            assert np.all(np.abs(vals_gpu[m] - logits[m, g]) <= 1e-3 * rms + 1e-6), (what, m)
+
+
+@pytest.mark.parametrize("M,V,K", [(1, 1, 64), (4, 17, 64), (8, 1000, 1024), (3, 5000, 256), (8, 70000, 128)])
+@pytest.mark.parametrize("k", [1, 5, 64])
+def test_lmhead_topk_small(M, V, K, k):
+    if k > V:
+        pytest.skip("k > V is rejected (checked on the host)")
+    d = synth.lm_head(M=M, V=V, K=K, seed=8000 + M + V + K + k)
+    ids, vals, _ = ops.lmhead_topk(dev_bf16(d["x"]), *_affine_dev(d), k)
+    _assert_topk(ids.cpu().numpy(), vals.cpu().numpy().astype(np.float64), d, k, f"topk M{M} V{V} K{K} k{k}")
+
+
+def test_lmhead_topk_order_ties_nan_and_signed_zero():
+    V, K = 3000, 64
+    x = dev_bf16(np.full((2, K), 0x3F80, np.uint16))  # ones: logit = 64 * bias
+    bias = np.full(V, 0x3F00, np.uint16)
+    bias[2040] = bias[10] = 0x3F80  # tied maximum across two selection blocks
+    bias[3] = bias[2999] = 0x3F40
+    bias[20] = 0x3F20
+    ids, vals, _ = ops.lmhead_topk(x, *_bias_rows(V, K, bias), 6)
+    assert ids.cpu().numpy().tolist() == [[10, 2040, 3, 2999, 20, 0]] * 2
+    assert vals.cpu().numpy()[0].tolist() == [64.0, 64.0, 48.0, 48.0, 40.0, 32.0]
+    bias[2555] = bias[50] = 0x7FC0  # NaN logits first, by index
+    ids, vals, _ = ops.lmhead_topk(x, *_bias_rows(V, K, bias), 3)
+    assert ids.cpu().numpy()[0].tolist() == [50, 2555, 10]
+    assert np.isnan(vals.cpu().numpy()[0, :2]).all()
+    neg = np.full(V, 0xBF00, np.uint16)  # -0.5 everywhere except -0 at 2100 and +0 at 7
+    neg[2100] = 0x8000
+    neg[7] = 0x0000
+    ids, _, _ = ops.lmhead_topk(x, *_bias_rows(V, K, neg), 3)
+    assert ids.cpu().numpy()[0].tolist() == [7, 2100, 0]
+
+
+def test_lmhead_topk_k1_is_argmax_and_deterministic():
+    d = synth.lm_head(M=8, V=20000, K=1024, seed=8101)
+    x, args = dev_bf16(d["x"]), _affine_dev(d)
+    am, _, _ = ops.lmhead_argmax(x, *args)
+    t1, _, _ = ops.lmhead_topk(x, *args, 1)
+    assert np.array_equal(t1.cpu().numpy()[:, 0], am.cpu().numpy())
+    outs = [ops.lmhead_topk(x, *args, 64)[0].cpu().numpy() for _ in range(4)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    # logits kept by the caller equal the ones the argmax path stores
+    _, _, lg = ops.lmhead_topk(x, *args, 8, want_logits=True)
+    _, _, lg2 = ops.lmhead_argmax(x, *args, want_logits=True)
+    assert torch.equal(lg, lg2)
+
+
+@pytest.mark.parametrize("k", [8, 64])
+def test_config_lm_head_topk(k):
+    d = synth.lm_head(M=8)
+    ids, vals, _ = ops.lmhead_topk(dev_bf16(d["x"]), *_affine_dev(d), k)
+    _assert_topk(ids.cpu().numpy(), vals.cpu().numpy().astype(np.float64), d, k, f"lm head top-{k}")
