@@ -432,25 +432,30 @@ __global__ void __launch_bounds__(256) k_split_reduce(QgAffineArgs p) {
 
 // Greedy verify: maximum key over all workgroups per row (order-independent),
 // then the ids and the number of leading rows that match the draft.  One
-// workgroup; each thread reads whole 64-byte key records of several workgroups.
-__global__ void __launch_bounds__(256) k_lmhead_finalize(QgAffineArgs p, int nwg) {
-  __shared__ unsigned long long red[4][8];
-  __shared__ int s_ids[8], s_draft[8];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // the draft ids are read up front, in parallel with the keys
-  if ((int)threadIdx.x < p.M) s_draft[threadIdx.x] = p.draft ? p.draft[threadIdx.x] : -1;
+// wave: lane l loads the 64-byte key records of workgroups l, l+64, ... (all
+// of its loads issued together), then a butterfly maximum per row.
+__global__ void __launch_bounds__(64) k_lmhead_finalize(QgAffineArgs p, int nwg) {
+  const int lane = threadIdx.x;
+  const int draft = (p.draft && lane < p.M) ? p.draft[lane] : -1;
   unsigned long long v[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) v[m] = 0ull;
-#pragma unroll 4
-  for (int w = threadIdx.x; w < nwg; w += blockDim.x) {
-    const ulonglong2* kp = reinterpret_cast<const ulonglong2*>(p.keys + (size_t)w * 8);
+  for (int w0 = 0; w0 < nwg; w0 += 64 * 8) {
+    ulonglong2 k[8][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const ulonglong2 k = kp[j];
-      v[2 * j] = k.x > v[2 * j] ? k.x : v[2 * j];
-      v[2 * j + 1] = k.y > v[2 * j + 1] ? k.y : v[2 * j + 1];
+    for (int q = 0; q < 8; ++q) {
+      const int w = min(w0 + lane + 64 * q, nwg - 1);  // clamped: a repeated record does not change a maximum
+      const ulonglong2* kp = reinterpret_cast<const ulonglong2*>(p.keys + (size_t)w * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) k[q][j] = kp[j];
     }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = k[q][j].x > v[2 * j] ? k[q][j].x : v[2 * j];
+        v[2 * j + 1] = k[q][j].y > v[2 * j + 1] ? k[q][j].y : v[2 * j + 1];
+      }
   }
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
@@ -460,25 +465,15 @@ __global__ void __launch_bounds__(256) k_lmhead_finalize(QgAffineArgs p, int nwg
       v[m] = o > v[m] ? o : v[m];
     }
   }
-  if (lane == 0) {
+  // every lane now holds the row maxima; lane m writes row m's id
+  int id = 0;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) red[wave][m] = v[m];
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < p.M) {
-    unsigned long long b = 0ull;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) b = red[w][threadIdx.x] > b ? red[w][threadIdx.x] : b;
-    const int id = (int)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
-    p.ids[threadIdx.x] = id;
-    s_ids[threadIdx.x] = id;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0 && p.accepted) {
-    int a = 0;
-    if (p.draft)
-      while (a < p.M && s_ids[a] == s_draft[a]) ++a;
-    *p.accepted = a;
-  }
+  for (int m = 0; m < 8; ++m)
+    if (lane == m) id = (int)(0xFFFFFFFFu - (uint32_t)(v[m] & 0xFFFFFFFFull));
+  if (lane < p.M) p.ids[lane] = id;
+  // accepted = leading rows whose id equals the draft's
+  const unsigned long long match = __ballot(lane < p.M && p.draft && id == draft);
+  if (lane == 0 && p.accepted) *p.accepted = (int)__builtin_ctzll(~match);
 }
 
 template <int M, bool WIDE>
@@ -508,7 +503,7 @@ static int launch_affine_m(int mode, const QgAffineArgs& a, size_t lds, hipStrea
   if (mode == QG_MODE_LMHEAD && a.topk > 0) {
     return qg_launch_topk(a, st);
   } else if (mode == QG_MODE_LMHEAD) {
-    hipLaunchKernelGGL(k_lmhead_finalize, dim3(1), dim3(256), 0, st, a, (int)grid.x);
+    hipLaunchKernelGGL(k_lmhead_finalize, dim3(1), dim3(64), 0, st, a, (int)grid.x);
   } else if (a.S > 1 || mode == QG_MODE_GATEUP) {
     const size_t outs = (size_t)a.M * (mode == QG_MODE_GATEUP ? a.N / 2 : a.N);
     const unsigned nblk = (unsigned)((outs + 255) / 256);
