@@ -314,7 +314,19 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     copy_gbs = 5 * 2 * src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
+    del dst
+    # context: a plain streaming read of 1 GiB with the library's read kernel
+    # (the practical HBM read ceiling a weight stream can reach on this device)
+    for _ in range(2):
+        ops.stream_read(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        ops.stream_read(src)
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = 5 * src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src
 
     cfg = None if args.no_configs else config_timings(torch, ops, synth, to_dev, dev)
 
@@ -369,6 +381,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "d2d_copy_gb_s": round(copy_gbs, 1),
+        "stream_read_gb_s": round(read_gbs, 1),
+        "roofline_frac_of_stream_read": round(dom_gbs / read_gbs, 4),
         "step_spread": {f"M{m}": v for m, v in spread.items()},
         "configs_context": cfg,
         "instrumented_ms_per_step": round(inst8, 5),

@@ -398,9 +398,45 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
   return launched(qg_launch_affine(mode, a, lds, stream), fn);
 }
 
+// Measurement aid: a plain streaming read of a buffer (each workgroup reads
+// consecutive 4-KB pieces, eight 16-byte non-temporal loads per lane in
+// flight, grid-stride), so the HBM read rate of the device can be reported
+// beside the kernels'.  The xor of the data goes to *sink only if it equals a
+// value no buffer of ours produces, so the loads are kept.
+__global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ p, size_t n16, unsigned* sink) {
+  typedef unsigned u4v __attribute__((ext_vector_type(4)));
+  uint32_t acc = 0;
+  const size_t per = (size_t)8 * 256;
+  for (size_t b = (size_t)blockIdx.x * per; b < n16; b += (size_t)gridDim.x * per) {
+    u4v v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t i = std::min(b + (size_t)u * 256 + threadIdx.x, n16 - 1);
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p + i));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9E3779B9u) *sink = acc;
+}
+
 }  // namespace
 
 extern "C" {
+
+qg_status qg_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  clear_err();
+  if (!buf || !sink) return fail(QG_EINVAL, "qg_stream_read: null pointer");
+  if (bytes < 16 || bytes % 16 != 0 || !aligned(buf, 16) || !aligned(sink, 4))
+    return fail(QG_EINVAL, "qg_stream_read: bytes must be a positive multiple of 16 and buf 16-byte aligned");
+  qg_status st;
+  if ((st = check_device())) return st;
+  const size_t n16 = bytes / 16;
+  const unsigned grid = (unsigned)std::min<size_t>(8192, (n16 + 2047) / 2048);
+  hipLaunchKernelGGL(k_stream_read, dim3(grid), dim3(256), 0, (hipStream_t)stream, static_cast<const uint4*>(buf), n16,
+                     sink);
+  return launched((int)hipGetLastError(), "qg_stream_read");
+}
 
 const char* qg_status_string(qg_status s) {
   switch (s) {

@@ -214,6 +214,18 @@ def lmhead_topk(x, codes, scales, biases, k, logits=None, want_logits=False, ids
     return ids, vals, logits
 
 
+def stream_read(buf):
+    """Measurement aid: one streaming read of a contiguous CUDA tensor's bytes."""
+    _need(buf, "buf", buf.element_size(), buf.device)
+    sink = torch.empty(1, dtype=torch.int32, device=buf.device)
+    l = lib()
+    l.qg_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
+    l.qg_stream_read.restype = ctypes.c_int32
+    with torch.cuda.device(buf.device):
+        _raise_on(l.qg_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream()),
+                  "qg_stream_read")
+
+
 # ------------------------------------------------------------- host checks --
 # The qg_check_* twins run the entry points' argument checks on the host only
 # (no GPU, no launch); they take raw addresses so tests can probe the rules.

@@ -171,6 +171,18 @@ qg_status lmhead_topk(const uint16_t* x, const uint32_t* codes,
                       int K, int k, void* stream);
 
 /*
+ * qg_stream_read -- measurement aid, not part of the decode path: one plain
+ * streaming read of `bytes` bytes at `buf` (16-byte aligned, bytes a positive
+ * multiple of 16) on `stream`, for reporting the device's HBM read rate
+ * beside the kernels' (a pure-stream reference, as the Husky page's
+ * "측정 환경과 검증 조건" section compares a step with a plain weight read).
+ * *sink (4-byte aligned) is written only in a case that does not occur for
+ * real data; it keeps the loads from being optimised away.
+ */
+qg_status qg_stream_read(const void* buf, size_t bytes, uint32_t* sink,
+                         void* stream);
+
+/*
  * Host-only twins of the entry points above: the same argument checks, no
  * GPU access, no launch.  They return what the entry point would return
  * before launching anything.

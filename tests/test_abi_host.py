@@ -199,3 +199,12 @@ def test_lmhead_topk_checks(lib):
     P = ops._P
     assert lib.lmhead_topk(P(A[0]), P(A[1]), P(A[2]), P(A[3]), None, P(A[5]), None, 1, 16, 64, 0,
                            None) == ops.QG_EINVAL
+
+
+def test_stream_read_checks(lib):
+    f = lib.qg_stream_read
+    f.argtypes = [ops._P, ops.ctypes.c_size_t, ops._P, ops._P]
+    f.restype = ops.ctypes.c_int32
+    assert f(None, 1024, ops._P(A[1]), None) == ops.QG_EINVAL
+    assert f(ops._P(A[0]), 1000, ops._P(A[1]), None) == ops.QG_EINVAL  # not a multiple of 16
+    assert f(ops._P(A[0] + 8), 1024, ops._P(A[1]), None) == ops.QG_EINVAL  # misaligned
