@@ -67,10 +67,12 @@ def _load():
         lib.oracle_moe.argtypes = [P, P, I, P, P, I, I64, I64, P, P, P]
         lib.oracle_lmhead.argtypes = [P, P, P, P, I, I64, I64, P, P, P, P, P]
         lib.oracle_lmhead_topk.argtypes = [P, P, P, P, I, I64, I64, I, P, P]
+        lib.oracle_rht.argtypes = [P, P, I, I, I64, P]
+        lib.oracle_qgemv_affine4_rht.argtypes = [P, P, I, P, P, P, I, I64, I64, P]
         for name in ("oracle_dequant_affine4", "oracle_dequant_q4k", "oracle_qgemv_affine4",
                      "oracle_qgemv_affine4_f64x", "oracle_qgemv_q4k", "oracle_rmsnorm",
                      "oracle_rmsnorm_gateup_swiglu", "oracle_mlp_block", "oracle_moe",
-                     "oracle_lmhead", "oracle_lmhead_topk"):
+                     "oracle_lmhead", "oracle_lmhead_topk", "oracle_rht", "oracle_qgemv_affine4_rht"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -271,3 +273,28 @@ def lmhead_topk(x, codes, scales, biases, k):
     _check(_load().oracle_lmhead_topk(px, pc, ps, pb, M, V, K, int(k), ids.ctypes.data_as(ctypes.c_void_p),
                                       vals.ctypes.data_as(ctypes.c_void_p)), "lmhead_topk")
     return ids, vals
+
+
+def rht(x, signs, had) -> np.ndarray:
+    """O10: blockwise (1/sqrt(had)) H_had . diag(s) . x of every bf16 row; fp64 [M, K]."""
+    x, px = _c(x, np.uint16)
+    signs, ps = _c(signs, np.int8)
+    M, K = x.shape
+    xr = np.empty((M, K), dtype=np.float64)
+    _check(_load().oracle_rht(px, ps, int(had), M, K, xr.ctypes.data_as(ctypes.c_void_p)), "rht")
+    return xr
+
+
+def qgemv_affine4_rht(x, signs, had, codes, scales, biases) -> np.ndarray:
+    """O11: dequant(W) . RHT(x) in fp64."""
+    x, px = _c(x, np.uint16)
+    signs, psg = _c(signs, np.int8)
+    codes, pc = _c(codes, np.uint32)
+    _, ps = _c(scales, np.uint16)
+    _, pb = _c(biases, np.uint16)
+    M, K = x.shape
+    N = codes.shape[0]
+    y = np.empty((M, N), dtype=np.float64)
+    _check(_load().oracle_qgemv_affine4_rht(px, psg, int(had), pc, ps, pb, M, N, K,
+                                           y.ctypes.data_as(ctypes.c_void_p)), "qgemv_affine4_rht")
+    return y

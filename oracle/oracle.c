@@ -455,3 +455,55 @@ int oracle_lmhead_topk(const uint16_t* x, const uint32_t* codes,
   free(taken);
   return rc;
 }
+
+/* --------------------------------------------------------------- O10 ---- */
+
+static int popcount_u32(uint32_t v) {
+  int c = 0;
+  while (v) {
+    c += (int)(v & 1u);
+    v >>= 1;
+  }
+  return c;
+}
+
+int oracle_rht(const uint16_t* x, const int8_t* signs, int had, int M,
+               int64_t K, double* xr) {
+  if (!x || !signs || !xr || M < 1 || K <= 0 || had < 1) return -1;
+  if ((had & (had - 1)) != 0 || K % had != 0) return -1;
+  double* sx = (double*)malloc(sizeof(double) * (size_t)had);
+  if (!sx) return -1;
+  const double norm = 1.0 / sqrt((double)had);
+  for (int m = 0; m < M; ++m) {
+    for (int64_t b = 0; b < K / had; ++b) {
+      const int64_t k0 = b * had;
+      for (int j = 0; j < had; ++j) {
+        const double v = o_bf16_to_f64(x[(int64_t)m * K + k0 + j]);
+        sx[j] = signs[k0 + j] < 0 ? -v : v;
+      }
+      for (int i = 0; i < had; ++i) {
+        double acc = 0.0; /* the plain matrix-vector product, j ascending */
+        for (int j = 0; j < had; ++j) {
+          const double h = (popcount_u32((uint32_t)(i & j)) & 1) ? -1.0 : 1.0;
+          acc += h * sx[j];
+        }
+        xr[(int64_t)m * K + k0 + i] = acc * norm;
+      }
+    }
+  }
+  free(sx);
+  return 0;
+}
+
+int oracle_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had,
+                             const uint32_t* codes, const uint16_t* scales,
+                             const uint16_t* biases, int M, int64_t N,
+                             int64_t K, double* y) {
+  if (M < 1 || K <= 0) return -1;
+  double* xr = (double*)malloc(sizeof(double) * (size_t)M * (size_t)K);
+  if (!xr) return -1;
+  int rc = oracle_rht(x, signs, had, M, K, xr);
+  if (rc == 0) rc = oracle_qgemv_affine4_f64x(xr, codes, scales, biases, M, N, K, y);
+  free(xr);
+  return rc;
+}

@@ -18,6 +18,9 @@
  *   O7  MoE: top-k routing, softmax over the selected logits, weighted sum of
  *       the selected experts' SwiGLU MLPs
  *   O8  LM-head readout, greedy argmax, accepted draft prefix
+ *   O9  LM-head top-k readout (candidate pools)
+ *   O10 input randomised Hadamard transform (blockwise, Sylvester order)
+ *   O11 affine-4 projection of the transformed input
  *
  * Sources (the four pages the method is taken from):
  *   [uzu]        "trymirai/uzu ... deep dive" (blog.123qwe.co.kr), section
@@ -128,6 +131,23 @@ int oracle_lmhead_topk(const uint16_t* x, const uint32_t* codes,
                        const uint16_t* scales, const uint16_t* biases, int M,
                        int64_t V, int64_t K, int k, int32_t* ids,
                        double* vals);
+
+/* O10: input randomised Hadamard transform (uzu page, section "내부 동작 1",
+ * linear row: an input-side random Hadamard transform that spreads the
+ * quantisation error; the Metal kernel list names a hadamard_transform).
+ * For each row m and each block b of `had` consecutive k (had a power of two
+ * dividing K):
+ *   xr[m][b*had + i] = (1/sqrt(had)) * sum_j H[i][j] * s[b*had + j] * x[m][b*had + j]
+ * with H[i][j] = (-1)^popcount(i & j) (Sylvester order) and s[k] = -1 where
+ * signs[k] < 0, else +1.  x is bf16 [M][K]; xr fp64 [M][K]. */
+int oracle_rht(const uint16_t* x, const int8_t* signs, int had, int M,
+               int64_t K, double* xr);
+
+/* O11: y = dequant(W) . RHT(x) (O10 then O3 on the fp64 transformed rows). */
+int oracle_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had,
+                             const uint32_t* codes, const uint16_t* scales,
+                             const uint16_t* biases, int M, int64_t N,
+                             int64_t K, double* y);
 
 #ifdef __cplusplus
 }

@@ -538,3 +538,71 @@ def test_lmhead_topk_matches_a_full_sort():
 def test_oracle_rejects_bad_shapes():
     with pytest.raises(ValueError):
         oracle.dequant_affine4(np.zeros((2, 3), np.uint32), np.zeros((2, 1), np.uint16), np.zeros((2, 1), np.uint16))
+
+
+# ------------------------------------------------------------- O10 / O11 --
+# Pins of the input randomised Hadamard transform: scipy's Hadamard matrix
+# (an independent construction of the Sylvester matrix), the textbook 2-point
+# case, orthonormality (H H^T = n I), the involution without signs, sign
+# handling, Parseval, and the projection against the plain O3 on the
+# transformed rows.
+
+def _ones_signs(K):
+    return np.ones(K, np.int8)
+
+
+def test_rht_matches_scipy_hadamard_blocks():
+    from scipy.linalg import hadamard
+    g = np.random.default_rng(501)
+    for had, K in ((2, 8), (4, 64), (64, 192), (256, 512)):
+        x = synth.normal_bf16(synth.rng(500 + had), (3, K))
+        s = g.choice(np.array([-1, 1], np.int8), size=K)
+        xr = oracle.rht(x, s, had)
+        xf = oracle.bf16_array_to_f64(x.reshape(-1)).reshape(x.shape)
+        H = hadamard(had).astype(np.float64) / np.sqrt(had)
+        want = np.concatenate([(xf[:, b * had:(b + 1) * had] * s[b * had:(b + 1) * had]) @ H.T
+                               for b in range(K // had)], axis=1)
+        np.testing.assert_allclose(xr, want, rtol=1e-12, atol=1e-12)
+
+
+def test_rht_two_point_closed_form_and_unit_vectors():
+    x = np.array([[0x4040, 0x3F80]], np.uint16)  # 3.0, 1.0
+    xr = oracle.rht(x, np.ones(2, np.int8), 2)
+    np.testing.assert_allclose(xr[0], [4.0 / np.sqrt(2), 2.0 / np.sqrt(2)], rtol=0, atol=1e-15)
+    had = 16
+    eye = np.zeros((had, had), np.uint16)
+    eye[np.arange(had), np.arange(had)] = 0x3F80
+    cols = oracle.rht(eye, _ones_signs(had), had)  # row i = transform of e_i
+    np.testing.assert_allclose(cols @ cols.T, np.eye(had), atol=1e-12)  # orthonormal
+    assert set(np.unique(np.round(cols * 4, 12))) == {-1.0, 1.0}  # entries +-1/sqrt(16)
+
+
+def test_rht_involution_signs_and_parseval():
+    K, had = 256, 64
+    x = synth.normal_bf16(synth.rng(502), (2, K))
+    xf = oracle.bf16_array_to_f64(x.reshape(-1)).reshape(x.shape)
+    once = oracle.rht(x, _ones_signs(K), had)
+    # the transform of the transform is the identity (H/sqrt(n) is symmetric and orthogonal);
+    # apply it to the exact fp64 result via the Sylvester matrix built independently here
+    n = had
+    H = np.array([[(-1.0) ** bin(i & j).count("1") for j in range(n)] for i in range(n)]) / np.sqrt(n)
+    twice = np.concatenate([once[:, b * n:(b + 1) * n] @ H.T for b in range(K // n)], axis=1)
+    np.testing.assert_allclose(twice, xf, atol=1e-12)
+    np.testing.assert_allclose(np.linalg.norm(once, axis=1), np.linalg.norm(xf, axis=1), rtol=1e-13)
+    s = _ones_signs(K)
+    s[[3, 70, 200]] = -1
+    neg = x.copy()
+    neg[:, [3, 70, 200]] ^= 0x8000  # negating the inputs equals flipping their signs
+    np.testing.assert_allclose(oracle.rht(x, s, had), oracle.rht(neg, _ones_signs(K), had), atol=0)
+
+
+def test_rht_projection_is_plain_projection_of_transformed_rows():
+    d = synth.single_projection(M=3, N=20, K=256, seed=503)
+    s = np.random.default_rng(504).choice(np.array([-1, 1], np.int8), size=256)
+    y = oracle.qgemv_affine4_rht(d["x"], s, 128, d["codes"], d["scales"], d["biases"])
+    w = oracle.dequant_affine4(d["codes"], d["scales"], d["biases"])
+    np.testing.assert_allclose(y, oracle.rht(d["x"], s, 128) @ w.T, rtol=1e-12, atol=1e-10)
+    with pytest.raises(ValueError):
+        oracle.rht(d["x"], s, 96)  # not a power of two
+    with pytest.raises(ValueError):
+        oracle.rht(d["x"], s, 512)  # does not divide K
