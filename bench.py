@@ -33,7 +33,7 @@ METRIC = "achieved HBM GB/s (% of peak) for 4-bit qGEMV at M=1 and M=8; verify c
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["bit_quantized_decode_group_amd/csrc/common.h", "bit_quantized_decode_group_amd/csrc/affine4.hip",
                   "bit_quantized_decode_group_amd/csrc/q4k.hip", "bit_quantized_decode_group_amd/csrc/abi.hip",
-                  "bit_quantized_decode_group_amd/csrc/topk.hip"]
+                  "bit_quantized_decode_group_amd/csrc/topk.hip", "bit_quantized_decode_group_amd/csrc/rht.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CALIB_BYTES = 384 << 20  # bytes read and written by the kernel that calibrates the HBM byte counters
 # kernels launched by each entry point (once per call) at M = 8
@@ -426,6 +426,17 @@ def config_timings(torch, ops, synth, to_dev, dev):
         res[f"M{M}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
     res["ratio_m8_m1"] = round(res["M8"]["us"] / res["M1"]["us"], 3)
     out["projection_3072x1024"] = res
+    # the same projection behind an input randomised Hadamard transform (blocks of 1024)
+    signs = torch.from_numpy(np.random.default_rng(1006).choice(np.array([-1, 1], np.int8), size=sp["K"])).to(dev)
+    res = {}
+    for M in (1, 8):
+        xm = x8[:M].contiguous()
+        ym = torch.empty((M, sp["N"]), dtype=torch.bfloat16, device=dev)
+        us = per_call(lambda i: ops.qgemv_affine4_rht(xm, signs, 1024, cps[i % n]["codes"], cps[i % n]["scales"],
+                                                      cps[i % n]["biases"], y=ym), n, 3 * n)
+        b = nb + M * sp["K"] * 2 + sp["K"] + M * sp["N"] * 2
+        res[f"M{M}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
+    out["projection_rht_3072x1024"] = res
     del cps
     # MLP block D=1024, I=3072 (RMSNorm -> gate/up -> SwiGLU -> down), M = 1 and 8
     mb = synth.mlp_block(M=8)

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -335,14 +336,41 @@ qg_status do_check_lmhead_topk(const uint16_t* x, const uint32_t* codes, const u
   return check_alias(out, 3, in, 4, fn);
 }
 
+qg_status do_check_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had, const uint32_t* codes,
+                                     const uint16_t* scales, const uint16_t* biases, uint16_t* y, int M, int N,
+                                     int K) {
+  const char* fn = "qgemv_affine4_rht";
+  qg_status st = check_affine_common(fn, M, N, K);
+  if (st) return st;
+  if (had < 2 || had > kRhtMax || (had & (had - 1)) != 0)
+    return fail(QG_EINVAL, "%s: had=%d must be a power of two in 2..%d", fn, had, kRhtMax);
+  if (K % had != 0) return fail(QG_EINVAL, "%s: had=%d must divide K=%d", fn, had, K);
+  const size_t n = (size_t)N, k = (size_t)K;
+  const Buf in[] = {{x, (size_t)M * k * 2, "x"},
+                    {codes, n * k / 2, "codes"},
+                    {scales, n * (k / 64) * 2, "scales"},
+                    {biases, n * (k / 64) * 2, "biases"},
+                    {signs, k, "signs"}};
+  const Buf out[] = {{y, (size_t)M * n * 2, "y"}};
+  if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(in[2], 2, fn)) ||
+      (st = check_ptr(in[3], 2, fn)) || (st = check_ptr(in[4], 1, fn)) || (st = check_ptr(out[0], 2, fn)))
+    return st;
+  return check_alias(out, 1, in, 5, fn);
+}
+
 // --------------------------------------------------------- dispatch --
-qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* fn) {
+// `reserve` bytes at the start of the workspace belong to the caller; `pre`
+// (if set) runs after the workspace is in place and before the projection is
+// launched, with that region and the arguments (the RHT entry point launches
+// its transform there and points the projection at the planes it writes).
+qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* fn, size_t reserve = 0,
+                     const std::function<int(unsigned char*, QgAffineArgs&)>& pre = nullptr) {
   const int G = a.K / 64;
   a.G = G;
   a.nchunks = (G + 1) / 2;
   a.ntiles = (a.N + 15) / 16;
   a.waves = kWaves;
-  const int PL = (mode == QG_MODE_GATEUP) ? 2 : 1;
+  const int PL = (mode == QG_MODE_GATEUP || mode == QG_MODE_PLANES) ? 2 : 1;
   const size_t per = affine_lds_per_chunk(a.M, PL);
   const int cps_max = (int)std::min<size_t>((size_t)a.nchunks, (kLdsBudget - affine_lds_fixed(a.M, PL)) / per);
   const bool split_ok = (mode != QG_MODE_LMHEAD);
@@ -388,8 +416,14 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
   // top-k: the blocks' candidates, and the logits when the caller keeps none
   const size_t cand_bytes = a.topk > 0 ? (size_t)a.M * ((a.N + kTopkBlock - 1) / kTopkBlock) * a.topk * 8 : 0;
   const size_t lg_bytes = (a.topk > 0 && !a.logits) ? (size_t)a.M * a.N * 4 : 0;
-  qg_status st = get_workspace(stream, part_bytes + ssq_bytes + key_bytes + cand_bytes + lg_bytes, &ws);
+  reserve = (reserve + 255) / 256 * 256;
+  qg_status st = get_workspace(stream, reserve + part_bytes + ssq_bytes + key_bytes + cand_bytes + lg_bytes, &ws);
   if (st) return st;
+  if (pre) {
+    const int err = pre(ws, a);
+    if (err) return fail(QG_EHIP, "%s: launch failed: %s", fn, hipGetErrorString((hipError_t)err));
+  }
+  ws += reserve;
   a.part = reinterpret_cast<float*>(ws);
   a.ssq_part = reinterpret_cast<float*>(ws + part_bytes);
   a.keys = reinterpret_cast<unsigned long long*>(ws + part_bytes + ssq_bytes);
@@ -501,6 +535,42 @@ qg_status qgemv_affine4(const uint16_t* x, const uint32_t* codes, const uint16_t
   a.N = N;
   a.K = K;
   return run_affine(QG_MODE_PLAIN, a, (hipStream_t)stream, "qgemv_affine4");
+}
+
+qg_status qg_check_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had, const uint32_t* codes,
+                                     const uint16_t* scales, const uint16_t* biases, uint16_t* y, int M, int N,
+                                     int K) {
+  clear_err();
+  return do_check_qgemv_affine4_rht(x, signs, had, codes, scales, biases, y, M, N, K);
+}
+
+qg_status qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had, const uint32_t* codes,
+                            const uint16_t* scales, const uint16_t* biases, uint16_t* y, int M, int N, int K,
+                            void* stream) {
+  clear_err();
+  qg_status st = do_check_qgemv_affine4_rht(x, signs, had, codes, scales, biases, y, M, N, K);
+  if (st) return st;
+  if (N == 0) return QG_OK;
+  if ((st = check_device())) return st;
+  QgAffineArgs a{};
+  a.codes = codes;
+  a.scales = scales;
+  a.biases = biases;
+  a.y = y;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  const size_t plane = (size_t)M * K * 2;
+  const size_t plane_al = (plane + 255) / 256 * 256;
+  hipStream_t s = (hipStream_t)stream;
+  return run_affine(QG_MODE_PLANES, a, s, "qgemv_affine4_rht", 2 * plane_al,
+                    [&](unsigned char* ws, QgAffineArgs& args) {
+                      uint16_t* hi = reinterpret_cast<uint16_t*>(ws);
+                      uint16_t* lo = reinterpret_cast<uint16_t*>(ws + plane_al);
+                      args.x = hi;
+                      args.x_lo = lo;
+                      return qg_launch_rht(x, signs, had, M, K, hi, lo, s);
+                    });
 }
 
 qg_status rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes_gu,

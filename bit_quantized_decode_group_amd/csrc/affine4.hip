@@ -61,12 +61,16 @@ namespace qg {
 // issued before any is used.  Gate/up also loads gamma, and its short K
 // slices need one round of two groups per wave, which keeps it within 128
 // registers per lane.
-__host__ __device__ constexpr int stage_groups(int mode) { return mode == QG_MODE_GATEUP ? 2 : 4; }
+__host__ __device__ constexpr int stage_groups(int mode) {
+  return (mode == QG_MODE_GATEUP || mode == QG_MODE_PLANES) ? 2 : 4;
+}
+// activation planes staged per value: (hi, lo) for gate/up and the RHT input
+__host__ __device__ constexpr int planes(int mode) { return (mode == QG_MODE_GATEUP || mode == QG_MODE_PLANES) ? 2 : 1; }
 
 template <int MODE>
 struct StageIn {
   uint4 x[stage_groups(MODE)];
-  uint4 gm[MODE == QG_MODE_GATEUP ? stage_groups(MODE) : 1];
+  uint4 gm[planes(MODE) == 2 ? stage_groups(MODE) : 1];  // gamma (GATEUP) or the lo plane (PLANES)
 };
 
 template <int M, int MODE>
@@ -83,13 +87,14 @@ __device__ __forceinline__ void stage_load(const QgAffineArgs& p, int c0, int nc
     const size_t k0 = (size_t)g * 64 + 32 * h + 8 * t;
     in.x[j] = *reinterpret_cast<const uint4*>(p.x + (size_t)m * p.K + k0);
     if constexpr (MODE == QG_MODE_GATEUP) in.gm[j] = *reinterpret_cast<const uint4*>(p.gamma + k0);
+    if constexpr (MODE == QG_MODE_PLANES) in.gm[j] = *reinterpret_cast<const uint4*>(p.x_lo + (size_t)m * p.K + k0);
   }
 }
 
 template <int M, int MODE>
 __device__ __forceinline__ void stage_store(const QgAffineArgs& p, uint4* xs, float* sx, float* ssq, int c0, int nc,
                                             int round, const StageIn<MODE>& in) {
-  constexpr int PL = (MODE == QG_MODE_GATEUP) ? 2 : 1;
+  constexpr int PL = planes(MODE);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
   const int m = lane & 7, h = (lane >> 3) & 1, t = lane >> 4;
   const int ngl = 2 * nc;
@@ -118,6 +123,14 @@ __device__ __forceinline__ void stage_store(const QgAffineArgs& p, uint4* xs, fl
         const uint32_t l1 = f32_to_bf16_bits(p1 - bf16_bits_to_f32(h1));
         v[0][d] = h0 | (h1 << 16);
         v[PL - 1][d] = l0 | (l1 << 16);
+      }
+    } else if constexpr (MODE == QG_MODE_PLANES) {
+      const uint32_t lo[4] = {live ? in.gm[j].x : 0u, live ? in.gm[j].y : 0u, live ? in.gm[j].z : 0u,
+                              live ? in.gm[j].w : 0u};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        v[0][d] = raw[d];
+        v[PL - 1][d] = lo[d];
       }
     } else {
 #pragma unroll
@@ -168,7 +181,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 template <int M, int MODE, bool WIDE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) k_affine(QgAffineArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int PL = (MODE == QG_MODE_GATEUP) ? 2 : 1;  // activation planes (hi, lo)
+  constexpr int PL = planes(MODE);  // activation planes (hi, lo)
   constexpr int BATCH = 4;                              // chunks whose loads are issued together
   constexpr int R = (MODE == QG_MODE_LMHEAD) ? 2 : 1;   // steps of weight loads in flight per wave
   const int lane = threadIdx.x & 63;
@@ -484,6 +497,9 @@ static void launch_main(int mode, const QgAffineArgs& a, dim3 grid, dim3 block, 
       break;
     case QG_MODE_GATEUP:
       hipLaunchKernelGGL((k_affine<M, QG_MODE_GATEUP, WIDE>), grid, block, lds, st, a);
+      break;
+    case QG_MODE_PLANES:
+      hipLaunchKernelGGL((k_affine<M, QG_MODE_PLANES, WIDE>), grid, block, lds, st, a);
       break;
     default:
       hipLaunchKernelGGL((k_affine<M, QG_MODE_LMHEAD, WIDE>), grid, block, lds, st, a);

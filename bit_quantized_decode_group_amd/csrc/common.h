@@ -106,10 +106,13 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) 
 // Launch descriptors filled by the ABI layer (abi.hip) and consumed by the
 // launchers in affine4.hip / q4k.hip.
 
-enum QgAffineMode { QG_MODE_PLAIN = 0, QG_MODE_GATEUP = 1, QG_MODE_LMHEAD = 2 };
+enum QgAffineMode { QG_MODE_PLAIN = 0, QG_MODE_GATEUP = 1, QG_MODE_LMHEAD = 2, QG_MODE_PLANES = 3 };
+// QG_MODE_PLANES: Y = (X_hi + X_lo) . dequant(W)^T with X given as two bf16
+// planes (the transformed input of the RHT projection), epilogue as PLAIN.
 
 struct QgAffineArgs {
   const uint16_t* x;
+  const uint16_t* x_lo;  // PLANES: the low plane of X [M][K]
   const uint16_t* gamma;
   float eps;
   const uint32_t* codes;
@@ -163,6 +166,11 @@ struct QgMoeArgs {
 int qg_launch_affine(int mode, const QgAffineArgs& a, size_t lds_bytes, hipStream_t stream);
 int qg_launch_q4k(const QgQ4kArgs& a, size_t lds_bytes, hipStream_t stream);
 int qg_launch_moe(const QgMoeArgs& a, hipStream_t stream);
+// Input randomised Hadamard transform: x [M][K] bf16 and signs [K] to the hi
+// and lo bf16 planes of (1/sqrt(had)) H_had diag(s) x, blockwise along K.
+constexpr int kRhtMax = 4096;  // largest transform block
+int qg_launch_rht(const uint16_t* x, const int8_t* signs, int had, int M, int K, uint16_t* hi, uint16_t* lo,
+                  hipStream_t stream);
 // Top-k selection over stored fp32 logits [M][V] (after the LM-head projection).
 constexpr int kTopkBlock = 2048;     // logits per first-stage selection block
 constexpr int kTopkMax = 64;         // largest k

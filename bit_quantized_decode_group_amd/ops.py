@@ -33,6 +33,8 @@ _F = ctypes.c_float
 _SIGS = {
     "qgemv_affine4": [_P, _P, _P, _P, _P, _I, _I, _I, _P],
     "qgemv_q4k": [_P, _P, _P, _I, _I, _I, _P],
+    "qgemv_affine4_rht": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P],
+    "qg_check_qgemv_affine4_rht": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I],
     "rmsnorm_gateup_swiglu": [_P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P],
     "moe_expert_qgemv": [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "lmhead_argmax": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
@@ -120,6 +122,23 @@ def qgemv_affine4(x, codes, scales, biases, y=None):
     with torch.cuda.device(x.device):
         _raise_on(lib().qgemv_affine4(_ptr(x), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(y), M, N, K, _stream()),
                   "qgemv_affine4")
+    return y
+
+
+def qgemv_affine4_rht(x, signs, had, codes, scales, biases, y=None):
+    """Y[M,N] (bf16) = RHT(X)[M,K] . dequant(W)[N,K]^T; signs int8 [K], had a power of two dividing K."""
+    M, K = _dims2(x, "x")
+    N = codes.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    for t, n, e in ((x, "x", 2), (signs, "signs", 1), (codes, "codes", 4), (scales, "scales", 2),
+                    (biases, "biases", 2), (y, "y", 2)):
+        _need(t, n, e, x.device)
+    if signs.numel() != K:
+        raise ValueError("signs must hold K values")
+    with torch.cuda.device(x.device):
+        _raise_on(lib().qgemv_affine4_rht(_ptr(x), _ptr(signs), int(had), _ptr(codes), _ptr(scales), _ptr(biases),
+                                          _ptr(y), M, N, K, _stream()), "qgemv_affine4_rht")
     return y
 
 

@@ -83,6 +83,26 @@ qg_status qgemv_affine4(const uint16_t* x, const uint32_t* codes,
                         uint16_t* y, int M, int N, int K, void* stream);
 
 /*
+ * qgemv_affine4_rht -- the projection of an input-side randomised Hadamard
+ * transform (uzu page, section "내부 동작 1", linear row: an input-side random
+ * Hadamard transform spreads the quantisation error; the weights were
+ * quantised in the rotated basis):
+ *   xr[m][b*had + i] = (1/sqrt(had)) sum_j H[i][j] s[b*had + j] x[m][b*had + j]
+ *   Y = xr . dequant(W)^T
+ *   H[i][j] = (-1)^popcount(i & j) (Sylvester order); s[k] = -1 where
+ *   signs[k] < 0, else +1 (the random signs are an input).
+ *   x bf16 [M][K]; signs int8 [K]; codes uint32 [N][K/8]; scales, biases
+ *   bf16 [N][K/64]; y bf16 [M][N].  had: a power of two, 2 <= had <= 4096,
+ *   dividing K; other shape rules as qgemv_affine4.  The transform runs in
+ *   fp32 and reaches the projection as two bf16 planes (16 significant bits).
+ *   A call enqueues the transform and the projection (and a split-K reduce).
+ */
+qg_status qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had,
+                            const uint32_t* codes, const uint16_t* scales,
+                            const uint16_t* biases, uint16_t* y, int M, int N,
+                            int K, void* stream);
+
+/*
  * qgemv_q4k -- Y = X . dequant(W)^T for Q4_K weights.
  *   x bf16 [M][K]; blocks uint8 [N][K/256][144]; y bf16 [M][N].
  *   1 <= M <= 8; N >= 0; K > 0, K % 256 == 0.
@@ -190,6 +210,11 @@ qg_status qg_stream_read(const void* buf, size_t bytes, uint32_t* sink,
 qg_status qg_check_qgemv_affine4(const uint16_t* x, const uint32_t* codes,
                                  const uint16_t* scales, const uint16_t* biases,
                                  uint16_t* y, int M, int N, int K);
+qg_status qg_check_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs,
+                                     int had, const uint32_t* codes,
+                                     const uint16_t* scales,
+                                     const uint16_t* biases, uint16_t* y, int M,
+                                     int N, int K);
 qg_status qg_check_qgemv_q4k(const uint16_t* x, const uint8_t* blocks,
                              uint16_t* y, int M, int N, int K);
 qg_status qg_check_rmsnorm_gateup_swiglu(const uint16_t* x,

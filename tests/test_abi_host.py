@@ -208,3 +208,22 @@ def test_stream_read_checks(lib):
     assert f(None, 1024, ops._P(A[1]), None) == ops.QG_EINVAL
     assert f(ops._P(A[0]), 1000, ops._P(A[1]), None) == ops.QG_EINVAL  # not a multiple of 16
     assert f(ops._P(A[0] + 8), 1024, ops._P(A[1]), None) == ops.QG_EINVAL  # misaligned
+
+
+def test_qgemv_affine4_rht_checks(lib):
+    c = lambda *a: ops.check("qgemv_affine4_rht", *a)
+    ok = [A[0], A[1], 1024, A[2], A[3], A[4], A[5], 8, 3072, 1024]
+    assert c(*ok) == ops.QG_OK
+    for had in (0, 1, 96, 8192, 2048):  # not a power of two, too large, or not dividing K
+        bad = list(ok)
+        bad[2] = had
+        assert c(*bad) == ops.QG_EINVAL, had
+    bad = list(ok)
+    bad[1] = 0  # signs required
+    assert c(*bad) == ops.QG_EINVAL
+    bad = list(ok)
+    bad[6] = A[1]  # y over signs
+    assert c(*bad) == ops.QG_EALIAS
+    split = list(ok)
+    split[8], split[9], split[2] = 2560, 12800, 512
+    assert c(*split) == ops.QG_OK

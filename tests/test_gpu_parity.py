@@ -435,3 +435,53 @@ def test_config_lm_head_topk(k):
     d = synth.lm_head(M=8)
     ids, vals, _ = ops.lmhead_topk(dev_bf16(d["x"]), *_affine_dev(d), k)
     _assert_topk(ids.cpu().numpy(), vals.cpu().numpy().astype(np.float64), d, k, f"lm head top-{k}")
+
+
+# ------------------------------------------------------- qgemv_affine4_rht --
+
+def _signs(K, seed):
+    return np.random.default_rng(seed).choice(np.array([-1, 1], np.int8), size=K)
+
+
+def _dev_i8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int8)).cuda()
+
+
+@pytest.mark.parametrize("K,had", [(64, 2), (64, 64), (256, 128), (1024, 1024), (1536, 512), (12800, 512)])
+@pytest.mark.parametrize("N", [1, 17, 40])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_qgemv_affine4_rht_small(M, N, K, had):
+    d = synth.single_projection(M=M, N=N, K=K, seed=9000 + M * 31 + N + K + had)
+    s = _signs(K, 9100 + K + had)
+    ref = oracle.qgemv_affine4_rht(d["x"], s, had, d["codes"], d["scales"], d["biases"])
+    y = ops.qgemv_affine4_rht(dev_bf16(d["x"]), _dev_i8(s), had, *_affine_dev(d))
+    assert_close(host_bf16_f64(y), ref, what=f"rht M{M} N{N} K{K} had{had}")
+
+
+def test_qgemv_affine4_rht_identity_signs_and_determinism():
+    """All signs +1 and had = 2 on rows whose pairs are equal: the transform
+    moves every pair (a, a) to (sqrt(2) a, 0), a case the oracle computes in
+    closed form; repeated calls give the same bytes."""
+    d = synth.single_projection(M=2, N=33, K=256, seed=9201)
+    x = d["x"].copy()
+    x[:, 1::2] = x[:, 0::2]
+    s = np.ones(256, np.int8)
+    ref = oracle.qgemv_affine4_rht(x, s, 2, d["codes"], d["scales"], d["biases"])
+    xr = oracle.rht(x, s, 2)
+    xf = bits_to_f64(x)
+    np.testing.assert_allclose(xr[:, 0::2], np.sqrt(2.0) * xf[:, 0::2], rtol=1e-15)
+    assert np.all(xr[:, 1::2] == 0.0)
+    args = (dev_bf16(x), _dev_i8(s), 2, *_affine_dev(d))
+    outs = [host_bits(ops.qgemv_affine4_rht(*args)) for _ in range(3)]
+    assert all(np.array_equal(o, outs[0]) for o in outs)
+    assert_close(bits_to_f64(outs[0]), ref, what="rht paired rows")
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_config_rht_projections(M):
+    for (N, K, had, seed) in ((3072, 1024, 1024, 9301), (2560, 12800, 512, 9302)):
+        d = synth.single_projection(M=M, N=N, K=K, seed=seed)
+        s = _signs(K, seed + 1)
+        ref = oracle.qgemv_affine4_rht(d["x"], s, had, d["codes"], d["scales"], d["biases"])
+        y = ops.qgemv_affine4_rht(dev_bf16(d["x"]), _dev_i8(s), had, *_affine_dev(d))
+        assert_close(host_bf16_f64(y), ref, what=f"rht config M{M} N{N} K{K}")
