@@ -437,7 +437,18 @@ def config_timings(torch, ops, synth, to_dev, dev):
         b = nb + M * sp["K"] * 2 + sp["K"] + M * sp["N"] * 2
         res[f"M{M}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
     out["projection_rht_3072x1024"] = res
+    # the same projection on tile-order weights (one contiguous KiB per wave load)
+    tcs = [ops.tile_pack(c["codes"], c["scales"], c["biases"]) for c in cps]
     del cps
+    res = {}
+    for M in (1, 8):
+        xm = x8[:M].contiguous()
+        ym = torch.empty((M, sp["N"]), dtype=torch.bfloat16, device=dev)
+        us = per_call(lambda i: ops.qgemv_affine4_tiled(xm, tcs[i % n][0], tcs[i % n][1], sp["N"], y=ym), n, 3 * n)
+        b = nb + M * sp["K"] * 2 + M * sp["N"] * 2
+        res[f"M{M}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
+    out["projection_tiled_3072x1024"] = res
+    del tcs
     # MLP block D=1024, I=3072 (RMSNorm -> gate/up -> SwiGLU -> down), M = 1 and 8
     mb = synth.mlp_block(M=8)
     keys = {"codes_gu": "u32", "scales_gu": "bf16", "biases_gu": "bf16", "codes_d": "u32", "scales_d": "bf16",
@@ -490,8 +501,18 @@ def config_timings(torch, ops, synth, to_dev, dev):
                                                 vals=tvals[:, :k].contiguous() if k < 64 else tvals), n, 6 * n)
         b = nb + 8 * lm["K"] * 2 + 8 * k * 8
         res[f"M8_top{k}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
-    out["lm_head_151936x1024"] = res
+    # greedy readout on tile-order weights, M = 1 and 8
+    tcs = [ops.tile_pack(c["codes"], c["scales"], c["biases"]) for c in cps]
     del cps
+    for M in (1, 8):
+        xm = x8[:M].contiguous()
+        us = per_call(lambda i: ops.lmhead_argmax_tiled(xm, tcs[i % n][0], tcs[i % n][1], lm["V"],
+                                                        draft=draft[:M].contiguous(), ids=ids[:M], accepted=acc),
+                      n, 6 * n)
+        b = nb + M * lm["K"] * 2 + M * 8
+        res[f"M{M}_tiled"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
+    out["lm_head_151936x1024"] = res
+    del tcs
     log("[bench] context: " + json.dumps(out))
     return out
 

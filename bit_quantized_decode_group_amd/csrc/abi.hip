@@ -358,6 +358,39 @@ qg_status do_check_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int
   return check_alias(out, 1, in, 5, fn);
 }
 
+// Sizes of the tile-order layout of an [N][K] affine-4 matrix.
+size_t tiled_codes_bytes(int N, int K) { return (size_t)((N + 15) / 16) * ((size_t)K / 128) * 1024; }
+size_t tiled_sb_bytes(int N, int K) { return (size_t)((N + 15) / 16) * ((size_t)K / 512) * 512; }
+
+qg_status do_check_tile_pack(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                             uint32_t* codes_t, uint16_t* sb_t, int N, int K) {
+  const char* fn = "affine4_tile_pack";
+  if (N < 1) return fail(QG_EINVAL, "%s: N=%d must be >= 1", fn, N);
+  if (K <= 0 || K % 512 != 0) return fail(QG_EINVAL, "%s: K=%d must be a positive multiple of 512", fn, K);
+  if ((long long)N * 16 > 0x7FFFFFFFLL) return fail(QG_EINVAL, "%s: N=%d too large", fn, N);
+  const size_t n = (size_t)N, k = (size_t)K;
+  const Buf in[] = {{codes, n * k / 2, "codes"}, {scales, n * (k / 64) * 2, "scales"},
+                    {biases, n * (k / 64) * 2, "biases"}};
+  const Buf out[] = {{codes_t, tiled_codes_bytes(N, K), "codes_t"}, {sb_t, tiled_sb_bytes(N, K), "sb_t"}};
+  qg_status st;
+  if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 2, fn)) || (st = check_ptr(in[2], 2, fn)) ||
+      (st = check_ptr(out[0], 16, fn)) || (st = check_ptr(out[1], 16, fn)))
+    return st;
+  return check_alias(out, 2, in, 3, fn);
+}
+
+qg_status do_check_tiled(const char* fn, const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, int M,
+                         int N, int K, const Buf* outs, int nout) {
+  qg_status st = check_affine_common(fn, M, N, K);
+  if (st) return st;
+  if (K % 512 != 0) return fail(QG_EINVAL, "%s: K=%d must be a multiple of 512 (tile-order layout)", fn, K);
+  const Buf in[] = {{x, (size_t)M * K * 2, "x"}, {codes_t, tiled_codes_bytes(N, K), "codes_t"},
+                    {sb_t, tiled_sb_bytes(N, K), "sb_t"}};
+  if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(in[2], 16, fn)))
+    return st;
+  return check_alias(outs, nout, in, 3, fn);
+}
+
 // --------------------------------------------------------- dispatch --
 // `reserve` bytes at the start of the workspace belong to the caller; `pre`
 // (if set) runs after the workspace is in place and before the projection is
@@ -406,6 +439,8 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
     a.wide = (a.G % (2 * batch) == 0) && (a.S == 1 || a.cps % batch == 0) &&
              ((uintptr_t)a.scales % vec == 0) && ((uintptr_t)a.biases % vec == 0);
   }
+  if (a.tiled && !a.wide)
+    return fail(QG_EUNSUPPORTED, "%s: no K split of whole 512-k batches fits for K=%d", fn, a.K);
   const size_t lds = (size_t)a.cps * per + affine_lds_fixed(a.M, PL);
   a.rgroups = affine_rgroups(a.ntiles, a.S, lds, 4, fill_pct);  // 128 registers per lane: 4 waves per SIMD
   unsigned char* ws = nullptr;
@@ -571,6 +606,102 @@ qg_status qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had, con
                       args.x_lo = lo;
                       return qg_launch_rht(x, signs, had, M, K, hi, lo, s);
                     });
+}
+
+size_t qg_tiled_bytes(int N, int K, size_t* sb_bytes) {
+  if (N < 1 || K <= 0 || K % 512 != 0) {
+    if (sb_bytes) *sb_bytes = 0;
+    return 0;
+  }
+  if (sb_bytes) *sb_bytes = tiled_sb_bytes(N, K);
+  return tiled_codes_bytes(N, K);
+}
+
+qg_status qg_check_affine4_tile_pack(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                                     uint32_t* codes_t, uint16_t* sb_t, int N, int K) {
+  clear_err();
+  return do_check_tile_pack(codes, scales, biases, codes_t, sb_t, N, K);
+}
+
+qg_status affine4_tile_pack(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, uint32_t* codes_t,
+                            uint16_t* sb_t, int N, int K, void* stream) {
+  clear_err();
+  qg_status st = do_check_tile_pack(codes, scales, biases, codes_t, sb_t, N, K);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  return launched(qg_launch_tile_pack(codes, scales, biases, codes_t, sb_t, N, K, (hipStream_t)stream),
+                  "affine4_tile_pack");
+}
+
+qg_status qg_check_qgemv_affine4_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, uint16_t* y,
+                                       int M, int N, int K) {
+  clear_err();
+  const Buf out[] = {{y, (size_t)M * N * 2, "y"}};
+  qg_status st = do_check_tiled("qgemv_affine4_tiled", x, codes_t, sb_t, M, N, K, out, 1);
+  if (st) return st;
+  return check_ptr(out[0], 2, "qgemv_affine4_tiled");
+}
+
+qg_status qgemv_affine4_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, uint16_t* y, int M,
+                              int N, int K, void* stream) {
+  qg_status st = qg_check_qgemv_affine4_tiled(x, codes_t, sb_t, y, M, N, K);
+  if (st) return st;
+  if (N == 0) return QG_OK;
+  if ((st = check_device())) return st;
+  QgAffineArgs a{};
+  a.x = x;
+  a.codes = codes_t;
+  a.scales = sb_t;
+  a.biases = sb_t;
+  a.tiled = 1;
+  a.y = y;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  return run_affine(QG_MODE_PLAIN, a, (hipStream_t)stream, "qgemv_affine4_tiled");
+}
+
+qg_status qg_check_lmhead_argmax_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t,
+                                       float* logits, int32_t* ids, const int32_t* draft, int32_t* accepted, int M,
+                                       int V, int K) {
+  clear_err();
+  const char* fn = "lmhead_argmax_tiled";
+  if (V < 1) return fail(QG_EINVAL, "%s: V=%d must be >= 1", fn, V);
+  if (!fits_lds_unsplit(M, K) && M >= 1 && M <= 8)
+    return fail(QG_EUNSUPPORTED, "%s: M=%d rows of K=%d do not fit the staged-activation LDS budget", fn, M, K);
+  const Buf out[] = {{logits, logits ? (size_t)M * V * 4 : 0, "logits"},
+                     {ids, (size_t)M * 4, "ids"},
+                     {accepted, accepted ? (size_t)4 : (size_t)0, "accepted"}};
+  qg_status st = do_check_tiled(fn, x, codes_t, sb_t, M, V, K, out, 3);
+  if (st) return st;
+  if ((st = check_ptr(out[1], 4, fn))) return st;
+  if (logits && (st = check_ptr(out[0], 4, fn))) return st;
+  if (accepted && (st = check_ptr(out[2], 4, fn))) return st;
+  const Buf dr = {draft, draft ? (size_t)M * 4 : 0, "draft"};
+  if (draft && (st = check_ptr(dr, 4, fn))) return st;
+  return check_alias(out, 3, &dr, 1, fn);
+}
+
+qg_status lmhead_argmax_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, float* logits,
+                              int32_t* ids, const int32_t* draft, int32_t* accepted, int M, int V, int K,
+                              void* stream) {
+  qg_status st = qg_check_lmhead_argmax_tiled(x, codes_t, sb_t, logits, ids, draft, accepted, M, V, K);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  QgAffineArgs a{};
+  a.x = x;
+  a.codes = codes_t;
+  a.scales = sb_t;
+  a.biases = sb_t;
+  a.tiled = 1;
+  a.logits = logits;
+  a.ids = ids;
+  a.draft = draft;
+  a.accepted = accepted;
+  a.M = M;
+  a.N = V;
+  a.K = K;
+  return run_affine(QG_MODE_LMHEAD, a, (hipStream_t)stream, "lmhead_argmax_tiled");
 }
 
 qg_status rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes_gu,

@@ -40,6 +40,8 @@
 // has at most 16 significant bits, so it is the sum of hi = bf16(x*gamma) and
 // lo = x*gamma - hi, both exact bf16 values.  Each MFMA step runs on the hi
 // plane and then the lo plane with the same unpacked weights.
+#include <algorithm>
+
 #include "common.h"
 
 namespace qg {
@@ -178,7 +180,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // projections' waves live for a few steps and run best with one (measured:
 // the extra registers and waits cost more than the overlap gains there).
 // Every mode keeps within 128 registers per lane (4 waves per SIMD).
-template <int M, int MODE, bool WIDE>
+template <int M, int MODE, bool WIDE, bool TILED = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) k_affine(QgAffineArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int PL = planes(MODE);  // activation planes (hi, lo)
@@ -236,6 +238,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     const int row = (gw + ti * nw) * 16 + nl;
     const size_t row_c = (size_t)min(row, p.N - 1);
     const int gb = 2 * (c0 + cb);  // first scale group of the batch
+    if constexpr (TILED) {
+      // tile order: every load of the wave reads 1 KB (codes) or 256 bytes
+      // (scales, biases) of consecutive memory
+      const size_t tile = (size_t)min(gw + ti * nw, p.ntiles - 1);  // a wave without work reloads a real tile
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+        bf.q[u] = *reinterpret_cast<const uint4*>(p.codes + ((tile * p.nchunks + c0 + cb + u) * 64 + lane) * 4);
+      const uint16_t* rec = p.scales + ((tile * (p.nchunks / BATCH) + (c0 + cb) / BATCH) * 2) * 128 + nl * 8;
+      const uint4 sv = *reinterpret_cast<const uint4*>(rec);
+      const uint4 bv = *reinterpret_cast<const uint4*>(rec + 128);
+      bf.sw[0] = sv.x; bf.sw[1] = sv.y; bf.sw[2] = sv.z; bf.sw[3] = sv.w;
+      bf.bw[0] = bv.x; bf.bw[1] = bv.y; bf.bw[2] = bv.z; bf.bw[3] = bv.w;
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int cg = WIDE ? c0 + cb + u : c0 + min(cb + u, nc - 1);
@@ -491,6 +507,13 @@ __global__ void __launch_bounds__(64) k_lmhead_finalize(QgAffineArgs p, int nwg)
 
 template <int M, bool WIDE>
 static void launch_main(int mode, const QgAffineArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
+  if (a.tiled) {  // tile-order weights: plain projection and LM head only
+    if (mode == QG_MODE_LMHEAD)
+      hipLaunchKernelGGL((k_affine<M, QG_MODE_LMHEAD, true, true>), grid, block, lds, st, a);
+    else
+      hipLaunchKernelGGL((k_affine<M, QG_MODE_PLAIN, true, true>), grid, block, lds, st, a);
+    return;
+  }
   switch (mode) {
     case QG_MODE_PLAIN:
       hipLaunchKernelGGL((k_affine<M, QG_MODE_PLAIN, WIDE>), grid, block, lds, st, a);
@@ -531,7 +554,54 @@ static int launch_affine_m(int mode, const QgAffineArgs& a, size_t lds, hipStrea
   return (int)hipGetLastError();
 }
 
+// Tile-order layout of affine-4 weights (K % 512 == 0; Husky page, section
+// "MSI의 네 가지 구현 요소": weights laid out in the order the kernel reads
+// them).  For 16-row tile t, 128-k chunk c and lane l = 16*kb + n of a wave:
+//   codes_t[((t*C + c)*64 + l)*4 + w] = codes[(16t + n)*(K/8) + 16c + 4kb + w]
+// (C = K/128 chunks; w = 0..3), i.e. the 16 bytes lane l loads for chunk c,
+// so a load of the whole wave reads 1 KB of consecutive memory; and for
+// batch b of 8 groups:
+//   sb_t[(((t*B + b)*2 + h)*16 + n)*8 + j] = (h ? biases : scales)[(16t + n)*G + 8b + j]
+// (B = K/512 batches, G = K/64 groups).  Rows past N are zero.
+__global__ void __launch_bounds__(256) k_tile_pack(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+                                                   const uint16_t* __restrict__ biases, uint32_t* __restrict__ codes_t,
+                                                   uint16_t* __restrict__ sb_t, int N, int K) {
+  const int C = K / 128, B = K / 512, G = K / 64;
+  const int ntiles = (N + 15) / 16;
+  const size_t ncode = (size_t)ntiles * C * 64;  // 16-byte pieces of codes_t
+  const size_t nsb = (size_t)ntiles * B * 2 * 16;  // 16-byte pieces of sb_t
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < ncode + nsb; i += (size_t)gridDim.x * blockDim.x) {
+    if (i < ncode) {
+      const int l = (int)(i % 64), n = l & 15, kb = l >> 4;
+      const size_t tc = i / 64;
+      const int c = (int)(tc % C), t = (int)(tc / C);
+      const int row = 16 * t + n;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (row < N) v = *reinterpret_cast<const uint4*>(codes + (size_t)row * (K / 8) + 16 * c + 4 * kb);
+      *reinterpret_cast<uint4*>(codes_t + i * 4) = v;
+    } else {
+      const size_t q = i - ncode;
+      const int n = (int)(q % 16), h = (int)((q / 16) % 2);
+      const size_t tb = q / 32;
+      const int b = (int)(tb % B), t = (int)(tb / B);
+      const int row = 16 * t + n;
+      const uint16_t* src = (h ? biases : scales) + (size_t)row * G + 8 * b;
+      uint16_t* dst = sb_t + q * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j] = row < N ? src[j] : (uint16_t)0;
+    }
+  }
+}
+
 }  // namespace qg
+
+int qg_launch_tile_pack(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, uint32_t* codes_t,
+                        uint16_t* sb_t, int N, int K, hipStream_t st) {
+  const size_t pieces = (size_t)((N + 15) / 16) * ((size_t)K / 128 * 64 + (size_t)K / 512 * 32);
+  const unsigned grid = (unsigned)std::min<size_t>(65535, (pieces + 255) / 256);
+  hipLaunchKernelGGL(qg::k_tile_pack, dim3(grid), dim3(256), 0, st, codes, scales, biases, codes_t, sb_t, N, K);
+  return (int)hipGetLastError();
+}
 
 int qg_launch_affine(int mode, const QgAffineArgs& a, size_t lds, hipStream_t st) {
   switch (a.M) {

@@ -131,6 +131,7 @@ struct QgAffineArgs {
   int rgroups;  // workgroups per K slice; workgroup r owns tiles [r*ntiles/rgroups, (r+1)*ntiles/rgroups)
   int waves;    // waves per workgroup
   int wide;     // scales/biases of a whole batch can be loaded as one aligned vector per row
+  int tiled;    // codes / scales hold the tile-order layout (see affine4.hip); biases unused
   // top-k readout (LM head mode with topk > 0): logits must be set; ids is
   // [M][topk]; the selection runs after the projection instead of the argmax
   int topk;
@@ -166,6 +167,10 @@ struct QgMoeArgs {
 int qg_launch_affine(int mode, const QgAffineArgs& a, size_t lds_bytes, hipStream_t stream);
 int qg_launch_q4k(const QgQ4kArgs& a, size_t lds_bytes, hipStream_t stream);
 int qg_launch_moe(const QgMoeArgs& a, hipStream_t stream);
+// Repack canonical affine-4 weights [N][K] (K % 512 == 0) into the tile-order
+// layout the tiled kernels read.
+int qg_launch_tile_pack(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, uint32_t* codes_t,
+                        uint16_t* sb_t, int N, int K, hipStream_t stream);
 // Input randomised Hadamard transform: x [M][K] bf16 and signs [K] to the hi
 // and lo bf16 planes of (1/sqrt(had)) H_had diag(s) x, blockwise along K.
 constexpr int kRhtMax = 4096;  // largest transform block

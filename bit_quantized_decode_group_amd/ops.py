@@ -34,6 +34,12 @@ _SIGS = {
     "qgemv_affine4": [_P, _P, _P, _P, _P, _I, _I, _I, _P],
     "qgemv_q4k": [_P, _P, _P, _I, _I, _I, _P],
     "qgemv_affine4_rht": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P],
+    "affine4_tile_pack": [_P, _P, _P, _P, _P, _I, _I, _P],
+    "qgemv_affine4_tiled": [_P, _P, _P, _P, _I, _I, _I, _P],
+    "lmhead_argmax_tiled": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "qg_check_affine4_tile_pack": [_P, _P, _P, _P, _P, _I, _I],
+    "qg_check_qgemv_affine4_tiled": [_P, _P, _P, _P, _I, _I, _I],
+    "qg_check_lmhead_argmax_tiled": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I],
     "qg_check_qgemv_affine4_rht": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I],
     "rmsnorm_gateup_swiglu": [_P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P],
     "moe_expert_qgemv": [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _P],
@@ -140,6 +146,58 @@ def qgemv_affine4_rht(x, signs, had, codes, scales, biases, y=None):
         _raise_on(lib().qgemv_affine4_rht(_ptr(x), _ptr(signs), int(had), _ptr(codes), _ptr(scales), _ptr(biases),
                                           _ptr(y), M, N, K, _stream()), "qgemv_affine4_rht")
     return y
+
+
+def tile_pack(codes, scales, biases):
+    """Tile-order copies (codes_t int32, sb_t bf16) of canonical affine-4 weights [N, K] (K % 512 == 0)."""
+    N = codes.shape[0]
+    K = codes.shape[1] * 8
+    l = lib()
+    l.qg_tiled_bytes.argtypes = [_I, _I, ctypes.POINTER(ctypes.c_size_t)]
+    l.qg_tiled_bytes.restype = ctypes.c_size_t
+    sbb = ctypes.c_size_t(0)
+    cb = int(l.qg_tiled_bytes(N, K, ctypes.byref(sbb)))
+    if cb == 0:
+        raise ValueError("tile order needs N >= 1 and K % 512 == 0")
+    codes_t = torch.empty(cb // 4, dtype=torch.int32, device=codes.device)
+    sb_t = torch.empty(sbb.value // 2, dtype=torch.bfloat16, device=codes.device)
+    for t, n, e in ((codes, "codes", 4), (scales, "scales", 2), (biases, "biases", 2)):
+        _need(t, n, e, codes.device)
+    with torch.cuda.device(codes.device):
+        _raise_on(l.affine4_tile_pack(_ptr(codes), _ptr(scales), _ptr(biases), _ptr(codes_t), _ptr(sb_t), N, K,
+                                      _stream()), "affine4_tile_pack")
+    return codes_t, sb_t
+
+
+def qgemv_affine4_tiled(x, codes_t, sb_t, N, y=None):
+    """qgemv_affine4 on tile-order weights (from tile_pack) of an [N, K] matrix."""
+    M, K = _dims2(x, "x")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    for t, n, e in ((x, "x", 2), (codes_t, "codes_t", 4), (sb_t, "sb_t", 2), (y, "y", 2)):
+        _need(t, n, e, x.device)
+    with torch.cuda.device(x.device):
+        _raise_on(lib().qgemv_affine4_tiled(_ptr(x), _ptr(codes_t), _ptr(sb_t), _ptr(y), M, N, K, _stream()),
+                  "qgemv_affine4_tiled")
+    return y
+
+
+def lmhead_argmax_tiled(x, codes_t, sb_t, V, draft=None, logits=None, want_logits=False, ids=None, accepted=None):
+    """lmhead_argmax on tile-order weights.  Returns (ids, accepted, logits or None)."""
+    M, K = _dims2(x, "x")
+    if logits is None and want_logits:
+        logits = torch.empty((M, V), dtype=torch.float32, device=x.device)
+    if ids is None:
+        ids = torch.empty(M, dtype=torch.int32, device=x.device)
+    if accepted is None:
+        accepted = torch.empty(1, dtype=torch.int32, device=x.device)
+    for t, n, e in ((x, "x", 2), (codes_t, "codes_t", 4), (sb_t, "sb_t", 2), (logits, "logits", 4),
+                    (ids, "ids", 4), (draft, "draft", 4), (accepted, "accepted", 4)):
+        _need(t, n, e, x.device)
+    with torch.cuda.device(x.device):
+        _raise_on(lib().lmhead_argmax_tiled(_ptr(x), _ptr(codes_t), _ptr(sb_t), _ptr(logits), _ptr(ids), _ptr(draft),
+                                            _ptr(accepted), M, V, K, _stream()), "lmhead_argmax_tiled")
+    return ids, accepted, logits
 
 
 def qgemv_q4k(x, blocks, y=None):

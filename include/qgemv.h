@@ -103,6 +103,41 @@ qg_status qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had,
                             int K, void* stream);
 
 /*
+ * Tile-order layout of affine4 weights (Husky page, section "MSI의 네 가지 구현
+ * 요소": weights stored in the order the projection kernel reads them), for
+ * K % 512 == 0.  With T = ceil(N/16) 16-row tiles, C = K/128 chunks, B = K/512
+ * batches and G = K/64 groups:
+ *   codes_t uint32 [T][C][64][4]:
+ *     codes_t[t][c][16*kb + n][w] = codes[16t + n][16c + 4kb + w]
+ *   sb_t bf16 [T][B][2][16][8]:
+ *     sb_t[t][b][0][n][j] = scales[16t + n][8b + j],
+ *     sb_t[t][b][1][n][j] = biases[16t + n][8b + j]
+ * (kb = 0..3, n = 0..15, w = 0..3, j = 0..7; rows past N are zero).  The same
+ * bytes as the canonical layout, reordered so that every load of a wave
+ * reads consecutive memory.  The tiled entry points compute exactly what
+ * their canonical twins compute, in the same order (bit-identical results).
+ *
+ * qg_tiled_bytes -- bytes of codes_t for [N][K] (0 if K % 512 != 0 or N < 1);
+ *   *sb_bytes (nullable) receives the bytes of sb_t.
+ * affine4_tile_pack -- writes codes_t and sb_t from the canonical arrays
+ *   (device memory, 16-byte aligned outputs); N >= 1, K % 512 == 0.
+ * qgemv_affine4_tiled -- qgemv_affine4 on tile-order weights.
+ * lmhead_argmax_tiled -- lmhead_argmax on tile-order weights.
+ */
+size_t qg_tiled_bytes(int N, int K, size_t* sb_bytes);
+qg_status affine4_tile_pack(const uint32_t* codes, const uint16_t* scales,
+                            const uint16_t* biases, uint32_t* codes_t,
+                            uint16_t* sb_t, int N, int K, void* stream);
+qg_status qgemv_affine4_tiled(const uint16_t* x, const uint32_t* codes_t,
+                              const uint16_t* sb_t, uint16_t* y, int M, int N,
+                              int K, void* stream);
+qg_status lmhead_argmax_tiled(const uint16_t* x, const uint32_t* codes_t,
+                              const uint16_t* sb_t, float* logits,
+                              int32_t* ids, const int32_t* draft,
+                              int32_t* accepted, int M, int V, int K,
+                              void* stream);
+
+/*
  * qgemv_q4k -- Y = X . dequant(W)^T for Q4_K weights.
  *   x bf16 [M][K]; blocks uint8 [N][K/256][144]; y bf16 [M][N].
  *   1 <= M <= 8; N >= 0; K > 0, K % 256 == 0.
@@ -215,6 +250,19 @@ qg_status qg_check_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs,
                                      const uint16_t* scales,
                                      const uint16_t* biases, uint16_t* y, int M,
                                      int N, int K);
+qg_status qg_check_affine4_tile_pack(const uint32_t* codes,
+                                     const uint16_t* scales,
+                                     const uint16_t* biases, uint32_t* codes_t,
+                                     uint16_t* sb_t, int N, int K);
+qg_status qg_check_qgemv_affine4_tiled(const uint16_t* x,
+                                       const uint32_t* codes_t,
+                                       const uint16_t* sb_t, uint16_t* y, int M,
+                                       int N, int K);
+qg_status qg_check_lmhead_argmax_tiled(const uint16_t* x,
+                                       const uint32_t* codes_t,
+                                       const uint16_t* sb_t, float* logits,
+                                       int32_t* ids, const int32_t* draft,
+                                       int32_t* accepted, int M, int V, int K);
 qg_status qg_check_qgemv_q4k(const uint16_t* x, const uint8_t* blocks,
                              uint16_t* y, int M, int N, int K);
 qg_status qg_check_rmsnorm_gateup_swiglu(const uint16_t* x,

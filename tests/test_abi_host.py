@@ -227,3 +227,22 @@ def test_qgemv_affine4_rht_checks(lib):
     split = list(ok)
     split[8], split[9], split[2] = 2560, 12800, 512
     assert c(*split) == ops.QG_OK
+
+
+def test_tiled_layout_checks(lib):
+    c = lambda *a: ops.check("affine4_tile_pack", *a)
+    assert c(A[0], A[1], A[2], A[3], A[4], 151936, 1024) == ops.QG_OK
+    assert c(A[0], A[1], A[2], A[3], A[4], 100, 448) == ops.QG_EINVAL  # K must be a multiple of 512
+    assert c(A[0], A[1], A[2], A[3], A[4], 0, 512) == ops.QG_EINVAL
+    assert c(A[0], A[1], A[2], A[0], A[4], 64, 512) == ops.QG_EALIAS  # codes_t over codes
+    assert c(A[0], A[1], A[2], A[3] + 8, A[4], 64, 512) == ops.QG_EINVAL  # codes_t alignment
+    t = lambda *a: ops.check("qgemv_affine4_tiled", *a)
+    assert t(A[0], A[1], A[2], A[3], 8, 2560, 12800) == ops.QG_OK
+    assert t(A[0], A[1], A[2], A[3], 8, 2560, 1088) == ops.QG_EINVAL
+    assert t(A[0], A[1], A[2], A[1], 8, 2560, 1024) == ops.QG_EALIAS
+    h = lambda *a: ops.check("lmhead_argmax_tiled", *a)
+    assert h(A[0], A[1], A[2], A[3], A[4], A[5], A[6], 8, 151936, 1024) == ops.QG_OK
+    assert h(A[0], A[1], A[2], 0, A[4], 0, 0, 8, 151936, 1024) == ops.QG_OK
+    assert h(A[0], A[1], A[2], A[3], 0, A[5], A[6], 8, 151936, 1024) == ops.QG_EINVAL  # ids required
+    assert h(A[0], A[1], A[2], A[3], A[4], A[5], A[4], 8, 151936, 1024) == ops.QG_EALIAS  # accepted over ids
+    assert h(A[0], A[1], A[2], A[3], A[4], A[5], A[6], 8, 151936, 9216) == ops.QG_EUNSUPPORTED

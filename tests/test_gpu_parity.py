@@ -485,3 +485,53 @@ def test_config_rht_projections(M):
         ref = oracle.qgemv_affine4_rht(d["x"], s, had, d["codes"], d["scales"], d["biases"])
         y = ops.qgemv_affine4_rht(dev_bf16(d["x"]), _dev_i8(s), had, *_affine_dev(d))
         assert_close(host_bf16_f64(y), ref, what=f"rht config M{M} N{N} K{K}")
+
+
+# ---------------------------------------------------- tile-order layout --
+
+def _tile_pack_reference(codes, scales, biases):
+    """The tile-order layout written out with numpy from its definition."""
+    N, W = codes.shape
+    K = W * 8
+    T, C, B, G = (N + 15) // 16, K // 128, K // 512, K // 64
+    cz = np.zeros((T * 16, W), np.uint32)
+    cz[:N] = codes
+    ct = cz.reshape(T, 16, C, 4, 4).transpose(0, 2, 3, 1, 4)  # [t][c][kb][n][w]
+    sz = np.zeros((2, T * 16, G), np.uint16)
+    sz[0, :N], sz[1, :N] = scales, biases
+    sb = sz.reshape(2, T, 16, B, 8).transpose(1, 3, 0, 2, 4)  # [t][b][h][n][j]
+    return np.ascontiguousarray(ct).reshape(-1), np.ascontiguousarray(sb).reshape(-1)
+
+
+@pytest.mark.parametrize("N,K", [(1, 512), (17, 1024), (100, 2560), (40, 12800)])
+def test_tile_pack_matches_definition(N, K):
+    d = synth.single_projection(M=1, N=N, K=K, seed=9400 + N + K)
+    ct, sb = ops.tile_pack(*_affine_dev(d))
+    want_c, want_s = _tile_pack_reference(d["codes"], d["scales"], d["biases"])
+    assert np.array_equal(ct.cpu().numpy().view(np.uint32), want_c)
+    assert np.array_equal(host_bits(sb).reshape(-1), want_s)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 17, 512), (8, 40, 1024), (3, 300, 2560), (8, 2560, 12800), (1, 3072, 1024)])
+def test_qgemv_affine4_tiled_equals_canonical(M, N, K):
+    d = synth.single_projection(M=M, N=N, K=K, seed=9500 + M + N + K)
+    x, (codes, scales, biases) = dev_bf16(d["x"]), _affine_dev(d)
+    y = host_bits(ops.qgemv_affine4(x, codes, scales, biases))
+    ct, sb = ops.tile_pack(codes, scales, biases)
+    yt = host_bits(ops.qgemv_affine4_tiled(x, ct, sb, N))
+    assert np.array_equal(yt, y)  # same arithmetic in the same order
+    ref = oracle.qgemv_affine4(d["x"], d["codes"], d["scales"], d["biases"])
+    assert_close(bits_to_f64(yt), ref, what=f"tiled M{M} N{N} K{K}")
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_lmhead_argmax_tiled_equals_canonical(M):
+    d = synth.lm_head(M=8)
+    xm = d["x"][:M].copy()
+    x, args = dev_bf16(xm), _affine_dev(d)
+    ct, sb = ops.tile_pack(*args)
+    ids, acc, lg = ops.lmhead_argmax(x, *args, draft=dev_i32(d["draft"][:M]), want_logits=True)
+    ids_t, acc_t, lg_t = ops.lmhead_argmax_tiled(x, ct, sb, d["V"], draft=dev_i32(d["draft"][:M]), want_logits=True)
+    assert torch.equal(lg_t, lg) and torch.equal(ids_t, ids) and torch.equal(acc_t, acc)
+    logits, ids_ref, gap, _ = oracle.lmhead(xm, d["codes"], d["scales"], d["biases"])
+    assert_ids(ids_t.cpu().numpy(), ids_ref, gap, logits, what=f"tiled lm head M{M}")
