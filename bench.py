@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m1", action="store_true", help="skip the M=1 step (verify ratio)")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration context timings")
+    ap.add_argument("--layout", choices=["tiled", "canonical"], default="tiled",
+                    help="storage of the affine-4 weights: tile order (packed once at set-up from the canonical "
+                         "arrays; same bytes, reordered) or the canonical [N][K/8] layout")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="short run for a rocprofv3 --pmc pass: a copy of CALIB_BYTES (counter calibration), "
                          "then --steps M=8 steps; prints one JSON line")
@@ -169,6 +172,14 @@ def main():
         "biases_lm": to_dev(lm["biases"], "bf16"),
     }
     copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(C - 1)]
+    tiled = args.layout == "tiled"
+    if tiled:
+        # tile-order copies of the same weights (one pack per matrix, outside the timed region)
+        for c in copies:
+            for key in ("gu", "d", "lm"):
+                ct, sb = ops.tile_pack(c["codes_" + key], c["scales_" + key], c["biases_" + key])
+                c["t_" + key] = (ct, sb)
+                del c["codes_" + key], c["scales_" + key], c["biases_" + key]
     moe_base = {"w_gu": to_dev(moe["w_gu"], "u8"), "w_down": to_dev(moe["w_down"], "u8")}
     moe_stacks = [moe_base, {k: v.clone() for k, v in moe_base.items()}]
     logits = to_dev(moe["logits"], "f32")
@@ -221,17 +232,28 @@ def main():
         lg = logits[i % n_logit_sets]
         if ev is not None:
             ev[0].record()
-        ops.rmsnorm_gateup_swiglu(b["x"], gamma, vb["eps"], c["codes_gu"], c["scales_gu"], c["biases_gu"], h=b["h"])
+        if tiled:
+            ops.rmsnorm_gateup_swiglu_tiled(b["x"], gamma, vb["eps"], *c["t_gu"], I, h=b["h"])
+        else:
+            ops.rmsnorm_gateup_swiglu(b["x"], gamma, vb["eps"], c["codes_gu"], c["scales_gu"], c["biases_gu"],
+                                      h=b["h"])
         if ev is not None:
             ev[1].record()
-        ops.qgemv_affine4(b["h"], c["codes_d"], c["scales_d"], c["biases_d"], y=b["y"])
+        if tiled:
+            ops.qgemv_affine4_tiled(b["h"], *c["t_d"], D, y=b["y"])
+        else:
+            ops.qgemv_affine4(b["h"], c["codes_d"], c["scales_d"], c["biases_d"], y=b["y"])
         if ev is not None:
             ev[2].record()
         ops.moe_expert_qgemv(xm, lg, top_k, ms["w_gu"], ms["w_down"], y=b["ym"], out_ids=b["mids"], out_w=b["mw"])
         if ev is not None:
             ev[3].record()
-        ops.lmhead_argmax(b["xl"], c["codes_lm"], c["scales_lm"], c["biases_lm"], draft=draft[:M].contiguous()
-                          if M < 8 else draft, ids=b["ids"], accepted=b["acc"])
+        dr = draft[:M].contiguous() if M < 8 else draft
+        if tiled:
+            ops.lmhead_argmax_tiled(b["xl"], *c["t_lm"], V, draft=dr, ids=b["ids"], accepted=b["acc"])
+        else:
+            ops.lmhead_argmax(b["xl"], c["codes_lm"], c["scales_lm"], c["biases_lm"], draft=dr, ids=b["ids"],
+                              accepted=b["acc"])
         if ev is not None:
             ev[4].record()
 
@@ -353,7 +375,7 @@ def main():
                 traffic = ent.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+    roofline = {"kernel": dom + ("_tiled" if tiled and dom != "moe_expert_qgemv" else ""), "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": bytes8[dom], "avg_launch_us": round(per8[dom], 2)}
 
@@ -369,7 +391,8 @@ def main():
                                "2560->2x12800->SwiGLU->down 12800->2560 (affine-4 g64) + Q4_K MoE token "
                                "(128 experts, top-8, 2048<->768) + untied LM head X[8,1024] x W[151936,1024] "
                                "(affine-4 g64) greedy verify",
-                   "M": 8, "weight_copies": C, "algorithmic_bytes_per_step": total8,
+                   "M": 8, "weight_copies": C,
+                   "layout": "tile-order (same bytes as canonical, packed at set-up)" if tiled else "canonical", "algorithmic_bytes_per_step": total8,
                    "weight_bytes_per_step": sum(wbytes.values()), "accum": "fp32", "weights": "4-bit"},
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "ms_per_step_m1": round(ms1, 5) if ms1 else None,

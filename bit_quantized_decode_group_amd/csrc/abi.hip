@@ -704,6 +704,41 @@ qg_status lmhead_argmax_tiled(const uint16_t* x, const uint32_t* codes_t, const 
   return run_affine(QG_MODE_LMHEAD, a, (hipStream_t)stream, "lmhead_argmax_tiled");
 }
 
+qg_status qg_check_rmsnorm_gateup_swiglu_tiled(const uint16_t* x, const uint16_t* gamma, float eps,
+                                                const uint32_t* codes_t, const uint16_t* sb_t, uint16_t* h, int M,
+                                                int I, int K) {
+  clear_err();
+  const char* fn = "rmsnorm_gateup_swiglu_tiled";
+  if (I < 1 || (long long)I * 2 * 16 > 0x7FFFFFFFLL) return fail(QG_EINVAL, "%s: I=%d out of range", fn, I);
+  if (!(eps > 0.0f) || eps != eps || eps > 3.0e38f) return fail(QG_EINVAL, "%s: eps must be positive and finite", fn);
+  const Buf out[] = {{h, (size_t)M * I * 2, "h"}};
+  qg_status st = do_check_tiled(fn, x, codes_t, sb_t, M, 2 * I, K, out, 1);
+  if (st) return st;
+  const Buf gm = {gamma, (size_t)K * 2, "gamma"};
+  if ((st = check_ptr(gm, 16, fn)) || (st = check_ptr(out[0], 2, fn))) return st;
+  return check_alias(out, 1, &gm, 1, fn);
+}
+
+qg_status rmsnorm_gateup_swiglu_tiled(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes_t,
+                                      const uint16_t* sb_t, uint16_t* h, int M, int I, int K, void* stream) {
+  qg_status st = qg_check_rmsnorm_gateup_swiglu_tiled(x, gamma, eps, codes_t, sb_t, h, M, I, K);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  QgAffineArgs a{};
+  a.x = x;
+  a.gamma = gamma;
+  a.eps = eps;
+  a.codes = codes_t;
+  a.scales = sb_t;
+  a.biases = sb_t;
+  a.tiled = 1;
+  a.y = h;
+  a.M = M;
+  a.N = 2 * I;  // the tile-order copy of the [2I][K] gate-then-up matrix
+  a.K = K;
+  return run_affine(QG_MODE_GATEUP, a, (hipStream_t)stream, "rmsnorm_gateup_swiglu_tiled");
+}
+
 qg_status rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes_gu,
                                 const uint16_t* scales_gu, const uint16_t* biases_gu, uint16_t* h, int M, int I,
                                 int K, void* stream) {

@@ -507,9 +507,11 @@ __global__ void __launch_bounds__(64) k_lmhead_finalize(QgAffineArgs p, int nwg)
 
 template <int M, bool WIDE>
 static void launch_main(int mode, const QgAffineArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
-  if (a.tiled) {  // tile-order weights: plain projection and LM head only
+  if (a.tiled) {  // tile-order weights: plain projection, gate/up and LM head
     if (mode == QG_MODE_LMHEAD)
       hipLaunchKernelGGL((k_affine<M, QG_MODE_LMHEAD, true, true>), grid, block, lds, st, a);
+    else if (mode == QG_MODE_GATEUP)
+      hipLaunchKernelGGL((k_affine<M, QG_MODE_GATEUP, true, true>), grid, block, lds, st, a);
     else
       hipLaunchKernelGGL((k_affine<M, QG_MODE_PLAIN, true, true>), grid, block, lds, st, a);
     return;

@@ -41,6 +41,8 @@ _SIGS = {
     "qg_check_qgemv_affine4_tiled": [_P, _P, _P, _P, _I, _I, _I],
     "qg_check_lmhead_argmax_tiled": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I],
     "qg_check_qgemv_affine4_rht": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I],
+    "rmsnorm_gateup_swiglu_tiled": [_P, _P, _F, _P, _P, _P, _I, _I, _I, _P],
+    "qg_check_rmsnorm_gateup_swiglu_tiled": [_P, _P, _F, _P, _P, _P, _I, _I, _I],
     "rmsnorm_gateup_swiglu": [_P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P],
     "moe_expert_qgemv": [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "lmhead_argmax": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
@@ -180,6 +182,20 @@ def qgemv_affine4_tiled(x, codes_t, sb_t, N, y=None):
         _raise_on(lib().qgemv_affine4_tiled(_ptr(x), _ptr(codes_t), _ptr(sb_t), _ptr(y), M, N, K, _stream()),
                   "qgemv_affine4_tiled")
     return y
+
+
+def rmsnorm_gateup_swiglu_tiled(x, gamma, eps, codes_t, sb_t, I, h=None):
+    """rmsnorm_gateup_swiglu on the tile-order copy of the [2I, K] gate-then-up matrix."""
+    M, K = _dims2(x, "x")
+    if h is None:
+        h = torch.empty((M, I), dtype=torch.bfloat16, device=x.device)
+    for t, n, e in ((x, "x", 2), (gamma, "gamma", 2), (codes_t, "codes_t", 4), (sb_t, "sb_t", 2), (h, "h", 2)):
+        _need(t, n, e, x.device)
+    with torch.cuda.device(x.device):
+        _raise_on(lib().rmsnorm_gateup_swiglu_tiled(_ptr(x), _ptr(gamma), float(eps), _ptr(codes_t),
+                                                    _ptr(sb_t), _ptr(h), M, I, K, _stream()),
+                  "rmsnorm_gateup_swiglu_tiled")
+    return h
 
 
 def lmhead_argmax_tiled(x, codes_t, sb_t, V, draft=None, logits=None, want_logits=False, ids=None, accepted=None):

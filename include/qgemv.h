@@ -123,6 +123,8 @@ qg_status qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had,
  *   (device memory, 16-byte aligned outputs); N >= 1, K % 512 == 0.
  * qgemv_affine4_tiled -- qgemv_affine4 on tile-order weights.
  * lmhead_argmax_tiled -- lmhead_argmax on tile-order weights.
+ * rmsnorm_gateup_swiglu_tiled -- rmsnorm_gateup_swiglu with codes_t / sb_t the
+ *   tile-order copy of the whole [2I][K] gate-then-up matrix (N = 2I).
  */
 size_t qg_tiled_bytes(int N, int K, size_t* sb_bytes);
 qg_status affine4_tile_pack(const uint32_t* codes, const uint16_t* scales,
@@ -136,6 +138,10 @@ qg_status lmhead_argmax_tiled(const uint16_t* x, const uint32_t* codes_t,
                               int32_t* ids, const int32_t* draft,
                               int32_t* accepted, int M, int V, int K,
                               void* stream);
+qg_status rmsnorm_gateup_swiglu_tiled(const uint16_t* x, const uint16_t* gamma,
+                                      float eps, const uint32_t* codes_t,
+                                      const uint16_t* sb_t, uint16_t* h, int M,
+                                      int I, int K, void* stream);
 
 /*
  * qgemv_q4k -- Y = X . dequant(W)^T for Q4_K weights.
@@ -263,6 +269,12 @@ qg_status qg_check_lmhead_argmax_tiled(const uint16_t* x,
                                        const uint16_t* sb_t, float* logits,
                                        int32_t* ids, const int32_t* draft,
                                        int32_t* accepted, int M, int V, int K);
+qg_status qg_check_rmsnorm_gateup_swiglu_tiled(const uint16_t* x,
+                                               const uint16_t* gamma, float eps,
+                                               const uint32_t* codes_t,
+                                               const uint16_t* sb_t,
+                                               uint16_t* h, int M, int I,
+                                               int K);
 qg_status qg_check_qgemv_q4k(const uint16_t* x, const uint8_t* blocks,
                              uint16_t* y, int M, int N, int K);
 qg_status qg_check_rmsnorm_gateup_swiglu(const uint16_t* x,

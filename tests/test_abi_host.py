@@ -246,3 +246,13 @@ def test_tiled_layout_checks(lib):
     assert h(A[0], A[1], A[2], A[3], 0, A[5], A[6], 8, 151936, 1024) == ops.QG_EINVAL  # ids required
     assert h(A[0], A[1], A[2], A[3], A[4], A[5], A[4], 8, 151936, 1024) == ops.QG_EALIAS  # accepted over ids
     assert h(A[0], A[1], A[2], A[3], A[4], A[5], A[6], 8, 151936, 9216) == ops.QG_EUNSUPPORTED
+
+
+def test_gateup_tiled_checks(lib):
+    c = lambda *a: ops.check("rmsnorm_gateup_swiglu_tiled", *a)
+    assert c(A[0], A[1], 1e-6, A[2], A[3], A[4], 8, 12800, 2560) == ops.QG_OK
+    assert c(A[0], A[1], 1e-6, A[2], A[3], A[4], 8, 12800, 2496) == ops.QG_EINVAL  # K % 512
+    assert c(A[0], A[1], 0.0, A[2], A[3], A[4], 8, 12800, 2560) == ops.QG_EINVAL  # eps
+    assert c(A[0], A[1], 1e-6, A[2], A[3], A[1], 8, 12800, 2560) == ops.QG_EALIAS  # h over gamma
+    assert c(A[0], A[1] + 2, 1e-6, A[2], A[3], A[4], 8, 12800, 2560) == ops.QG_EINVAL  # gamma alignment
+    assert c(A[0], A[1], 1e-6, A[2], A[3], A[4], 9, 12800, 2560) == ops.QG_EINVAL

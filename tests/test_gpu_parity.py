@@ -535,3 +535,31 @@ def test_lmhead_argmax_tiled_equals_canonical(M):
     assert torch.equal(lg_t, lg) and torch.equal(ids_t, ids) and torch.equal(acc_t, acc)
     logits, ids_ref, gap, _ = oracle.lmhead(xm, d["codes"], d["scales"], d["biases"])
     assert_ids(ids_t.cpu().numpy(), ids_ref, gap, logits, what=f"tiled lm head M{M}")
+
+
+@pytest.mark.parametrize("M,I,K", [(1, 16, 512), (8, 33, 1024), (3, 100, 2560)])
+def test_gateup_tiled_equals_canonical(M, I, K):
+    g = synth.rng(9600 + 11 * M + I + K)
+    gu = synth.affine4_matrix(g, 2 * I, K)
+    x, gam = synth.normal_bf16(g, (M, K)), synth.uniform_bf16(g, 0.8, 1.2, (K,))
+    args = (dev_u32(gu["codes"]), dev_bf16(gu["scales"]), dev_bf16(gu["biases"]))
+    h = host_bits(ops.rmsnorm_gateup_swiglu(dev_bf16(x), dev_bf16(gam), 1e-6, *args))
+    ct, sb = ops.tile_pack(*args)
+    ht = host_bits(ops.rmsnorm_gateup_swiglu_tiled(dev_bf16(x), dev_bf16(gam), 1e-6, ct, sb, I))
+    assert np.array_equal(ht, h)
+    ref = oracle.rmsnorm_gateup_swiglu(x, gam, 1e-6, gu["codes"], gu["scales"], gu["biases"])
+    assert_close(bits_to_f64(ht), ref, slack=5e-3, what=f"tiled gateup M{M} I{I} K{K}")
+
+
+@pytest.mark.parametrize("M", [8, 1])
+def test_config_verify_block_4b_tiled(M):
+    """The 4B-class block on tile-order weights: bit-identical to the canonical path."""
+    d = synth.verify_block()
+    if M == 1:
+        d = dict(d, x=d["x"][:1].copy())
+    h, y = _block(d)
+    gu_t = ops.tile_pack(dev_u32(d["codes_gu"]), dev_bf16(d["scales_gu"]), dev_bf16(d["biases_gu"]))
+    dn_t = ops.tile_pack(dev_u32(d["codes_d"]), dev_bf16(d["scales_d"]), dev_bf16(d["biases_d"]))
+    ht = ops.rmsnorm_gateup_swiglu_tiled(dev_bf16(d["x"]), dev_bf16(d["gamma"]), d["eps"], *gu_t, d["I"])
+    yt = ops.qgemv_affine4_tiled(ht, *dn_t, d["D"])
+    assert torch.equal(ht, h) and torch.equal(yt, y)
