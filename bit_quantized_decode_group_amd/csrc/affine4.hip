@@ -245,11 +245,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
       for (int u = 0; u < BATCH; ++u)
         bf.q[u] = *reinterpret_cast<const uint4*>(p.codes + ((tile * p.nchunks + c0 + cb + u) * 64 + lane) * 4);
-      const uint16_t* rec = p.scales + ((tile * (p.nchunks / BATCH) + (c0 + cb) / BATCH) * 2) * 128 + nl * 8;
+      // one 16-byte record per (row, group parity): dword u = (scale, bias) of group 2(c0+cb+u) + half
+      const uint16_t* rec = p.scales + ((tile * (p.nchunks / BATCH) + (c0 + cb) / BATCH) * 2 + half) * 128 + nl * 8;
       const uint4 sv = *reinterpret_cast<const uint4*>(rec);
-      const uint4 bv = *reinterpret_cast<const uint4*>(rec + 128);
       bf.sw[0] = sv.x; bf.sw[1] = sv.y; bf.sw[2] = sv.z; bf.sw[3] = sv.w;
-      bf.bw[0] = bv.x; bf.bw[1] = bv.y; bf.bw[2] = bv.z; bf.bw[3] = bv.w;
       return;
     }
 #pragma unroll
@@ -337,8 +336,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     for (int u = 0; u < BATCH; ++u) {
       if (WIDE || cb + u < nc) {
         const float4 sxv = *reinterpret_cast<const float4*>(sx_base + (cb + u) * 16);
-        const float sc = __uint_as_float((bf.sw[u] >> (16 * half)) << 16);
-        const float cbias = fmaf(-128.0f, sc, __uint_as_float((bf.bw[u] >> (16 * half)) << 16));
+        float sc, cbias;
+        if constexpr (TILED) {  // (scale, bias) of this lane's group in one dword
+          sc = __uint_as_float(bf.sw[u] << 16);
+          cbias = fmaf(-128.0f, sc, __uint_as_float(bf.sw[u] & 0xFFFF0000u));
+        } else {
+          sc = __uint_as_float((bf.sw[u] >> (16 * half)) << 16);
+          cbias = fmaf(-128.0f, sc, __uint_as_float((bf.bw[u] >> (16 * half)) << 16));
+        }
         acc[0] = fmaf(sc, C[u][0], fmaf(cbias, sxv.x, acc[0]));
         acc[1] = fmaf(sc, C[u][1], fmaf(cbias, sxv.y, acc[1]));
         acc[2] = fmaf(sc, C[u][2], fmaf(cbias, sxv.z, acc[2]));
@@ -562,9 +567,11 @@ static int launch_affine_m(int mode, const QgAffineArgs& a, size_t lds, hipStrea
 //   codes_t[((t*C + c)*64 + l)*4 + w] = codes[(16t + n)*(K/8) + 16c + 4kb + w]
 // (C = K/128 chunks; w = 0..3), i.e. the 16 bytes lane l loads for chunk c,
 // so a load of the whole wave reads 1 KB of consecutive memory; and for
-// batch b of 8 groups:
-//   sb_t[(((t*B + b)*2 + h)*16 + n)*8 + j] = (h ? biases : scales)[(16t + n)*G + 8b + j]
-// (B = K/512 batches, G = K/64 groups).  Rows past N are zero.
+// batch b of 8 groups, group parity h and u = 0..3:
+//   sb_t[(((t*B + b)*2 + h)*16 + n)*8 + 2u]     = scales[(16t + n)*G + 8b + 2u + h]
+//   sb_t[(((t*B + b)*2 + h)*16 + n)*8 + 2u + 1] = biases[(16t + n)*G + 8b + 2u + h]
+// (B = K/512 batches, G = K/64 groups): the 16 bytes a lane of parity h needs
+// for one step.  Rows past N are zero.
 __global__ void __launch_bounds__(256) k_tile_pack(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                                    const uint16_t* __restrict__ biases, uint32_t* __restrict__ codes_t,
                                                    uint16_t* __restrict__ sb_t, int N, int K) {
@@ -587,10 +594,13 @@ __global__ void __launch_bounds__(256) k_tile_pack(const uint32_t* __restrict__ 
       const size_t tb = q / 32;
       const int b = (int)(tb % B), t = (int)(tb / B);
       const int row = 16 * t + n;
-      const uint16_t* src = (h ? biases : scales) + (size_t)row * G + 8 * b;
+      const size_t g0 = (size_t)row * G + 8 * b + h;
       uint16_t* dst = sb_t + q * 8;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) dst[j] = row < N ? src[j] : (uint16_t)0;
+      for (int u = 0; u < 4; ++u) {
+        dst[2 * u] = row < N ? scales[g0 + 2 * u] : (uint16_t)0;
+        dst[2 * u + 1] = row < N ? biases[g0 + 2 * u] : (uint16_t)0;
+      }
     }
   }
 }

@@ -109,10 +109,11 @@ qg_status qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had,
  * batches and G = K/64 groups:
  *   codes_t uint32 [T][C][64][4]:
  *     codes_t[t][c][16*kb + n][w] = codes[16t + n][16c + 4kb + w]
- *   sb_t bf16 [T][B][2][16][8]:
- *     sb_t[t][b][0][n][j] = scales[16t + n][8b + j],
- *     sb_t[t][b][1][n][j] = biases[16t + n][8b + j]
- * (kb = 0..3, n = 0..15, w = 0..3, j = 0..7; rows past N are zero).  The same
+ *   sb_t bf16 [T][B][2][16][4][2]:
+ *     sb_t[t][b][h][n][u][0] = scales[16t + n][8b + 2u + h],
+ *     sb_t[t][b][h][n][u][1] = biases[16t + n][8b + 2u + h]
+ * (kb = 0..3, n = 0..15, w = 0..3, h = 0..1, u = 0..3; rows past N are zero:
+ * the (scale, bias) pairs of the even, then the odd groups).  The same
  * bytes as the canonical layout, reordered so that every load of a wave
  * reads consecutive memory.  The tiled entry points compute exactly what
  * their canonical twins compute, in the same order (bit-identical results).

@@ -497,9 +497,10 @@ def _tile_pack_reference(codes, scales, biases):
     cz = np.zeros((T * 16, W), np.uint32)
     cz[:N] = codes
     ct = cz.reshape(T, 16, C, 4, 4).transpose(0, 2, 3, 1, 4)  # [t][c][kb][n][w]
-    sz = np.zeros((2, T * 16, G), np.uint16)
+    sz = np.zeros((2, T * 16, G), np.uint16)  # [scale or bias][row][group]
     sz[0, :N], sz[1, :N] = scales, biases
-    sb = sz.reshape(2, T, 16, B, 8).transpose(1, 3, 0, 2, 4)  # [t][b][h][n][j]
+    # group 8b + 2u + h -> [s][t][n][b][u][h]
+    sb = sz.reshape(2, T, 16, B, 4, 2).transpose(1, 3, 5, 2, 4, 0)  # [t][b][h][n][u][s]
     return np.ascontiguousarray(ct).reshape(-1), np.ascontiguousarray(sb).reshape(-1)
 
 
