@@ -35,6 +35,7 @@ KERNEL_SOURCES = ["bit_quantized_decode_group_amd/csrc/common.h", "bit_quantized
                   "bit_quantized_decode_group_amd/csrc/q4k.hip", "bit_quantized_decode_group_amd/csrc/abi.hip",
                   "bit_quantized_decode_group_amd/csrc/topk.hip", "bit_quantized_decode_group_amd/csrc/rht.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+GRAPH_STEPS = 10  # at most this many consecutive steps (rotating weights, MoE stacks, router logits) per graph
 CALIB_BYTES = 384 << 20  # bytes read and written by the kernel that calibrates the HBM byte counters
 # kernels launched by each entry point (once per call) at M = 8
 ENTRY_KERNELS = {
@@ -66,6 +67,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m1", action="store_true", help="skip the M=1 step (verify ratio)")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration context timings")
+    ap.add_argument("--submission", choices=["graph", "eager"], default="eager",
+                    help="timed steps replayed from a HIP graph of GRAPH_STEPS captured steps, or launched eagerly")
     ap.add_argument("--layout", choices=["tiled", "canonical"], default="tiled",
                     help="storage of the affine-4 weights: tile order (packed once at set-up from the canonical "
                          "arrays; same bytes, reordered) or the canonical [N][K/8] layout")
@@ -259,32 +262,66 @@ def main():
 
     spread = {}
 
+    graph_checks = {}
+
     def timed(M, steps, warmup):
         b = bufs(M)
-        for i in range(warmup):
-            run_step(i, M, b)
+        use_graph = args.submission == "graph"
+        s = torch.cuda.Stream() if use_graph else torch.cuda.current_stream()
+        with torch.cuda.stream(s):
+            for i in range(warmup):
+                run_step(i, M, b)
         torch.cuda.synchronize()
+        # graph length: the largest divisor of the step count up to GRAPH_STEPS, so
+        # that exactly `steps` steps are timed
+        glen = max(d for d in range(1, GRAPH_STEPS + 1) if steps % d == 0) if use_graph else 1
+        if use_graph:
+            # the library's per-stream workspace is in place after the warm-up on s;
+            # the graph holds glen consecutive steps and every replay repeats them
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for i in range(glen):
+                    run_step(i, M, b)
+            torch.cuda.synchronize()
         # K steps timed start to end; events at five sub-batch boundaries (no
         # synchronisation between them) give the spread of the per-step time
-        nsub = 5 if steps >= 5 else 1
-        cut = [round(steps * j / nsub) for j in range(nsub + 1)]
+        units = steps // glen
+        nsub = 5 if units >= 5 else 1
+        cut = [round(units * j / nsub) for j in range(nsub + 1)]
         evb = [torch.cuda.Event(enable_timing=True) for _ in range(nsub + 1)]
         w0 = time.perf_counter()
-        evb[0].record()
-        for j in range(nsub):
-            for i in range(cut[j], cut[j + 1]):
-                run_step(warmup + i, M, b)
-            evb[j + 1].record()
+        with torch.cuda.stream(s):
+            evb[0].record()
+            for j in range(nsub):
+                for i in range(cut[j], cut[j + 1]):
+                    if use_graph:
+                        g.replay()
+                    else:
+                        run_step(warmup + i, M, b)
+                evb[j + 1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
+        per_unit = glen
         ms_step = evb[0].elapsed_time(evb[nsub]) / steps
-        sub = [evb[j].elapsed_time(evb[j + 1]) / (cut[j + 1] - cut[j]) for j in range(nsub)]
+        if use_graph:
+            # the replayed outputs (those of captured step glen - 1) against the same step run eagerly
+            b2 = bufs(M)
+            with torch.cuda.stream(s):
+                run_step(glen - 1, M, b2)
+            torch.cuda.synchronize()
+            same = all(torch.equal(b[k], b2[k]) for k in ("h", "y", "ym", "mids", "mw", "ids", "acc"))
+            if not same:
+                raise SystemExit(f"bench.py: graph replay at M={M} differs from the eager step")
+            graph_checks[f"M{M}"] = f"{glen}-step graph: replay == eager (bit-identical)"
+            del g
+        sub = [evb[j].elapsed_time(evb[j + 1]) / ((cut[j + 1] - cut[j]) * per_unit) for j in range(nsub)]
         spread[M] = {"median_ms": round(float(np.median(sub)), 5), "p10_ms": round(float(np.percentile(sub, 10)), 5),
                      "p90_ms": round(float(np.percentile(sub, 90)), 5), "sub_batches": nsub}
         # per-kernel durations: the same steps again with events around each launch
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
-        for i in range(steps):
-            run_step(warmup + steps + i, M, b, evs[i])
+        with torch.cuda.stream(s):
+            for i in range(steps):
+                run_step(warmup + steps + i, M, b, evs[i])
         torch.cuda.synchronize()
         per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)])) * 1e3
                for j, n in enumerate(names)}
@@ -392,6 +429,8 @@ def main():
                                "(128 experts, top-8, 2048<->768) + untied LM head X[8,1024] x W[151936,1024] "
                                "(affine-4 g64) greedy verify",
                    "M": 8, "weight_copies": C,
+                   "submission": ("HIP graph replays of captured steps" if args.submission == "graph"
+                                  else "eager launches"),
                    "layout": "tile-order (same bytes as canonical, packed at set-up)" if tiled else "canonical", "algorithmic_bytes_per_step": total8,
                    "weight_bytes_per_step": sum(wbytes.values()), "accum": "fp32", "weights": "4-bit"},
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
@@ -409,6 +448,7 @@ def main():
         "step_spread": {f"M{m}": v for m, v in spread.items()},
         "configs_context": cfg,
         "instrumented_ms_per_step": round(inst8, 5),
+        "graph_check": graph_checks or None,
         "wall_s_timed": round(wall8, 4),
         "kernel_source_hash": kernel_source_hash(),
     }
