@@ -75,6 +75,23 @@ def affine4_matrix(g: np.random.Generator, N: int, K: int, s_lo=0.005, s_hi=0.02
     return {"codes": codes, "scales": scales, "biases": biases}
 
 
+def affine8_matrix(g: np.random.Generator, N: int, K: int, s_lo=0.0003, s_hi=0.0012, b_lo=-0.1, b_hi=0.1):
+    """8-bit affine weights: dict(codes uint32 [N, K/4] of uniform random bytes, scales and biases
+    uint16 [N, K/64]); scales span the same weight range as the 4-bit matrices' over 255 steps."""
+    assert K % AFFINE_GROUP == 0
+    codes = g.integers(0, 2**32, size=(N, K // 4), dtype=np.uint64).astype(np.uint32)
+    scales = uniform_bf16(g, s_lo, s_hi, (N, K // AFFINE_GROUP))
+    biases = uniform_bf16(g, b_lo, b_hi, (N, K // AFFINE_GROUP))
+    return {"codes": codes, "scales": scales, "biases": biases}
+
+
+def single_projection8(M=1, N=3072, K=1024, seed=1006):
+    """X[M,K] ~ N(0,1) bf16 and an 8-bit affine W[N,K] (group 64)."""
+    g = rng(seed)
+    x = normal_bf16(g, (M, K))
+    return {"x": x, **affine8_matrix(g, N, K), "M": M, "N": N, "K": K, "seed": seed}
+
+
 def q4k_matrix(g: np.random.Generator, N: int, K: int, d_lo=1e-3, d_hi=1e-2) -> np.ndarray:
     """Returns uint8 [N, K/256, 144] Q4_K blocks."""
     assert K % Q4K_BLOCK_WEIGHTS == 0

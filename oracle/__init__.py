@@ -7,7 +7,7 @@ lives in ``oracle.c`` (plain C, double precision, ascending summation order),
 and this module only marshals numpy arrays into it.
 
 Which step of the method each function follows is documented in ``oracle.h``
-next to its declaration (O0-O8), with the page and section it comes from.
+next to its declaration (O0-O13), with the page and section it comes from.
 """
 from __future__ import annotations
 
@@ -58,6 +58,8 @@ def _load():
         lib.oracle_dequant_q4k.argtypes = [P, I64, I64, I64, I64, P]
         lib.oracle_qgemv_affine4.argtypes = [P, P, P, P, I, I64, I64, P]
         lib.oracle_qgemv_affine4_f64x.argtypes = [P, P, P, P, I, I64, I64, P]
+        lib.oracle_dequant_affine8.argtypes = [P, P, P, I64, I64, I64, I64, P]
+        lib.oracle_qgemv_affine8.argtypes = [P, P, P, P, I, I64, I64, P]
         lib.oracle_qgemv_q4k.argtypes = [P, P, I, I64, I64, P]
         lib.oracle_rmsnorm.argtypes = [P, P, D, I, I64, P]
         lib.oracle_silu.argtypes = [D]
@@ -72,7 +74,8 @@ def _load():
         for name in ("oracle_dequant_affine4", "oracle_dequant_q4k", "oracle_qgemv_affine4",
                      "oracle_qgemv_affine4_f64x", "oracle_qgemv_q4k", "oracle_rmsnorm",
                      "oracle_rmsnorm_gateup_swiglu", "oracle_mlp_block", "oracle_moe",
-                     "oracle_lmhead", "oracle_lmhead_topk", "oracle_rht", "oracle_qgemv_affine4_rht"):
+                     "oracle_lmhead", "oracle_lmhead_topk", "oracle_rht", "oracle_qgemv_affine4_rht",
+                     "oracle_dequant_affine8", "oracle_qgemv_affine8"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -145,6 +148,33 @@ def qgemv_affine4(x, codes, scales, biases) -> np.ndarray:
     y = np.empty((M, N), dtype=np.float64)
     _check(_load().oracle_qgemv_affine4(px, pc, ps, pb, M, N, K, y.ctypes.data_as(ctypes.c_void_p)),
            "qgemv_affine4")
+    return y
+
+
+def dequant_affine8(codes, scales, biases) -> np.ndarray:
+    """O12: the whole affine-8 matrix as fp64 [N, K]."""
+    codes, pc = _c(codes, np.uint32)
+    _, ps = _c(scales, np.uint16)
+    _, pb = _c(biases, np.uint16)
+    N, K = codes.shape[0], codes.shape[1] * 4
+    w = np.empty((N, K), dtype=np.float64)
+    _check(_load().oracle_dequant_affine8(pc, ps, pb, N, K, 0, N, w.ctypes.data_as(ctypes.c_void_p)),
+           "dequant_affine8")
+    return w
+
+
+def qgemv_affine8(x, codes, scales, biases) -> np.ndarray:
+    """O13: Y = X . dequant8(W)^T in fp64."""
+    x, px = _c(x, np.uint16)
+    codes, pc = _c(codes, np.uint32)
+    _, ps = _c(scales, np.uint16)
+    _, pb = _c(biases, np.uint16)
+    M, K = x.shape
+    N = codes.shape[0]
+    assert codes.shape[1] * 4 == K
+    y = np.empty((M, N), dtype=np.float64)
+    _check(_load().oracle_qgemv_affine8(px, pc, ps, pb, M, N, K, y.ctypes.data_as(ctypes.c_void_p)),
+           "qgemv_affine8")
     return y
 
 

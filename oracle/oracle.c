@@ -507,3 +507,52 @@ int oracle_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had,
   free(xr);
   return rc;
 }
+
+/* ---------------------------------------------------------------- O12 --- */
+/* Affine 8-bit, group 64 along K (the uzu page's weight_matrix row names MLX
+ * 4- and 8-bit quantized weights).  Reading, the 8-bit twin of O1: code k of
+ * row n is byte k%4 (least significant first) of word k/4 of that row, an
+ * unsigned value 0..255; the weight is scale*code + bias with the bf16 scale
+ * and bias of group k/64. */
+int oracle_dequant_affine8(const uint32_t* codes, const uint16_t* scales,
+                           const uint16_t* biases, int64_t N, int64_t K,
+                           int64_t n0, int64_t nr, double* w) {
+  if (!codes || !scales || !biases || !w) return -1;
+  if (N < 0 || K <= 0 || K % 64 != 0 || n0 < 0 || nr < 0 || n0 + nr > N)
+    return -1;
+  const int64_t words = K / 4, groups = K / 64;
+  for (int64_t r = 0; r < nr; ++r) {
+    const int64_t n = n0 + r;
+    for (int64_t k = 0; k < K; ++k) {
+      uint32_t word = codes[n * words + k / 4];
+      unsigned q = (unsigned)((word >> (8 * (k % 4))) & 255u);
+      double s = o_bf16_to_f64(scales[n * groups + k / 64]);
+      double b = o_bf16_to_f64(biases[n * groups + k / 64]);
+      w[r * K + k] = s * (double)q + b;
+    }
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------- O13 --- */
+/* O3 on affine-8 weights: y[m][n] = sum_k x[m][k] * w[n][k], ascending k. */
+int oracle_qgemv_affine8(const uint16_t* x, const uint32_t* codes,
+                         const uint16_t* scales, const uint16_t* biases, int M,
+                         int64_t N, int64_t K, double* y) {
+  if (!x || !y || M < 1 || N < 0 || K <= 0) return -1;
+  double* xd = decode_bf16_rows(x, M, K);
+  if (!xd) return -1;
+  double* wrow = (double*)malloc(sizeof(double) * (size_t)K);
+  if (!wrow) {
+    free(xd);
+    return -1;
+  }
+  int rc = 0;
+  for (int64_t n = 0; n < N && rc == 0; ++n) {
+    rc = oracle_dequant_affine8(codes, scales, biases, N, K, n, 1, wrow);
+    for (int m = 0; m < M && rc == 0; ++m) y[(int64_t)m * N + n] = dot_asc(xd + (int64_t)m * K, wrow, K);
+  }
+  free(wrow);
+  free(xd);
+  return rc;
+}

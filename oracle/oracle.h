@@ -21,6 +21,8 @@
  *   O9  LM-head top-k readout (candidate pools)
  *   O10 input randomised Hadamard transform (blockwise, Sylvester order)
  *   O11 affine-4 projection of the transformed input
+ *   O12 MLX-style affine 8-bit dequantisation, group 64
+ *   O13 Y = X . W^T on affine-8 weights
  *
  * Sources (the four pages the method is taken from):
  *   [uzu]        "trymirai/uzu ... deep dive" (blog.123qwe.co.kr), section
@@ -148,6 +150,18 @@ int oracle_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had,
                              const uint32_t* codes, const uint16_t* scales,
                              const uint16_t* biases, int M, int64_t N,
                              int64_t K, double* y);
+
+/* O12: rows [n0, n0+nr) of an affine-8 matrix W[N][K] -> w[nr][K].
+ * codes: uint32 [N][K/4] (code k in byte k%4 of word k/4, least significant
+ * byte first), scales/biases: bf16 [N][K/64]. K % 64 == 0. */
+int oracle_dequant_affine8(const uint32_t* codes, const uint16_t* scales,
+                           const uint16_t* biases, int64_t N, int64_t K,
+                           int64_t n0, int64_t nr, double* w);
+
+/* O13: O3 on affine-8 weights; x bf16 [M][K], y fp64 [M][N]. */
+int oracle_qgemv_affine8(const uint16_t* x, const uint32_t* codes,
+                         const uint16_t* scales, const uint16_t* biases,
+                         int M, int64_t N, int64_t K, double* y);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,15 @@ def pack_affine4_codes(q):
     return words.astype(np.uint32)
 
 
+def pack_affine8_codes(q):
+    """q: int array [N, K] with values 0..255 -> uint32 [N, K/4]: the bytes laid out in order and
+    read back as little-endian words (a byte view, no shifts)."""
+    q = np.ascontiguousarray(np.asarray(q).astype(np.uint8))
+    N, K = q.shape
+    assert K % 4 == 0
+    return q.view("<u4").reshape(N, K // 4).astype(np.uint32)
+
+
 def pack_q4k_scales(sc, m):
     """sc, m: int arrays [..., 8] of 6-bit values -> uint8 [..., 12]."""
     sc = np.asarray(sc, dtype=np.uint8)

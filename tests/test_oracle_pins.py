@@ -606,3 +606,121 @@ def test_rht_projection_is_plain_projection_of_transformed_rows():
         oracle.rht(d["x"], s, 96)  # not a power of two
     with pytest.raises(ValueError):
         oracle.rht(d["x"], s, 512)  # does not divide K
+
+
+# ------------------------------------------------- affine-8 (hand-packed) --
+# K = 128 (two groups of 64), two rows, codes one byte each, least significant
+# byte of a word first.
+# Row 0: code of weight k is 2k           -> words 0x06040200, 0x0E0C0A08, ...
+#        group 0: scale 0.5, bias -2.0;  group 1: scale 0.25, bias 1.0
+# Row 1: code of weight k is 255 - k      -> words 0xFCFDFEFF, 0xF8F9FAFB, ...
+#        group 0: scale 2.0, bias 0.0;   group 1: scale 0.125, bias -0.5
+HAND8_WORDS = {(0, 0): 0x06040200, (0, 1): 0x0E0C0A08, (0, 31): 0xFEFCFAF8,
+               (1, 0): 0xFCFDFEFF, (1, 1): 0xF8F9FAFB, (1, 31): 0x80818283}
+HAND8_SCALES = np.array([[0x3F00, 0x3E80], [0x4000, 0x3E00]], dtype=np.uint16)
+HAND8_BIASES = np.array([[0xC000, 0x3F80], [0x0000, 0xBF00]], dtype=np.uint16)
+HAND8_VALUES = {
+    (0, 0): -2.0, (0, 3): 1.0, (0, 63): 61.0, (0, 64): 33.0, (0, 127): 64.5,
+    (1, 0): 510.0, (1, 5): 500.0, (1, 63): 384.0, (1, 64): 23.375, (1, 127): 15.5,
+}
+
+
+def _hand8_codes():
+    k = np.arange(128)
+    return packers.pack_affine8_codes(np.stack([2 * k, 255 - k]))
+
+
+def test_affine8_hand_packed_words_and_dequant():
+    codes = _hand8_codes()
+    for (n, j), word in HAND8_WORDS.items():
+        assert int(codes[n, j]) == word, (n, j, hex(int(codes[n, j])))
+    w = oracle.dequant_affine8(codes, HAND8_SCALES, HAND8_BIASES)
+    for (n, k), v in HAND8_VALUES.items():
+        assert w[n, k] == v, (n, k, w[n, k], v)
+    k = np.arange(128)
+    assert np.array_equal(w[0], np.where(k < 64, k - 2.0, k / 2.0 + 1.0))
+    assert np.array_equal(w[1], np.where(k < 64, 2.0 * (255 - k), 0.125 * (255 - k) - 0.5))
+
+
+def test_affine8_one_hot_reads_single_weights():
+    ks = [0, 3, 63, 64, 127, 5]
+    x = np.zeros((len(ks), 128), dtype=np.uint16)
+    for m, k in enumerate(ks):
+        x[m, k] = 0x3F80
+    y = oracle.qgemv_affine8(x, _hand8_codes(), HAND8_SCALES, HAND8_BIASES)
+    for m, k in enumerate(ks):
+        for n in range(2):
+            if (n, k) in HAND8_VALUES:
+                assert y[m, n] == HAND8_VALUES[(n, k)]
+
+
+def test_affine8_small_codes_equal_affine4():
+    """Codes below 16 are the same weights in either format: the two oracles,
+    with their own unpackers, must agree exactly."""
+    g = np.random.default_rng(21)
+    N, K, M = 7, 512, 3
+    q = g.integers(0, 16, (N, K))
+    sc = synth.uniform_bf16(g, 0.005, 0.02, (N, K // 64))
+    bi = synth.uniform_bf16(g, -0.1, 0.1, (N, K // 64))
+    x = synth.normal_bf16(g, (M, K))
+    y8 = oracle.qgemv_affine8(x, packers.pack_affine8_codes(q), sc, bi)
+    y4 = oracle.qgemv_affine4(x, packers.pack_affine4_codes(q), sc, bi)
+    assert np.array_equal(y8, y4)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 5, 256), (8, 7, 1024)])
+def test_affine8_exact_integer_arithmetic(M, N, K):
+    g = np.random.default_rng(200 + M)
+    q = g.integers(0, 256, (N, K))
+    s_int = g.choice([1, 2], size=(N, K // 64))
+    b_int = g.integers(-8, 9, (N, K // 64))
+    x_int = g.integers(-16, 17, (M, K))  # |partial sums| stay far below 2^53
+    y = oracle.qgemv_affine8(_bf16_of_small_ints(x_int), packers.pack_affine8_codes(q), _bf16_of_small_ints(s_int),
+                             _bf16_of_small_ints(b_int))
+    w_int = s_int.repeat(64, axis=1) * q + b_int.repeat(64, axis=1)
+    exact = x_int.astype(np.int64) @ w_int.astype(np.int64).T
+    assert np.array_equal(y, exact.astype(np.float64))
+
+
+def test_affine8_requant_recovers_every_code():
+    g = np.random.default_rng(22)
+    N, K = 4, 512
+    q = np.stack([g.permutation(512) % 256 for _ in range(N)])  # every code 0..255 in every row
+    sc = synth.uniform_bf16(g, 0.0003, 0.0012, (N, K // 64))
+    bi = synth.uniform_bf16(g, -0.1, 0.1, (N, K // 64))
+    w = oracle.dequant_affine8(packers.pack_affine8_codes(q), sc, bi)
+    s = _bf16_bits_to_f64(sc).repeat(64, axis=1)
+    b = _bf16_bits_to_f64(bi).repeat(64, axis=1)
+    assert np.array_equal(np.rint((w - b) / s).astype(np.int64), q)
+
+
+def test_affine8_packed_words_round_trip_through_oracle():
+    g = np.random.default_rng(23)
+    words = g.integers(0, 2**32, (3, 32), dtype=np.uint64).astype(np.uint32)
+    ones = np.full((3, 2), 0x3F80, np.uint16)
+    zeros = np.zeros((3, 2), np.uint16)
+    q = oracle.dequant_affine8(words, ones, zeros).astype(np.int64)
+    assert q.min() >= 0 and q.max() <= 255
+    assert np.array_equal(packers.pack_affine8_codes(q), words)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+@pytest.mark.parametrize("N", [1, 16])
+def test_affine8_brute_force_small(M, N):
+    d = synth.single_projection8(M=M, N=N, K=64, seed=2100 + M + N)
+    y = oracle.qgemv_affine8(d["x"], d["codes"], d["scales"], d["biases"])
+    q = d["codes"].view("<u1").reshape(N, 64).astype(np.float64)  # bytes in memory order
+    w = q * _bf16_bits_to_f64(d["scales"]) + _bf16_bits_to_f64(d["biases"])
+    x = _bf16_bits_to_f64(d["x"])
+    ref = np.zeros((M, N))
+    for k in reversed(range(64)):
+        ref += np.outer(x[:, k], w[:, k])
+    assert np.max(np.abs(y - ref)) <= 1e-12 * math.sqrt(np.mean(ref ** 2))
+
+
+def test_affine8_rejects_bad_shapes():
+    codes = np.zeros((2, 16), np.uint32)
+    sc = np.zeros((2, 1), np.uint16)
+    with pytest.raises(Exception):
+        oracle.qgemv_affine8(np.zeros((1, 60), np.uint16), np.zeros((2, 15), np.uint32), sc, sc)
+    assert oracle.qgemv_affine8(np.zeros((1, 64), np.uint16), codes, sc, sc).shape == (1, 2)
