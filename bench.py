@@ -512,6 +512,24 @@ def config_timings(torch, ops, synth, to_dev, dev):
         res[f"M{M}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
     out["projection_tiled_3072x1024"] = res
     del tcs
+    # 8-bit affine projections: X[M,1024] x W[3072,1024] and the 4B-class down shape W[2560,12800]
+    res = {}
+    for (N8, K8) in ((3072, 1024), (2560, 12800)):
+        d8 = synth.single_projection8(M=8, N=N8, K=K8, seed=1006 + K8)
+        w = {k: to_dev(d8[k], "u32" if k == "codes" else "bf16") for k in ("codes", "scales", "biases")}
+        nb = int(d8["codes"].nbytes + d8["scales"].nbytes + d8["biases"].nbytes)
+        n = max(2, (512 << 20) // nb + 1)
+        cps = [w] + [{k: v.clone() for k, v in w.items()} for _ in range(n - 1)]
+        x8a = to_dev(d8["x"], "bf16")
+        for M in (1, 8):
+            xm = x8a[:M].contiguous()
+            ym = torch.empty((M, N8), dtype=torch.bfloat16, device=dev)
+            us = per_call(lambda i: ops.qgemv_affine8(xm, cps[i % n]["codes"], cps[i % n]["scales"],
+                                                      cps[i % n]["biases"], y=ym), n, 3 * n)
+            b = nb + M * K8 * 2 + M * N8 * 2
+            res[f"{N8}x{K8}_M{M}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
+        del cps
+    out["projection_affine8"] = res
     # MLP block D=1024, I=3072 (RMSNorm -> gate/up -> SwiGLU -> down), M = 1 and 8
     mb = synth.mlp_block(M=8)
     keys = {"codes_gu": "u32", "scales_gu": "bf16", "biases_gu": "bf16", "codes_d": "u32", "scales_d": "bf16",

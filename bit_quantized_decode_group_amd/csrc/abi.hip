@@ -215,6 +215,23 @@ qg_status do_check_qgemv_affine4(const uint16_t* x, const uint32_t* codes, const
   return check_alias(out, 1, in, 4, fn);
 }
 
+qg_status do_check_qgemv_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                                 const uint16_t* biases, uint16_t* y, int M, int N, int K) {
+  const char* fn = "qgemv_affine8";
+  qg_status st = check_affine_common(fn, M, N, K);
+  if (st) return st;
+  const size_t n = (size_t)N, k = (size_t)K;
+  const Buf in[] = {{x, (size_t)M * k * 2, "x"},
+                    {codes, n * k, "codes"},
+                    {scales, n * (k / 64) * 2, "scales"},
+                    {biases, n * (k / 64) * 2, "biases"}};
+  const Buf out[] = {{y, (size_t)M * n * 2, "y"}};
+  if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(in[2], 2, fn)) ||
+      (st = check_ptr(in[3], 2, fn)) || (st = check_ptr(out[0], 2, fn)))
+    return st;
+  return check_alias(out, 1, in, 4, fn);
+}
+
 qg_status do_check_qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K) {
   const char* fn = "qgemv_q4k";
   if (M < 1 || M > 8) return fail(QG_EINVAL, "%s: M=%d must be in 1..8", fn, M);
@@ -570,6 +587,31 @@ qg_status qgemv_affine4(const uint16_t* x, const uint32_t* codes, const uint16_t
   a.N = N;
   a.K = K;
   return run_affine(QG_MODE_PLAIN, a, (hipStream_t)stream, "qgemv_affine4");
+}
+
+qg_status qg_check_qgemv_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                                 const uint16_t* biases, uint16_t* y, int M, int N, int K) {
+  clear_err();
+  return do_check_qgemv_affine8(x, codes, scales, biases, y, M, N, K);
+}
+
+qg_status qgemv_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                        uint16_t* y, int M, int N, int K, void* stream) {
+  clear_err();
+  qg_status st = do_check_qgemv_affine8(x, codes, scales, biases, y, M, N, K);
+  if (st) return st;
+  if (N == 0) return QG_OK;
+  if ((st = check_device())) return st;
+  QgAffineArgs a{};
+  a.x = x;
+  a.codes = codes;
+  a.scales = scales;
+  a.biases = biases;
+  a.y = y;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  return run_affine(QG_MODE_PLAIN8, a, (hipStream_t)stream, "qgemv_affine8");
 }
 
 qg_status qg_check_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had, const uint32_t* codes,

@@ -7,6 +7,8 @@
 //                   (rmsnorm_gateup_swiglu: norm fused into the projection,
 //                   gate and up computed together -- Husky page, section
 //                   "MSI의 네 가지 구현 요소")
+//   QG_MODE_PLAIN8  Y = X . dequant8(W)^T for 8-bit affine codes   (qgemv_affine8;
+//                   uzu page: MLX 4- and 8-bit weights)
 //   QG_MODE_LMHEAD  logits = X . dequant(W)^T, greedy argmax per row and the
 //                   accepted draft prefix, all on the device (uzu page: untied
 //                   readout; Husky page: next token handed over on the GPU)
@@ -186,6 +188,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   constexpr int PL = planes(MODE);  // activation planes (hi, lo)
   constexpr int BATCH = 4;                              // chunks whose loads are issued together
   constexpr int R = (MODE == QG_MODE_LMHEAD) ? 2 : 1;   // steps of weight loads in flight per wave
+  constexpr int CW = (MODE == QG_MODE_PLAIN8) ? 2 : 1;  // 16-byte code loads per lane and chunk
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
@@ -220,8 +223,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   // operand entry of this lane for (chunk cl, step t, plane pl): a_lane + (cl*16 + t*4)*PL*M + pl*M of xs
   const uint32_t a_lane = (uint32_t)(ZR + kb * PL * M + (rho & 7));
   const float* sx_base = sx + half * 8 + 4 * (kb & 1);
-  const size_t wrow_words = (size_t)p.K / 8;
-  const uint32_t wmax = (uint32_t)(wrow_words - 4);  // last in-row 16-byte load
+  const size_t wrow_words = (size_t)p.K / (CW == 2 ? 4 : 8);
+  const uint32_t wmax = (uint32_t)(wrow_words - 4 * CW);  // last in-row load (CW 16-byte pieces)
   const int mbase = 4 * (lane >> 4);                 // activation row of C element 0 (lanes < 32)
   const UnpackK uk = unpack_constants();
 
@@ -229,7 +232,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   // sw / bw dword u holds the bf16 scales / biases of groups 2(c0+cb+u) (low half) and
   // 2(c0+cb+u)+1 (high half); lane l uses the half of its group parity.
   struct Buf {
-    uint4 q[BATCH];
+    uint4 q[BATCH * CW];
     uint32_t sw[BATCH], bw[BATCH];
   };
   auto load_step = [&](Buf& bf, int st) {
@@ -254,8 +257,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int cg = WIDE ? c0 + cb + u : c0 + min(cb + u, nc - 1);
-      const uint32_t wo = min((uint32_t)(cg * 16 + kb * 4), wmax);
-      bf.q[u] = *reinterpret_cast<const uint4*>(p.codes + row_c * wrow_words + wo);
+      if constexpr (CW == 2) {
+        // 8-bit: lane kb's 32 codes of chunk cg are bytes 32kb..32kb+31 of the chunk's 128
+        const uint32_t wo = min((uint32_t)(cg * 32 + kb * 8), wmax);
+        bf.q[2 * u] = *reinterpret_cast<const uint4*>(p.codes + row_c * wrow_words + wo);
+        bf.q[2 * u + 1] = *reinterpret_cast<const uint4*>(p.codes + row_c * wrow_words + wo + 4);
+      } else {
+        const uint32_t wo = min((uint32_t)(cg * 16 + kb * 4), wmax);
+        bf.q[u] = *reinterpret_cast<const uint4*>(p.codes + row_c * wrow_words + wo);
+      }
     }
     if constexpr (WIDE) {
       const size_t off = row_c * p.G + gb;
@@ -322,8 +332,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
         if (WIDE || cb + u < nc) {
-          const uint32_t w = t == 0 ? bf.q[u].x : t == 1 ? bf.q[u].y : t == 2 ? bf.q[u].z : bf.q[u].w;
-          const uint4 bw = unpack_affine_word(w, uk);
+          uint4 bw;
+          if constexpr (CW == 2) {  // MFMA t takes codes 8t..8t+7 of the lane's 32: words 2t and 2t+1
+            const uint4& qq = bf.q[2 * u + (t >> 1)];
+            bw = unpack_affine8_pair((t & 1) ? qq.z : qq.x, (t & 1) ? qq.w : qq.y);
+          } else {
+            const uint32_t w = t == 0 ? bf.q[u].x : t == 1 ? bf.q[u].y : t == 2 ? bf.q[u].z : bf.q[u].w;
+            bw = unpack_affine_word(w, uk);
+          }
 #pragma unroll
           for (int pl = 0; pl < PL; ++pl) {
             const uint4 a = zr[a_base + (uint32_t)((u * 16 + t * 4) * PL * M + pl * M)];
@@ -340,6 +356,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
         if constexpr (TILED) {  // (scale, bias) of this lane's group in one dword
           sc = __uint_as_float(bf.sw[u] << 16);
           cbias = fmaf(-128.0f, sc, __uint_as_float(bf.sw[u] & 0xFFFF0000u));
+        } else if constexpr (CW == 2) {  // 8-bit operands carry q itself: no offset to fold
+          sc = __uint_as_float((bf.sw[u] >> (16 * half)) << 16);
+          cbias = __uint_as_float((bf.bw[u] >> (16 * half)) << 16);
         } else {
           sc = __uint_as_float((bf.sw[u] >> (16 * half)) << 16);
           cbias = fmaf(-128.0f, sc, __uint_as_float((bf.bw[u] >> (16 * half)) << 16));
@@ -530,6 +549,9 @@ static void launch_main(int mode, const QgAffineArgs& a, dim3 grid, dim3 block, 
       break;
     case QG_MODE_PLANES:
       hipLaunchKernelGGL((k_affine<M, QG_MODE_PLANES, WIDE>), grid, block, lds, st, a);
+      break;
+    case QG_MODE_PLAIN8:
+      hipLaunchKernelGGL((k_affine<M, QG_MODE_PLAIN8, WIDE>), grid, block, lds, st, a);
       break;
     default:
       hipLaunchKernelGGL((k_affine<M, QG_MODE_LMHEAD, WIDE>), grid, block, lds, st, a);

@@ -75,6 +75,25 @@ __device__ __forceinline__ uint4 unpack_affine_word(uint32_t w, const UnpackK& k
   return r;
 }
 
+// Eight affine 8-bit codes (bytes of w0 = codes 0..3, w1 = codes 4..7, least
+// significant byte first) as eight bf16 values q: a byte converts to fp32
+// exactly and its upper half is the exact bf16 (q has at most 8 significant
+// bits).  As in unpack_affine_word, dword j holds code j (low half) and code
+// j+4 (high half).
+__device__ __forceinline__ uint32_t bf16_pair_of_floats(float lo, float hi) {
+  // bytes 2,3 of lo, then bytes 2,3 of hi (v_perm_b32: selectors 0..3 pick the
+  // second operand's bytes, 4..7 the first's)
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+__device__ __forceinline__ uint4 unpack_affine8_pair(uint32_t w0, uint32_t w1) {
+  uint4 r;
+  r.x = bf16_pair_of_floats((float)(w0 & 0xFFu), (float)(w1 & 0xFFu));
+  r.y = bf16_pair_of_floats((float)((w0 >> 8) & 0xFFu), (float)((w1 >> 8) & 0xFFu));
+  r.z = bf16_pair_of_floats((float)((w0 >> 16) & 0xFFu), (float)((w1 >> 16) & 0xFFu));
+  r.w = bf16_pair_of_floats((float)(w0 >> 24), (float)(w1 >> 24));
+  return r;
+}
+
 // Eight Q4_K codes from eight consecutive code bytes (w0 = bytes 0..3, w1 =
 // bytes 4..7): the low nibbles when sh == 0, the high nibbles when sh == 4.
 // Slot s holds the code of byte {0,2,1,3,4,6,5,7}[s].
@@ -106,9 +125,11 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) 
 // Launch descriptors filled by the ABI layer (abi.hip) and consumed by the
 // launchers in affine4.hip / q4k.hip.
 
-enum QgAffineMode { QG_MODE_PLAIN = 0, QG_MODE_GATEUP = 1, QG_MODE_LMHEAD = 2, QG_MODE_PLANES = 3 };
+enum QgAffineMode { QG_MODE_PLAIN = 0, QG_MODE_GATEUP = 1, QG_MODE_LMHEAD = 2, QG_MODE_PLANES = 3, QG_MODE_PLAIN8 = 4 };
 // QG_MODE_PLANES: Y = (X_hi + X_lo) . dequant(W)^T with X given as two bf16
 // planes (the transformed input of the RHT projection), epilogue as PLAIN.
+// QG_MODE_PLAIN8: Y = X . dequant(W)^T with 8-bit affine codes ([N][K/4]
+// words), epilogue as PLAIN.
 
 struct QgAffineArgs {
   const uint16_t* x;

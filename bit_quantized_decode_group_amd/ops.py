@@ -41,6 +41,8 @@ _SIGS = {
     "qg_check_qgemv_affine4_tiled": [_P, _P, _P, _P, _I, _I, _I],
     "qg_check_lmhead_argmax_tiled": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I],
     "qg_check_qgemv_affine4_rht": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I],
+    "qgemv_affine8": [_P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "qg_check_qgemv_affine8": [_P, _P, _P, _P, _P, _I, _I, _I],
     "rmsnorm_gateup_swiglu_tiled": [_P, _P, _F, _P, _P, _P, _I, _I, _I, _P],
     "qg_check_rmsnorm_gateup_swiglu_tiled": [_P, _P, _F, _P, _P, _P, _I, _I, _I],
     "rmsnorm_gateup_swiglu": [_P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P],
@@ -169,6 +171,22 @@ def tile_pack(codes, scales, biases):
         _raise_on(l.affine4_tile_pack(_ptr(codes), _ptr(scales), _ptr(biases), _ptr(codes_t), _ptr(sb_t), N, K,
                                       _stream()), "affine4_tile_pack")
     return codes_t, sb_t
+
+
+def qgemv_affine8(x, codes, scales, biases, y=None):
+    """Y = X . dequant8(W)^T: codes int32 [N, K/4] (four 8-bit codes per word), scales/biases bf16 [N, K/64]."""
+    M, K = _dims2(x, "x")
+    N = codes.shape[0]
+    if codes.dim() != 2 or codes.shape[1] * 4 != K:
+        raise ValueError(f"codes must be [N, K/4] = [N, {K // 4}], got {tuple(codes.shape)}")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    for t, n, e in ((x, "x", 2), (codes, "codes", 4), (scales, "scales", 2), (biases, "biases", 2), (y, "y", 2)):
+        _need(t, n, e, x.device)
+    with torch.cuda.device(x.device):
+        _raise_on(lib().qgemv_affine8(_ptr(x), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(y), M, N, K, _stream()),
+                  "qgemv_affine8")
+    return y
 
 
 def qgemv_affine4_tiled(x, codes_t, sb_t, N, y=None):

@@ -103,6 +103,22 @@ qg_status qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had,
                             int K, void* stream);
 
 /*
+ * qgemv_affine8 -- Y = X . dequant8(W)^T for MLX-style affine 8-bit weights
+ * (uzu page, section "내부 동작 1: 모델은 설정으로 조립된다": the weight_matrix
+ * row names MLX 4- and 8-bit quantized weights).  Code k of row n is byte k%4
+ * (least significant first) of codes[n][k/4], an unsigned value 0..255; the
+ * weight is scale * code + bias with the bf16 scale and bias of group k/64.
+ *   x      bf16 [M][K]
+ *   codes  uint32 [N][K/4] (16-byte aligned); scales, biases bf16 [N][K/64]
+ *   y      bf16 [M][N]
+ *   1 <= M <= 8; N >= 0 (N = 0 does nothing); K > 0, K % 64 == 0.
+ *   Errors as qgemv_affine4.
+ */
+qg_status qgemv_affine8(const uint16_t* x, const uint32_t* codes,
+                        const uint16_t* scales, const uint16_t* biases,
+                        uint16_t* y, int M, int N, int K, void* stream);
+
+/*
  * Tile-order layout of affine4 weights (Husky page, section "MSI의 네 가지 구현
  * 요소": weights stored in the order the projection kernel reads them), for
  * K % 512 == 0.  With T = ceil(N/16) 16-row tiles, C = K/128 chunks, B = K/512
@@ -250,6 +266,9 @@ qg_status qg_stream_read(const void* buf, size_t bytes, uint32_t* sink,
  * before launching anything.
  */
 qg_status qg_check_qgemv_affine4(const uint16_t* x, const uint32_t* codes,
+                                 const uint16_t* scales, const uint16_t* biases,
+                                 uint16_t* y, int M, int N, int K);
+qg_status qg_check_qgemv_affine8(const uint16_t* x, const uint32_t* codes,
                                  const uint16_t* scales, const uint16_t* biases,
                                  uint16_t* y, int M, int N, int K);
 qg_status qg_check_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs,

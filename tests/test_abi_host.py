@@ -256,3 +256,14 @@ def test_gateup_tiled_checks(lib):
     assert c(A[0], A[1], 1e-6, A[2], A[3], A[1], 8, 12800, 2560) == ops.QG_EALIAS  # h over gamma
     assert c(A[0], A[1] + 2, 1e-6, A[2], A[3], A[4], 8, 12800, 2560) == ops.QG_EINVAL  # gamma alignment
     assert c(A[0], A[1], 1e-6, A[2], A[3], A[4], 9, 12800, 2560) == ops.QG_EINVAL
+
+
+def test_qgemv_affine8_checks(lib):
+    c = lambda *a: ops.check("qgemv_affine8", *a)
+    assert c(A[0], A[1], A[2], A[3], A[4], 8, 3072, 1024) == ops.QG_OK
+    assert c(A[0], A[1], A[2], A[3], A[4], 0, 3072, 1024) == ops.QG_EINVAL
+    assert c(A[0], A[1], A[2], A[3], A[4], 8, 3072, 1000) == ops.QG_EINVAL
+    assert c(A[0], A[1] + 4, A[2], A[3], A[4], 8, 16, 64) == ops.QG_EINVAL  # codes alignment
+    assert c(A[0], A[1], A[2], A[3], A[1] + 64, 8, 16, 64) == ops.QG_EALIAS  # y inside codes (16*64 bytes)
+    assert c(A[0], A[1], A[2], A[3], A[1] + 1024, 8, 16, 64) == ops.QG_OK    # just past codes
+    assert c(0, A[1], A[2], A[3], A[4], 1, 16, 64) == ops.QG_EINVAL

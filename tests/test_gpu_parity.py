@@ -564,3 +564,56 @@ def test_config_verify_block_4b_tiled(M):
     ht = ops.rmsnorm_gateup_swiglu_tiled(dev_bf16(d["x"]), dev_bf16(d["gamma"]), d["eps"], *gu_t, d["I"])
     yt = ops.qgemv_affine4_tiled(ht, *dn_t, d["D"])
     assert torch.equal(ht, h) and torch.equal(yt, y)
+
+
+# ------------------------------------------------------------ qgemv_affine8 --
+
+def _affine8_dev(d):
+    return dev_u32(d["codes"]), dev_bf16(d["scales"]), dev_bf16(d["biases"])
+
+
+@pytest.mark.parametrize("K", [64, 192, 1024, 12800])
+@pytest.mark.parametrize("N", [1, 16, 17, 40])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_qgemv_affine8_small(M, N, K):
+    d = synth.single_projection8(M=M, N=N, K=K, seed=9700 + 97 * M + 7 * N + K)
+    ref = oracle.qgemv_affine8(d["x"], d["codes"], d["scales"], d["biases"])
+    y = ops.qgemv_affine8(dev_bf16(d["x"]), *_affine8_dev(d))
+    assert_close(host_bf16_f64(y), ref, what=f"affine8 M{M} N{N} K{K}")
+
+
+def test_qgemv_affine8_hand_packed_exact():
+    from tests.test_oracle_pins import HAND8_BIASES, HAND8_SCALES, HAND8_VALUES, _hand8_codes
+    ks = [0, 3, 63, 64, 127, 5]
+    x = np.zeros((len(ks), 128), dtype=np.uint16)
+    for m, k in enumerate(ks):
+        x[m, k] = 0x3F80
+    y = host_bf16_f64(ops.qgemv_affine8(dev_bf16(x), dev_u32(_hand8_codes()), dev_bf16(HAND8_SCALES),
+                                        dev_bf16(HAND8_BIASES)))
+    for m, k in enumerate(ks):
+        for n in range(2):
+            if (n, k) in HAND8_VALUES:
+                assert y[m, n] == HAND8_VALUES[(n, k)], (m, k, n, y[m, n])
+
+
+def test_qgemv_affine8_all_codes_exact():
+    """Every code value 0..255 in every byte position, unit scale and zero bias, one-hot rows: the
+    output is the code itself (exact in bf16)."""
+    k = np.arange(256)
+    q = np.stack([k, 255 - k, (7 * k) % 256, (k * 13 + 5) % 256])
+    codes = packers.pack_affine8_codes(q)
+    ones = np.full((4, 4), 0x3F80, np.uint16)
+    zeros = np.zeros((4, 4), np.uint16)
+    x = np.zeros((8, 256), np.uint16)
+    for r in range(8):
+        x[r, 31 * r + 3] = 0x3F80
+    y = host_bf16_f64(ops.qgemv_affine8(dev_bf16(x), dev_u32(codes), dev_bf16(ones), dev_bf16(zeros)))
+    assert np.array_equal(y, q[:, [31 * r + 3 for r in range(8)]].T.astype(np.float64))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 3072, 1024), (8, 3072, 1024), (8, 2560, 12800)])
+def test_config_affine8_projection(M, N, K):
+    d = synth.single_projection8(M=M, N=N, K=K, seed=1006 + K)
+    ref = oracle.qgemv_affine8(d["x"], d["codes"], d["scales"], d["biases"])
+    y = ops.qgemv_affine8(dev_bf16(d["x"]), *_affine8_dev(d))
+    assert_close(host_bf16_f64(y), ref, what=f"affine8 {N}x{K} M{M}")
