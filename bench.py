@@ -33,7 +33,8 @@ METRIC = "achieved HBM GB/s (% of peak) for 4-bit qGEMV at M=1 and M=8; verify c
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["bit_quantized_decode_group_amd/csrc/common.h", "bit_quantized_decode_group_amd/csrc/affine4.hip",
                   "bit_quantized_decode_group_amd/csrc/q4k.hip", "bit_quantized_decode_group_amd/csrc/abi.hip",
-                  "bit_quantized_decode_group_amd/csrc/topk.hip", "bit_quantized_decode_group_amd/csrc/rht.hip"]
+                  "bit_quantized_decode_group_amd/csrc/topk.hip", "bit_quantized_decode_group_amd/csrc/rht.hip",
+                  "bit_quantized_decode_group_amd/csrc/mlp.hip", "bit_quantized_decode_group_amd/csrc/affine_stage.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GRAPH_STEPS = 10  # at most this many consecutive steps (rotating weights, MoE stacks, router logits) per graph
 CALIB_BYTES = 384 << 20  # bytes read and written by the kernel that calibrates the HBM byte counters
@@ -43,6 +44,7 @@ ENTRY_KERNELS = {
     "qgemv_affine4": ["qg::k_affine<8, 0,", "qg::k_split_reduce<0>"],
     "moe_expert_qgemv": ["qg::k_moe_gateup", "qg::k_moe_down"],
     "lmhead_argmax": ["qg::k_affine<8, 2,", "qg::k_lmhead_finalize"],
+    "mlp_block": ["qg::k_mlp_block<8>"],
 }
 
 
@@ -69,6 +71,9 @@ def parse():
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration context timings")
     ap.add_argument("--submission", choices=["graph", "eager"], default="eager",
                     help="timed steps replayed from a HIP graph of GRAPH_STEPS captured steps, or launched eagerly")
+    ap.add_argument("--mlp", choices=["persistent", "separate"], default="separate",
+                    help="MLP block as one persistent launch (mlp_block_affine4_tiled; tile-order layout only) or "
+                         "as the two entry points rmsnorm_gateup_swiglu + qgemv_affine4")
     ap.add_argument("--layout", choices=["tiled", "canonical"], default="tiled",
                     help="storage of the affine-4 weights: tile order (packed once at set-up from the canonical "
                          "arrays; same bytes, reordered) or the canonical [N][K/8] layout")
@@ -212,6 +217,8 @@ def main():
     # Algorithmic bytes per step: every weight byte once (0.5625 B/weight), the
     # activations read, the outputs written, and the two intermediates (h of
     # the MLP block, the MoE expert activations) written once and read once.
+    persistent = tiled and args.mlp == "persistent"
+
     def step_bytes(M):
         w = {
             "rmsnorm_gateup_swiglu": 2 * I * D // 2 + 2 * (2 * I * D // 64) * 2,
@@ -225,40 +232,52 @@ def main():
             "moe_expert_qgemv": Dm * 2 + E * 4 + 2 * top_k * Im * 2 + Dm * 2 + top_k * 8,
             "lmhead_argmax": M * K5 * 2 + M * 4 * 2 + 4,
         }
-        return {k: w[k] + a[k] for k in w}, w
+        tot = {k: w[k] + a[k] for k in w}
+        if persistent:  # the block is one launch: its bytes are those of its two projections
+            for dct in (tot, w):
+                dct["mlp_block"] = dct.pop("rmsnorm_gateup_swiglu") + dct.pop("qgemv_affine4")
+        return tot, w
 
-    names = ["rmsnorm_gateup_swiglu", "qgemv_affine4", "moe_expert_qgemv", "lmhead_argmax"]
+    names = (["mlp_block"] if persistent else ["rmsnorm_gateup_swiglu", "qgemv_affine4"]) + \
+        ["moe_expert_qgemv", "lmhead_argmax"]
 
     def run_step(i, M, b, ev=None):
         c = copies[i % C]
         ms = moe_stacks[i % 2]
         lg = logits[i % n_logit_sets]
-        if ev is not None:
-            ev[0].record()
-        if tiled:
+        e = iter(ev) if ev is not None else None
+        if e is not None:
+            next(e).record()
+        if persistent:
+            ops.mlp_block_affine4_tiled(b["x"], gamma, vb["eps"], c["t_gu"], c["t_d"], D, I, h=b["h"], y=b["y"])
+        elif tiled:
             ops.rmsnorm_gateup_swiglu_tiled(b["x"], gamma, vb["eps"], *c["t_gu"], I, h=b["h"])
         else:
             ops.rmsnorm_gateup_swiglu(b["x"], gamma, vb["eps"], c["codes_gu"], c["scales_gu"], c["biases_gu"],
                                       h=b["h"])
-        if ev is not None:
-            ev[1].record()
-        if tiled:
+        if e is not None:
+            next(e).record()
+        if persistent:
+            pass
+        elif tiled:
             ops.qgemv_affine4_tiled(b["h"], *c["t_d"], D, y=b["y"])
+            if e is not None:
+                next(e).record()
         else:
             ops.qgemv_affine4(b["h"], c["codes_d"], c["scales_d"], c["biases_d"], y=b["y"])
-        if ev is not None:
-            ev[2].record()
+            if e is not None:
+                next(e).record()
         ops.moe_expert_qgemv(xm, lg, top_k, ms["w_gu"], ms["w_down"], y=b["ym"], out_ids=b["mids"], out_w=b["mw"])
-        if ev is not None:
-            ev[3].record()
+        if e is not None:
+            next(e).record()
         dr = draft[:M].contiguous() if M < 8 else draft
         if tiled:
             ops.lmhead_argmax_tiled(b["xl"], *c["t_lm"], V, draft=dr, ids=b["ids"], accepted=b["acc"])
         else:
             ops.lmhead_argmax(b["xl"], c["codes_lm"], c["scales_lm"], c["biases_lm"], draft=dr, ids=b["ids"],
                               accepted=b["acc"])
-        if ev is not None:
-            ev[4].record()
+        if e is not None:
+            next(e).record()
 
     spread = {}
 
@@ -318,14 +337,14 @@ def main():
         spread[M] = {"median_ms": round(float(np.median(sub)), 5), "p10_ms": round(float(np.percentile(sub, 10)), 5),
                      "p90_ms": round(float(np.percentile(sub, 90)), 5), "sub_batches": nsub}
         # per-kernel durations: the same steps again with events around each launch
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
         with torch.cuda.stream(s):
             for i in range(steps):
                 run_step(warmup + steps + i, M, b, evs[i])
         torch.cuda.synchronize()
         per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)])) * 1e3
                for j, n in enumerate(names)}
-        inst = float(np.mean([evs[i][0].elapsed_time(evs[i][4]) for i in range(steps)]))
+        inst = float(np.mean([evs[i][0].elapsed_time(evs[i][len(names)]) for i in range(steps)]))
         return ms_step, wall, per, inst, b
 
     if args.pmc_pass:
@@ -412,7 +431,9 @@ def main():
                 traffic = ent.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
-    roofline = {"kernel": dom + ("_tiled" if tiled and dom != "moe_expert_qgemv" else ""), "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+    entry = {"mlp_block": "mlp_block_affine4_tiled", "moe_expert_qgemv": "moe_expert_qgemv"}.get(
+        dom, dom + ("_tiled" if tiled else ""))
+    roofline = {"kernel": entry, "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": bytes8[dom], "avg_launch_us": round(per8[dom], 2)}
 
@@ -429,6 +450,8 @@ def main():
                                "(128 experts, top-8, 2048<->768) + untied LM head X[8,1024] x W[151936,1024] "
                                "(affine-4 g64) greedy verify",
                    "M": 8, "weight_copies": C,
+                   "mlp": ("one persistent launch (mlp_block_affine4_tiled)" if persistent
+                           else "rmsnorm_gateup_swiglu + qgemv_affine4"),
                    "submission": ("HIP graph replays of captured steps" if args.submission == "graph"
                                   else "eager launches"),
                    "layout": "tile-order (same bytes as canonical, packed at set-up)" if tiled else "canonical", "algorithmic_bytes_per_step": total8,

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <functional>
 #include <map>
+#include <tuple>
 #include <mutex>
 #include <utility>
 
@@ -413,8 +414,11 @@ qg_status do_check_tiled(const char* fn, const uint16_t* x, const uint32_t* code
 // (if set) runs after the workspace is in place and before the projection is
 // launched, with that region and the arguments (the RHT entry point launches
 // its transform there and points the projection at the planes it writes).
-qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* fn, size_t reserve = 0,
-                     const std::function<int(unsigned char*, QgAffineArgs&)>& pre = nullptr) {
+// Split plan of an affine projection (a.M, a.N, a.K and a.tiled set): fills
+// G, nchunks, ntiles, waves, S, cps and wide, and *lds (bytes of LDS per
+// workgroup).  The persistent MLP block uses the same plans, so its results
+// equal those of the separate entry points.
+qg_status plan_affine(int mode, QgAffineArgs& a, const char* fn, size_t* lds_out) {
   const int G = a.K / 64;
   a.G = G;
   a.nchunks = (G + 1) / 2;
@@ -458,8 +462,16 @@ qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* f
   }
   if (a.tiled && !a.wide)
     return fail(QG_EUNSUPPORTED, "%s: no K split of whole 512-k batches fits for K=%d", fn, a.K);
-  const size_t lds = (size_t)a.cps * per + affine_lds_fixed(a.M, PL);
-  a.rgroups = affine_rgroups(a.ntiles, a.S, lds, 4, fill_pct);  // 128 registers per lane: 4 waves per SIMD
+  *lds_out = (size_t)a.cps * per + affine_lds_fixed(a.M, PL);
+  a.rgroups = affine_rgroups(a.ntiles, a.S, *lds_out, 4, fill_pct);  // 128 registers per lane: 4 waves per SIMD
+  return QG_OK;
+}
+
+qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* fn, size_t reserve = 0,
+                     const std::function<int(unsigned char*, QgAffineArgs&)>& pre = nullptr) {
+  size_t lds = 0;
+  qg_status pst = plan_affine(mode, a, fn, &lds);
+  if (pst) return pst;
   unsigned char* ws = nullptr;
   const bool partials = a.S > 1 || mode == QG_MODE_GATEUP;
   const size_t part_bytes = partials ? (size_t)a.S * a.M * a.N * 4 : 0;
@@ -506,6 +518,71 @@ __global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ p
   if (acc == 0x9E3779B9u) *sink = acc;
 }
 
+// ------------------------------------------------ persistent MLP block --
+// Barrier state of the persistent kernel per (device, stream, M, D, I):
+// arrival counters that only grow, release words and a failure flag, zeroed
+// once when created.  The grid (resident slots at this configuration's LDS)
+// depends only on the key, so a state always sees the same grid.
+struct MlpState {
+  unsigned char* ptr = nullptr;
+  size_t bytes = 0;
+  int off_h = 0, off_y = 0, off_r = 0;
+  int grid = 0;
+};
+std::mutex g_mlp_mu;
+std::map<std::tuple<int, hipStream_t, int, int, int>, MlpState> g_mlp;
+constexpr int kMlpSpinLimit = 200000;  // polls of one wait before a workgroup gives up (tens of ms)
+
+qg_status mlp_state(hipStream_t stream, int M, int D, int I, int S_down, size_t lds, MlpState** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QG_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_mlp_mu);
+  MlpState& s = g_mlp[std::make_tuple(dev, stream, M, D, I)];
+  if (!s.ptr) {
+    int occ = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, qg_mlp_kernel(M), 256, lds);
+    if (e != hipSuccess || occ < 1)
+      return fail(QG_EUNSUPPORTED, "mlp_block_affine4_tiled: no resident workgroup fits (%d)", (int)e);
+    s.grid = device_cus() * std::min(occ, 4) / 32 * 32;  // the grid barrier takes 32 groups of equal size
+    if (s.grid < 32) return fail(QG_EUNSUPPORTED, "mlp_block_affine4_tiled: fewer than 32 resident workgroups");
+    s.bytes = qg_mlp_state_bytes(D, I, S_down, &s.off_h, &s.off_y, &s.off_r);
+    void* p = nullptr;
+    e = hipMalloc(&p, s.bytes);
+    if (e != hipSuccess) return fail(QG_ENOMEM, "mlp state hipMalloc: %s", hipGetErrorString(e));
+    e = hipMemset(p, 0, s.bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(QG_EHIP, "mlp state init: %s", hipGetErrorString(e));
+    s.ptr = static_cast<unsigned char*>(p);
+  }
+  *out = &s;
+  return QG_OK;
+}
+
+qg_status do_check_mlp(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* gu_codes_t,
+                       const uint16_t* gu_sb_t, const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
+                       uint16_t* y, int M, int D, int I) {
+  const char* fn = "mlp_block_affine4_tiled";
+  if (M < 1 || M > 8) return fail(QG_EINVAL, "%s: M=%d must be in 1..8", fn, M);
+  if (D <= 0 || D % 512 != 0) return fail(QG_EINVAL, "%s: D=%d must be a positive multiple of 512", fn, D);
+  if (I <= 0 || I % 512 != 0) return fail(QG_EINVAL, "%s: I=%d must be a positive multiple of 512", fn, I);
+  if ((long long)I * 2 * 16 > 0x7FFFFFFFLL || (long long)D * 16 > 0x7FFFFFFFLL)
+    return fail(QG_EINVAL, "%s: D=%d or I=%d too large", fn, D, I);
+  if (!(eps > 0.0f) || eps != eps || eps > 3.0e38f) return fail(QG_EINVAL, "%s: eps must be positive and finite", fn);
+  const Buf in[] = {{x, (size_t)M * D * 2, "x"},
+                    {gamma, (size_t)D * 2, "gamma"},
+                    {gu_codes_t, tiled_codes_bytes(2 * I, D), "gu_codes_t"},
+                    {gu_sb_t, tiled_sb_bytes(2 * I, D), "gu_sb_t"},
+                    {dn_codes_t, tiled_codes_bytes(D, I), "dn_codes_t"},
+                    {dn_sb_t, tiled_sb_bytes(D, I), "dn_sb_t"}};
+  const Buf out[] = {{h, (size_t)M * I * 2, "h"}, {y, (size_t)M * D * 2, "y"}};
+  qg_status st;
+  for (const Buf& b : in)
+    if ((st = check_ptr(b, 16, fn))) return st;
+  if ((st = check_ptr(out[0], 16, fn)) || (st = check_ptr(out[1], 4, fn))) return st;
+  return check_alias(out, 2, in, 6, fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -522,6 +599,78 @@ qg_status qg_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* st
   hipLaunchKernelGGL(k_stream_read, dim3(grid), dim3(256), 0, (hipStream_t)stream, static_cast<const uint4*>(buf), n16,
                      sink);
   return launched((int)hipGetLastError(), "qg_stream_read");
+}
+
+qg_status qg_check_mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma, float eps,
+                                           const uint32_t* gu_codes_t, const uint16_t* gu_sb_t,
+                                           const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
+                                           uint16_t* y, int M, int D, int I) {
+  clear_err();
+  return do_check_mlp(x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, y, M, D, I);
+}
+
+qg_status mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* gu_codes_t,
+                                  const uint16_t* gu_sb_t, const uint32_t* dn_codes_t, const uint16_t* dn_sb_t,
+                                  uint16_t* h, uint16_t* y, int M, int D, int I, void* stream) {
+  const char* fn = "mlp_block_affine4_tiled";
+  clear_err();
+  qg_status st = do_check_mlp(x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, y, M, D, I);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  QgAffineArgs pa{}, pc{};
+  pa.x = x;
+  pa.gamma = gamma;
+  pa.eps = eps;
+  pa.codes = gu_codes_t;
+  pa.scales = gu_sb_t;
+  pa.biases = gu_sb_t;
+  pa.tiled = 1;
+  pa.y = h;
+  pa.M = M;
+  pa.N = 2 * I;
+  pa.K = D;
+  pc.x = h;
+  pc.codes = dn_codes_t;
+  pc.scales = dn_sb_t;
+  pc.biases = dn_sb_t;
+  pc.tiled = 1;
+  pc.y = y;
+  pc.M = M;
+  pc.N = D;
+  pc.K = I;
+  size_t lds_a = 0, lds_c = 0;
+  if ((st = plan_affine(QG_MODE_GATEUP, pa, fn, &lds_a)) || (st = plan_affine(QG_MODE_PLAIN, pc, fn, &lds_c)))
+    return st;
+  const size_t lds = std::max(lds_a, lds_c);
+  MlpState* sy = nullptr;
+  if ((st = mlp_state(s, M, D, I, pc.S, lds, &sy))) return st;
+  // every job of a phase gets its own resident workgroup when the plan allows
+  const int P = sy->grid;
+  pa.rgroups = std::max(1, std::min(P / pa.S, (pa.ntiles + kWaves - 1) / kWaves));
+  pc.rgroups = std::max(1, std::min(P / pc.S, (pc.ntiles + kWaves - 1) / kWaves));
+  const size_t part_a = (size_t)pa.S * M * pa.N * 4, ssq_a = (size_t)pa.S * 8 * 4, part_c = (size_t)pc.S * M * pc.N * 4;
+  unsigned char* ws = nullptr;
+  if ((st = get_workspace(s, part_a + ssq_a + part_c + 256, &ws))) return st;
+  pa.part = reinterpret_cast<float*>(ws);
+  pa.ssq_part = reinterpret_cast<float*>(ws + part_a);
+  pc.part = reinterpret_cast<float*>(ws + (part_a + ssq_a + 255) / 256 * 256);
+  return launched(qg_launch_mlp(pa, pc, sy->ptr, sy->off_h, sy->off_y, sy->off_r, kMlpSpinLimit, P, lds, s), fn);
+}
+
+int32_t qg_mlp_failures(void* stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lk(g_mlp_mu);
+  int32_t total = 0;
+  for (auto& kv : g_mlp) {
+    if (std::get<0>(kv.first) != dev || std::get<1>(kv.first) != (hipStream_t)stream) continue;
+    unsigned v = 0;
+    if (hipMemcpy(&v, kv.second.ptr + 16, 4, hipMemcpyDeviceToHost) != hipSuccess) return -1;
+    total += (int32_t)(v != 0);
+  }
+  return total;
 }
 
 const char* qg_status_string(qg_status s) {

@@ -42,6 +42,9 @@ _SIGS = {
     "qg_check_lmhead_argmax_tiled": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I],
     "qg_check_qgemv_affine4_rht": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I],
     "qgemv_affine8": [_P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "mlp_block_affine4_tiled": [_P, _P, _F, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "qg_check_mlp_block_affine4_tiled": [_P, _P, _F, _P, _P, _P, _P, _P, _P, _I, _I, _I],
+    "qg_mlp_failures": [_P],
     "qg_check_qgemv_affine8": [_P, _P, _P, _P, _P, _I, _I, _I],
     "rmsnorm_gateup_swiglu_tiled": [_P, _P, _F, _P, _P, _P, _I, _I, _I, _P],
     "qg_check_rmsnorm_gateup_swiglu_tiled": [_P, _P, _F, _P, _P, _P, _I, _I, _I],
@@ -187,6 +190,33 @@ def qgemv_affine8(x, codes, scales, biases, y=None):
         _raise_on(lib().qgemv_affine8(_ptr(x), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(y), M, N, K, _stream()),
                   "qgemv_affine8")
     return y
+
+
+def mlp_block_affine4_tiled(x, gamma, eps, gu_t, dn_t, D, I, h=None, y=None):
+    """The MLP block (RMSNorm -> gate/up -> SwiGLU -> down) in one persistent launch on tile-order
+    weights: gu_t = tile_pack of the [2I, D] gate-then-up matrix, dn_t = tile_pack of [D, I].
+    Returns (h, y)."""
+    M, K = _dims2(x, "x")
+    if K != D:
+        raise ValueError(f"x has {K} columns, D = {D}")
+    if h is None:
+        h = torch.empty((M, I), dtype=torch.bfloat16, device=x.device)
+    if y is None:
+        y = torch.empty((M, D), dtype=torch.bfloat16, device=x.device)
+    for t, n, e in ((x, "x", 2), (gamma, "gamma", 2), (gu_t[0], "gu_codes_t", 4), (gu_t[1], "gu_sb_t", 2),
+                    (dn_t[0], "dn_codes_t", 4), (dn_t[1], "dn_sb_t", 2), (h, "h", 2), (y, "y", 2)):
+        _need(t, n, e, x.device)
+    with torch.cuda.device(x.device):
+        _raise_on(lib().mlp_block_affine4_tiled(_ptr(x), _ptr(gamma), float(eps), _ptr(gu_t[0]), _ptr(gu_t[1]),
+                                                _ptr(dn_t[0]), _ptr(dn_t[1]), _ptr(h), _ptr(y), M, D, I, _stream()),
+                  "mlp_block_affine4_tiled")
+    return h, y
+
+
+def mlp_failures(device=None):
+    """Synchronises the current stream; the number of its persistent-MLP states whose waits gave up."""
+    with torch.cuda.device(device or torch.cuda.current_device()):
+        return int(lib().qg_mlp_failures(_stream()))
 
 
 def qgemv_affine4_tiled(x, codes_t, sb_t, N, y=None):

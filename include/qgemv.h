@@ -119,6 +119,39 @@ qg_status qgemv_affine8(const uint16_t* x, const uint32_t* codes,
                         uint16_t* y, int M, int N, int K, void* stream);
 
 /*
+ * mlp_block_affine4_tiled -- the whole MLP block in one persistent launch
+ * (Husky page, section "MSI의 네 가지 구현 요소": one dispatch per layer MLP,
+ * useful when one projection's weight reads overlap the tail of the previous):
+ *   h = silu(xn . Wg^T) * (xn . Wu^T), xn = RMSNorm(x)  (as rmsnorm_gateup_swiglu)
+ *   y = h . Wd^T                                          (as qgemv_affine4)
+ *   x       bf16 [M][D]; gamma bf16 [D]; eps > 0
+ *   gu_codes_t, gu_sb_t  tile-order copy of the [2I][D] gate-then-up matrix
+ *   dn_codes_t, dn_sb_t  tile-order copy of the [D][I] down matrix
+ *   h       bf16 [M][I] output (16-byte aligned); y bf16 [M][D] output
+ *   1 <= M <= 8; D % 512 == 0; I % 512 == 0.
+ * h and y are bit-identical to rmsnorm_gateup_swiglu_tiled followed by
+ * qgemv_affine4_tiled (same K splits, same summation order).  The launch
+ * keeps one workgroup per resident slot and separates its phases (gate/up,
+ * h, down, y) with grid barriers whose state is kept per (stream, M, D, I).
+ * Waits are bounded: if the workgroups cannot all be resident (other work
+ * holding the device for long), a wait gives up, the output is undefined and
+ * qg_mlp_failures reports it; that state then stays unusable until the
+ * process ends.  The first call for a (stream, M, D, I) allocates and clears
+ * its state (do not make it under graph capture).  Calls on one stream are
+ * ordered; calls on different streams use separate states.
+ */
+qg_status mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma,
+                                  float eps, const uint32_t* gu_codes_t,
+                                  const uint16_t* gu_sb_t,
+                                  const uint32_t* dn_codes_t,
+                                  const uint16_t* dn_sb_t, uint16_t* h,
+                                  uint16_t* y, int M, int D, int I,
+                                  void* stream);
+/* Synchronises the stream and returns how many of its MLP-block states saw a
+ * wait give up (0: none; -1: HIP error). */
+int32_t qg_mlp_failures(void* stream);
+
+/*
  * Tile-order layout of affine4 weights (Husky page, section "MSI의 네 가지 구현
  * 요소": weights stored in the order the projection kernel reads them), for
  * K % 512 == 0.  With T = ceil(N/16) 16-row tiles, C = K/128 chunks, B = K/512
@@ -268,6 +301,11 @@ qg_status qg_stream_read(const void* buf, size_t bytes, uint32_t* sink,
 qg_status qg_check_qgemv_affine4(const uint16_t* x, const uint32_t* codes,
                                  const uint16_t* scales, const uint16_t* biases,
                                  uint16_t* y, int M, int N, int K);
+qg_status qg_check_mlp_block_affine4_tiled(
+    const uint16_t* x, const uint16_t* gamma, float eps,
+    const uint32_t* gu_codes_t, const uint16_t* gu_sb_t,
+    const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
+    uint16_t* y, int M, int D, int I);
 qg_status qg_check_qgemv_affine8(const uint16_t* x, const uint32_t* codes,
                                  const uint16_t* scales, const uint16_t* biases,
                                  uint16_t* y, int M, int N, int K);

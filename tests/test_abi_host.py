@@ -267,3 +267,23 @@ def test_qgemv_affine8_checks(lib):
     assert c(A[0], A[1], A[2], A[3], A[1] + 64, 8, 16, 64) == ops.QG_EALIAS  # y inside codes (16*64 bytes)
     assert c(A[0], A[1], A[2], A[3], A[1] + 1024, 8, 16, 64) == ops.QG_OK    # just past codes
     assert c(0, A[1], A[2], A[3], A[4], 1, 16, 64) == ops.QG_EINVAL
+
+
+def test_mlp_block_checks(lib):
+    c = lambda *a: ops.check("mlp_block_affine4_tiled", *a)
+    ok = [A[0], A[1], 1e-6, A[2], A[3], A[4], A[5], A[6], A[7], 8, 2560, 12800]
+    assert c(*ok) == ops.QG_OK
+    bad = list(ok); bad[10] = 2496
+    assert c(*bad) == ops.QG_EINVAL          # D % 512
+    bad = list(ok); bad[11] = 12864
+    assert c(*bad) == ops.QG_EINVAL          # I % 512
+    bad = list(ok); bad[9] = 9
+    assert c(*bad) == ops.QG_EINVAL
+    bad = list(ok); bad[2] = -1.0
+    assert c(*bad) == ops.QG_EINVAL
+    bad = list(ok); bad[7] = A[0]
+    assert c(*bad) == ops.QG_EALIAS          # h over x
+    bad = list(ok); bad[8] = A[6] + 16
+    assert c(*bad) == ops.QG_EALIAS          # y over h
+    bad = list(ok); bad[7] = A[6] + 8
+    assert c(*bad) == ops.QG_EINVAL          # h alignment

@@ -617,3 +617,50 @@ def test_config_affine8_projection(M, N, K):
     ref = oracle.qgemv_affine8(d["x"], d["codes"], d["scales"], d["biases"])
     y = ops.qgemv_affine8(dev_bf16(d["x"]), *_affine8_dev(d))
     assert_close(host_bf16_f64(y), ref, what=f"affine8 {N}x{K} M{M}")
+
+
+# ------------------------------------------------- persistent MLP block --
+
+def _mlp_dev(d):
+    gu = ops.tile_pack(dev_u32(d["codes_gu"]), dev_bf16(d["scales_gu"]), dev_bf16(d["biases_gu"]))
+    dn = ops.tile_pack(dev_u32(d["codes_d"]), dev_bf16(d["scales_d"]), dev_bf16(d["biases_d"]))
+    return gu, dn
+
+
+def _mlp_separate(x, gam, eps, gu, dn, D, I):
+    h = ops.rmsnorm_gateup_swiglu_tiled(x, gam, eps, *gu, I)
+    return h, ops.qgemv_affine4_tiled(h, *dn, D)
+
+
+@pytest.mark.parametrize("M,D,I", [(3, 512, 512), (8, 1024, 3072), (1, 1024, 3072), (8, 2560, 12800),
+                                   (1, 2560, 12800)])
+def test_mlp_block_persistent_equals_separate(M, D, I):
+    d = synth.mlp_block(M=M, D=D, I=I, seed=9800 + M + D + I)
+    gu, dn = _mlp_dev(d)
+    x, gam = dev_bf16(d["x"]), dev_bf16(d["gamma"])
+    h_ref, y_ref = _mlp_separate(x, gam, d["eps"], gu, dn, D, I)
+    for rep in range(3):  # the barrier state carries over between launches
+        h, y = ops.mlp_block_affine4_tiled(x, gam, d["eps"], gu, dn, D, I)
+        assert ops.mlp_failures() == 0
+        assert torch.equal(h, h_ref), f"h differs (call {rep})"
+        assert torch.equal(y, y_ref), f"y differs (call {rep})"
+    h_or = oracle.rmsnorm_gateup_swiglu(d["x"], d["gamma"], d["eps"], d["codes_gu"], d["scales_gu"], d["biases_gu"])
+    assert_close(host_bf16_f64(h), h_or, slack=5e-3, what=f"persistent h M{M} D{D} I{I}")
+    y_or = oracle.qgemv_affine4(host_bits(h), d["codes_d"], d["scales_d"], d["biases_d"])
+    assert_close(host_bf16_f64(y), y_or, what=f"persistent y M{M} D{D} I{I}")
+
+
+def test_mlp_block_persistent_alternating_rows():
+    """Launches with different M on one stream (separate barrier state per M) interleaved."""
+    D, I = 1024, 3072
+    outs = {}
+    for M in (8, 1, 5, 8, 1):
+        d = synth.mlp_block(M=M, D=D, I=I, seed=9900 + M)
+        gu, dn = _mlp_dev(d)
+        x, gam = dev_bf16(d["x"]), dev_bf16(d["gamma"])
+        h, y = ops.mlp_block_affine4_tiled(x, gam, d["eps"], gu, dn, D, I)
+        h_ref, y_ref = _mlp_separate(x, gam, d["eps"], gu, dn, D, I)
+        assert torch.equal(h, h_ref) and torch.equal(y, y_ref), f"M{M}"
+        outs[M] = y
+    for M in (8, 1, 5):
+        assert ops.mlp_failures() == 0
