@@ -7,7 +7,7 @@ lives in ``oracle.c`` (plain C, double precision, ascending summation order),
 and this module only marshals numpy arrays into it.
 
 Which step of the method each function follows is documented in ``oracle.h``
-next to its declaration (O0-O13), with the page and section it comes from.
+next to its declaration (O0-O15), with the page and section it comes from.
 """
 from __future__ import annotations
 
@@ -60,6 +60,8 @@ def _load():
         lib.oracle_qgemv_affine4_f64x.argtypes = [P, P, P, P, I, I64, I64, P]
         lib.oracle_dequant_affine8.argtypes = [P, P, P, I64, I64, I64, I64, P]
         lib.oracle_qgemv_affine8.argtypes = [P, P, P, P, I, I64, I64, P]
+        lib.oracle_dequant_q6k.argtypes = [P, I64, I64, I64, I64, P]
+        lib.oracle_qgemv_q6k.argtypes = [P, P, I, I64, I64, P]
         lib.oracle_qgemv_q4k.argtypes = [P, P, I, I64, I64, P]
         lib.oracle_rmsnorm.argtypes = [P, P, D, I, I64, P]
         lib.oracle_silu.argtypes = [D]
@@ -75,7 +77,7 @@ def _load():
                      "oracle_qgemv_affine4_f64x", "oracle_qgemv_q4k", "oracle_rmsnorm",
                      "oracle_rmsnorm_gateup_swiglu", "oracle_mlp_block", "oracle_moe",
                      "oracle_lmhead", "oracle_lmhead_topk", "oracle_rht", "oracle_qgemv_affine4_rht",
-                     "oracle_dequant_affine8", "oracle_qgemv_affine8"):
+                     "oracle_dequant_affine8", "oracle_qgemv_affine8", "oracle_dequant_q6k", "oracle_qgemv_q6k"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -175,6 +177,29 @@ def qgemv_affine8(x, codes, scales, biases) -> np.ndarray:
     y = np.empty((M, N), dtype=np.float64)
     _check(_load().oracle_qgemv_affine8(px, pc, ps, pb, M, N, K, y.ctypes.data_as(ctypes.c_void_p)),
            "qgemv_affine8")
+    return y
+
+
+def dequant_q6k(blocks) -> np.ndarray:
+    """O14: a Q6_K matrix [N, K/256, 210] bytes as fp64 [N, K]."""
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    N, K = blocks.shape[0], blocks.shape[1] * 256
+    w = np.empty((N, K), dtype=np.float64)
+    _check(_load().oracle_dequant_q6k(blocks.ctypes.data_as(ctypes.c_void_p), N, K, 0, N,
+                                      w.ctypes.data_as(ctypes.c_void_p)), "dequant_q6k")
+    return w
+
+
+def qgemv_q6k(x, blocks) -> np.ndarray:
+    """O15: Y = X . dequant_q6k(W)^T in fp64."""
+    x, px = _c(x, np.uint16)
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    M, K = x.shape
+    N = blocks.shape[0]
+    assert blocks.shape[1] * 256 == K and blocks.shape[2] == 210
+    y = np.empty((M, N), dtype=np.float64)
+    _check(_load().oracle_qgemv_q6k(px, blocks.ctypes.data_as(ctypes.c_void_p), M, N, K,
+                                    y.ctypes.data_as(ctypes.c_void_p)), "qgemv_q6k")
     return y
 
 

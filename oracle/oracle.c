@@ -556,3 +556,59 @@ int oracle_qgemv_affine8(const uint16_t* x, const uint32_t* codes,
   free(xd);
   return rc;
 }
+
+/* ---------------------------------------------------------------- O14 --- */
+/* GGUF Q6_K (Q4_K_M files mix it in; the pages do not print the layout).
+ * Reading -- the public 210-byte block of 256 weights:
+ *   bytes 0-127 ql (low 4 bits), 128-191 qh (high 2 bits), 192-207 sixteen
+ *   int8 scales (one per 16 weights), 208-209 d (fp16).
+ *   Weight o of the block: half h = o/128, quarter j = (o%128)/32, l = o%32;
+ *   its low bits are the low nibble of ql[64h + 32*(j%2) + l] for j < 2 and
+ *   the high nibble for j >= 2; its high bits are bits 2j, 2j+1 of
+ *   qh[32h + l]; q = (low | high << 4) - 32 and the weight is d * sc[o/16] * q. */
+int oracle_dequant_q6k(const uint8_t* blocks, int64_t N, int64_t K, int64_t n0,
+                       int64_t nr, double* w) {
+  if (!blocks || !w) return -1;
+  if (N < 0 || K <= 0 || K % 256 != 0 || n0 < 0 || nr < 0 || n0 + nr > N) return -1;
+  const int64_t nb = K / 256;
+  for (int64_t r = 0; r < nr; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint8_t* blk = blocks + ((n0 + r) * nb + b) * 210;
+      const uint8_t* ql = blk;
+      const uint8_t* qh = blk + 128;
+      const int8_t* sc = (const int8_t*)(blk + 192);
+      const double d = o_f16_to_f64((uint16_t)(blk[208] | (blk[209] << 8)));
+      for (int o = 0; o < 256; ++o) {
+        const int h = o / 128, j = (o % 128) / 32, l = o % 32;
+        const unsigned lb = ql[64 * h + 32 * (j % 2) + l];
+        const unsigned lo = (j < 2) ? (lb & 15u) : (lb >> 4);
+        const unsigned hi = (qh[32 * h + l] >> (2 * j)) & 3u;
+        const int q = (int)(lo | (hi << 4)) - 32;
+        w[r * K + b * 256 + o] = d * (double)sc[o / 16] * (double)q;
+      }
+    }
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------- O15 --- */
+/* O3 on Q6_K weights: y[m][n] = sum_k x[m][k] * w[n][k], ascending k. */
+int oracle_qgemv_q6k(const uint16_t* x, const uint8_t* blocks, int M, int64_t N,
+                     int64_t K, double* y) {
+  if (!x || !y || M < 1 || N < 0 || K <= 0) return -1;
+  double* xd = decode_bf16_rows(x, M, K);
+  if (!xd) return -1;
+  double* wrow = (double*)malloc(sizeof(double) * (size_t)K);
+  if (!wrow) {
+    free(xd);
+    return -1;
+  }
+  int rc = 0;
+  for (int64_t n = 0; n < N && rc == 0; ++n) {
+    rc = oracle_dequant_q6k(blocks, N, K, n, 1, wrow);
+    for (int m = 0; m < M && rc == 0; ++m) y[(int64_t)m * N + n] = dot_asc(xd + (int64_t)m * K, wrow, K);
+  }
+  free(wrow);
+  free(xd);
+  return rc;
+}

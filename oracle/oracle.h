@@ -23,6 +23,8 @@
  *   O11 affine-4 projection of the transformed input
  *   O12 MLX-style affine 8-bit dequantisation, group 64
  *   O13 Y = X . W^T on affine-8 weights
+ *   O14 GGUF Q6_K superblock dequantisation (256 weights, 16 int8 scales)
+ *   O15 Y = X . W^T on Q6_K weights
  *
  * Sources (the four pages the method is taken from):
  *   [uzu]        "trymirai/uzu ... deep dive" (blog.123qwe.co.kr), section
@@ -162,6 +164,15 @@ int oracle_dequant_affine8(const uint32_t* codes, const uint16_t* scales,
 int oracle_qgemv_affine8(const uint16_t* x, const uint32_t* codes,
                          const uint16_t* scales, const uint16_t* biases,
                          int M, int64_t N, int64_t K, double* y);
+
+/* O14: rows [n0, n0+nr) of a Q6_K matrix (blocks: [N][K/256][210] bytes:
+ * ql 128, qh 64, int8 scales 16, fp16 d). K % 256 == 0. */
+int oracle_dequant_q6k(const uint8_t* blocks, int64_t N, int64_t K, int64_t n0,
+                       int64_t nr, double* w);
+
+/* O15: O3 on Q6_K weights; x bf16 [M][K], y fp64 [M][N]. */
+int oracle_qgemv_q6k(const uint16_t* x, const uint8_t* blocks, int M, int64_t N,
+                     int64_t K, double* y);
 
 #ifdef __cplusplus
 }

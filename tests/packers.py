@@ -66,3 +66,26 @@ def q4k_block(d_bits, dmin_bits, sc, m, q):
     out[..., 4:16] = pack_q4k_scales(sc, m)
     out[..., 16:144] = pack_q4k_codes(q)
     return out
+
+
+def q6k_block(d_bits, sc, q):
+    """Assemble Q6_K blocks (210 bytes). d_bits: uint16 [...]; sc: int8-valued [..., 16];
+    q: [..., 256] with values -32..31.  Weight o = 128h + 32j + l sits in the low (j < 2) or
+    high (j >= 2) nibble of ql[64h + 32(j%2) + l] and in bits 2j, 2j+1 of qh[32h + l]."""
+    d_bits = np.asarray(d_bits, dtype=np.uint16)
+    u = np.asarray(q, dtype=np.int64) + 32
+    assert u.min() >= 0 and u.max() <= 63
+    shape = d_bits.shape
+    u = u.reshape(shape + (2, 4, 32))  # [..., h, j, l]
+    lo, hi = u & 15, u >> 4
+    ql = np.zeros(shape + (2, 2, 32), dtype=np.int64)  # [..., h, j%2, l]
+    ql[..., 0, :] = lo[..., 0, :] | (lo[..., 2, :] << 4)
+    ql[..., 1, :] = lo[..., 1, :] | (lo[..., 3, :] << 4)
+    qh = hi[..., 0, :] | (hi[..., 1, :] << 2) | (hi[..., 2, :] << 4) | (hi[..., 3, :] << 6)  # [..., h, l]
+    out = np.zeros(shape + (210,), dtype=np.uint8)
+    out[..., 0:128] = ql.reshape(shape + (128,))
+    out[..., 128:192] = qh.reshape(shape + (64,))
+    out[..., 192:208] = np.asarray(sc, dtype=np.int64).astype(np.int8).view(np.uint8)
+    out[..., 208] = d_bits & 0xFF
+    out[..., 209] = d_bits >> 8
+    return out

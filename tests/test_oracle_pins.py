@@ -724,3 +724,106 @@ def test_affine8_rejects_bad_shapes():
     with pytest.raises(Exception):
         oracle.qgemv_affine8(np.zeros((1, 60), np.uint16), np.zeros((2, 15), np.uint32), sc, sc)
     assert oracle.qgemv_affine8(np.zeros((1, 64), np.uint16), codes, sc, sc).shape == (1, 2)
+
+
+# ----------------------------------------------------- Q6_K (hand-packed) --
+# One block: d = 0.5 (fp16 0x3800); scales (int8) per 16 weights:
+#   [1, -1, 2, -2, 3, -3, 4, -4, 127, -128, 5, -5, 6, -6, 7, -7];
+# weight o has q = (o % 64) - 32, i.e. stored 6-bit value u = o % 64.
+# Bytes worked out by hand from the layout (ql low nibble: quarters 0, 1;
+# high nibble: quarters 2, 3; qh bits 2j..2j+1):
+#   ql[0] = 0x00, ql[1] = 0x11, ql[33] = 0x11, ql[47] = 0xFF, ql[64] = 0x00
+#   qh[0] = 0x88 (u = 0, 32, 0, 32 -> high bits 0, 2, 0, 2), qh[16] = 0xDD, qh[32] = 0x88
+Q6K_SCALES = [1, -1, 2, -2, 3, -3, 4, -4, 127, -128, 5, -5, 6, -6, 7, -7]
+Q6K_BYTES = {0: 0x00, 1: 0x11, 33: 0x11, 47: 0xFF, 64: 0x00, 128: 0x88, 144: 0xDD, 160: 0x88,
+             192: 0x01, 193: 0xFF, 200: 0x7F, 201: 0x80, 208: 0x00, 209: 0x38}
+Q6K_VALUES = {0: -16.0, 17: 7.5, 63: -31.0, 130: -1905.0, 150: 640.0, 255: -108.5}
+
+
+def _q6k_hand():
+    o = np.arange(256)
+    return packers.q6k_block(np.array([0x3800], np.uint16), np.array([Q6K_SCALES]), (o % 64 - 32)[None])
+
+
+def test_q6k_hand_packed_bytes_and_values():
+    blk = _q6k_hand()
+    for i, v in Q6K_BYTES.items():
+        assert int(blk[0, i]) == v, (i, hex(int(blk[0, i])), hex(v))
+    w = oracle.dequant_q6k(blk.reshape(1, 1, 210))[0]
+    for o, v in Q6K_VALUES.items():
+        assert w[o] == v, (o, w[o], v)
+    o = np.arange(256)
+    assert np.array_equal(w, 0.5 * np.array(Q6K_SCALES).repeat(16) * (o % 64 - 32))
+
+
+def test_q6k_one_hot_through_qgemv():
+    blk = _q6k_hand().reshape(1, 1, 210)
+    ks = list(Q6K_VALUES)
+    x = np.zeros((len(ks), 256), np.uint16)
+    for r, k in enumerate(ks):
+        x[r, k] = 0x3F80
+    y = oracle.qgemv_q6k(x, blk)
+    assert [y[r, 0] for r in range(len(ks))] == [Q6K_VALUES[k] for k in ks]
+
+
+def _q6k_unpack_numpy(blocks):
+    """The Q6_K reading restated with numpy over (h, j, l), for comparison with the C oracle."""
+    b = blocks.astype(np.int64)
+    ql = b[..., 0:128].reshape(b.shape[:-1] + (2, 2, 32))
+    qh = b[..., 128:192].reshape(b.shape[:-1] + (2, 32))
+    sc = blocks[..., 192:208].view(np.int8).astype(np.float64)
+    d = (blocks[..., 208].astype(np.uint16) | (blocks[..., 209].astype(np.uint16) << 8)).view(np.float16)
+    u = np.empty(b.shape[:-1] + (2, 4, 32), np.int64)
+    for j in range(4):
+        nib = (ql[..., j % 2, :] >> (4 * (j // 2))) & 15
+        u[..., j, :] = nib | (((qh >> (2 * j)) & 3) << 4)
+    q = (u - 32).reshape(b.shape[:-1] + (256,))
+    return d.astype(np.float64)[..., None] * sc.repeat(16, axis=-1) * q
+
+
+def test_q6k_random_blocks_match_numpy_restatement():
+    g = np.random.default_rng(31)
+    blocks = g.integers(0, 256, (5, 3, 210), dtype=np.uint8)
+    d = synth.to_f16_bits(g.uniform(1e-3, 1e-2, (5, 3)))
+    blocks[..., 208] = d & 0xFF
+    blocks[..., 209] = d >> 8
+    assert np.array_equal(oracle.dequant_q6k(blocks), _q6k_unpack_numpy(blocks).reshape(5, 768))
+
+
+def test_q6k_pack_round_trip_every_code():
+    g = np.random.default_rng(32)
+    N, nb = 4, 2
+    q = np.stack([np.stack([g.permutation(256) % 64 - 32 for _ in range(nb)]) for _ in range(N)])
+    sc = g.integers(1, 128, (N, nb, 16)) * g.choice([-1, 1], (N, nb, 16))
+    blocks = packers.q6k_block(np.full((N, nb), 0x3C00, np.uint16), sc, q)  # d = 1
+    w = oracle.dequant_q6k(blocks).reshape(N, nb, 256)
+    assert np.array_equal(np.rint(w / sc.repeat(16, axis=-1)).astype(np.int64), q)
+
+
+def test_q6k_exact_integer_arithmetic():
+    g = np.random.default_rng(33)
+    N, nb, M = 5, 2, 3
+    q = g.integers(-32, 32, (N, nb, 256))
+    sc = g.integers(-8, 9, (N, nb, 16))
+    blocks = packers.q6k_block(np.full((N, nb), 0x4000, np.uint16), sc, q)  # d = 2
+    x_int = g.integers(-16, 17, (M, nb * 256))
+    y = oracle.qgemv_q6k(_bf16_of_small_ints(x_int), blocks)
+    w_int = (2 * sc.repeat(16, axis=-1) * q).reshape(N, nb * 256)
+    assert np.array_equal(y, (x_int.astype(np.int64) @ w_int.astype(np.int64).T).astype(np.float64))
+
+
+@pytest.mark.parametrize("M,N", [(1, 1), (8, 5)])
+def test_q6k_brute_force_small(M, N):
+    g = np.random.default_rng(34 + M + N)
+    blocks = g.integers(0, 256, (N, 1, 210), dtype=np.uint8)
+    d = synth.to_f16_bits(g.uniform(1e-3, 1e-2, (N, 1)))
+    blocks[..., 208] = d & 0xFF
+    blocks[..., 209] = d >> 8
+    x = synth.normal_bf16(g, (M, 256))
+    y = oracle.qgemv_q6k(x, blocks)
+    w = _q6k_unpack_numpy(blocks).reshape(N, 256)
+    xf = _bf16_bits_to_f64(x)
+    ref = np.zeros((M, N))
+    for k in reversed(range(256)):
+        ref += np.outer(xf[:, k], w[:, k])
+    assert np.max(np.abs(y - ref)) <= 1e-12 * math.sqrt(np.mean(ref ** 2))
