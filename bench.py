@@ -34,7 +34,8 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["bit_quantized_decode_group_amd/csrc/common.h", "bit_quantized_decode_group_amd/csrc/affine4.hip",
                   "bit_quantized_decode_group_amd/csrc/q4k.hip", "bit_quantized_decode_group_amd/csrc/abi.hip",
                   "bit_quantized_decode_group_amd/csrc/topk.hip", "bit_quantized_decode_group_amd/csrc/rht.hip",
-                  "bit_quantized_decode_group_amd/csrc/mlp.hip", "bit_quantized_decode_group_amd/csrc/affine_stage.h"]
+                  "bit_quantized_decode_group_amd/csrc/mlp.hip", "bit_quantized_decode_group_amd/csrc/affine_stage.h",
+                  "bit_quantized_decode_group_amd/csrc/q6k.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GRAPH_STEPS = 10  # at most this many consecutive steps (rotating weights, MoE stacks, router logits) per graph
 CALIB_BYTES = 384 << 20  # bytes read and written by the kernel that calibrates the HBM byte counters
@@ -553,6 +554,23 @@ def config_timings(torch, ops, synth, to_dev, dev):
             res[f"{N8}x{K8}_M{M}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
         del cps
     out["projection_affine8"] = res
+    # GGUF Q6_K projections, the same two shapes (210-byte superblocks as stored)
+    res = {}
+    for (N6, K6) in ((3072, 1024), (2560, 12800)):
+        d6 = synth.single_projection_q6k(M=8, N=N6, K=K6, seed=1007 + K6)
+        wb = to_dev(d6["blocks"], "u8")
+        nb = int(d6["blocks"].nbytes)
+        n = max(2, (512 << 20) // nb + 1)
+        cps = [wb] + [wb.clone() for _ in range(n - 1)]
+        x6 = to_dev(d6["x"], "bf16")
+        for M in (1, 8):
+            xm = x6[:M].contiguous()
+            ym = torch.empty((M, N6), dtype=torch.bfloat16, device=dev)
+            us = per_call(lambda i: ops.qgemv_q6k(xm, cps[i % n], y=ym), n, 3 * n)
+            b = nb + M * K6 * 2 + M * N6 * 2
+            res[f"{N6}x{K6}_M{M}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
+        del cps
+    out["projection_q6k"] = res
     # MLP block D=1024, I=3072 (RMSNorm -> gate/up -> SwiGLU -> down), M = 1 and 8
     mb = synth.mlp_block(M=8)
     keys = {"codes_gu": "u32", "scales_gu": "bf16", "biases_gu": "bf16", "codes_d": "u32", "scales_d": "bf16",

@@ -77,6 +77,7 @@ constexpr int kMaxUnsplitSteps = 4;        // batches of loads per tile a plain 
 size_t affine_lds_per_chunk(int M, int PL) { return (size_t)256 * M * PL + 64 + (size_t)8 * M; }
 size_t affine_lds_fixed(int M, int PL) { return (size_t)1024 * PL * M + (size_t)kWaves * 64; }
 size_t q4k_lds_per_sb(int M) { return (size_t)512 * M + 256; }
+size_t q6k_lds_per_sb(int M) { return (size_t)512 * M + 512; }  // operands + 16 scale-block sums x 8 rows
 
 // The LM-head mode stages all of K (no split): ceil(K/128) chunks must fit.
 bool fits_lds_unsplit(int M, int K) {
@@ -244,6 +245,21 @@ qg_status do_check_qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t*
   const Buf out[] = {{y, (size_t)M * n * 2, "y"}};
   qg_status st;
   if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(out[0], 2, fn)))
+    return st;
+  return check_alias(out, 1, in, 2, fn);
+}
+
+qg_status do_check_qgemv_q6k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K) {
+  const char* fn = "qgemv_q6k";
+  if (M < 1 || M > 8) return fail(QG_EINVAL, "%s: M=%d must be in 1..8", fn, M);
+  if (N < 0) return fail(QG_EINVAL, "%s: N=%d must be >= 0", fn, N);
+  if (K <= 0 || K % 256 != 0) return fail(QG_EINVAL, "%s: K=%d must be a positive multiple of 256", fn, K);
+  if ((long long)N * 16 > 0x7FFFFFFFLL) return fail(QG_EINVAL, "%s: N=%d too large", fn, N);
+  const size_t n = (size_t)N, k = (size_t)K;
+  const Buf in[] = {{x, (size_t)M * k * 2, "x"}, {blocks, n * (k / 256) * 210, "blocks"}};
+  const Buf out[] = {{y, (size_t)M * n * 2, "y"}};
+  qg_status st;
+  if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 2, fn)) || (st = check_ptr(out[0], 2, fn)))
     return st;
   return check_alias(out, 1, in, 2, fn);
 }
@@ -1030,6 +1046,41 @@ qg_status qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M
   if ((st = get_workspace((hipStream_t)stream, part_bytes, &ws))) return st;
   a.part = reinterpret_cast<float*>(ws);
   return launched(qg_launch_q4k(a, 16 + (size_t)a.cps * per, (hipStream_t)stream), "qgemv_q4k");
+}
+
+qg_status qg_check_qgemv_q6k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K) {
+  clear_err();
+  return do_check_qgemv_q6k(x, blocks, y, M, N, K);
+}
+
+qg_status qgemv_q6k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K, void* stream) {
+  clear_err();
+  qg_status st = do_check_qgemv_q6k(x, blocks, y, M, N, K);
+  if (st) return st;
+  if (N == 0) return QG_OK;
+  if ((st = check_device())) return st;
+  QgQ4kArgs a{};
+  a.x = x;
+  a.blocks = blocks;
+  a.y = y;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.nchunks = K / 256;
+  a.ntiles = (N + 15) / 16;
+  a.waves = kWaves;
+  const size_t per = q6k_lds_per_sb(M);
+  const int cps_max = (int)std::max<size_t>(1, std::min<size_t>((size_t)a.nchunks, (kQ4kLdsBudget - 16) / per));
+  Plan pl = plan_split(a.ntiles, a.nchunks, cps_max, true);
+  a.S = pl.S;
+  a.cps = pl.cps;
+  a.tpw = pl.tpw;
+  a.rgroups = pl.rgroups;
+  unsigned char* ws = nullptr;
+  const size_t part_bytes = (a.S > 1) ? (size_t)a.S * M * N * 4 : 0;
+  if ((st = get_workspace((hipStream_t)stream, part_bytes, &ws))) return st;
+  a.part = reinterpret_cast<float*>(ws);
+  return launched(qg_launch_q6k(a, 16 + (size_t)a.cps * per, (hipStream_t)stream), "qgemv_q6k");
 }
 
 qg_status moe_expert_qgemv(const uint16_t* x, const float* router_logits, int top_k, const uint8_t* w_gu,

@@ -187,6 +187,10 @@ struct QgMoeArgs {
 // Launchers return a hipError_t value (0 on success).
 int qg_launch_affine(int mode, const QgAffineArgs& a, size_t lds_bytes, hipStream_t stream);
 int qg_launch_q4k(const QgQ4kArgs& a, size_t lds_bytes, hipStream_t stream);
+// GGUF Q6_K projection (q6k.hip): QgQ4kArgs with blocks of 210 bytes, the
+// split plan in superblocks; k_q4k_reduce adds the slices when S > 1.
+int qg_launch_q6k(const QgQ4kArgs& a, size_t lds_bytes, hipStream_t stream);
+int qg_launch_q4k_reduce(const QgQ4kArgs& a, hipStream_t stream);
 int qg_launch_moe(const QgMoeArgs& a, hipStream_t stream);
 // Repack canonical affine-4 weights [N][K] (K % 512 == 0) into the tile-order
 // layout the tiled kernels read.

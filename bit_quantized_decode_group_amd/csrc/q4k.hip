@@ -465,6 +465,11 @@ static int launch_q4k_m(const QgQ4kArgs& a, size_t lds, hipStream_t st) {
 
 }  // namespace qg
 
+int qg_launch_q4k_reduce(const QgQ4kArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(qg::k_q4k_reduce, dim3((unsigned)(((size_t)a.M * a.N + 255) / 256)), dim3(256), 0, st, a);
+  return (int)hipGetLastError();
+}
+
 int qg_launch_q4k(const QgQ4kArgs& a, size_t lds, hipStream_t st) {
   switch (a.M) {
     case 1: return qg::launch_q4k_m<1>(a, lds, st);

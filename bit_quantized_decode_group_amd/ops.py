@@ -42,6 +42,8 @@ _SIGS = {
     "qg_check_lmhead_argmax_tiled": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I],
     "qg_check_qgemv_affine4_rht": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I],
     "qgemv_affine8": [_P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "qgemv_q6k": [_P, _P, _P, _I, _I, _I, _P],
+    "qg_check_qgemv_q6k": [_P, _P, _P, _I, _I, _I],
     "mlp_block_affine4_tiled": [_P, _P, _F, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "qg_check_mlp_block_affine4_tiled": [_P, _P, _F, _P, _P, _P, _P, _P, _P, _I, _I, _I],
     "qg_mlp_failures": [_P],
@@ -217,6 +219,21 @@ def mlp_failures(device=None):
     """Synchronises the current stream; the number of its persistent-MLP states whose waits gave up."""
     with torch.cuda.device(device or torch.cuda.current_device()):
         return int(lib().qg_mlp_failures(_stream()))
+
+
+def qgemv_q6k(x, blocks, y=None):
+    """Y = X . dequant(W)^T for GGUF Q6_K blocks: uint8 [N, K/256, 210] (or [N, K/256*210])."""
+    M, K = _dims2(x, "x")
+    N = blocks.shape[0]
+    if blocks.numel() != N * (K // 256) * 210 or K % 256:
+        raise ValueError(f"blocks must hold N x K/256 Q6_K blocks of 210 bytes, got {tuple(blocks.shape)}")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    for t, n, e in ((x, "x", 2), (blocks, "blocks", 1), (y, "y", 2)):
+        _need(t, n, e, x.device)
+    with torch.cuda.device(x.device):
+        _raise_on(lib().qgemv_q6k(_ptr(x), _ptr(blocks), _ptr(y), M, N, K, _stream()), "qgemv_q6k")
+    return y
 
 
 def qgemv_affine4_tiled(x, codes_t, sb_t, N, y=None):

@@ -92,6 +92,25 @@ def single_projection8(M=1, N=3072, K=1024, seed=1006):
     return {"x": x, **affine8_matrix(g, N, K), "M": M, "N": N, "K": K, "seed": seed}
 
 
+def q6k_matrix(g: np.random.Generator, N: int, K: int, d_lo=1e-3, d_hi=1e-2) -> np.ndarray:
+    """Returns uint8 [N, K/256, 210] Q6_K blocks: uniform random bytes (codes and int8 scales),
+    fp16 d ~ U(d_lo, d_hi) written over bytes 208..209."""
+    assert K % 256 == 0
+    nb = K // 256
+    blocks = g.integers(0, 256, size=(N, nb, 210), dtype=np.uint8)
+    d = to_f16_bits(g.uniform(d_lo, d_hi, (N, nb)))
+    blocks[..., 208] = (d & 0xFF).astype(np.uint8)
+    blocks[..., 209] = (d >> 8).astype(np.uint8)
+    return blocks
+
+
+def single_projection_q6k(M=1, N=3072, K=1024, seed=1007):
+    """X[M,K] ~ N(0,1) bf16 and a Q6_K W[N,K]."""
+    g = rng(seed)
+    x = normal_bf16(g, (M, K))
+    return {"x": x, "blocks": q6k_matrix(g, N, K), "M": M, "N": N, "K": K, "seed": seed}
+
+
 def q4k_matrix(g: np.random.Generator, N: int, K: int, d_lo=1e-3, d_hi=1e-2) -> np.ndarray:
     """Returns uint8 [N, K/256, 144] Q4_K blocks."""
     assert K % Q4K_BLOCK_WEIGHTS == 0

@@ -152,6 +152,23 @@ qg_status mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma,
 int32_t qg_mlp_failures(void* stream);
 
 /*
+ * qgemv_q6k -- Y = X . dequant(W)^T for GGUF Q6_K weights as stored (runNburn
+ * page, section "GGUF를 그대로 진실의 원본으로 둡니다": Q4_K_M files mix Q6_K
+ * in).  Reading of the public 210-byte block of 256 weights: bytes 0..127 ql
+ * (low 4 bits), 128..191 qh (high 2 bits), 192..207 sixteen int8 scales (one
+ * per 16 weights), 208..209 fp16 d; weight o (h = o/128, j = (o%128)/32,
+ * l = o%32) has low bits = low (j < 2) or high nibble of ql[64h + 32(j%2) + l],
+ * high bits = bits 2j..2j+1 of qh[32h + l], q = (low | high << 4) - 32, and
+ * value d * sc[o/16] * q.
+ *   x      bf16 [M][K] (16-byte aligned)
+ *   blocks uint8 [N][K/256][210] (2-byte aligned)
+ *   y      bf16 [M][N]
+ *   1 <= M <= 8; N >= 0 (N = 0 does nothing); K > 0, K % 256 == 0.
+ */
+qg_status qgemv_q6k(const uint16_t* x, const uint8_t* blocks, uint16_t* y,
+                    int M, int N, int K, void* stream);
+
+/*
  * Tile-order layout of affine4 weights (Husky page, section "MSI의 네 가지 구현
  * 요소": weights stored in the order the projection kernel reads them), for
  * K % 512 == 0.  With T = ceil(N/16) 16-row tiles, C = K/128 chunks, B = K/512
@@ -306,6 +323,8 @@ qg_status qg_check_mlp_block_affine4_tiled(
     const uint32_t* gu_codes_t, const uint16_t* gu_sb_t,
     const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
     uint16_t* y, int M, int D, int I);
+qg_status qg_check_qgemv_q6k(const uint16_t* x, const uint8_t* blocks,
+                             uint16_t* y, int M, int N, int K);
 qg_status qg_check_qgemv_affine8(const uint16_t* x, const uint32_t* codes,
                                  const uint16_t* scales, const uint16_t* biases,
                                  uint16_t* y, int M, int N, int K);

@@ -287,3 +287,14 @@ def test_mlp_block_checks(lib):
     assert c(*bad) == ops.QG_EALIAS          # y over h
     bad = list(ok); bad[7] = A[6] + 8
     assert c(*bad) == ops.QG_EINVAL          # h alignment
+
+
+def test_qgemv_q6k_checks(lib):
+    c = lambda *a: ops.check("qgemv_q6k", *a)
+    assert c(A[0], A[1], A[2], 8, 3072, 1024) == ops.QG_OK
+    assert c(A[0], A[1] + 2, A[2], 8, 3072, 1024) == ops.QG_OK      # blocks need 2-byte alignment only
+    assert c(A[0], A[1] + 1, A[2], 8, 3072, 1024) == ops.QG_EINVAL
+    assert c(A[0], A[1], A[2], 8, 3072, 1000) == ops.QG_EINVAL       # K % 256
+    assert c(A[0], A[1], A[1] + 210, 1, 16, 256) == ops.QG_EALIAS    # y inside the blocks (16 * 210 bytes)
+    assert c(A[0], A[1], A[1] + 16 * 210, 1, 16, 256) == ops.QG_OK
+    assert c(A[0], A[1], A[2], 0, 16, 256) == ops.QG_EINVAL

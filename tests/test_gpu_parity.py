@@ -664,3 +664,57 @@ def test_mlp_block_persistent_alternating_rows():
         outs[M] = y
     for M in (8, 1, 5):
         assert ops.mlp_failures() == 0
+
+
+# ---------------------------------------------------------------- qgemv_q6k --
+
+@pytest.mark.parametrize("K", [256, 768, 4096])
+@pytest.mark.parametrize("N", [1, 16, 17, 40])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_qgemv_q6k_small(M, N, K):
+    d = synth.single_projection_q6k(M=M, N=N, K=K, seed=9900 + 97 * M + 7 * N + K)
+    ref = oracle.qgemv_q6k(d["x"], d["blocks"])
+    y = ops.qgemv_q6k(dev_bf16(d["x"]), dev_u8(d["blocks"]))
+    assert_close(host_bf16_f64(y), ref, what=f"q6k M{M} N{N} K{K}")
+
+
+def test_qgemv_q6k_hand_packed_exact():
+    from tests.test_oracle_pins import Q6K_VALUES, _q6k_hand
+    blk = _q6k_hand().reshape(1, 1, 210)
+    ks = list(Q6K_VALUES)
+    x = np.zeros((len(ks), 256), np.uint16)
+    for r, k in enumerate(ks):
+        x[r, k] = 0x3F80
+    y = host_bf16_f64(ops.qgemv_q6k(dev_bf16(x), dev_u8(blk)))
+    # the output is bf16: each hand value after one round to nearest even (-1905 -> -1904)
+    want = [oracle.bf16_to_f64(oracle.f64_to_bf16_rne(Q6K_VALUES[k])) for k in ks]
+    assert [y[r, 0] for r in range(len(ks))] == want
+
+
+def test_qgemv_q6k_every_code_and_scale_sign():
+    """d = 1, scales +-1: one-hot rows read back q exactly for every code value in every
+    position class (half, quarter, lane run)."""
+    g = np.random.default_rng(77)
+    N = 8
+    q = np.stack([np.stack([g.permutation(256) % 64 - 32 for _ in range(2)]) for _ in range(N)])
+    sc = g.choice([-1, 1], (N, 2, 16))
+    blocks = packers.q6k_block(np.full((N, 2), 0x3C00, np.uint16), sc, q)
+    want = (sc.repeat(16, axis=-1) * q).reshape(N, 512).astype(np.float64)
+    cols = list(range(0, 512, 37)) + [255, 256, 511]
+    x = np.zeros((8, 512), np.uint16)
+    for start in range(0, len(cols), 8):
+        ks = cols[start:start + 8]
+        x[:] = 0
+        for r, k in enumerate(ks):
+            x[r, k] = 0x3F80
+        y = host_bf16_f64(ops.qgemv_q6k(dev_bf16(x[:len(ks)].copy()), dev_u8(blocks)))
+        for r, k in enumerate(ks):
+            assert np.array_equal(y[r], want[:, k]), (k, y[r], want[:, k])
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 3072, 1024), (8, 3072, 1024), (8, 2560, 12800)])
+def test_config_q6k_projection(M, N, K):
+    d = synth.single_projection_q6k(M=M, N=N, K=K, seed=1007 + K)
+    ref = oracle.qgemv_q6k(d["x"], d["blocks"])
+    y = ops.qgemv_q6k(dev_bf16(d["x"]), dev_u8(d["blocks"]))
+    assert_close(host_bf16_f64(y), ref, what=f"q6k {N}x{K} M{M}")
