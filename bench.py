@@ -123,6 +123,8 @@ def traffic_from_counters(fetch_csv, write_csv):
             f, w = avgs["fetch"].get(n, 0.0), avgs["write"].get(n, 0.0)
             ent["kernels"][n] = {"fetch_bytes": round(f), "write_bytes": round(w)}
             total += f + w
+        if not ent["kernels"]:
+            continue  # entry point not in this run (e.g. the persistent MLP block when --mlp separate)
         ent["bytes_per_launch"] = round(total)
         out["kernels"][entry] = ent
     with open(TRAFFIC_FILE, "w") as f:
