@@ -1,10 +1,11 @@
 """Test-side packers: write known codes / scales into the byte formats.
 
 These are written independently of both the oracle (which only unpacks) and
-the GPU library.  The layouts they produce are the readings documented in
-the design doc (affine-4: low nibble first, 8 codes per little-endian 32-bit word;
-Q4_K: the public 144-byte GGUF block); the hand-packed pins in
-test_oracle_pins.py fix those layouts byte by byte.
+the GPU library.  The layouts they produce: affine-4 low nibble first, 8 codes
+per little-endian 32-bit word; affine-8 one byte per code, least significant
+byte first; Q4_K the public 144-byte GGUF block; Q6_K the public 210-byte GGUF
+block.  The hand-packed pins in test_oracle_pins.py fix those layouts byte by
+byte.
 """
 import numpy as np
 
