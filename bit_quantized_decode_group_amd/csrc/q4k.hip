@@ -23,7 +23,7 @@
 
 namespace qg {
 
-constexpr int kSbBatch = 2;  // superblocks whose loads are issued together
+constexpr int kSbBatch = 2;  // superblocks whose loads are issued together (default)
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
@@ -100,20 +100,20 @@ __device__ __forceinline__ void stage_q4k_x(const T* src, size_t ld, int K, uint
   }
 }
 
-// Loads of one batch of kSbBatch superblocks for NB tiles: each block's
-// 16-byte header and this lane's eight code bytes of each of its four chunks.
-template <int NB>
+// Loads of one batch of SB superblocks for NB tiles: each block's 16-byte
+// header and this lane's eight code bytes of each of its four chunks.
+template <int NB, int SB = kSbBatch>
 struct Q4kBuf {
-  uint4 hdr[NB][kSbBatch];
-  uint2 cq[NB][kSbBatch][4];
+  uint4 hdr[NB][SB];
+  uint2 cq[NB][SB][4];
 };
 
 // Issues the loads of the batch starting at superblock sb (clamped to the
 // last of nsb, so every address is in bounds; the caller clamps the row).
-template <int NB>
-__device__ __forceinline__ void q4k_load(Q4kBuf<NB>& bf, const uint8_t* const (&blk)[NB], int sb, int nsb, int kb) {
+template <int NB, int SB>
+__device__ __forceinline__ void q4k_load(Q4kBuf<NB, SB>& bf, const uint8_t* const (&blk)[NB], int sb, int nsb, int kb) {
 #pragma unroll
-  for (int u = 0; u < kSbBatch; ++u) {
+  for (int u = 0; u < SB; ++u) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const uint8_t* bp = blk[b] + (size_t)min(sb + u, nsb - 1) * 144;
@@ -131,10 +131,10 @@ __device__ __forceinline__ void q4k_load(Q4kBuf<NB>& bf, const uint8_t* const (&
 // is loaded before the batch is used.  xs / sx are this slice's staged activations,
 // read from lds[region + entry]; lds[0] is a zero entry that lanes whose
 // slots carry the other sub-block (or a padding row) read instead.
-template <int M, int NB>
+template <int M, int NB, int SB = kSbBatch>
 __device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* const (&blk)[NB], int nsb,
                                          const uint4* lds, uint32_t region, const float* sx, int lane,
-                                         Q4kBuf<NB> cur) {
+                                         Q4kBuf<NB, SB> cur) {
   const int kb = lane >> 4;
   const int half = lane >> 5;
   const int rho = lane & 15;
@@ -145,9 +145,9 @@ __device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* cons
   const float* sx_base = sx + half * 8 + 4 * (kb & 1);
   const UnpackK uk = unpack_constants();
 
-  auto compute = [&](const Q4kBuf<NB>& cur, int sb) {
+  auto compute = [&](const Q4kBuf<NB, SB>& cur, int sb) {
 #pragma unroll
-    for (int u = 0; u < kSbBatch; ++u) {
+    for (int u = 0; u < SB; ++u) {
       const int sbl = sb + u;
       if (sbl >= nsb) break;
 #pragma unroll
@@ -184,9 +184,9 @@ __device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* cons
   // every batch but the last has a successor to load first; the loop body has
   // no branch around its loads
   int sb = 0;
-  for (; sb + kSbBatch < nsb; sb += kSbBatch) {
-    Q4kBuf<NB> nxt;
-    q4k_load<NB>(nxt, blk, sb + kSbBatch, nsb, kb);
+  for (; sb + SB < nsb; sb += SB) {
+    Q4kBuf<NB, SB> nxt;
+    q4k_load<NB, SB>(nxt, blk, sb + SB, nsb, kb);
     __builtin_amdgcn_sched_barrier(0);
     compute(cur, sb);
     cur = nxt;
@@ -272,9 +272,12 @@ __global__ void __launch_bounds__(256) k_q4k_reduce(QgQ4kArgs p) {
 // E <= 4 * blockDim; other loads can be issued while they are in flight),
 // route_store puts them and their keys into LDS (keys[] has two zero entries
 // past E), route_rank starts with a barrier, ranks and ends with a barrier.
+// When the workgroup has threads to spare, each expert's count is split over
+// up to four key ranges (partial counts in LDS, added in range order).
 struct RouteIn {
   float v[4];
 };
+constexpr int kRouteMaxThreads = 256;  // workgroup size route_rank is used with
 
 __device__ __forceinline__ void route_load(const float* logits, int E, RouteIn& in) {
 #pragma unroll
@@ -295,16 +298,33 @@ __device__ __forceinline__ void route_store(const RouteIn& in, int E, float* lg,
 
 __device__ void route_rank(int E, int top_k, const float* lg, const unsigned long long* keys, int* sel, float* pw,
                            int* asc, float* pasc) {
+  __shared__ int rpart[kRouteMaxThreads];
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+  const int P = min(4, max(1, (int)blockDim.x / E));  // key ranges per expert (E * P <= blockDim when P > 1)
+  const int chunk = ((E + 2 * P - 1) / (2 * P)) * 2;  // even: pairs stay inside keys[0 .. E+1]
+  for (int idx = threadIdx.x; idx < E * P; idx += blockDim.x) {
+    const int e = idx % E, part = idx / E;
     const unsigned long long ke = keys[e];
+    const int j1 = min((part + 1) * chunk, E);
     int rank = 0;
 #pragma unroll 8
-    for (int j = 0; j < E; j += 2) {
+    for (int j = part * chunk; j < j1; j += 2) {
       const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(keys + j);
       rank += (kk.x > ke ? 1 : 0) + (kk.y > ke ? 1 : 0);
     }
-    if (rank < top_k) sel[rank] = e;
+    if (P == 1) {
+      if (rank < top_k) sel[rank] = e;
+    } else {
+      rpart[idx] = rank;
+    }
+  }
+  if (P > 1) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      int rank = 0;
+      for (int q = 0; q < P; ++q) rank += rpart[q * E + e];
+      if (rank < top_k) sel[rank] = e;
+    }
   }
   __syncthreads();
   if (threadIdx.x < 64) {  // one wave: softmax over the selected logits, then the ascending order
@@ -334,6 +354,7 @@ __device__ void route_rank(int E, int top_k, const float* lg, const unsigned lon
 // caller (out_ids / out_w).  h is stored in bf16, the precision k_moe_down
 // consumes it in.
 constexpr int kMoeWaves = 4;
+static_assert(64 * kMoeWaves <= kRouteMaxThreads, "route_rank's partial counts are sized for this workgroup");
 
 __global__ void __launch_bounds__(256) k_moe_gateup(QgMoeArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -401,6 +422,7 @@ __global__ void __launch_bounds__(256) k_moe_gateup(QgMoeArgs p) {
 // in wave order.  Each wave's first weight batch is in flight while the
 // experts' activations are staged.
 constexpr int kMoeDownWaves = 8;
+constexpr int kMoeDownBatch = 3;  // superblocks per load batch (I = 768: one batch per expert)
 
 __global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -423,7 +445,7 @@ __global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
   };
   const int s0 = min(wave, p.top_k - 1);
   const uint8_t* blk0[1] = {expert_blocks(s0)};
-  Q4kBuf<1> first;
+  Q4kBuf<1, kMoeDownBatch> first;
   q4k_load<1>(first, blk0, 0, nsb, lane >> 4);
   __builtin_amdgcn_sched_barrier(0);
 

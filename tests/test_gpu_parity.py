@@ -243,7 +243,8 @@ def test_lmhead_accepted_prefix_and_repeat_calls():
 # -------------------------------------------------------- moe_expert_qgemv --
 
 @pytest.mark.parametrize("E,D,I,top_k", [(8, 256, 256, 1), (8, 256, 512, 8), (16, 512, 256, 2), (32, 768, 512, 8),
-                                         (128, 256, 256, 64)])
+                                         (128, 256, 256, 64), (3, 256, 256, 2), (200, 256, 256, 64),
+                                         (1024, 256, 256, 8)])
 def test_moe_small(E, D, I, top_k):
     d = synth.moe_token(E=E, D=D, I=I, top_k=top_k, seed=7000 + E + D + I + top_k, n_logit_sets=2)
     for s in range(2):
