@@ -35,7 +35,7 @@ KERNEL_SOURCES = ["bit_quantized_decode_group_amd/csrc/common.h", "bit_quantized
                   "bit_quantized_decode_group_amd/csrc/q4k.hip", "bit_quantized_decode_group_amd/csrc/abi.hip",
                   "bit_quantized_decode_group_amd/csrc/topk.hip", "bit_quantized_decode_group_amd/csrc/rht.hip",
                   "bit_quantized_decode_group_amd/csrc/mlp.hip", "bit_quantized_decode_group_amd/csrc/affine_stage.h",
-                  "bit_quantized_decode_group_amd/csrc/q6k.hip"]
+                  "bit_quantized_decode_group_amd/csrc/q6k.hip", "bit_quantized_decode_group_amd/csrc/valu.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GRAPH_STEPS = 10  # at most this many consecutive steps (rotating weights, MoE stacks, router logits) per graph
 CALIB_BYTES = 384 << 20  # bytes read and written by the kernel that calibrates the HBM byte counters
@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--pmc-pass", action="store_true",
                     help="short run for a rocprofv3 --pmc pass: a copy of CALIB_BYTES (counter calibration), "
                          "then --steps M=8 steps; prints one JSON line")
+    ap.add_argument("--compare-valu", metavar="NxK",
+                    help="only time the affine-4 projection W[N,K] with the products on the matrix cores and on "
+                         "the vector ALU (M = 1 and 8), print one JSON line; for a rocprofv3 run of that pair")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the counter CSVs of a FETCH_SIZE and a WRITE_SIZE --pmc pass into "
                          "profiles/traffic.json (no GPU needed)")
@@ -166,6 +169,12 @@ def main():
         if kind == "i32":
             return torch.from_numpy(a.astype(np.int32)).to(dev)
         raise ValueError(kind)
+
+    if args.compare_valu:
+        N, K = (int(v) for v in args.compare_valu.lower().split("x"))
+        r = compare_valu(torch, ops, synth, to_dev, dev, N, K, lambda fn, n, reps: per_call_us(torch, fn, reps))
+        print(json.dumps({"products_mfma_vs_valu": {f"{N}x{K}": r}}), flush=True)
+        return
 
     t0 = time.time()
     vb = synth.verify_block()          # M=8, D=2560, I=12800, seed 1003
@@ -481,21 +490,50 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def per_call_us(torch, fn, reps):
+    """Microseconds per call of fn(i): a short warm-up, then HIP events around reps back-to-back calls."""
+    for i in range(min(reps, 20)):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def compare_valu(torch, ops, synth, to_dev, dev, N, K, per_call):
+    """Per-call times of the affine-4 projection X[M,K] x W[N,K] at M = 1 and 8 with the
+    M-row products on the matrix cores (qgemv_affine4) and on the vector ALU
+    (qg_affine4_valu: same plan, staging and reduce), on identical weights rotated
+    over >= 512 MB of copies."""
+    dv = synth.single_projection(M=8, N=N, K=K, seed=1008 + K)
+    w = {k: to_dev(dv[k], "u32" if k == "codes" else "bf16") for k in ("codes", "scales", "biases")}
+    nb = int(dv["codes"].nbytes + dv["scales"].nbytes + dv["biases"].nbytes)
+    n = max(2, (512 << 20) // nb + 1)
+    cps = [w] + [{k: v.clone() for k, v in w.items()} for _ in range(n - 1)]
+    x8 = to_dev(dv["x"], "bf16")
+    r = {}
+    for M in (1, 8):
+        xm = x8[:M].contiguous()
+        ym = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        b = nb + M * K * 2 + M * N * 2
+        for name, fn in (("mfma", ops.qgemv_affine4), ("valu", ops.affine4_valu)):
+            us = per_call(lambda i: fn(xm, cps[i % n]["codes"], cps[i % n]["scales"], cps[i % n]["biases"], y=ym),
+                          n, max(3 * n, 30))
+            r[f"M{M}_{name}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
+        r[f"M{M}_valu_over_mfma"] = round(r[f"M{M}_valu"]["us"] / r[f"M{M}_mfma"]["us"], 3)
+    return r
+
+
 def config_timings(torch, ops, synth, to_dev, dev):
     """Context (not the bench value): per-call times of the smaller workloads
     and variants, each rotating enough weight copies (>= 512 MB) that the
     Infinity Cache cannot serve a call; HIP events around R back-to-back calls."""
     def per_call(fn, n_copies, reps):
-        for i in range(min(reps, 20)):
-            fn(i)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(reps):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps * 1e3
+        return per_call_us(torch, fn, reps)
 
     out = {}
     # single projection X[M,1024] x W[3072,1024] affine-4 (M = 1 and 8)
@@ -573,6 +611,9 @@ def config_timings(torch, ops, synth, to_dev, dev):
             res[f"{N6}x{K6}_M{M}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
         del cps
     out["projection_q6k"] = res
+    # the M-row products on the matrix cores or on the vector ALU, same work
+    out["products_mfma_vs_valu"] = {f"{N}x{K}": compare_valu(torch, ops, synth, to_dev, dev, N, K, per_call)
+                                    for (N, K) in ((3072, 1024), (2560, 12800), (151936, 1024))}
     # MLP block D=1024, I=3072 (RMSNorm -> gate/up -> SwiGLU -> down), M = 1 and 8
     mb = synth.mlp_block(M=8)
     keys = {"codes_gu": "u32", "scales_gu": "bf16", "biases_gu": "bf16", "codes_d": "u32", "scales_d": "bf16",

@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["abi.hip", "affine4.hip", "q4k.hip", "q6k.hip", "topk.hip", "rht.hip", "mlp.hip"]
+SOURCES = ["abi.hip", "affine4.hip", "q4k.hip", "q6k.hip", "topk.hip", "rht.hip", "mlp.hip", "valu.hip"]
 LIB = os.path.join(HERE, "libqgemv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -754,6 +754,31 @@ qg_status qgemv_affine4(const uint16_t* x, const uint32_t* codes, const uint16_t
   return run_affine(QG_MODE_PLAIN, a, (hipStream_t)stream, "qgemv_affine4");
 }
 
+qg_status qg_affine4_valu(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                          uint16_t* y, int M, int N, int K, void* stream) {
+  clear_err();
+  qg_status st = do_check_qgemv_affine4(x, codes, scales, biases, y, M, N, K);
+  if (st) return st;
+  if (N == 0) return QG_OK;
+  if ((st = check_device())) return st;
+  QgAffineArgs a{};
+  a.x = x;
+  a.codes = codes;
+  a.scales = scales;
+  a.biases = biases;
+  a.y = y;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  size_t lds = 0;  // qgemv_affine4's plan; the vector-ALU kernel needs less LDS than it
+  if ((st = plan_affine(QG_MODE_PLAIN, a, "qg_affine4_valu", &lds))) return st;
+  if (qg_valu_lds_bytes(a.M, a.cps) > lds) return fail(QG_EUNSUPPORTED, "qg_affine4_valu: slice does not fit");
+  unsigned char* ws = nullptr;
+  if ((st = get_workspace((hipStream_t)stream, a.S > 1 ? (size_t)a.S * a.M * a.N * 4 : 16, &ws))) return st;
+  a.part = reinterpret_cast<float*>(ws);
+  return launched(qg_launch_affine_valu(a, (hipStream_t)stream), "qg_affine4_valu");
+}
+
 qg_status qg_check_qgemv_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                                  const uint16_t* biases, uint16_t* y, int M, int N, int K) {
   clear_err();

@@ -514,6 +514,12 @@ __global__ void __launch_bounds__(256) k_tile_pack(const uint32_t* __restrict__ 
 
 }  // namespace qg
 
+int qg_launch_split_reduce_plain(const QgAffineArgs& a, hipStream_t st) {
+  const unsigned nblk = (unsigned)(((size_t)a.M * a.N + 255) / 256);
+  hipLaunchKernelGGL(qg::k_split_reduce<QG_MODE_PLAIN>, dim3(nblk), dim3(256), 0, st, a);
+  return (int)hipGetLastError();
+}
+
 int qg_launch_tile_pack(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, uint32_t* codes_t,
                         uint16_t* sb_t, int N, int K, hipStream_t st) {
   const size_t pieces = (size_t)((N + 15) / 16) * ((size_t)K / 128 * 64 + (size_t)K / 512 * 32);

@@ -187,6 +187,13 @@ struct QgMoeArgs {
 // Launchers return a hipError_t value (0 on success).
 int qg_launch_affine(int mode, const QgAffineArgs& a, size_t lds_bytes, hipStream_t stream);
 int qg_launch_q4k(const QgQ4kArgs& a, size_t lds_bytes, hipStream_t stream);
+// k_split_reduce of a plain projection (adds the S slices' partial sums in
+// slice order and stores bf16 Y), for kernels that share qgemv_affine4's plan.
+int qg_launch_split_reduce_plain(const QgAffineArgs& a, hipStream_t stream);
+// valu.hip: the affine-4 projection with vector-ALU dot products (measurement
+// aid); LDS bytes it needs for a slice of cps chunks.
+int qg_launch_affine_valu(const QgAffineArgs& a, hipStream_t stream);
+size_t qg_valu_lds_bytes(int M, int cps);
 // GGUF Q6_K projection (q6k.hip): QgQ4kArgs with blocks of 210 bytes, the
 // split plan in superblocks; k_q4k_reduce adds the slices when S > 1.
 int qg_launch_q6k(const QgQ4kArgs& a, size_t lds_bytes, hipStream_t stream);

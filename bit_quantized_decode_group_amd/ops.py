@@ -32,6 +32,7 @@ _I = ctypes.c_int
 _F = ctypes.c_float
 _SIGS = {
     "qgemv_affine4": [_P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "qg_affine4_valu": [_P, _P, _P, _P, _P, _I, _I, _I, _P],
     "qgemv_q4k": [_P, _P, _P, _I, _I, _I, _P],
     "qgemv_affine4_rht": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P],
     "affine4_tile_pack": [_P, _P, _P, _P, _P, _I, _I, _P],
@@ -137,6 +138,20 @@ def qgemv_affine4(x, codes, scales, biases, y=None):
     with torch.cuda.device(x.device):
         _raise_on(lib().qgemv_affine4(_ptr(x), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(y), M, N, K, _stream()),
                   "qgemv_affine4")
+    return y
+
+
+def affine4_valu(x, codes, scales, biases, y=None):
+    """Measurement aid: qgemv_affine4 with the products on the vector ALU (qg_affine4_valu)."""
+    M, K = _dims2(x, "x")
+    N = codes.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    for t, n, e in ((x, "x", 2), (codes, "codes", 4), (scales, "scales", 2), (biases, "biases", 2), (y, "y", 2)):
+        _need(t, n, e, x.device)
+    with torch.cuda.device(x.device):
+        _raise_on(lib().qg_affine4_valu(_ptr(x), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(y), M, N, K,
+                                        _stream()), "qg_affine4_valu")
     return y
 
 

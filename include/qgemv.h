@@ -311,6 +311,20 @@ qg_status qg_stream_read(const void* buf, size_t bytes, uint32_t* sink,
                          void* stream);
 
 /*
+ * qg_affine4_valu -- measurement aid, not part of the decode path: the same
+ * projection as qgemv_affine4 (same arguments, layout, checks and errors;
+ * same K-slice / workgroup plan and the same split-K reduce), with the M-row
+ * products formed on the vector ALU (v_dot2_f32_bf16 on bf16 activation
+ * pairs and the exact bf16 values 128+q of the codes) instead of on the
+ * matrix cores.  It exists so the two ways of computing the products can be
+ * timed against each other on identical work at M = 1..8; its results agree
+ * with qgemv_affine4's within fp32 summation order.
+ */
+qg_status qg_affine4_valu(const uint16_t* x, const uint32_t* codes,
+                          const uint16_t* scales, const uint16_t* biases,
+                          uint16_t* y, int M, int N, int K, void* stream);
+
+/*
  * Host-only twins of the entry points above: the same argument checks, no
  * GPU access, no launch.  They return what the entry point would return
  * before launching anything.

@@ -719,3 +719,47 @@ def test_config_q6k_projection(M, N, K):
     ref = oracle.qgemv_q6k(d["x"], d["blocks"])
     y = ops.qgemv_q6k(dev_bf16(d["x"]), dev_u8(d["blocks"]))
     assert_close(host_bf16_f64(y), ref, what=f"q6k {N}x{K} M{M}")
+
+
+# ------------------------------------------- vector-ALU comparison kernel --
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 64), (3, 17, 192), (8, 40, 1024), (5, 33, 576), (8, 100, 12800),
+                                   (2, 1, 128), (7, 3072, 1024)])
+def test_affine4_valu_small(M, N, K):
+    """qg_affine4_valu (vector-ALU products, same plan) against the oracle: odd group
+    counts, ragged tiles, split K."""
+    d = synth.single_projection(M=M, N=N, K=K, seed=3300 + 97 * M + 7 * N + K)
+    ref = oracle.qgemv_affine4(d["x"], d["codes"], d["scales"], d["biases"])
+    y = ops.affine4_valu(dev_bf16(d["x"]), *_affine_dev(d))
+    assert_close(host_bf16_f64(y), ref, what=f"valu M{M} N{N} K{K}")
+
+
+def test_affine4_valu_hand_packed_exact():
+    """One-hot rows read out single dequantised weights, exactly as qgemv_affine4 does."""
+    ks = [0, 7, 8, 63, 64, 100, 127, 1]
+    x = np.zeros((8, 128), dtype=np.uint16)
+    for m, k in enumerate(ks):
+        x[m, k] = 0x3F80
+    args = (dev_u32(HAND_CODES), dev_bf16(HAND_SCALES), dev_bf16(HAND_BIASES))
+    yv = host_bits(ops.affine4_valu(dev_bf16(x), *args))
+    ym = host_bits(ops.qgemv_affine4(dev_bf16(x), *args))
+    assert np.array_equal(yv, ym)
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 2560, 12800), (1, 2560, 12800), (8, 151936, 1024), (1, 151936, 1024)])
+def test_affine4_valu_full_size_sampled(M, N, K):
+    """The bench's shapes (down projection, LM-head-sized projection): 512 sampled rows
+    against the oracle, all rows against qgemv_affine4 within the same bar."""
+    g = synth.rng(3400 + M + K)
+    d = synth.single_projection(M=M, N=N, K=K, seed=3400 + M + K)
+    args = _affine_dev(d)
+    yv = host_bf16_f64(ops.affine4_valu(dev_bf16(d["x"]), *args))
+    ym = host_bf16_f64(ops.qgemv_affine4(dev_bf16(d["x"]), *args))
+    rows = np.sort(g.choice(N, size=512, replace=False))
+    ref = oracle.qgemv_affine4(d["x"], d["codes"][rows], d["scales"][rows], d["biases"][rows])
+    assert_close(yv[:, rows], ref, what=f"valu sampled M{M} N{N} K{K}")
+    # two GPU results, each rounded to bf16 from its own fp32 sum: they may differ by one bf16 ulp
+    # (up to 2^-7 |y|) plus both kernels' fp32 summation error
+    rms = float(np.sqrt(np.mean(ym ** 2)))
+    bad = np.abs(yv - ym) > 2.0 ** -7 * np.abs(ym) + 2e-3 * rms
+    assert not bad.any(), f"valu vs mfma M{M} N{N} K{K}: {int(bad.sum())} outputs differ by more than one ulp"
