@@ -130,9 +130,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
       // tile order: every load of the wave reads 1 KB (codes) or 256 bytes
       // (scales, biases) of consecutive memory
       const size_t tile = (size_t)min(gw + ti * nw, p.ntiles - 1);  // a wave without work reloads a real tile
+      const uint4* cbase = reinterpret_cast<const uint4*>(p.codes) + (tile * p.nchunks + c0 + cb) * 64 + lane;
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u)
-        bf.q[u] = *reinterpret_cast<const uint4*>(p.codes + ((tile * p.nchunks + c0 + cb + u) * 64 + lane) * 4);
+      for (int u = 0; u < BATCH; ++u) bf.q[u] = cbase[u * 64];  // one base address, 1-KB immediate offsets
       // one 16-byte record per (row, group parity): dword u = (scale, bias) of group 2(c0+cb+u) + half
       const uint16_t* rec = p.scales + ((tile * (p.nchunks / BATCH) + (c0 + cb) / BATCH) * 2 + half) * 128 + nl * 8;
       const uint4 sv = *reinterpret_cast<const uint4*>(rec);
