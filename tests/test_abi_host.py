@@ -95,6 +95,10 @@ def test_entry_points_refuse_before_launch(lib):
     assert lib.lmhead_argmax(P(A[0]), P(A[1]), P(A[2]), P(A[3]), None, P(A[4]), None, None, 1, 0, 64,
                              None) == ops.QG_EINVAL
     assert lib.qgemv_affine4(P(A[0]), P(A[1]), P(A[2]), P(A[3]), P(A[0]), 1, 16, 64, None) == ops.QG_EALIAS
+    # the vector-ALU measurement aid applies qgemv_affine4's checks
+    assert lib.qg_affine4_valu(P(A[0]), P(A[1]), P(A[2]), P(A[3]), P(A[4]), 9, 16, 64, None) == ops.QG_EINVAL
+    assert lib.qg_affine4_valu(P(A[0]), P(A[1]), P(A[2]), P(A[3]), P(A[4]), 1, 16, 96, None) == ops.QG_EINVAL
+    assert lib.qg_affine4_valu(P(A[0]), P(A[1]), P(A[2]), P(A[3]), P(A[0]), 1, 16, 64, None) == ops.QG_EALIAS
 
 
 def test_qgemv_q4k_checks(lib):
