@@ -43,7 +43,9 @@
  *     calls on different streams use different workspaces.  A call that must
  *     grow the workspace synchronises that stream once.  A call may enqueue
  *     more than one kernel (a split-K or argmax reduction follows its main
- *     kernel on the same stream).
+ *     kernel on the same stream), so calls that share a stream must be issued
+ *     by one host thread at a time: interleaved launches of two calls on one
+ *     stream would share the workspace between their kernels.
  *   * Floating point: fp32 accumulation; bf16 outputs rounded to nearest even.
  *     Results are deterministic: the same inputs give the same bytes on every
  *     call (fixed reduction order, no atomics).
