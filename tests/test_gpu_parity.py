@@ -205,6 +205,28 @@ def _bias_rows(V, K, bias_bits):
     return dev_u32(codes), dev_bf16(scales), dev_bf16(biases)
 
 
+@pytest.mark.parametrize("M,K", [(8, 9088), (1, 9088), (4, 18176)])
+def test_lmhead_longest_k(M, K):
+    """The longest K the LM head's single slice holds in LDS for M rows (8 rows: 9088;
+    4 rows: 18,176): logits and ids against the oracle."""
+    d = synth.lm_head(M=M, V=300, K=K, seed=6100 + M + K)
+    logits, ids, gap, _ = oracle.lmhead(d["x"], d["codes"], d["scales"], d["biases"])
+    gi, acc, gl = ops.lmhead_argmax(dev_bf16(d["x"]), *_affine_dev(d), want_logits=True)
+    assert_close(gl.cpu().numpy().astype(np.float64), logits, slack=1e-4, what=f"longest K logits M{M} K{K}")
+    assert_ids(gi.cpu().numpy(), ids, gap, logits, what=f"longest K ids M{M} K{K}")
+
+
+def test_lmhead_tiled_longest_k():
+    """Tile order at the longest 512-aligned K for 8 rows (8704): equal to the canonical call."""
+    d = synth.lm_head(M=8, V=300, K=8704, seed=6200)
+    args = _affine_dev(d)
+    ct, sb = ops.tile_pack(*args)
+    x = dev_bf16(d["x"])
+    ids, acc, lg = ops.lmhead_argmax(x, *args, want_logits=True)
+    ids_t, acc_t, lg_t = ops.lmhead_argmax_tiled(x, ct, sb, d["V"], want_logits=True)
+    assert torch.equal(lg_t, lg) and torch.equal(ids_t, ids)
+
+
 def test_lmhead_ties_nan_and_planted():
     V, K = 3000, 128
     x = dev_bf16(np.full((2, K), 0x3F80, np.uint16))
