@@ -326,8 +326,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
 // Split-K epilogue: one thread per output (m, n); the S slices' partial sums
 // ([S][M][N] fp32) are added in slice order, then the mode's epilogue: a bf16
 // store, or for gate/up (N = 2I: gate rows 0..I-1, up rows I..2I-1) the RMS
-// scaling and SwiGLU of the gate and up sums of row n.  Loads are issued eight
-// slices at a time.
+// scaling and SwiGLU of the gate and up sums of row n.
 template <int MODE>
 __global__ void __launch_bounds__(256) k_split_reduce(QgAffineArgs p) {
   constexpr int NB = (MODE == QG_MODE_GATEUP) ? 2 : 1;
@@ -338,29 +337,34 @@ __global__ void __launch_bounds__(256) k_split_reduce(QgAffineArgs p) {
   const int n = (int)(idx - (size_t)m * NO);
   const size_t stride = (size_t)p.M * p.N;  // one slice
   const size_t base = (size_t)m * p.N + n;
-  float t[NB];
+  // all loads of up to SC slices (gate, up and the sums of squares together) are
+  // issued before any is added, so a call waits for one round of load latency per
+  // SC slices instead of one per 8 slices and per operand; the additions keep
+  // slice order
+  constexpr int SC = (MODE == QG_MODE_GATEUP) ? 16 : 32;
+  float t[NB], ss = 0.f;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    t[b] = 0.f;
-    for (int s0 = 0; s0 < p.S; s0 += 8) {
-      float v[8];
+  for (int b = 0; b < NB; ++b) t[b] = 0.f;
+  for (int s0 = 0; s0 < p.S; s0 += SC) {
+    float v[NB][SC], q[SC];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = p.part[(size_t)min(s0 + j, p.S - 1) * stride + base + (size_t)b * NO];
+    for (int j = 0; j < SC; ++j) {
+      if (s0 + j < p.S) {  // uniform across the launch
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (s0 + j < p.S) t[b] += v[j];
+        for (int b = 0; b < NB; ++b) v[b][j] = p.part[(size_t)(s0 + j) * stride + base + (size_t)b * NO];
+        if (MODE == QG_MODE_GATEUP) q[j] = p.ssq_part[(size_t)(s0 + j) * 8 + m];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < SC; ++j) {
+      if (s0 + j < p.S) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) t[b] += v[b][j];
+        if (MODE == QG_MODE_GATEUP) ss += q[j];
+      }
     }
   }
   if (MODE == QG_MODE_GATEUP) {
-    float ss = 0.f;
-    for (int s0 = 0; s0 < p.S; s0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = p.ssq_part[(size_t)min(s0 + j, p.S - 1) * 8 + m];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (s0 + j < p.S) ss += v[j];
-    }
     const float ri = 1.0f / sqrtf(ss / (float)p.K + p.eps);
     p.y[idx] = f32_to_bf16_bits(silu_mul(t[0] * ri, t[NB - 1] * ri));
   } else {

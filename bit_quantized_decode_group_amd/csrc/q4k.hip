@@ -248,13 +248,24 @@ __global__ void __launch_bounds__(256) k_q4k(QgQ4kArgs p) {
   }
 }
 
-// Split-K epilogue: one thread per output, slices added in slice order.
+// Split-K epilogue: one thread per output, slices added in slice order; the
+// loads of up to 32 slices are issued before any is added (one round of load
+// latency per 32 slices).
 __global__ void __launch_bounds__(256) k_q4k_reduce(QgQ4kArgs p) {
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t total = (size_t)p.M * p.N;
   if (idx >= total) return;
+  constexpr int SC = 32;
   float t = 0.f;
-  for (int s2 = 0; s2 < p.S; ++s2) t += p.part[(size_t)s2 * total + idx];
+  for (int s0 = 0; s0 < p.S; s0 += SC) {
+    float v[SC];
+#pragma unroll
+    for (int j = 0; j < SC; ++j)
+      if (s0 + j < p.S) v[j] = p.part[(size_t)(s0 + j) * total + idx];  // uniform across the launch
+#pragma unroll
+    for (int j = 0; j < SC; ++j)
+      if (s0 + j < p.S) t += v[j];
+  }
   p.y[idx] = f32_to_bf16_bits(t);
 }
 
