@@ -458,6 +458,7 @@ __global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
   const uint8_t* blk0[1] = {expert_blocks(s0)};
   Q4kBuf<1, kMoeDownBatch> first;
   q4k_load<1>(first, blk0, 0, nsb, lane >> 4);
+  const float pe0 = p.route_w[s0];  // in flight with the weights, used after the MFMAs
   __builtin_amdgcn_sched_barrier(0);
 
   if (threadIdx.x == 0) lds[0] = make_uint4(0u, 0u, 0u, 0u);
@@ -471,7 +472,7 @@ __global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
     if (s != wave) q4k_load<1>(first, blk, 0, nsb, lane >> 4);
     f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
     q4k_tile<1, 1>(acc, blk, nsb, lds, 1u + (uint32_t)(xs_per * s), sx + (size_t)s * nsb * 64, lane, first);
-    const float pe = p.route_w[s];
+    const float pe = (s == wave) ? pe0 : p.route_w[s];
     tot[0] = fmaf(pe, acc[0][0], tot[0]);
     tot[1] = fmaf(pe, acc[0][1], tot[1]);
     tot[2] = fmaf(pe, acc[0][2], tot[2]);
