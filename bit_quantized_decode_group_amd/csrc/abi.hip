@@ -455,10 +455,11 @@ qg_status plan_affine(int mode, QgAffineArgs& a, const char* fn, size_t* lds_out
                                         a.nchunks > cps_max);
   // Pieces to aim for and share of the resident workgroup slots to fill, per
   // mode (measured on the decode shapes): gate/up, whose staging is the
-  // costliest, prefers many short slices on every slot; the weight-streaming
-  // modes run best with half the slots and two or more tiles per wave.
+  // costliest, prefers many short slices on every slot; plain projections run
+  // best on three quarters of the slots, the LM head and the other modes on
+  // half, with two or more tiles per wave.
   const int target = (mode == QG_MODE_GATEUP) ? 4 * kTargetWaves : 2 * kTargetWaves;
-  const int fill_pct = (mode == QG_MODE_GATEUP) ? 100 : 50;
+  const int fill_pct = (mode == QG_MODE_GATEUP) ? 100 : (mode == QG_MODE_PLAIN ? 75 : 50);
   Plan pl = plan_split(a.ntiles, a.nchunks, std::max(cps_max, 1), allow_split, target);
   // slices start on a batch boundary (4 chunks) when that keeps them within LDS
   const int batch = 4;
