@@ -13,12 +13,14 @@
 //
 // Operand mapping (see common.h for the MFMA scheme).  A Q4_K "chunk" is 64
 // consecutive weights = 32 code bytes = sub-blocks 2c (low nibbles) and 2c+1
-// (high nibbles).  Lane l (row l%16, kb = l/16) loads code bytes 8kb..8kb+7
-// of the chunk.  MFMA t (t = 0, 1) of the chunk uses the low nibbles in lanes
-// with (kb/2) ^ t == 0 and the high nibbles in the others, so C rows 0..7 sum
-// sub-block 2c and rows 8..15 sub-block 2c+1, and lane l's C values belong to
-// sub-block 2c + l/32.  Slot s of a lane holds code byte
-// {0,2,1,3,4,6,5,7}[s] of its eight bytes.
+// (high nibbles).  Lane l (row l%16, kb = l/16) loads 16 consecutive code
+// bytes from each half of the block: bytes 64p + 16kb .. +15 (p = 0, 1), i.e.
+// lanes kb = 0, 1 hold chunk 2p and lanes kb = 2, 3 chunk 2p+1 -- one
+// 16-byte load per half instead of four 8-byte ones.  MFMA (p, t, n) takes the
+// nibbles n (0 low, 1 high) of bytes 8t..8t+7 of every lane's 16: C rows 0..7
+// then sum sub-block j = 4p + n (chunk 2p) and rows 8..15 sub-block j + 2
+// (chunk 2p+1), and lane l's C values belong to sub-block 4p + n + 2*(l/32).
+// Slot s of a lane holds code byte {0,2,1,3,4,6,5,7}[s] of its eight bytes.
 #include "common.h"
 
 namespace qg {
@@ -30,11 +32,12 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
 }
 
 // Stage activation rows [M][K-slice of nsb superblocks starting at sb0] into
-// LDS in operand order.  Entry ((cc*2 + t)*4 + kb)*M + m holds the eight
-// activations at k = 64cc + 32pk + 8kb + byte(s), pk = (kb/2) ^ t, for chunk
-// cc of the slice; sx[jl*8 + m] is the fp32 sum of sub-block jl's 32 staged
-// values.  Source rows are bf16 (T = uint16_t) or fp32 rounded to bf16
-// (T = float).
+// LDS in operand order.  Entry ((((sbl*2 + p)*2 + t)*2 + n)*4 + kb)*M + m
+// holds, for superblock sbl of the slice, the eight activations of row m at
+// k = 256*sbl + 64c + 32n + 16(kb%2) + 8t + byte(s) with c = 2p + kb/2 (the
+// operand of MFMA (p, t, n) for lane kb); sx[jl*8 + m] is the fp32 sum of
+// sub-block jl's 32 staged values.  Source rows are bf16 (T = uint16_t) or
+// fp32 rounded to bf16 (T = float).
 template <int M, typename T>
 __device__ __forceinline__ void stage_q4k_x(const T* src, size_t ld, int K, uint4* xs, float* sx, int sb0,
                                             int nsb, int tid, int nthr, int regions = 1) {
@@ -77,20 +80,22 @@ __device__ __forceinline__ void stage_q4k_x(const T* src, size_t ld, int K, uint
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = 0u;
     }
-    const int cc = jl >> 1, pk = jl & 1;
+    // sub-block jl = 8*sbl + 2c + n; its values 8g .. 8g+7 (g = 0..3) go to lane
+    // kb = 2(c%2) + g/2 of MFMA (p = c/2, t = g%2, n)
+    const int sbl = jl >> 3, c = (jl >> 1) & 3, nb = jl & 1, pp = c >> 1;
     constexpr int kByte[8] = {0, 2, 1, 3, 4, 6, 5, 7};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int t = pk ^ (kb >> 1);
+    for (int g = 0; g < 4; ++g) {
+      const int kbn = 2 * (c & 1) + (g >> 1), t = g & 1;
       uint32_t e[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int klo = 8 * kb + kByte[2 * j], khi = 8 * kb + kByte[2 * j + 1];
+        const int klo = 8 * g + kByte[2 * j], khi = 8 * g + kByte[2 * j + 1];
         const uint32_t lo = (klo & 1) ? (v[klo >> 1] >> 16) : (v[klo >> 1] & 0xFFFFu);
         const uint32_t hi = (khi & 1) ? (v[khi >> 1] >> 16) : (v[khi >> 1] & 0xFFFFu);
         e[j] = lo | (hi << 16);
       }
-      rxs[((cc * 2 + t) * 4 + kb) * M + m] = make_uint4(e[0], e[1], e[2], e[3]);
+      rxs[((((sbl * 2 + pp) * 2 + t) * 2 + nb) * 4 + kbn) * M + m] = make_uint4(e[0], e[1], e[2], e[3]);
     }
     rsx[jl * 8 + m] = sum;
   }
@@ -101,11 +106,11 @@ __device__ __forceinline__ void stage_q4k_x(const T* src, size_t ld, int K, uint
 }
 
 // Loads of one batch of SB superblocks for NB tiles: each block's 16-byte
-// header and this lane's eight code bytes of each of its four chunks.
+// header and this lane's 16 code bytes of each half of the block.
 template <int NB, int SB = kSbBatch>
 struct Q4kBuf {
   uint4 hdr[NB][SB];
-  uint2 cq[NB][SB][4];
+  uint4 cq[NB][SB][2];
 };
 
 // Issues the loads of the batch starting at superblock sb (clamped to the
@@ -119,7 +124,7 @@ __device__ __forceinline__ void q4k_load(Q4kBuf<NB, SB>& bf, const uint8_t* cons
       const uint8_t* bp = blk[b] + (size_t)min(sb + u, nsb - 1) * 144;
       bf.hdr[b][u] = *reinterpret_cast<const uint4*>(bp);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bf.cq[b][u][c] = *reinterpret_cast<const uint2*>(bp + 16 + 32 * c + 8 * kb);
+      for (int hh = 0; hh < 2; ++hh) bf.cq[b][u][hh] = *reinterpret_cast<const uint4*>(bp + 16 + 64 * hh + 16 * kb);
     }
   }
 }
@@ -138,11 +143,10 @@ __device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* cons
   const int kb = lane >> 4;
   const int half = lane >> 5;
   const int rho = lane & 15;
-  const uint32_t mask0 = (((rho >> 3) == ((kb >> 1) ^ 0)) && ((rho & 7) < M)) ? 0xFFFFFFFFu : 0u;
-  const uint32_t mask1 = (((rho >> 3) == ((kb >> 1) ^ 1)) && ((rho & 7) < M)) ? 0xFFFFFFFFu : 0u;
-  const uint32_t sh0 = 4u * (uint32_t)((kb >> 1) ^ 0), sh1 = 4u * (uint32_t)((kb >> 1) ^ 1);
+  // A rows 0..7 take k-slots of lanes kb = 0, 1 and rows 8..15 those of kb = 2, 3
+  const uint32_t amask = (((rho >> 3) == (kb >> 1)) && ((rho & 7) < M)) ? 0xFFFFFFFFu : 0u;
   const uint32_t a_lane = region + (uint32_t)(kb * M + (rho & 7));
-  const float* sx_base = sx + half * 8 + 4 * (kb & 1);
+  const float* sx_base = sx + half * 16 + 4 * (kb & 1);  // + 8*(8*sbl + 4p + n): sub-block 4p + n + 2*half
   const UnpackK uk = unpack_constants();
 
   auto compute = [&](const Q4kBuf<NB, SB>& cur, int sb) {
@@ -155,22 +159,25 @@ __device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* cons
         const uint4 h = cur.hdr[b][u];
         const float d = f16_bits_to_f32(h.x & 0xFFFFu);
         const float dmin = f16_bits_to_f32(h.x >> 16);
-        const uint32_t Y = h.y >> (8 * half), Z = h.z >> (8 * half), Wd = h.w >> (8 * half);
-        // six-bit scale / min of sub-block j = 2c + half (public Q4_K packing)
-        const uint32_t sc[4] = {Y & 63u, (Y >> 16) & 63u, (Wd & 15u) | ((Y >> 2) & 0x30u),
-                                ((Wd >> 16) & 15u) | ((Y >> 18) & 0x30u)};
-        const uint32_t mn[4] = {Z & 63u, (Z >> 16) & 63u, ((Wd >> 4) & 15u) | ((Z >> 2) & 0x30u),
-                                ((Wd >> 20) & 15u) | ((Z >> 18) & 0x30u)};
+        const uint32_t Y = h.y >> (16 * half), Z = h.z >> (16 * half), Wd = h.w >> (16 * half);
+        // six-bit scale / min of sub-block j = 4p + n + 2*half, q = 2p + n (public
+        // Q4_K packing: j < 4 in the low six bits of bytes j, j+4; j >= 4 from
+        // byte j+4's nibbles and the top two bits of bytes j-4, j)
+        const uint32_t sc[4] = {Y & 63u, (Y >> 8) & 63u, (Wd & 15u) | ((Y >> 2) & 0x30u),
+                                ((Wd >> 8) & 15u) | ((Y >> 10) & 0x30u)};
+        const uint32_t mn[4] = {Z & 63u, (Z >> 8) & 63u, ((Wd >> 4) & 15u) | ((Z >> 2) & 0x30u),
+                                ((Wd >> 12) & 15u) | ((Z >> 10) & 0x30u)};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int cc = sbl * 4 + c;
-          const uint32_t ai = a_lane + (uint32_t)(cc * 8 * M);
-          const uint4 a0 = lds[ai & mask0];
-          const uint4 a1 = lds[(ai + 4 * M) & mask1];
+        for (int c = 0; c < 4; ++c) {  // c = 2p + n
+          const int pp = c >> 1, nb = c & 1;
+          const uint32_t ai = a_lane + (uint32_t)((((sbl * 2 + pp) * 2) * 2 + nb) * 4 * M);
+          const uint4 a0 = lds[ai & amask];                  // t = 0
+          const uint4 a1 = lds[(ai + 8 * M) & amask];        // t = 1: eight entries on (two n x four kb)
+          const uint4 q = cur.cq[b][u][pp];
           f32x4_t C = {0.f, 0.f, 0.f, 0.f};
-          C = mfma_bf16(a0, unpack_q4k_bytes(cur.cq[b][u][c].x, cur.cq[b][u][c].y, sh0, uk), C);
-          C = mfma_bf16(a1, unpack_q4k_bytes(cur.cq[b][u][c].x, cur.cq[b][u][c].y, sh1, uk), C);
-          const float4 sxv = *reinterpret_cast<const float4*>(sx_base + cc * 16);
+          C = mfma_bf16(a0, unpack_q4k_bytes(q.x, q.y, 4u * (uint32_t)nb, uk), C);
+          C = mfma_bf16(a1, unpack_q4k_bytes(q.z, q.w, 4u * (uint32_t)nb, uk), C);
+          const float4 sxv = *reinterpret_cast<const float4*>(sx_base + (8 * sbl + 4 * pp + nb) * 8);
           const float a = d * (float)sc[c];                 // exact in fp32
           const float bt = fmaf(dmin, (float)mn[c], 128.0f * a);
           acc[b][0] = fmaf(a, C[0], fmaf(-bt, sxv.x, acc[b][0]));
