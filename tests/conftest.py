@@ -27,3 +27,21 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """The literal figure max|err| / rms(y_oracle) of every full-size workload
+    compared in this run (and, for bf16 outputs, the figure the tests bound:
+    max(|err| - 2^-8 |y|) / rms), so it can be read beside the 2e-2 bar."""
+    try:
+        from tests.gpu_util import LITERAL
+    except Exception:
+        return
+    rows = sorted((w, v) for w, v in LITERAL.items() if w.startswith("config"))
+    if not rows:
+        return
+    tr = terminalreporter
+    tr.write_sep("-", "max|err|/rms per full-size workload (bar 2e-2)")
+    for w, (lit, r15) in rows:
+        extra = "" if r15 is None else f"   max(|err|-2^-8|y|)/rms {r15:.3e}"
+        tr.write_line(f"{w:48s} max|err|/rms {lit:.3e}{extra}")

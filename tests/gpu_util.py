@@ -11,8 +11,17 @@ Pass bar (the same for every floating-point output):
     rounding of the output plus fp32 accumulation.  slack is 1e-3 for a
     projection; the MLP block's bf16 intermediate h (part of its definition
     here) gets 8e-3, the MoE's bf16 expert activations likewise.
-Argmax ids: equal to the oracle's wherever the oracle's top-2 gap is > 1e-2;
-elsewhere the chosen id's oracle logit is within 1e-2 of the maximum.
+fp32 outputs (the LM-head logits) have no bf16 rounding, so they get the
+literal bar with no 2^-8 allowance: max|err| <= 2e-2 * rms, and as the tighter
+check |err| <= slack * rms (slack 1e-4: fp32 accumulation only).
+Argmax ids: equal to the oracle's wherever the oracle's top-2 gap is > 1e-2,
+where its top logits are exactly tied (duplicated rows: the lowest index
+wins) and in rows holding a NaN logit (the first NaN wins); elsewhere the
+chosen id's oracle logit is within 1e-2 of the maximum.
+
+Every comparison records the literal figure max|err| / rms(y_oracle) in
+LITERAL (printed at the end of a pytest run), so the outputs that also meet
+the stated bar without the rounding allowance can be read off.
 """
 import math
 
@@ -52,6 +61,10 @@ def host_bf16_f64(t):
     return bits_to_f64(host_bits(t))
 
 
+# what -> (max|err|/rms, max(|err| - 2^-8|y|)/rms or None for fp32 outputs)
+LITERAL = {}
+
+
 def assert_close(y_gpu_f64, ref, slack=1e-3, what=""):
     y = np.asarray(y_gpu_f64, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -62,6 +75,8 @@ def assert_close(y_gpu_f64, ref, slack=1e-3, what=""):
     err = np.abs(y - ref)
     mx = float(err.max())
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    if rms > 0:
+        LITERAL[what] = (mx / rms, float((err - (2.0 ** -8) * np.abs(ref)).max()) / rms)
     over = err - (2.0 ** -8) * np.abs(ref)
     assert float(over.max()) <= 2e-2 * rms, (f"{what}: max(|err| - 2^-8|y|) {float(over.max()):.4g} > 2e-2*rms "
                                             f"({rms:.4g}); max|err| {mx:.4g}")
@@ -71,11 +86,41 @@ def assert_close(y_gpu_f64, ref, slack=1e-3, what=""):
     return mx / rms if rms > 0 else 0.0
 
 
+def assert_close_f32(y_gpu, ref, slack=1e-4, what=""):
+    """fp32 outputs: the literal bar max|err| <= 2e-2*rms and |err| <= slack*rms, no rounding allowance."""
+    y = np.asarray(y_gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert y.shape == ref.shape, (what, y.shape, ref.shape)
+    if ref.size == 0:
+        return 0.0
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    err = np.abs(y - ref)
+    mx = float(err.max())
+    if rms > 0:
+        LITERAL[what] = (mx / rms, None)
+    assert mx <= 2e-2 * rms, f"{what}: max|err| {mx:.4g} > 2e-2*rms ({rms:.4g})"
+    assert mx <= slack * rms, (f"{what}: max|err| {mx:.4g} > {slack}*rms; worst at "
+                               f"{np.unravel_index(int(np.argmax(err)), ref.shape)}")
+    return mx / rms if rms > 0 else 0.0
+
+
 def assert_ids(ids_gpu, ids_ref, gap_ref, logits_ref, what=""):
     ids_gpu = np.asarray(ids_gpu).reshape(-1)
     for m in range(len(ids_ref)):
-        if gap_ref[m] > 1e-2:
+        exact = (gap_ref[m] > 1e-2 or gap_ref[m] == 0.0 or bool(np.isnan(gap_ref[m]))
+                 or bool(np.isnan(logits_ref[m]).any()))
+        if exact:
             assert ids_gpu[m] == ids_ref[m], f"{what}: row {m} id {ids_gpu[m]} != {ids_ref[m]} (gap {gap_ref[m]:.3g})"
         else:
             mx = logits_ref[m].max()
             assert logits_ref[m, ids_gpu[m]] >= mx - 1e-2, f"{what}: row {m} id {ids_gpu[m]} not within 1e-2 of max"
+
+
+def rows_identical(y_batch, y_rows):
+    """Batch invariance (TensorFold page, section "핵심 메커니즘 2 — 정확 디코딩": a
+    row's result does not depend on what else is in the batch): row i of an
+    M-row call equals, bit for bit, the 1-row call on row i alone.  Arrays of
+    raw output bits; returns the rows that differ."""
+    yb = np.asarray(y_batch)
+    return [i for i, yr in enumerate(y_rows) if not np.array_equal(yb[i], np.asarray(yr).reshape(yb[i].shape))]

@@ -12,7 +12,7 @@ import torch
 import oracle
 from bit_quantized_decode_group_amd import ops, synth
 from tests import packers
-from tests.gpu_util import (assert_close, assert_ids, bits_to_f64, dev_bf16, dev_f32, dev_i32, dev_u8, dev_u32,
+from tests.gpu_util import (assert_close, assert_close_f32, assert_ids, bits_to_f64, dev_bf16, dev_f32, dev_i32, dev_u8, dev_u32,
                             host_bf16_f64, host_bits)
 from tests.test_oracle_pins import HAND_BIASES, HAND_CODES, HAND_SCALES, HAND_VALUES, Q4K_HAND, Q4K_HAND_VALUES
 
@@ -193,7 +193,7 @@ def test_lmhead_small(M, V, K):
     logits, ids, gap, _ = oracle.lmhead(d["x"], d["codes"], d["scales"], d["biases"])
     gi, acc, gl = ops.lmhead_argmax(dev_bf16(d["x"]), *_affine_dev(d), want_logits=True)
     gl = gl.cpu().numpy().astype(np.float64)
-    assert_close(gl, logits, slack=1e-4, what=f"logits M{M} V{V} K{K}")
+    assert_close_f32(gl, logits, what=f"logits M{M} V{V} K{K}")
     assert_ids(gi.cpu().numpy(), ids, gap, logits, what=f"lmhead M{M} V{V} K{K}")
     assert int(acc.cpu()[0]) == 0  # no draft given
 
@@ -212,7 +212,7 @@ def test_lmhead_longest_k(M, K):
     d = synth.lm_head(M=M, V=300, K=K, seed=6100 + M + K)
     logits, ids, gap, _ = oracle.lmhead(d["x"], d["codes"], d["scales"], d["biases"])
     gi, acc, gl = ops.lmhead_argmax(dev_bf16(d["x"]), *_affine_dev(d), want_logits=True)
-    assert_close(gl.cpu().numpy().astype(np.float64), logits, slack=1e-4, what=f"longest K logits M{M} K{K}")
+    assert_close_f32(gl.cpu().numpy(), logits, what=f"longest K logits M{M} K{K}")
     assert_ids(gi.cpu().numpy(), ids, gap, logits, what=f"longest K ids M{M} K{K}")
 
 
@@ -292,7 +292,7 @@ def test_config_single_projection_m1_and_m8():
         d = synth.single_projection(M=M)
         ref = oracle.qgemv_affine4(d["x"], d["codes"], d["scales"], d["biases"])
         y = ops.qgemv_affine4(dev_bf16(d["x"]), *_affine_dev(d))
-        assert_close(host_bf16_f64(y), ref, what=f"single projection M{M}")
+        assert_close(host_bf16_f64(y), ref, what=f"config c1 single projection 3072x1024 y M{M}")
 
 
 def _block(d):
@@ -310,8 +310,8 @@ def test_config_mlp_block_06b(M):
     h_ref = oracle.rmsnorm_gateup_swiglu(d["x"], d["gamma"], d["eps"], d["codes_gu"], d["scales_gu"], d["biases_gu"])
     y_ref = oracle.mlp_block(d["x"], d["gamma"], d["eps"], d["codes_gu"], d["scales_gu"], d["biases_gu"],
                              d["codes_d"], d["scales_d"], d["biases_d"])
-    assert_close(host_bf16_f64(h), h_ref, slack=5e-3, what="0.6B h")
-    assert_close(host_bf16_f64(y), y_ref, slack=8e-3, what="0.6B block")
+    assert_close(host_bf16_f64(h), h_ref, slack=5e-3, what=f"config c2 0.6B block h M{M}")
+    assert_close(host_bf16_f64(y), y_ref, slack=8e-3, what=f"config c2 0.6B block y M{M}")
 
 
 @pytest.mark.parametrize("M", [8, 1])
@@ -324,9 +324,9 @@ def test_config_verify_block_4b(M):
     # the down projection checked on the GPU's own h (a bf16 input), and the block end to end
     y_ref_h = oracle.qgemv_affine4(host_bits(h), d["codes_d"], d["scales_d"], d["biases_d"])
     y_ref = oracle.qgemv_affine4_f64x(h_ref, d["codes_d"], d["scales_d"], d["biases_d"])
-    assert_close(host_bf16_f64(h), h_ref, slack=5e-3, what="4B h")
-    assert_close(host_bf16_f64(y), y_ref_h, what="4B down on gpu h")
-    assert_close(host_bf16_f64(y), y_ref, slack=8e-3, what="4B block")
+    assert_close(host_bf16_f64(h), h_ref, slack=5e-3, what=f"config c3 4B verify block h M{M}")
+    assert_close(host_bf16_f64(y), y_ref_h, what=f"config c3 4B down on gpu h y M{M}")
+    assert_close(host_bf16_f64(y), y_ref, slack=8e-3, what=f"config c3 4B verify block y M{M}")
 
 
 def test_config_moe_q4k():
@@ -338,7 +338,7 @@ def test_config_moe_q4k():
         y, ids, w = ops.moe_expert_qgemv(x, dev_f32(d["logits"][s]), k, wgu, wdn)
         assert list(ids.cpu().numpy()) == list(ids_ref)
         assert np.allclose(w.cpu().numpy(), p_ref, rtol=1e-5, atol=1e-7)
-        assert_close(host_bf16_f64(y)[0], y_ref, slack=8e-3, what=f"moe config set {s}")
+        assert_close(host_bf16_f64(y)[0], y_ref, slack=8e-3, what=f"config c4 moe q4k y set {s}")
 
 
 @pytest.mark.parametrize("M", [1, 4, 8])
@@ -348,7 +348,7 @@ def test_config_lm_head(M):
     logits, ids_ref, gap, _ = oracle.lmhead(xm, d["codes"], d["scales"], d["biases"])
     x, args = dev_bf16(xm), _affine_dev(d)
     gi, acc, gl = ops.lmhead_argmax(x, *args, want_logits=True)
-    assert_close(gl.cpu().numpy().astype(np.float64), logits, slack=1e-4, what=f"lm head logits M{M}")
+    assert_close_f32(gl.cpu().numpy(), logits, what=f"config c5 lm head logits M{M}")
     assert_ids(gi.cpu().numpy(), ids_ref, gap, logits, what=f"lm head M{M}")
     # ids-only path (no logits stored) gives the same ids; planted draft prefix
     k = M // 2

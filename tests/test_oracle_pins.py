@@ -440,6 +440,50 @@ def test_moe_all_experts_and_tie_order():
     assert sorted(ids8) == list(range(8)) and math.isclose(p8.sum(), 1.0, rel_tol=1e-14)
 
 
+def _dense_swiglu_expert(x64, w_gu_e, w_down_e, I):
+    """One expert's MLP written out with numpy on the oracle's dequantised
+    weights (pinned by the hand-packed Q4_K tests): down . (silu(gate.x) * up.x)."""
+    wgu = oracle.dequant_q4k(w_gu_e)
+    wd = oracle.dequant_q4k(w_down_e)
+    g = wgu[:I] @ x64
+    u = wgu[I:] @ x64
+    return wd @ (g / (1.0 + np.exp(-g)) * u)
+
+
+@pytest.mark.parametrize("top_k", [2, 8])
+def test_moe_weighted_sum_of_dense_experts(top_k):
+    """y = sum over the selected experts of p_e times that expert's dense SwiGLU
+    MLP, with p = softmax over the selected logits only (uzu page, section
+    "내부 동작 1", mlp row: MixtureOfExperts with a routing function; the
+    softmax-weighted top-k sum).  Selection, weights and the per-expert MLPs
+    are recomputed here with numpy; an unweighted sum and a full-softmax
+    weighting are controls that must fail the same comparison."""
+    d = _moe_small(E=16, D=256, I=256, seed=36 + top_k)
+    E, D, I = 16, d["D"], d["I"]
+    logits = d["logits"][0]
+    y, ids, p = oracle.moe(d["x"], logits, top_k, d["w_gu"], d["w_down"], E, D, I)
+    lg = logits.astype(np.float64)
+    order = sorted(range(E), key=lambda e: (-lg[e], e))[:top_k]
+    pe = np.exp(lg[order] - lg[order].max())
+    pe /= pe.sum()
+    x64 = oracle.bf16_array_to_f64(d["x"]).reshape(-1)
+    ye = np.stack([_dense_swiglu_expert(x64, d["w_gu"][e], d["w_down"][e], I) for e in order])
+    want = (pe[:, None] * ye).sum(axis=0)
+    tol = 1e-12 * np.abs(want).max()
+
+    def agrees(v):
+        return float(np.abs(np.asarray(v) - want).max()) <= tol
+
+    assert list(ids) == order
+    assert agrees(y), float(np.abs(y - want).max())
+    # controls: plausible slips in the weighted sum must not pass this comparison
+    assert not agrees(ye.sum(axis=0)), "unweighted sum passed"
+    full = np.exp(lg - lg.max())
+    full /= full.sum()
+    assert not agrees((full[order][:, None] * ye).sum(axis=0)), "full-softmax weights passed"
+    assert not agrees((pe[::-1][:, None] * ye).sum(axis=0)), "weights in reverse order passed"
+
+
 def test_moe_rejects_bad_args():
     d = _moe_small(E=8, seed=34)
     with pytest.raises(ValueError):
