@@ -224,6 +224,15 @@ def main():
             "mw": torch.empty(top_k, dtype=torch.float32, device=dev),
             "ids": torch.empty(M, dtype=torch.int32, device=dev),
             "acc": torch.empty(1, dtype=torch.int32, device=dev),
+            # one caller-owned workspace serves every call of the step (the calls are ordered on the stream)
+            "ws": ops.workspace(max(ops.workspace_bytes("rmsnorm_gateup_swiglu_tiled", M, I, D),
+                                    ops.workspace_bytes("rmsnorm_gateup_swiglu", M, I, D),
+                                    ops.workspace_bytes("qgemv_affine4_tiled", M, D, I),
+                                    ops.workspace_bytes("qgemv_affine4", M, D, I),
+                                    ops.workspace_bytes("mlp_block_affine4_tiled", M, D, I),
+                                    ops.workspace_bytes("moe_expert_qgemv", top_k, E, Dm, Im),
+                                    ops.workspace_bytes("lmhead_argmax_tiled", M, V, K5),
+                                    ops.workspace_bytes("lmhead_argmax", M, V, K5), 256), dev),
         }
 
     # Algorithmic bytes per step: every weight byte once (0.5625 B/weight), the
@@ -261,33 +270,35 @@ def main():
         if e is not None:
             next(e).record()
         if persistent:
-            ops.mlp_block_affine4_tiled(b["x"], gamma, vb["eps"], c["t_gu"], c["t_d"], D, I, h=b["h"], y=b["y"])
+            ops.mlp_block_affine4_tiled(b["x"], gamma, vb["eps"], c["t_gu"], c["t_d"], D, I, h=b["h"], y=b["y"],
+                                        ws=b["ws"])
         elif tiled:
-            ops.rmsnorm_gateup_swiglu_tiled(b["x"], gamma, vb["eps"], *c["t_gu"], I, h=b["h"])
+            ops.rmsnorm_gateup_swiglu_tiled(b["x"], gamma, vb["eps"], *c["t_gu"], I, h=b["h"], ws=b["ws"])
         else:
             ops.rmsnorm_gateup_swiglu(b["x"], gamma, vb["eps"], c["codes_gu"], c["scales_gu"], c["biases_gu"],
-                                      h=b["h"])
+                                      h=b["h"], ws=b["ws"])
         if e is not None:
             next(e).record()
         if persistent:
             pass
         elif tiled:
-            ops.qgemv_affine4_tiled(b["h"], *c["t_d"], D, y=b["y"])
+            ops.qgemv_affine4_tiled(b["h"], *c["t_d"], D, y=b["y"], ws=b["ws"])
             if e is not None:
                 next(e).record()
         else:
-            ops.qgemv_affine4(b["h"], c["codes_d"], c["scales_d"], c["biases_d"], y=b["y"])
+            ops.qgemv_affine4(b["h"], c["codes_d"], c["scales_d"], c["biases_d"], y=b["y"], ws=b["ws"])
             if e is not None:
                 next(e).record()
-        ops.moe_expert_qgemv(xm, lg, top_k, ms["w_gu"], ms["w_down"], y=b["ym"], out_ids=b["mids"], out_w=b["mw"])
+        ops.moe_expert_qgemv(xm, lg, top_k, ms["w_gu"], ms["w_down"], y=b["ym"], out_ids=b["mids"], out_w=b["mw"],
+                             ws=b["ws"])
         if e is not None:
             next(e).record()
         dr = draft[:M].contiguous() if M < 8 else draft
         if tiled:
-            ops.lmhead_argmax_tiled(b["xl"], *c["t_lm"], V, draft=dr, ids=b["ids"], accepted=b["acc"])
+            ops.lmhead_argmax_tiled(b["xl"], *c["t_lm"], V, draft=dr, ids=b["ids"], accepted=b["acc"], ws=b["ws"])
         else:
             ops.lmhead_argmax(b["xl"], c["codes_lm"], c["scales_lm"], c["biases_lm"], draft=dr, ids=b["ids"],
-                              accepted=b["acc"])
+                              accepted=b["acc"], ws=b["ws"])
         if e is not None:
             next(e).record()
 
@@ -307,7 +318,6 @@ def main():
         # that exactly `steps` steps are timed
         glen = max(d for d in range(1, GRAPH_STEPS + 1) if steps % d == 0) if use_graph else 1
         if use_graph:
-            # the library's per-stream workspace is in place after the warm-up on s;
             # the graph holds glen consecutive steps and every replay repeats them
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=s):

@@ -1,6 +1,8 @@
 // abi.hip -- the C ABI of libqgemv.so (declared in include/qgemv.h):
-// argument checks, the per-(device, stream) workspace, the work decomposition
-// (split-K, tiles per wave) and dispatch to the kernel launchers.
+// argument checks (shared by every entry point and its host-only qg_check_
+// twin), the caller-owned workspace (size queries and checks), the work
+// decomposition (split-K, tiles per wave) and dispatch to the kernel
+// launchers.  Nothing here allocates, frees or synchronises on the call path.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -63,6 +65,17 @@ qg_status check_alias(const Buf* outs, int nout, const Buf* ins, int nin, const 
   return QG_OK;
 }
 
+// Every input and output buffer of a call, for the workspace overlap check.
+struct BufList {
+  Buf b[16];
+  int n = 0;
+};
+void collect(BufList* all, const Buf* outs, int nout, const Buf* ins, int nin) {
+  if (!all) return;
+  for (int i = 0; i < nout && all->n < 16; ++i) all->b[all->n++] = outs[i];
+  for (int i = 0; i < nin && all->n < 16; ++i) all->b[all->n++] = ins[i];
+}
+
 constexpr size_t kLdsBudget = 163840;      // bytes of LDS one workgroup may use (all of a gfx950 CU's)
 constexpr size_t kQ4kLdsBudget = 65536;    // staged-slice bound of the Q4_K projection (keeps 2+ workgroups per CU)
 constexpr int kWaves = 4;                  // waves per workgroup of the projection kernels
@@ -108,39 +121,38 @@ Plan plan_split(int ntiles, int nchunks, int cps_max, bool allow_split, int targ
 }
 
 // ---------------------------------------------------------- workspace --
-struct Workspace {
-  void* ptr = nullptr;
-  size_t bytes = 0;
-};
-std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Scratch memory comes from the caller (ws, ws_bytes): the library never
+// allocates, frees or synchronises.  Layout of a workspace:
+//   [0, kWsHeader)  state words (barrier counters, failure flags) that must be
+//                   zero before the first call; every call that uses them
+//                   leaves them zero again (so one workspace can serve every
+//                   entry point and every shape, one call at a time);
+//   [kWsHeader, ...) per-call scratch (split-K partial sums, argmax keys,
+//                   top-k candidates, RHT planes, MoE routing and expert
+//                   activations); written before it is read within a call.
+// A call that needs neither returns 0 from its size query and accepts ws = NULL.
+constexpr size_t kWsHeader = 16384;
+constexpr size_t kWsAlign = 256;
+constexpr int kMaxCus = 256;  // workspace sizes are computed for this many compute units (gfx950)
 
-// Returns the workspace of the current device and this stream, grown to at
-// least `need` bytes.  Its contents carry nothing between calls (every kernel
-// writes what it later reads), so it needs no initialisation.
-qg_status get_workspace(hipStream_t stream, size_t need, unsigned char** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return fail(QG_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  Workspace& w = g_ws[{dev, stream}];
-  const size_t total = std::max(need, (size_t)256);
-  if (w.bytes < total) {
-    if (w.ptr) {
-      e = hipStreamSynchronize(stream);
-      if (e != hipSuccess) return fail(QG_EHIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
-      (void)hipFree(w.ptr);
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
-    size_t nb = std::max(total, (size_t)4 << 20);
-    void* p = nullptr;
-    e = hipMalloc(&p, nb);
-    if (e != hipSuccess) return fail(QG_ENOMEM, "workspace hipMalloc(%zu): %s", nb, hipGetErrorString(e));
-    w.ptr = p;
-    w.bytes = nb;
-  }
-  *out = static_cast<unsigned char*>(w.ptr);
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Total workspace bytes for `scratch` bytes of per-call scratch (0 if none is needed).
+size_t ws_total(size_t scratch, bool state = false) {
+  if (scratch == 0 && !state) return 0;
+  return kWsHeader + align_up(scratch, kWsAlign);
+}
+
+// Checks the caller's workspace against the `need` bytes the plan requires:
+// present, 256-byte aligned, large enough, and overlapping no input or output.
+qg_status check_ws(const char* fn, const void* ws, size_t ws_bytes, size_t need, const Buf* others, int nothers) {
+  if (need == 0) return QG_OK;
+  if (!ws) return fail(QG_EINVAL, "%s: needs a workspace of %zu bytes (ws is null)", fn, need);
+  if (!aligned(ws, kWsAlign)) return fail(QG_EINVAL, "%s: ws must be %zu-byte aligned", fn, kWsAlign);
+  if (ws_bytes < need) return fail(QG_EINVAL, "%s: ws_bytes=%zu, needs %zu", fn, ws_bytes, need);
+  const Buf w = {ws, ws_bytes, "ws"};
+  for (int i = 0; i < nothers; ++i)
+    if (overlaps(w, others[i])) return fail(QG_EALIAS, "%s: ws overlaps %s", fn, others[i].name);
   return QG_OK;
 }
 
@@ -166,20 +178,21 @@ qg_status check_device() {
   return QG_OK;
 }
 
+// Compute units of the current device (set by check_device), at most kMaxCus.
 int device_cus() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || g_cus[dev] <= 0) return 256;
-  return g_cus[dev];
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || g_cus[dev] <= 0) return kMaxCus;
+  return std::min(g_cus[dev], kMaxCus);
 }
 
 // Workgroups per K slice for the persistent affine kernel: `fill_pct` percent
 // of the device's resident workgroup slots (4 waves per workgroup, at most
 // max_occ workgroups per CU, fewer if the staged slice limits LDS occupancy),
 // and no more workgroups than it takes to give every wave a tile.
-int affine_rgroups(int ntiles, int S, size_t lds, int max_occ, int fill_pct) {
+int affine_rgroups(int ntiles, int S, size_t lds, int max_occ, int fill_pct, int cus) {
   const size_t lds_cu = 160 * 1024;
   const int occ = (int)std::max<size_t>(1, std::min<size_t>((size_t)max_occ, lds_cu / std::max<size_t>(lds, 1)));
-  const long long slots = (long long)device_cus() * occ * fill_pct / 100;
+  const long long slots = (long long)cus * occ * fill_pct / 100;
   const long long per_slice = std::max<long long>(1, slots / S);
   const long long max_r = std::max<long long>(1, (ntiles + kWaves - 1) / kWaves);
   return (int)std::min(per_slice, max_r);
@@ -201,7 +214,7 @@ qg_status check_affine_common(const char* fn, int M, int N, int K) {
 }
 
 qg_status do_check_qgemv_affine4(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
-                                 const uint16_t* biases, uint16_t* y, int M, int N, int K) {
+                                 const uint16_t* biases, uint16_t* y, int M, int N, int K, BufList* all = nullptr) {
   const char* fn = "qgemv_affine4";
   qg_status st = check_affine_common(fn, M, N, K);
   if (st) return st;
@@ -214,11 +227,12 @@ qg_status do_check_qgemv_affine4(const uint16_t* x, const uint32_t* codes, const
   if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(in[2], 2, fn)) ||
       (st = check_ptr(in[3], 2, fn)) || (st = check_ptr(out[0], 2, fn)))
     return st;
+  collect(all, out, 1, in, 4);
   return check_alias(out, 1, in, 4, fn);
 }
 
 qg_status do_check_qgemv_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
-                                 const uint16_t* biases, uint16_t* y, int M, int N, int K) {
+                                 const uint16_t* biases, uint16_t* y, int M, int N, int K, BufList* all = nullptr) {
   const char* fn = "qgemv_affine8";
   qg_status st = check_affine_common(fn, M, N, K);
   if (st) return st;
@@ -231,10 +245,11 @@ qg_status do_check_qgemv_affine8(const uint16_t* x, const uint32_t* codes, const
   if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(in[2], 2, fn)) ||
       (st = check_ptr(in[3], 2, fn)) || (st = check_ptr(out[0], 2, fn)))
     return st;
+  collect(all, out, 1, in, 4);
   return check_alias(out, 1, in, 4, fn);
 }
 
-qg_status do_check_qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K) {
+qg_status do_check_qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K, BufList* all = nullptr) {
   const char* fn = "qgemv_q4k";
   if (M < 1 || M > 8) return fail(QG_EINVAL, "%s: M=%d must be in 1..8", fn, M);
   if (N < 0) return fail(QG_EINVAL, "%s: N=%d must be >= 0", fn, N);
@@ -246,10 +261,11 @@ qg_status do_check_qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t*
   qg_status st;
   if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(out[0], 2, fn)))
     return st;
+  collect(all, out, 1, in, 2);
   return check_alias(out, 1, in, 2, fn);
 }
 
-qg_status do_check_qgemv_q6k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K) {
+qg_status do_check_qgemv_q6k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K, BufList* all = nullptr) {
   const char* fn = "qgemv_q6k";
   if (M < 1 || M > 8) return fail(QG_EINVAL, "%s: M=%d must be in 1..8", fn, M);
   if (N < 0) return fail(QG_EINVAL, "%s: N=%d must be >= 0", fn, N);
@@ -261,11 +277,12 @@ qg_status do_check_qgemv_q6k(const uint16_t* x, const uint8_t* blocks, uint16_t*
   qg_status st;
   if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 2, fn)) || (st = check_ptr(out[0], 2, fn)))
     return st;
+  collect(all, out, 1, in, 2);
   return check_alias(out, 1, in, 2, fn);
 }
 
 qg_status do_check_gateup(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes,
-                          const uint16_t* scales, const uint16_t* biases, uint16_t* h, int M, int I, int K) {
+                          const uint16_t* scales, const uint16_t* biases, uint16_t* h, int M, int I, int K, BufList* all = nullptr) {
   const char* fn = "rmsnorm_gateup_swiglu";
   qg_status st = check_affine_common(fn, M, I, K);
   if (st) return st;
@@ -281,11 +298,12 @@ qg_status do_check_gateup(const uint16_t* x, const uint16_t* gamma, float eps, c
   if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(in[2], 16, fn)) ||
       (st = check_ptr(in[3], 2, fn)) || (st = check_ptr(in[4], 2, fn)) || (st = check_ptr(out[0], 2, fn)))
     return st;
+  collect(all, out, 1, in, 5);
   return check_alias(out, 1, in, 5, fn);
 }
 
 qg_status do_check_moe(const uint16_t* x, const float* logits, int top_k, const uint8_t* w_gu,
-                       const uint8_t* w_down, uint16_t* y, int32_t* out_ids, float* out_w, int E, int D, int I) {
+                       const uint8_t* w_down, uint16_t* y, int32_t* out_ids, float* out_w, int E, int D, int I, BufList* all = nullptr) {
   const char* fn = "moe_expert_qgemv";
   if (E < 1 || E > 1024) return fail(QG_EINVAL, "%s: E=%d must be in 1..1024", fn, E);
   if (top_k < 1 || top_k > E) return fail(QG_EINVAL, "%s: top_k=%d must be in 1..E", fn, top_k);
@@ -310,12 +328,13 @@ qg_status do_check_moe(const uint16_t* x, const float* logits, int top_k, const 
     return st;
   if (out_ids && (st = check_ptr(out[1], 4, fn))) return st;
   if (out_w && (st = check_ptr(out[2], 4, fn))) return st;
+  collect(all, out, 3, in, 4);
   return check_alias(out, 3, in, 4, fn);
 }
 
 qg_status do_check_lmhead(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
                           float* logits, int32_t* ids, const int32_t* draft, int32_t* accepted, int M, int V,
-                          int K) {
+                          int K, BufList* all = nullptr) {
   const char* fn = "lmhead_argmax";
   qg_status st = check_affine_common(fn, M, V, K);
   if (st) return st;
@@ -337,12 +356,13 @@ qg_status do_check_lmhead(const uint16_t* x, const uint32_t* codes, const uint16
   if (draft && (st = check_ptr(in[4], 4, fn))) return st;
   if (logits && (st = check_ptr(out[0], 4, fn))) return st;
   if (accepted && (st = check_ptr(out[2], 4, fn))) return st;
+  collect(all, out, 3, in, 5);
   return check_alias(out, 3, in, 5, fn);
 }
 
 qg_status do_check_lmhead_topk(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                                const uint16_t* biases, float* logits, int32_t* ids, float* vals, int M, int V, int K,
-                               int k) {
+                               int k, BufList* all = nullptr) {
   const char* fn = "lmhead_topk";
   qg_status st = check_affine_common(fn, M, V, K);
   if (st) return st;
@@ -367,12 +387,13 @@ qg_status do_check_lmhead_topk(const uint16_t* x, const uint32_t* codes, const u
     return st;
   if (logits && (st = check_ptr(out[0], 4, fn))) return st;
   if (vals && (st = check_ptr(out[2], 4, fn))) return st;
+  collect(all, out, 3, in, 4);
   return check_alias(out, 3, in, 4, fn);
 }
 
 qg_status do_check_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had, const uint32_t* codes,
                                      const uint16_t* scales, const uint16_t* biases, uint16_t* y, int M, int N,
-                                     int K) {
+                                     int K, BufList* all = nullptr) {
   const char* fn = "qgemv_affine4_rht";
   qg_status st = check_affine_common(fn, M, N, K);
   if (st) return st;
@@ -389,6 +410,7 @@ qg_status do_check_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int
   if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(in[2], 2, fn)) ||
       (st = check_ptr(in[3], 2, fn)) || (st = check_ptr(in[4], 1, fn)) || (st = check_ptr(out[0], 2, fn)))
     return st;
+  collect(all, out, 1, in, 5);
   return check_alias(out, 1, in, 5, fn);
 }
 
@@ -414,7 +436,7 @@ qg_status do_check_tile_pack(const uint32_t* codes, const uint16_t* scales, cons
 }
 
 qg_status do_check_tiled(const char* fn, const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, int M,
-                         int N, int K, const Buf* outs, int nout) {
+                         int N, int K, const Buf* outs, int nout, BufList* all = nullptr) {
   qg_status st = check_affine_common(fn, M, N, K);
   if (st) return st;
   if (K % 512 != 0) return fail(QG_EINVAL, "%s: K=%d must be a multiple of 512 (tile-order layout)", fn, K);
@@ -422,19 +444,66 @@ qg_status do_check_tiled(const char* fn, const uint16_t* x, const uint32_t* code
                     {sb_t, tiled_sb_bytes(N, K), "sb_t"}};
   if ((st = check_ptr(in[0], 16, fn)) || (st = check_ptr(in[1], 16, fn)) || (st = check_ptr(in[2], 16, fn)))
     return st;
+  collect(all, outs, nout, in, 3);
   return check_alias(outs, nout, in, 3, fn);
 }
 
+qg_status do_check_qgemv_affine4_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, uint16_t* y,
+                                       int M, int N, int K, BufList* all) {
+  const char* fn = "qgemv_affine4_tiled";
+  const Buf out[] = {{y, (size_t)M * N * 2, "y"}};
+  qg_status st = do_check_tiled(fn, x, codes_t, sb_t, M, N, K, out, 1, all);
+  if (st) return st;
+  return check_ptr(out[0], 2, fn);
+}
+
+qg_status do_check_lmhead_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, float* logits,
+                                int32_t* ids, const int32_t* draft, int32_t* accepted, int M, int V, int K,
+                                BufList* all) {
+  const char* fn = "lmhead_argmax_tiled";
+  if (V < 1) return fail(QG_EINVAL, "%s: V=%d must be >= 1", fn, V);
+  if (!fits_lds_unsplit(M, K) && M >= 1 && M <= 8)
+    return fail(QG_EUNSUPPORTED, "%s: M=%d rows of K=%d do not fit the staged-activation LDS budget", fn, M, K);
+  const Buf out[] = {{logits, logits ? (size_t)M * V * 4 : 0, "logits"},
+                     {ids, (size_t)M * 4, "ids"},
+                     {accepted, accepted ? (size_t)4 : (size_t)0, "accepted"}};
+  qg_status st = do_check_tiled(fn, x, codes_t, sb_t, M, V, K, out, 3, all);
+  if (st) return st;
+  if ((st = check_ptr(out[1], 4, fn))) return st;
+  if (logits && (st = check_ptr(out[0], 4, fn))) return st;
+  if (accepted && (st = check_ptr(out[2], 4, fn))) return st;
+  const Buf dr = {draft, draft ? (size_t)M * 4 : 0, "draft"};
+  if (draft && (st = check_ptr(dr, 4, fn))) return st;
+  collect(all, nullptr, 0, &dr, 1);
+  return check_alias(out, 3, &dr, 1, fn);
+}
+
+qg_status do_check_gateup_tiled(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes_t,
+                                const uint16_t* sb_t, uint16_t* h, int M, int I, int K, BufList* all) {
+  const char* fn = "rmsnorm_gateup_swiglu_tiled";
+  if (I < 1 || (long long)I * 2 * 16 > 0x7FFFFFFFLL) return fail(QG_EINVAL, "%s: I=%d out of range", fn, I);
+  if (!(eps > 0.0f) || eps != eps || eps > 3.0e38f) return fail(QG_EINVAL, "%s: eps must be positive and finite", fn);
+  const Buf out[] = {{h, (size_t)M * I * 2, "h"}};
+  qg_status st = do_check_tiled(fn, x, codes_t, sb_t, M, 2 * I, K, out, 1, all);
+  if (st) return st;
+  const Buf gm = {gamma, (size_t)K * 2, "gamma"};
+  if ((st = check_ptr(gm, 16, fn)) || (st = check_ptr(out[0], 2, fn))) return st;
+  collect(all, nullptr, 0, &gm, 1);
+  return check_alias(out, 1, &gm, 1, fn);
+}
+
 // --------------------------------------------------------- dispatch --
-// `reserve` bytes at the start of the workspace belong to the caller; `pre`
-// (if set) runs after the workspace is in place and before the projection is
-// launched, with that region and the arguments (the RHT entry point launches
-// its transform there and points the projection at the planes it writes).
 // Split plan of an affine projection (a.M, a.N, a.K and a.tiled set): fills
-// G, nchunks, ntiles, waves, S, cps and wide, and *lds (bytes of LDS per
-// workgroup).  The persistent MLP block uses the same plans, so its results
-// equal those of the separate entry points.
-qg_status plan_affine(int mode, QgAffineArgs& a, const char* fn, size_t* lds_out) {
+// G, nchunks, ntiles, waves, S, cps and wide, *lds (bytes of LDS per
+// workgroup) and rgroups (workgroups per slice on `cus` compute units).  The
+// persistent MLP block uses the same plans, so its results equal those of the
+// separate entry points.
+//
+// The K split is chosen with the LDS footprint of an 8-row call, so that a
+// call's slices -- and with them the order in which partial sums are added --
+// do not depend on M: row i of an M-row call equals, bit for bit, the 1-row
+// call on row i (TensorFold page, section "핵심 메커니즘 2 — 정확 디코딩").
+qg_status plan_affine(int mode, QgAffineArgs& a, const char* fn, size_t* lds_out, int cus) {
   const int G = a.K / 64;
   a.G = G;
   a.nchunks = (G + 1) / 2;
@@ -442,8 +511,10 @@ qg_status plan_affine(int mode, QgAffineArgs& a, const char* fn, size_t* lds_out
   a.waves = kWaves;
   const int PL = (mode == QG_MODE_GATEUP || mode == QG_MODE_PLANES) ? 2 : 1;
   const size_t per = affine_lds_per_chunk(a.M, PL);
-  const int cps_max = (int)std::min<size_t>((size_t)a.nchunks, (kLdsBudget - affine_lds_fixed(a.M, PL)) / per);
   const bool split_ok = (mode != QG_MODE_LMHEAD);
+  const int Ms = split_ok ? 8 : a.M;  // rows the slice length is sized for
+  const int cps_max = (int)std::min<size_t>(
+      (size_t)a.nchunks, (kLdsBudget - affine_lds_fixed(Ms, PL)) / affine_lds_per_chunk(Ms, PL));
   if (!split_ok && a.nchunks > cps_max)
     return fail(QG_EUNSUPPORTED, "%s: K=%d needs a split of K this mode or size lacks", fn, a.K);
   // A split costs a follow-up kernel (a few microseconds); a plain projection
@@ -480,38 +551,109 @@ qg_status plan_affine(int mode, QgAffineArgs& a, const char* fn, size_t* lds_out
   if (a.tiled && !a.wide)
     return fail(QG_EUNSUPPORTED, "%s: no K split of whole 512-k batches fits for K=%d", fn, a.K);
   *lds_out = (size_t)a.cps * per + affine_lds_fixed(a.M, PL);
-  a.rgroups = affine_rgroups(a.ntiles, a.S, *lds_out, 4, fill_pct);  // 128 registers per lane: 4 waves per SIMD
+  a.rgroups = affine_rgroups(a.ntiles, a.S, *lds_out, 4, fill_pct, cus);  // 128 registers per lane: 4 waves per SIMD
   return QG_OK;
 }
 
-qg_status run_affine(int mode, QgAffineArgs a, hipStream_t stream, const char* fn, size_t reserve = 0,
-                     const std::function<int(unsigned char*, QgAffineArgs&)>& pre = nullptr) {
+// One affine call: its mode, launch arguments, plan and scratch layout
+// (offsets from the start of the scratch region, kWsHeader into ws).
+struct AffineCall {
+  int mode = QG_MODE_PLAIN;
+  QgAffineArgs a{};
   size_t lds = 0;
-  qg_status pst = plan_affine(mode, a, fn, &lds);
-  if (pst) return pst;
-  unsigned char* ws = nullptr;
-  const bool partials = a.S > 1 || mode == QG_MODE_GATEUP;
-  const size_t part_bytes = partials ? (size_t)a.S * a.M * a.N * 4 : 0;
-  const size_t ssq_bytes = (mode == QG_MODE_GATEUP) ? (size_t)a.S * 8 * 4 : 0;
-  const size_t key_bytes = (mode == QG_MODE_LMHEAD) ? (size_t)a.S * a.rgroups * 8 * 8 : 0;
-  // top-k: the blocks' candidates, and the logits when the caller keeps none
-  const size_t cand_bytes = a.topk > 0 ? (size_t)a.M * ((a.N + kTopkBlock - 1) / kTopkBlock) * a.topk * 8 : 0;
-  const size_t lg_bytes = (a.topk > 0 && !a.logits) ? (size_t)a.M * a.N * 4 : 0;
-  reserve = (reserve + 255) / 256 * 256;
-  qg_status st = get_workspace(stream, reserve + part_bytes + ssq_bytes + key_bytes + cand_bytes + lg_bytes, &ws);
+  size_t reserve = 0;  // leading scratch of the entry point (the RHT planes)
+  size_t off_part = 0, off_ssq = 0, off_keys = 0, off_cand = 0, off_lg = 0, scratch = 0;
+};
+
+qg_status affine_layout(AffineCall& c, const char* fn, int cus) {
+  qg_status st = plan_affine(c.mode, c.a, fn, &c.lds, cus);
   if (st) return st;
+  const QgAffineArgs& a = c.a;
+  size_t off = align_up(c.reserve, kWsAlign);
+  const bool partials = a.S > 1 || c.mode == QG_MODE_GATEUP;
+  c.off_part = off;
+  off += partials ? align_up((size_t)a.S * a.M * a.N * 4, kWsAlign) : 0;
+  c.off_ssq = off;
+  off += (c.mode == QG_MODE_GATEUP) ? align_up((size_t)a.S * 8 * 4, kWsAlign) : 0;
+  c.off_keys = off;
+  off += (c.mode == QG_MODE_LMHEAD) ? align_up((size_t)a.S * a.rgroups * 8 * 8, kWsAlign) : 0;
+  // top-k: the blocks' candidates, and the logits when the caller keeps none
+  c.off_cand = off;
+  off += a.topk > 0 ? align_up((size_t)a.M * ((a.N + kTopkBlock - 1) / kTopkBlock) * a.topk * 8, kWsAlign) : 0;
+  c.off_lg = off;
+  off += (a.topk > 0 && !a.logits) ? align_up((size_t)a.M * a.N * 4, kWsAlign) : 0;
+  c.scratch = off;
+  return QG_OK;
+}
+
+// Shared by an entry point and its host-only twin: the plan for kMaxCus
+// compute units (the largest scratch any device needs) and the workspace check.
+qg_status affine_prepare(AffineCall& c, const char* fn, const void* ws, size_t ws_bytes, const BufList& bl) {
+  qg_status st = affine_layout(c, fn, kMaxCus);
+  if (st) return st;
+  return check_ws(fn, ws, ws_bytes, ws_total(c.scratch), bl.b, bl.n);
+}
+
+// Workspace bytes of an affine call of this shape (0 if it needs none or the
+// shape has no plan; the entry point reports the latter).
+size_t affine_query(AffineCall c, const char* fn) {
+  if (c.a.M < 1 || c.a.M > 8 || c.a.N < 1 || c.a.K < 64 || c.a.K % 64) return 0;
+  if (affine_layout(c, fn, kMaxCus)) return 0;
+  return ws_total(c.scratch);
+}
+
+// After the checks: the plan's workgroup count for this device (the K split
+// and so the scratch needed are unchanged; the per-workgroup keys need no
+// more than was checked), the scratch pointers, and the launch.  `pre` (if
+// set) enqueues work that the projection reads (the RHT planes) and may
+// change the arguments.
+qg_status affine_launch(AffineCall c, const char* fn, void* ws, hipStream_t stream,
+                        const std::function<int(unsigned char*, QgAffineArgs&)>& pre = nullptr) {
+  qg_status st = affine_layout(c, fn, device_cus());
+  if (st) return st;
+  unsigned char* base = ws ? static_cast<unsigned char*>(ws) + kWsHeader : nullptr;
   if (pre) {
-    const int err = pre(ws, a);
+    const int err = pre(base, c.a);
     if (err) return fail(QG_EHIP, "%s: launch failed: %s", fn, hipGetErrorString((hipError_t)err));
   }
-  ws += reserve;
-  a.part = reinterpret_cast<float*>(ws);
-  a.ssq_part = reinterpret_cast<float*>(ws + part_bytes);
-  a.keys = reinterpret_cast<unsigned long long*>(ws + part_bytes + ssq_bytes);
-  a.cand = reinterpret_cast<unsigned long long*>(ws + part_bytes + ssq_bytes + key_bytes);
-  if (lg_bytes) a.logits = reinterpret_cast<float*>(ws + part_bytes + ssq_bytes + key_bytes + cand_bytes);
-  return launched(qg_launch_affine(mode, a, lds, stream), fn);
+  if (base) {
+    c.a.part = reinterpret_cast<float*>(base + c.off_part);
+    c.a.ssq_part = reinterpret_cast<float*>(base + c.off_ssq);
+    c.a.keys = reinterpret_cast<unsigned long long*>(base + c.off_keys);
+    c.a.cand = reinterpret_cast<unsigned long long*>(base + c.off_cand);
+    if (c.a.topk > 0 && !c.a.logits) c.a.logits = reinterpret_cast<float*>(base + c.off_lg);
+  }
+  return launched(qg_launch_affine(c.mode, c.a, c.lds, stream), fn);
 }
+
+// ------------------------------------------------------------ Q4_K / Q6_K --
+struct Q4kCall {
+  QgQ4kArgs a{};
+  size_t lds = 0, scratch = 0;
+};
+
+// Split plan of a Q4_K (bpb = 144) or Q6_K (bpb = 210) projection; the slice
+// length is sized for 8 rows, so the split does not depend on M.
+void q4k_layout(Q4kCall& c, int bpb) {
+  QgQ4kArgs& a = c.a;
+  a.nchunks = a.K / 256;
+  a.ntiles = (a.N + 15) / 16;
+  a.waves = kWaves;
+  const size_t per8 = bpb == 144 ? q4k_lds_per_sb(8) : q6k_lds_per_sb(8);
+  const size_t per = bpb == 144 ? q4k_lds_per_sb(a.M) : q6k_lds_per_sb(a.M);
+  const int cps_max = (int)std::max<size_t>(1, std::min<size_t>((size_t)a.nchunks, (kQ4kLdsBudget - 16) / per8));
+  Plan pl = plan_split(a.ntiles, a.nchunks, cps_max, true);
+  a.S = pl.S;
+  a.cps = pl.cps;
+  a.tpw = pl.tpw;
+  a.rgroups = pl.rgroups;
+  c.lds = 16 + (size_t)a.cps * per;
+  c.scratch = (a.S > 1) ? align_up((size_t)a.S * a.M * a.N * 4, kWsAlign) : 0;
+}
+
+// ------------------------------------------------------------------ MoE --
+constexpr size_t kMoeRouteBytes = 512;  // selected ids [64] then their weights [64]
+size_t moe_scratch(int top_k, int I) { return kMoeRouteBytes + align_up((size_t)top_k * I * 2, kWsAlign); }
 
 // Measurement aid: a plain streaming read of a buffer (each workgroup reads
 // consecutive 4-KB pieces, eight 16-byte non-temporal loads per lane in
@@ -536,49 +678,11 @@ __global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ p
 }
 
 // ------------------------------------------------ persistent MLP block --
-// Barrier state of the persistent kernel per (device, stream, M, D, I):
-// arrival counters that only grow, release words and a failure flag, zeroed
-// once when created.  The grid (resident slots at this configuration's LDS)
-// depends only on the key, so a state always sees the same grid.
-struct MlpState {
-  unsigned char* ptr = nullptr;
-  size_t bytes = 0;
-  int off_h = 0, off_y = 0, off_r = 0;
-  int grid = 0;
-};
-std::mutex g_mlp_mu;
-std::map<std::tuple<int, hipStream_t, int, int, int>, MlpState> g_mlp;
 constexpr int kMlpSpinLimit = 200000;  // polls of one wait before a workgroup gives up (tens of ms)
-
-qg_status mlp_state(hipStream_t stream, int M, int D, int I, int S_down, size_t lds, MlpState** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return fail(QG_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
-  std::lock_guard<std::mutex> lk(g_mlp_mu);
-  MlpState& s = g_mlp[std::make_tuple(dev, stream, M, D, I)];
-  if (!s.ptr) {
-    int occ = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, qg_mlp_kernel(M), 256, lds);
-    if (e != hipSuccess || occ < 1)
-      return fail(QG_EUNSUPPORTED, "mlp_block_affine4_tiled: no resident workgroup fits (%d)", (int)e);
-    s.grid = device_cus() * std::min(occ, 4) / 32 * 32;  // the grid barrier takes 32 groups of equal size
-    if (s.grid < 32) return fail(QG_EUNSUPPORTED, "mlp_block_affine4_tiled: fewer than 32 resident workgroups");
-    s.bytes = qg_mlp_state_bytes(D, I, S_down, &s.off_h, &s.off_y, &s.off_r);
-    void* p = nullptr;
-    e = hipMalloc(&p, s.bytes);
-    if (e != hipSuccess) return fail(QG_ENOMEM, "mlp state hipMalloc: %s", hipGetErrorString(e));
-    e = hipMemset(p, 0, s.bytes);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) return fail(QG_EHIP, "mlp state init: %s", hipGetErrorString(e));
-    s.ptr = static_cast<unsigned char*>(p);
-  }
-  *out = &s;
-  return QG_OK;
-}
 
 qg_status do_check_mlp(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* gu_codes_t,
                        const uint16_t* gu_sb_t, const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
-                       uint16_t* y, int M, int D, int I) {
+                       uint16_t* y, int M, int D, int I, BufList* all = nullptr) {
   const char* fn = "mlp_block_affine4_tiled";
   if (M < 1 || M > 8) return fail(QG_EINVAL, "%s: M=%d must be in 1..8", fn, M);
   if (D <= 0 || D % 512 != 0) return fail(QG_EINVAL, "%s: D=%d must be a positive multiple of 512", fn, D);
@@ -597,45 +701,34 @@ qg_status do_check_mlp(const uint16_t* x, const uint16_t* gamma, float eps, cons
   for (const Buf& b : in)
     if ((st = check_ptr(b, 16, fn))) return st;
   if ((st = check_ptr(out[0], 16, fn)) || (st = check_ptr(out[1], 4, fn))) return st;
+  collect(all, out, 2, in, 6);
   return check_alias(out, 2, in, 6, fn);
 }
 
-}  // namespace
+struct MlpCall {
+  AffineCall gu, dn;  // gate/up (y = h) and down (x = h) plans
+  size_t lds = 0, off_part_a = 0, off_ssq_a = 0, off_part_c = 0, scratch = 0;
+};
 
-extern "C" {
-
-qg_status qg_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
-  clear_err();
-  if (!buf || !sink) return fail(QG_EINVAL, "qg_stream_read: null pointer");
-  if (bytes < 16 || bytes % 16 != 0 || !aligned(buf, 16) || !aligned(sink, 4))
-    return fail(QG_EINVAL, "qg_stream_read: bytes must be a positive multiple of 16 and buf 16-byte aligned");
+qg_status mlp_layout(MlpCall& c, const char* fn, int cus) {
   qg_status st;
-  if ((st = check_device())) return st;
-  const size_t n16 = bytes / 16;
-  const unsigned grid = (unsigned)std::min<size_t>(8192, (n16 + 2047) / 2048);
-  hipLaunchKernelGGL(k_stream_read, dim3(grid), dim3(256), 0, (hipStream_t)stream, static_cast<const uint4*>(buf), n16,
-                     sink);
-  return launched((int)hipGetLastError(), "qg_stream_read");
+  if ((st = affine_layout(c.gu, fn, cus)) || (st = affine_layout(c.dn, fn, cus))) return st;
+  c.lds = std::max(c.gu.lds, c.dn.lds);
+  const QgAffineArgs &pa = c.gu.a, &pc = c.dn.a;
+  c.off_part_a = 0;
+  c.off_ssq_a = align_up((size_t)pa.S * pa.M * pa.N * 4, kWsAlign);
+  c.off_part_c = c.off_ssq_a + align_up((size_t)pa.S * 8 * 4, kWsAlign);
+  c.scratch = c.off_part_c + align_up((size_t)pc.S * pc.M * pc.N * 4, kWsAlign);
+  return QG_OK;
 }
 
-qg_status qg_check_mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma, float eps,
-                                           const uint32_t* gu_codes_t, const uint16_t* gu_sb_t,
-                                           const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
-                                           uint16_t* y, int M, int D, int I) {
-  clear_err();
-  return do_check_mlp(x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, y, M, D, I);
-}
-
-qg_status mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* gu_codes_t,
-                                  const uint16_t* gu_sb_t, const uint32_t* dn_codes_t, const uint16_t* dn_sb_t,
-                                  uint16_t* h, uint16_t* y, int M, int D, int I, void* stream) {
-  const char* fn = "mlp_block_affine4_tiled";
-  clear_err();
-  qg_status st = do_check_mlp(x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, y, M, D, I);
-  if (st) return st;
-  if ((st = check_device())) return st;
-  hipStream_t s = (hipStream_t)stream;
-  QgAffineArgs pa{}, pc{};
+void mlp_fill(MlpCall& c, const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* gu_codes_t,
+              const uint16_t* gu_sb_t, const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h, uint16_t* y,
+              int M, int D, int I) {
+  QgAffineArgs& pa = c.gu.a;
+  QgAffineArgs& pc = c.dn.a;
+  c.gu.mode = QG_MODE_GATEUP;
+  c.dn.mode = QG_MODE_PLAIN;
   pa.x = x;
   pa.gamma = gamma;
   pa.eps = eps;
@@ -656,113 +749,199 @@ qg_status mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma, floa
   pc.M = M;
   pc.N = D;
   pc.K = I;
-  size_t lds_a = 0, lds_c = 0;
-  if ((st = plan_affine(QG_MODE_GATEUP, pa, fn, &lds_a)) || (st = plan_affine(QG_MODE_PLAIN, pc, fn, &lds_c)))
-    return st;
-  const size_t lds = std::max(lds_a, lds_c);
-  MlpState* sy = nullptr;
-  if ((st = mlp_state(s, M, D, I, pc.S, lds, &sy))) return st;
-  // every job of a phase gets its own resident workgroup when the plan allows
-  const int P = sy->grid;
-  pa.rgroups = std::max(1, std::min(P / pa.S, (pa.ntiles + kWaves - 1) / kWaves));
-  pc.rgroups = std::max(1, std::min(P / pc.S, (pc.ntiles + kWaves - 1) / kWaves));
-  const size_t part_a = (size_t)pa.S * M * pa.N * 4, ssq_a = (size_t)pa.S * 8 * 4, part_c = (size_t)pc.S * M * pc.N * 4;
-  unsigned char* ws = nullptr;
-  if ((st = get_workspace(s, part_a + ssq_a + part_c + 256, &ws))) return st;
-  pa.part = reinterpret_cast<float*>(ws);
-  pa.ssq_part = reinterpret_cast<float*>(ws + part_a);
-  pc.part = reinterpret_cast<float*>(ws + (part_a + ssq_a + 255) / 256 * 256);
-  return launched(qg_launch_mlp(pa, pc, sy->ptr, sy->off_h, sy->off_y, sy->off_r, kMlpSpinLimit, P, lds, s), fn);
 }
 
-int32_t qg_mlp_failures(void* stream) {
+// Resident workgroups of the persistent kernel for M rows at this LDS size on
+// the current device, rounded down to the barrier's 32 groups (0 if none).
+int mlp_grid(int M, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, size_t>, int> cache;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return -1;
-  std::lock_guard<std::mutex> lk(g_mlp_mu);
-  int32_t total = 0;
-  for (auto& kv : g_mlp) {
-    if (std::get<0>(kv.first) != dev || std::get<1>(kv.first) != (hipStream_t)stream) continue;
-    unsigned v = 0;
-    if (hipMemcpy(&v, kv.second.ptr + 16, 4, hipMemcpyDeviceToHost) != hipSuccess) return -1;
-    total += (int32_t)(v != 0);
-  }
-  return total;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lk(mu);
+  auto key = std::make_tuple(dev, M, lds);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, qg_mlp_kernel(M), 256, lds) != hipSuccess) occ = 0;
+  const int grid = occ < 1 ? 0 : device_cus() * std::min(occ, 4) / 32 * 32;
+  cache[key] = grid;
+  return grid;
+}
+
+}  // namespace
+
+extern "C" {
+
+qg_status qg_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  clear_err();
+  if (!buf || !sink) return fail(QG_EINVAL, "qg_stream_read: null pointer");
+  if (bytes < 16 || bytes % 16 != 0 || !aligned(buf, 16) || !aligned(sink, 4))
+    return fail(QG_EINVAL, "qg_stream_read: bytes must be a positive multiple of 16 and buf 16-byte aligned");
+  qg_status st;
+  if ((st = check_device())) return st;
+  const size_t n16 = bytes / 16;
+  const unsigned grid = (unsigned)std::min<size_t>(8192, (n16 + 2047) / 2048);
+  hipLaunchKernelGGL(k_stream_read, dim3(grid), dim3(256), 0, (hipStream_t)stream, static_cast<const uint4*>(buf), n16,
+                     sink);
+  return launched((int)hipGetLastError(), "qg_stream_read");
 }
 
 const char* qg_status_string(qg_status s) {
   switch (s) {
     case QG_OK: return "ok";
-    case QG_EINVAL: return "invalid argument (shape, null pointer or alignment)";
-    case QG_EALIAS: return "an output overlaps an input or another output";
+    case QG_EINVAL: return "invalid argument (shape, null pointer, alignment or workspace size)";
+    case QG_EALIAS: return "an output or the workspace overlaps an input or another output";
     case QG_EUNSUPPORTED: return "valid request with no kernel instance";
     case QG_EHIP: return "HIP runtime or launch error";
-    case QG_ENOMEM: return "workspace allocation failed";
     default: return "unknown status";
   }
 }
 
 const char* qg_last_error(void) { return g_err; }
 
+size_t qg_workspace_header_bytes(void) { return kWsHeader; }
+
+// ------------------------------------------------------ mlp_block_affine4 --
+static qg_status prep_mlp(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* gu_codes_t,
+                          const uint16_t* gu_sb_t, const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
+                          uint16_t* y, int M, int D, int I, const void* ws, size_t ws_bytes, MlpCall& c) {
+  const char* fn = "mlp_block_affine4_tiled";
+  BufList bl;
+  qg_status st = do_check_mlp(x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, y, M, D, I, &bl);
+  if (st) return st;
+  mlp_fill(c, x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, y, M, D, I);
+  if ((st = mlp_layout(c, fn, kMaxCus))) return st;
+  return check_ws(fn, ws, ws_bytes, ws_total(c.scratch, true), bl.b, bl.n);
+}
+
+size_t mlp_block_affine4_tiled_workspace(int M, int D, int I) {
+  if (M < 1 || M > 8 || D <= 0 || D % 512 || I <= 0 || I % 512) return 0;
+  MlpCall c;
+  mlp_fill(c, nullptr, nullptr, 1e-6f, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M, D, I);
+  if (mlp_layout(c, "mlp_block_affine4_tiled", kMaxCus)) return 0;
+  return ws_total(c.scratch, true);
+}
+
+qg_status qg_check_mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma, float eps,
+                                           const uint32_t* gu_codes_t, const uint16_t* gu_sb_t,
+                                           const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
+                                           uint16_t* y, int M, int D, int I, const void* ws, size_t ws_bytes) {
+  clear_err();
+  MlpCall c;
+  return prep_mlp(x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, y, M, D, I, ws, ws_bytes, c);
+}
+
+qg_status mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* gu_codes_t,
+                                  const uint16_t* gu_sb_t, const uint32_t* dn_codes_t, const uint16_t* dn_sb_t,
+                                  uint16_t* h, uint16_t* y, int M, int D, int I, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  const char* fn = "mlp_block_affine4_tiled";
+  clear_err();
+  MlpCall c;
+  qg_status st = prep_mlp(x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, y, M, D, I, ws, ws_bytes, c);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  if ((st = mlp_layout(c, fn, device_cus()))) return st;
+  const int P = mlp_grid(M, c.lds);
+  if (P < 32) return fail(QG_EUNSUPPORTED, "%s: fewer than 32 workgroups can be resident", fn);
+  // every job of a phase gets its own resident workgroup when the plan allows
+  QgAffineArgs pa = c.gu.a, pc = c.dn.a;
+  pa.rgroups = std::max(1, std::min(P / pa.S, (pa.ntiles + kWaves - 1) / kWaves));
+  pc.rgroups = std::max(1, std::min(P / pc.S, (pc.ntiles + kWaves - 1) / kWaves));
+  unsigned char* base = static_cast<unsigned char*>(ws) + kWsHeader;
+  pa.part = reinterpret_cast<float*>(base + c.off_part_a);
+  pa.ssq_part = reinterpret_cast<float*>(base + c.off_ssq_a);
+  pc.part = reinterpret_cast<float*>(base + c.off_part_c);
+  return launched(qg_launch_mlp(pa, pc, static_cast<unsigned char*>(ws), kMlpSpinLimit, P, c.lds,
+                                (hipStream_t)stream),
+                  fn);
+}
+
+int32_t mlp_block_affine4_tiled_failures(void* ws, void* stream) {
+  clear_err();
+  if (!ws) return -1;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return -1;
+  uint32_t v = 0, zero = 0;
+  unsigned char* cnt = static_cast<unsigned char*>(ws) + 20;
+  if (hipMemcpy(&v, cnt, 4, hipMemcpyDeviceToHost) != hipSuccess) return -1;
+  if (v && hipMemcpy(cnt, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return -1;
+  return (int32_t)v;
+}
+
+// ------------------------------------------------------------ qgemv_affine4 --
+static qg_status prep_qgemv_affine4(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                                    const uint16_t* biases, uint16_t* y, int M, int N, int K, const void* ws,
+                                    size_t ws_bytes, AffineCall& c, const char* fn = "qgemv_affine4") {
+  BufList bl;
+  qg_status st = do_check_qgemv_affine4(x, codes, scales, biases, y, M, N, K, &bl);
+  if (st || N == 0) return st;
+  c.mode = QG_MODE_PLAIN;
+  QgAffineArgs& a = c.a;
+  a.x = x;
+  a.codes = codes;
+  a.scales = scales;
+  a.biases = biases;
+  a.y = y;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  return affine_prepare(c, fn, ws, ws_bytes, bl);
+}
+
+size_t qgemv_affine4_workspace(int M, int N, int K) {
+  AffineCall c;
+  c.a.M = M;
+  c.a.N = N;
+  c.a.K = K;
+  return affine_query(c, "qgemv_affine4");
+}
+
 qg_status qg_check_qgemv_affine4(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
-                                 const uint16_t* biases, uint16_t* y, int M, int N, int K) {
+                                 const uint16_t* biases, uint16_t* y, int M, int N, int K, const void* ws,
+                                 size_t ws_bytes) {
   clear_err();
-  return do_check_qgemv_affine4(x, codes, scales, biases, y, M, N, K);
-}
-
-qg_status qg_check_qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K) {
-  clear_err();
-  return do_check_qgemv_q4k(x, blocks, y, M, N, K);
-}
-
-qg_status qg_check_rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma, float eps,
-                                         const uint32_t* codes_gu, const uint16_t* scales_gu,
-                                         const uint16_t* biases_gu, uint16_t* h, int M, int I, int K) {
-  clear_err();
-  return do_check_gateup(x, gamma, eps, codes_gu, scales_gu, biases_gu, h, M, I, K);
-}
-
-qg_status qg_check_moe_expert_qgemv(const uint16_t* x, const float* router_logits, int top_k, const uint8_t* w_gu,
-                                    const uint8_t* w_down, uint16_t* y, int32_t* out_ids, float* out_w, int E, int D,
-                                    int I) {
-  clear_err();
-  return do_check_moe(x, router_logits, top_k, w_gu, w_down, y, out_ids, out_w, E, D, I);
-}
-
-qg_status qg_check_lmhead_argmax(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
-                                 const uint16_t* biases, float* logits, int32_t* ids, const int32_t* draft,
-                                 int32_t* accepted, int M, int V, int K) {
-  clear_err();
-  return do_check_lmhead(x, codes, scales, biases, logits, ids, draft, accepted, M, V, K);
+  AffineCall c;
+  return prep_qgemv_affine4(x, codes, scales, biases, y, M, N, K, ws, ws_bytes, c);
 }
 
 qg_status qgemv_affine4(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
-                        uint16_t* y, int M, int N, int K, void* stream) {
+                        uint16_t* y, int M, int N, int K, void* ws, size_t ws_bytes, void* stream) {
   clear_err();
-  qg_status st = do_check_qgemv_affine4(x, codes, scales, biases, y, M, N, K);
-  if (st) return st;
-  if (N == 0) return QG_OK;
+  AffineCall c;
+  qg_status st = prep_qgemv_affine4(x, codes, scales, biases, y, M, N, K, ws, ws_bytes, c);
+  if (st || N == 0) return st;
   if ((st = check_device())) return st;
-  QgAffineArgs a{};
-  a.x = x;
-  a.codes = codes;
-  a.scales = scales;
-  a.biases = biases;
-  a.y = y;
-  a.M = M;
-  a.N = N;
-  a.K = K;
-  return run_affine(QG_MODE_PLAIN, a, (hipStream_t)stream, "qgemv_affine4");
+  return affine_launch(c, "qgemv_affine4", ws, (hipStream_t)stream);
 }
 
+// The same projection with the products on the vector ALU (measurement aid):
+// qgemv_affine4's plan, arguments and workspace.
+size_t qg_affine4_valu_workspace(int M, int N, int K) { return qgemv_affine4_workspace(M, N, K); }
+
 qg_status qg_affine4_valu(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
-                          uint16_t* y, int M, int N, int K, void* stream) {
+                          uint16_t* y, int M, int N, int K, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "qg_affine4_valu";
   clear_err();
-  qg_status st = do_check_qgemv_affine4(x, codes, scales, biases, y, M, N, K);
-  if (st) return st;
-  if (N == 0) return QG_OK;
+  AffineCall c;
+  qg_status st = prep_qgemv_affine4(x, codes, scales, biases, y, M, N, K, ws, ws_bytes, c, fn);
+  if (st || N == 0) return st;
   if ((st = check_device())) return st;
-  QgAffineArgs a{};
+  if ((st = affine_layout(c, fn, device_cus()))) return st;
+  if (qg_valu_lds_bytes(c.a.M, c.a.cps) > c.lds) return fail(QG_EUNSUPPORTED, "%s: slice does not fit", fn);
+  if (ws) c.a.part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + kWsHeader + c.off_part);
+  return launched(qg_launch_affine_valu(c.a, (hipStream_t)stream), fn);
+}
+
+// ------------------------------------------------------------ qgemv_affine8 --
+static qg_status prep_qgemv_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                                    const uint16_t* biases, uint16_t* y, int M, int N, int K, const void* ws,
+                                    size_t ws_bytes, AffineCall& c) {
+  BufList bl;
+  qg_status st = do_check_qgemv_affine8(x, codes, scales, biases, y, M, N, K, &bl);
+  if (st || N == 0) return st;
+  c.mode = QG_MODE_PLAIN8;
+  QgAffineArgs& a = c.a;
   a.x = x;
   a.codes = codes;
   a.scales = scales;
@@ -771,30 +950,45 @@ qg_status qg_affine4_valu(const uint16_t* x, const uint32_t* codes, const uint16
   a.M = M;
   a.N = N;
   a.K = K;
-  size_t lds = 0;  // qgemv_affine4's plan; the vector-ALU kernel needs less LDS than it
-  if ((st = plan_affine(QG_MODE_PLAIN, a, "qg_affine4_valu", &lds))) return st;
-  if (qg_valu_lds_bytes(a.M, a.cps) > lds) return fail(QG_EUNSUPPORTED, "qg_affine4_valu: slice does not fit");
-  unsigned char* ws = nullptr;
-  if ((st = get_workspace((hipStream_t)stream, a.S > 1 ? (size_t)a.S * a.M * a.N * 4 : 16, &ws))) return st;
-  a.part = reinterpret_cast<float*>(ws);
-  return launched(qg_launch_affine_valu(a, (hipStream_t)stream), "qg_affine4_valu");
+  return affine_prepare(c, "qgemv_affine8", ws, ws_bytes, bl);
+}
+
+size_t qgemv_affine8_workspace(int M, int N, int K) {
+  AffineCall c;
+  c.mode = QG_MODE_PLAIN8;
+  c.a.M = M;
+  c.a.N = N;
+  c.a.K = K;
+  return affine_query(c, "qgemv_affine8");
 }
 
 qg_status qg_check_qgemv_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
-                                 const uint16_t* biases, uint16_t* y, int M, int N, int K) {
+                                 const uint16_t* biases, uint16_t* y, int M, int N, int K, const void* ws,
+                                 size_t ws_bytes) {
   clear_err();
-  return do_check_qgemv_affine8(x, codes, scales, biases, y, M, N, K);
+  AffineCall c;
+  return prep_qgemv_affine8(x, codes, scales, biases, y, M, N, K, ws, ws_bytes, c);
 }
 
 qg_status qgemv_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
-                        uint16_t* y, int M, int N, int K, void* stream) {
+                        uint16_t* y, int M, int N, int K, void* ws, size_t ws_bytes, void* stream) {
   clear_err();
-  qg_status st = do_check_qgemv_affine8(x, codes, scales, biases, y, M, N, K);
-  if (st) return st;
-  if (N == 0) return QG_OK;
+  AffineCall c;
+  qg_status st = prep_qgemv_affine8(x, codes, scales, biases, y, M, N, K, ws, ws_bytes, c);
+  if (st || N == 0) return st;
   if ((st = check_device())) return st;
-  QgAffineArgs a{};
-  a.x = x;
+  return affine_launch(c, "qgemv_affine8", ws, (hipStream_t)stream);
+}
+
+// -------------------------------------------------------- qgemv_affine4_rht --
+static qg_status prep_rht(const uint16_t* x, const int8_t* signs, int had, const uint32_t* codes,
+                          const uint16_t* scales, const uint16_t* biases, uint16_t* y, int M, int N, int K,
+                          const void* ws, size_t ws_bytes, AffineCall& c) {
+  BufList bl;
+  qg_status st = do_check_qgemv_affine4_rht(x, signs, had, codes, scales, biases, y, M, N, K, &bl);
+  if (st || N == 0) return st;
+  c.mode = QG_MODE_PLANES;
+  QgAffineArgs& a = c.a;
   a.codes = codes;
   a.scales = scales;
   a.biases = biases;
@@ -802,45 +996,49 @@ qg_status qgemv_affine8(const uint16_t* x, const uint32_t* codes, const uint16_t
   a.M = M;
   a.N = N;
   a.K = K;
-  return run_affine(QG_MODE_PLAIN8, a, (hipStream_t)stream, "qgemv_affine8");
+  c.reserve = 2 * align_up((size_t)M * K * 2, kWsAlign);  // the transformed rows: hi and lo bf16 planes
+  return affine_prepare(c, "qgemv_affine4_rht", ws, ws_bytes, bl);
+}
+
+size_t qgemv_affine4_rht_workspace(int M, int N, int K) {
+  if (M < 1 || M > 8 || K < 64 || K % 64) return 0;
+  AffineCall c;
+  c.mode = QG_MODE_PLANES;
+  c.a.M = M;
+  c.a.N = N;
+  c.a.K = K;
+  c.reserve = 2 * align_up((size_t)M * K * 2, kWsAlign);
+  return N < 1 ? 0 : affine_query(c, "qgemv_affine4_rht");
 }
 
 qg_status qg_check_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had, const uint32_t* codes,
-                                     const uint16_t* scales, const uint16_t* biases, uint16_t* y, int M, int N,
-                                     int K) {
+                                     const uint16_t* scales, const uint16_t* biases, uint16_t* y, int M, int N, int K,
+                                     const void* ws, size_t ws_bytes) {
   clear_err();
-  return do_check_qgemv_affine4_rht(x, signs, had, codes, scales, biases, y, M, N, K);
+  AffineCall c;
+  return prep_rht(x, signs, had, codes, scales, biases, y, M, N, K, ws, ws_bytes, c);
 }
 
 qg_status qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had, const uint32_t* codes,
                             const uint16_t* scales, const uint16_t* biases, uint16_t* y, int M, int N, int K,
-                            void* stream) {
+                            void* ws, size_t ws_bytes, void* stream) {
   clear_err();
-  qg_status st = do_check_qgemv_affine4_rht(x, signs, had, codes, scales, biases, y, M, N, K);
-  if (st) return st;
-  if (N == 0) return QG_OK;
+  AffineCall c;
+  qg_status st = prep_rht(x, signs, had, codes, scales, biases, y, M, N, K, ws, ws_bytes, c);
+  if (st || N == 0) return st;
   if ((st = check_device())) return st;
-  QgAffineArgs a{};
-  a.codes = codes;
-  a.scales = scales;
-  a.biases = biases;
-  a.y = y;
-  a.M = M;
-  a.N = N;
-  a.K = K;
-  const size_t plane = (size_t)M * K * 2;
-  const size_t plane_al = (plane + 255) / 256 * 256;
   hipStream_t s = (hipStream_t)stream;
-  return run_affine(QG_MODE_PLANES, a, s, "qgemv_affine4_rht", 2 * plane_al,
-                    [&](unsigned char* ws, QgAffineArgs& args) {
-                      uint16_t* hi = reinterpret_cast<uint16_t*>(ws);
-                      uint16_t* lo = reinterpret_cast<uint16_t*>(ws + plane_al);
-                      args.x = hi;
-                      args.x_lo = lo;
-                      return qg_launch_rht(x, signs, had, M, K, hi, lo, s);
-                    });
+  const size_t plane_al = align_up((size_t)M * K * 2, kWsAlign);
+  return affine_launch(c, "qgemv_affine4_rht", ws, s, [&](unsigned char* base, QgAffineArgs& args) {
+    uint16_t* hi = reinterpret_cast<uint16_t*>(base);
+    uint16_t* lo = reinterpret_cast<uint16_t*>(base + plane_al);
+    args.x = hi;
+    args.x_lo = lo;
+    return qg_launch_rht(x, signs, had, M, K, hi, lo, s);
+  });
 }
 
+// --------------------------------------------------------------- tile order --
 size_t qg_tiled_bytes(int N, int K, size_t* sb_bytes) {
   if (N < 1 || K <= 0 || K % 512 != 0) {
     if (sb_bytes) *sb_bytes = 0;
@@ -866,22 +1064,13 @@ qg_status affine4_tile_pack(const uint32_t* codes, const uint16_t* scales, const
                   "affine4_tile_pack");
 }
 
-qg_status qg_check_qgemv_affine4_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, uint16_t* y,
-                                       int M, int N, int K) {
-  clear_err();
-  const Buf out[] = {{y, (size_t)M * N * 2, "y"}};
-  qg_status st = do_check_tiled("qgemv_affine4_tiled", x, codes_t, sb_t, M, N, K, out, 1);
-  if (st) return st;
-  return check_ptr(out[0], 2, "qgemv_affine4_tiled");
-}
-
-qg_status qgemv_affine4_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, uint16_t* y, int M,
-                              int N, int K, void* stream) {
-  qg_status st = qg_check_qgemv_affine4_tiled(x, codes_t, sb_t, y, M, N, K);
-  if (st) return st;
-  if (N == 0) return QG_OK;
-  if ((st = check_device())) return st;
-  QgAffineArgs a{};
+static qg_status prep_affine4_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, uint16_t* y,
+                                    int M, int N, int K, const void* ws, size_t ws_bytes, AffineCall& c) {
+  BufList bl;
+  qg_status st = do_check_qgemv_affine4_tiled(x, codes_t, sb_t, y, M, N, K, &bl);
+  if (st || N == 0) return st;
+  c.mode = QG_MODE_PLAIN;
+  QgAffineArgs& a = c.a;
   a.x = x;
   a.codes = codes_t;
   a.scales = sb_t;
@@ -891,121 +1080,137 @@ qg_status qgemv_affine4_tiled(const uint16_t* x, const uint32_t* codes_t, const 
   a.M = M;
   a.N = N;
   a.K = K;
-  return run_affine(QG_MODE_PLAIN, a, (hipStream_t)stream, "qgemv_affine4_tiled");
+  return affine_prepare(c, "qgemv_affine4_tiled", ws, ws_bytes, bl);
 }
 
-qg_status qg_check_lmhead_argmax_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t,
-                                       float* logits, int32_t* ids, const int32_t* draft, int32_t* accepted, int M,
-                                       int V, int K) {
+size_t qgemv_affine4_tiled_workspace(int M, int N, int K) {
+  if (K % 512) return 0;
+  AffineCall c;
+  c.a.tiled = 1;
+  c.a.M = M;
+  c.a.N = N;
+  c.a.K = K;
+  return affine_query(c, "qgemv_affine4_tiled");
+}
+
+qg_status qg_check_qgemv_affine4_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, uint16_t* y,
+                                       int M, int N, int K, const void* ws, size_t ws_bytes) {
   clear_err();
-  const char* fn = "lmhead_argmax_tiled";
-  if (V < 1) return fail(QG_EINVAL, "%s: V=%d must be >= 1", fn, V);
-  if (!fits_lds_unsplit(M, K) && M >= 1 && M <= 8)
-    return fail(QG_EUNSUPPORTED, "%s: M=%d rows of K=%d do not fit the staged-activation LDS budget", fn, M, K);
-  const Buf out[] = {{logits, logits ? (size_t)M * V * 4 : 0, "logits"},
-                     {ids, (size_t)M * 4, "ids"},
-                     {accepted, accepted ? (size_t)4 : (size_t)0, "accepted"}};
-  qg_status st = do_check_tiled(fn, x, codes_t, sb_t, M, V, K, out, 3);
-  if (st) return st;
-  if ((st = check_ptr(out[1], 4, fn))) return st;
-  if (logits && (st = check_ptr(out[0], 4, fn))) return st;
-  if (accepted && (st = check_ptr(out[2], 4, fn))) return st;
-  const Buf dr = {draft, draft ? (size_t)M * 4 : 0, "draft"};
-  if (draft && (st = check_ptr(dr, 4, fn))) return st;
-  return check_alias(out, 3, &dr, 1, fn);
+  AffineCall c;
+  return prep_affine4_tiled(x, codes_t, sb_t, y, M, N, K, ws, ws_bytes, c);
 }
 
-qg_status lmhead_argmax_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, float* logits,
-                              int32_t* ids, const int32_t* draft, int32_t* accepted, int M, int V, int K,
-                              void* stream) {
-  qg_status st = qg_check_lmhead_argmax_tiled(x, codes_t, sb_t, logits, ids, draft, accepted, M, V, K);
-  if (st) return st;
-  if ((st = check_device())) return st;
-  QgAffineArgs a{};
-  a.x = x;
-  a.codes = codes_t;
-  a.scales = sb_t;
-  a.biases = sb_t;
-  a.tiled = 1;
-  a.logits = logits;
-  a.ids = ids;
-  a.draft = draft;
-  a.accepted = accepted;
-  a.M = M;
-  a.N = V;
-  a.K = K;
-  return run_affine(QG_MODE_LMHEAD, a, (hipStream_t)stream, "lmhead_argmax_tiled");
-}
-
-qg_status qg_check_rmsnorm_gateup_swiglu_tiled(const uint16_t* x, const uint16_t* gamma, float eps,
-                                                const uint32_t* codes_t, const uint16_t* sb_t, uint16_t* h, int M,
-                                                int I, int K) {
+qg_status qgemv_affine4_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, uint16_t* y, int M,
+                              int N, int K, void* ws, size_t ws_bytes, void* stream) {
   clear_err();
-  const char* fn = "rmsnorm_gateup_swiglu_tiled";
-  if (I < 1 || (long long)I * 2 * 16 > 0x7FFFFFFFLL) return fail(QG_EINVAL, "%s: I=%d out of range", fn, I);
-  if (!(eps > 0.0f) || eps != eps || eps > 3.0e38f) return fail(QG_EINVAL, "%s: eps must be positive and finite", fn);
-  const Buf out[] = {{h, (size_t)M * I * 2, "h"}};
-  qg_status st = do_check_tiled(fn, x, codes_t, sb_t, M, 2 * I, K, out, 1);
-  if (st) return st;
-  const Buf gm = {gamma, (size_t)K * 2, "gamma"};
-  if ((st = check_ptr(gm, 16, fn)) || (st = check_ptr(out[0], 2, fn))) return st;
-  return check_alias(out, 1, &gm, 1, fn);
+  AffineCall c;
+  qg_status st = prep_affine4_tiled(x, codes_t, sb_t, y, M, N, K, ws, ws_bytes, c);
+  if (st || N == 0) return st;
+  if ((st = check_device())) return st;
+  return affine_launch(c, "qgemv_affine4_tiled", ws, (hipStream_t)stream);
 }
 
-qg_status rmsnorm_gateup_swiglu_tiled(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes_t,
-                                      const uint16_t* sb_t, uint16_t* h, int M, int I, int K, void* stream) {
-  qg_status st = qg_check_rmsnorm_gateup_swiglu_tiled(x, gamma, eps, codes_t, sb_t, h, M, I, K);
-  if (st) return st;
-  if ((st = check_device())) return st;
-  QgAffineArgs a{};
+// ---------------------------------------------------- rmsnorm_gateup_swiglu --
+static void fill_gateup(AffineCall& c, const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes,
+                        const uint16_t* scales, const uint16_t* biases, uint16_t* h, int M, int I, int K, int tiled) {
+  c.mode = QG_MODE_GATEUP;
+  QgAffineArgs& a = c.a;
   a.x = x;
   a.gamma = gamma;
   a.eps = eps;
-  a.codes = codes_t;
-  a.scales = sb_t;
-  a.biases = sb_t;
-  a.tiled = 1;
-  a.y = h;
-  a.M = M;
-  a.N = 2 * I;  // the tile-order copy of the [2I][K] gate-then-up matrix
-  a.K = K;
-  return run_affine(QG_MODE_GATEUP, a, (hipStream_t)stream, "rmsnorm_gateup_swiglu_tiled");
-}
-
-qg_status rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes_gu,
-                                const uint16_t* scales_gu, const uint16_t* biases_gu, uint16_t* h, int M, int I,
-                                int K, void* stream) {
-  clear_err();
-  qg_status st = do_check_gateup(x, gamma, eps, codes_gu, scales_gu, biases_gu, h, M, I, K);
-  if (st) return st;
-  if (I == 0) return QG_OK;
-  if ((st = check_device())) return st;
-  QgAffineArgs a{};
-  a.x = x;
-  a.gamma = gamma;
-  a.eps = eps;
-  a.codes = codes_gu;
-  a.scales = scales_gu;
-  a.biases = biases_gu;
+  a.codes = codes;
+  a.scales = scales;
+  a.biases = biases;
+  a.tiled = tiled;
   a.y = h;
   a.M = M;
   a.N = 2 * I;  // gate rows then up rows, one matrix for the projection kernel
   a.K = K;
-  return run_affine(QG_MODE_GATEUP, a, (hipStream_t)stream, "rmsnorm_gateup_swiglu");
 }
 
-qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
-                        float* logits, int32_t* ids, const int32_t* draft, int32_t* accepted, int M, int V, int K,
-                        void* stream) {
+static qg_status prep_gateup(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes,
+                             const uint16_t* scales, const uint16_t* biases, uint16_t* h, int M, int I, int K,
+                             const void* ws, size_t ws_bytes, AffineCall& c) {
+  BufList bl;
+  qg_status st = do_check_gateup(x, gamma, eps, codes, scales, biases, h, M, I, K, &bl);
+  if (st || I == 0) return st;
+  fill_gateup(c, x, gamma, eps, codes, scales, biases, h, M, I, K, 0);
+  return affine_prepare(c, "rmsnorm_gateup_swiglu", ws, ws_bytes, bl);
+}
+
+static qg_status prep_gateup_tiled(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes_t,
+                                   const uint16_t* sb_t, uint16_t* h, int M, int I, int K, const void* ws,
+                                   size_t ws_bytes, AffineCall& c) {
+  BufList bl;
+  qg_status st = do_check_gateup_tiled(x, gamma, eps, codes_t, sb_t, h, M, I, K, &bl);
+  if (st) return st;
+  fill_gateup(c, x, gamma, eps, codes_t, sb_t, sb_t, h, M, I, K, 1);
+  return affine_prepare(c, "rmsnorm_gateup_swiglu_tiled", ws, ws_bytes, bl);
+}
+
+size_t rmsnorm_gateup_swiglu_workspace(int M, int I, int K) {
+  AffineCall c;
+  fill_gateup(c, nullptr, nullptr, 1e-6f, nullptr, nullptr, nullptr, nullptr, M, I, K, 0);
+  return I < 1 ? 0 : affine_query(c, "rmsnorm_gateup_swiglu");
+}
+
+size_t rmsnorm_gateup_swiglu_tiled_workspace(int M, int I, int K) {
+  if (K % 512) return 0;
+  AffineCall c;
+  fill_gateup(c, nullptr, nullptr, 1e-6f, nullptr, nullptr, nullptr, nullptr, M, I, K, 1);
+  return I < 1 ? 0 : affine_query(c, "rmsnorm_gateup_swiglu_tiled");
+}
+
+qg_status qg_check_rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma, float eps,
+                                         const uint32_t* codes_gu, const uint16_t* scales_gu,
+                                         const uint16_t* biases_gu, uint16_t* h, int M, int I, int K, const void* ws,
+                                         size_t ws_bytes) {
   clear_err();
-  qg_status st = do_check_lmhead(x, codes, scales, biases, logits, ids, draft, accepted, M, V, K);
+  AffineCall c;
+  return prep_gateup(x, gamma, eps, codes_gu, scales_gu, biases_gu, h, M, I, K, ws, ws_bytes, c);
+}
+
+qg_status rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes_gu,
+                                const uint16_t* scales_gu, const uint16_t* biases_gu, uint16_t* h, int M, int I,
+                                int K, void* ws, size_t ws_bytes, void* stream) {
+  clear_err();
+  AffineCall c;
+  qg_status st = prep_gateup(x, gamma, eps, codes_gu, scales_gu, biases_gu, h, M, I, K, ws, ws_bytes, c);
+  if (st || I == 0) return st;
+  if ((st = check_device())) return st;
+  return affine_launch(c, "rmsnorm_gateup_swiglu", ws, (hipStream_t)stream);
+}
+
+qg_status qg_check_rmsnorm_gateup_swiglu_tiled(const uint16_t* x, const uint16_t* gamma, float eps,
+                                               const uint32_t* codes_t, const uint16_t* sb_t, uint16_t* h, int M,
+                                               int I, int K, const void* ws, size_t ws_bytes) {
+  clear_err();
+  AffineCall c;
+  return prep_gateup_tiled(x, gamma, eps, codes_t, sb_t, h, M, I, K, ws, ws_bytes, c);
+}
+
+qg_status rmsnorm_gateup_swiglu_tiled(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes_t,
+                                      const uint16_t* sb_t, uint16_t* h, int M, int I, int K, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  clear_err();
+  AffineCall c;
+  qg_status st = prep_gateup_tiled(x, gamma, eps, codes_t, sb_t, h, M, I, K, ws, ws_bytes, c);
   if (st) return st;
   if ((st = check_device())) return st;
-  QgAffineArgs a{};
+  return affine_launch(c, "rmsnorm_gateup_swiglu_tiled", ws, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------- lmhead_argmax --
+static void fill_lmhead(AffineCall& c, const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                        const uint16_t* biases, float* logits, int32_t* ids, const int32_t* draft, int32_t* accepted,
+                        int M, int V, int K, int tiled) {
+  c.mode = QG_MODE_LMHEAD;
+  QgAffineArgs& a = c.a;
   a.x = x;
   a.codes = codes;
   a.scales = scales;
   a.biases = biases;
+  a.tiled = tiled;
   a.logits = logits;
   a.ids = ids;
   a.draft = draft;
@@ -1013,111 +1218,218 @@ qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes, const uint16_t
   a.M = M;
   a.N = V;
   a.K = K;
-  return run_affine(QG_MODE_LMHEAD, a, (hipStream_t)stream, "lmhead_argmax");
+}
+
+static qg_status prep_lmhead(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                             float* logits, int32_t* ids, const int32_t* draft, int32_t* accepted, int M, int V,
+                             int K, const void* ws, size_t ws_bytes, AffineCall& c) {
+  BufList bl;
+  qg_status st = do_check_lmhead(x, codes, scales, biases, logits, ids, draft, accepted, M, V, K, &bl);
+  if (st) return st;
+  fill_lmhead(c, x, codes, scales, biases, logits, ids, draft, accepted, M, V, K, 0);
+  return affine_prepare(c, "lmhead_argmax", ws, ws_bytes, bl);
+}
+
+static qg_status prep_lmhead_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, float* logits,
+                                   int32_t* ids, const int32_t* draft, int32_t* accepted, int M, int V, int K,
+                                   const void* ws, size_t ws_bytes, AffineCall& c) {
+  BufList bl;
+  qg_status st = do_check_lmhead_tiled(x, codes_t, sb_t, logits, ids, draft, accepted, M, V, K, &bl);
+  if (st) return st;
+  fill_lmhead(c, x, codes_t, sb_t, sb_t, logits, ids, draft, accepted, M, V, K, 1);
+  return affine_prepare(c, "lmhead_argmax_tiled", ws, ws_bytes, bl);
+}
+
+size_t lmhead_argmax_workspace(int M, int V, int K) {
+  AffineCall c;
+  fill_lmhead(c, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M, V, K, 0);
+  return affine_query(c, "lmhead_argmax");
+}
+
+size_t lmhead_argmax_tiled_workspace(int M, int V, int K) {
+  if (K % 512) return 0;
+  AffineCall c;
+  fill_lmhead(c, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M, V, K, 1);
+  return affine_query(c, "lmhead_argmax_tiled");
+}
+
+qg_status qg_check_lmhead_argmax(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                                 const uint16_t* biases, float* logits, int32_t* ids, const int32_t* draft,
+                                 int32_t* accepted, int M, int V, int K, const void* ws, size_t ws_bytes) {
+  clear_err();
+  AffineCall c;
+  return prep_lmhead(x, codes, scales, biases, logits, ids, draft, accepted, M, V, K, ws, ws_bytes, c);
+}
+
+qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                        float* logits, int32_t* ids, const int32_t* draft, int32_t* accepted, int M, int V, int K,
+                        void* ws, size_t ws_bytes, void* stream) {
+  clear_err();
+  AffineCall c;
+  qg_status st = prep_lmhead(x, codes, scales, biases, logits, ids, draft, accepted, M, V, K, ws, ws_bytes, c);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  return affine_launch(c, "lmhead_argmax", ws, (hipStream_t)stream);
+}
+
+qg_status qg_check_lmhead_argmax_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t,
+                                       float* logits, int32_t* ids, const int32_t* draft, int32_t* accepted, int M,
+                                       int V, int K, const void* ws, size_t ws_bytes) {
+  clear_err();
+  AffineCall c;
+  return prep_lmhead_tiled(x, codes_t, sb_t, logits, ids, draft, accepted, M, V, K, ws, ws_bytes, c);
+}
+
+qg_status lmhead_argmax_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, float* logits,
+                              int32_t* ids, const int32_t* draft, int32_t* accepted, int M, int V, int K, void* ws,
+                              size_t ws_bytes, void* stream) {
+  clear_err();
+  AffineCall c;
+  qg_status st = prep_lmhead_tiled(x, codes_t, sb_t, logits, ids, draft, accepted, M, V, K, ws, ws_bytes, c);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  return affine_launch(c, "lmhead_argmax_tiled", ws, (hipStream_t)stream);
+}
+
+// --------------------------------------------------------------- lmhead_topk --
+static qg_status prep_topk(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                           float* logits, int32_t* ids, float* vals, int M, int V, int K, int k, const void* ws,
+                           size_t ws_bytes, AffineCall& c) {
+  BufList bl;
+  qg_status st = do_check_lmhead_topk(x, codes, scales, biases, logits, ids, vals, M, V, K, k, &bl);
+  if (st) return st;
+  fill_lmhead(c, x, codes, scales, biases, logits, ids, nullptr, nullptr, M, V, K, 0);
+  c.a.topk = k;
+  c.a.topk_vals = vals;
+  return affine_prepare(c, "lmhead_topk", ws, ws_bytes, bl);
+}
+
+size_t lmhead_topk_workspace(int M, int V, int K, int k, int logits_kept) {
+  if (k < 1 || k > kTopkMax) return 0;
+  AffineCall c;
+  fill_lmhead(c, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M, V, K, 0);
+  c.a.topk = k;
+  c.a.logits = logits_kept ? reinterpret_cast<float*>(kWsAlign) : nullptr;  // only its presence matters here
+  return affine_query(c, "lmhead_topk");
 }
 
 qg_status qg_check_lmhead_topk(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
                                const uint16_t* biases, float* logits, int32_t* ids, float* vals, int M, int V, int K,
-                               int k) {
+                               int k, const void* ws, size_t ws_bytes) {
   clear_err();
-  return do_check_lmhead_topk(x, codes, scales, biases, logits, ids, vals, M, V, K, k);
+  AffineCall c;
+  return prep_topk(x, codes, scales, biases, logits, ids, vals, M, V, K, k, ws, ws_bytes, c);
 }
 
 qg_status lmhead_topk(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
-                      float* logits, int32_t* ids, float* vals, int M, int V, int K, int k, void* stream) {
+                      float* logits, int32_t* ids, float* vals, int M, int V, int K, int k, void* ws, size_t ws_bytes,
+                      void* stream) {
   clear_err();
-  qg_status st = do_check_lmhead_topk(x, codes, scales, biases, logits, ids, vals, M, V, K, k);
+  AffineCall c;
+  qg_status st = prep_topk(x, codes, scales, biases, logits, ids, vals, M, V, K, k, ws, ws_bytes, c);
   if (st) return st;
   if ((st = check_device())) return st;
-  QgAffineArgs a{};
-  a.x = x;
-  a.codes = codes;
-  a.scales = scales;
-  a.biases = biases;
-  a.logits = logits;
-  a.ids = ids;
-  a.topk = k;
-  a.topk_vals = vals;
-  a.M = M;
-  a.N = V;
-  a.K = K;
-  return run_affine(QG_MODE_LMHEAD, a, (hipStream_t)stream, "lmhead_topk");
+  return affine_launch(c, "lmhead_topk", ws, (hipStream_t)stream);
 }
 
-qg_status qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K, void* stream) {
-  clear_err();
-  qg_status st = do_check_qgemv_q4k(x, blocks, y, M, N, K);
-  if (st) return st;
-  if (N == 0) return QG_OK;
-  if ((st = check_device())) return st;
-  QgQ4kArgs a{};
+// ------------------------------------------------------- qgemv_q4k / q6k --
+static qg_status prep_q4k(int bpb, const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K,
+                          const void* ws, size_t ws_bytes, Q4kCall& c) {
+  const char* fn = bpb == 144 ? "qgemv_q4k" : "qgemv_q6k";
+  BufList bl;
+  qg_status st = bpb == 144 ? do_check_qgemv_q4k(x, blocks, y, M, N, K, &bl)
+                            : do_check_qgemv_q6k(x, blocks, y, M, N, K, &bl);
+  if (st || N == 0) return st;
+  QgQ4kArgs& a = c.a;
   a.x = x;
   a.blocks = blocks;
   a.y = y;
   a.M = M;
   a.N = N;
   a.K = K;
-  a.nchunks = K / 256;
-  a.ntiles = (N + 15) / 16;
-  a.waves = kWaves;
-  const size_t per = q4k_lds_per_sb(M);
-  const int cps_max = (int)std::max<size_t>(1, std::min<size_t>((size_t)a.nchunks, (kQ4kLdsBudget - 16) / per));
-  Plan pl = plan_split(a.ntiles, a.nchunks, cps_max, true);
-  a.S = pl.S;
-  a.cps = pl.cps;
-  a.tpw = pl.tpw;
-  a.rgroups = pl.rgroups;
-  unsigned char* ws = nullptr;
-  const size_t part_bytes = (a.S > 1) ? (size_t)a.S * M * N * 4 : 0;
-  if ((st = get_workspace((hipStream_t)stream, part_bytes, &ws))) return st;
-  a.part = reinterpret_cast<float*>(ws);
-  return launched(qg_launch_q4k(a, 16 + (size_t)a.cps * per, (hipStream_t)stream), "qgemv_q4k");
+  q4k_layout(c, bpb);
+  return check_ws(fn, ws, ws_bytes, ws_total(c.scratch), bl.b, bl.n);
 }
 
-qg_status qg_check_qgemv_q6k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K) {
-  clear_err();
-  return do_check_qgemv_q6k(x, blocks, y, M, N, K);
+static size_t q4k_query(int bpb, int M, int N, int K) {
+  if (M < 1 || M > 8 || N < 1 || K < 256 || K % 256) return 0;
+  Q4kCall c;
+  c.a.M = M;
+  c.a.N = N;
+  c.a.K = K;
+  q4k_layout(c, bpb);
+  return ws_total(c.scratch);
 }
 
-qg_status qgemv_q6k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K, void* stream) {
+size_t qgemv_q4k_workspace(int M, int N, int K) { return q4k_query(144, M, N, K); }
+size_t qgemv_q6k_workspace(int M, int N, int K) { return q4k_query(210, M, N, K); }
+
+qg_status qg_check_qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K,
+                             const void* ws, size_t ws_bytes) {
   clear_err();
-  qg_status st = do_check_qgemv_q6k(x, blocks, y, M, N, K);
-  if (st) return st;
-  if (N == 0) return QG_OK;
+  Q4kCall c;
+  return prep_q4k(144, x, blocks, y, M, N, K, ws, ws_bytes, c);
+}
+
+qg_status qg_check_qgemv_q6k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K,
+                             const void* ws, size_t ws_bytes) {
+  clear_err();
+  Q4kCall c;
+  return prep_q4k(210, x, blocks, y, M, N, K, ws, ws_bytes, c);
+}
+
+qg_status qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K, void* ws,
+                    size_t ws_bytes, void* stream) {
+  clear_err();
+  Q4kCall c;
+  qg_status st = prep_q4k(144, x, blocks, y, M, N, K, ws, ws_bytes, c);
+  if (st || N == 0) return st;
   if ((st = check_device())) return st;
-  QgQ4kArgs a{};
-  a.x = x;
-  a.blocks = blocks;
-  a.y = y;
-  a.M = M;
-  a.N = N;
-  a.K = K;
-  a.nchunks = K / 256;
-  a.ntiles = (N + 15) / 16;
-  a.waves = kWaves;
-  const size_t per = q6k_lds_per_sb(M);
-  const int cps_max = (int)std::max<size_t>(1, std::min<size_t>((size_t)a.nchunks, (kQ4kLdsBudget - 16) / per));
-  Plan pl = plan_split(a.ntiles, a.nchunks, cps_max, true);
-  a.S = pl.S;
-  a.cps = pl.cps;
-  a.tpw = pl.tpw;
-  a.rgroups = pl.rgroups;
-  unsigned char* ws = nullptr;
-  const size_t part_bytes = (a.S > 1) ? (size_t)a.S * M * N * 4 : 0;
-  if ((st = get_workspace((hipStream_t)stream, part_bytes, &ws))) return st;
-  a.part = reinterpret_cast<float*>(ws);
-  return launched(qg_launch_q6k(a, 16 + (size_t)a.cps * per, (hipStream_t)stream), "qgemv_q6k");
+  if (ws) c.a.part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + kWsHeader);
+  return launched(qg_launch_q4k(c.a, c.lds, (hipStream_t)stream), "qgemv_q4k");
+}
+
+qg_status qgemv_q6k(const uint16_t* x, const uint8_t* blocks, uint16_t* y, int M, int N, int K, void* ws,
+                    size_t ws_bytes, void* stream) {
+  clear_err();
+  Q4kCall c;
+  qg_status st = prep_q4k(210, x, blocks, y, M, N, K, ws, ws_bytes, c);
+  if (st || N == 0) return st;
+  if ((st = check_device())) return st;
+  if (ws) c.a.part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + kWsHeader);
+  return launched(qg_launch_q6k(c.a, c.lds, (hipStream_t)stream), "qgemv_q6k");
+}
+
+// --------------------------------------------------------- moe_expert_qgemv --
+static qg_status prep_moe(const uint16_t* x, const float* logits, int top_k, const uint8_t* w_gu,
+                          const uint8_t* w_down, uint16_t* y, int32_t* out_ids, float* out_w, int E, int D, int I,
+                          const void* ws, size_t ws_bytes) {
+  BufList bl;
+  qg_status st = do_check_moe(x, logits, top_k, w_gu, w_down, y, out_ids, out_w, E, D, I, &bl);
+  if (st) return st;
+  return check_ws("moe_expert_qgemv", ws, ws_bytes, ws_total(moe_scratch(top_k, I)), bl.b, bl.n);
+}
+
+size_t moe_expert_qgemv_workspace(int top_k, int E, int D, int I) {
+  if (top_k < 1 || top_k > 64 || top_k > E || I < 256 || I % 256 || D < 256 || D % 256) return 0;
+  return ws_total(moe_scratch(top_k, I));
+}
+
+qg_status qg_check_moe_expert_qgemv(const uint16_t* x, const float* router_logits, int top_k, const uint8_t* w_gu,
+                                    const uint8_t* w_down, uint16_t* y, int32_t* out_ids, float* out_w, int E, int D,
+                                    int I, const void* ws, size_t ws_bytes) {
+  clear_err();
+  return prep_moe(x, router_logits, top_k, w_gu, w_down, y, out_ids, out_w, E, D, I, ws, ws_bytes);
 }
 
 qg_status moe_expert_qgemv(const uint16_t* x, const float* router_logits, int top_k, const uint8_t* w_gu,
                            const uint8_t* w_down, uint16_t* y, int32_t* out_ids, float* out_w, int E, int D, int I,
-                           void* stream) {
+                           void* ws, size_t ws_bytes, void* stream) {
   clear_err();
-  qg_status st = do_check_moe(x, router_logits, top_k, w_gu, w_down, y, out_ids, out_w, E, D, I);
+  qg_status st = prep_moe(x, router_logits, top_k, w_gu, w_down, y, out_ids, out_w, E, D, I, ws, ws_bytes);
   if (st) return st;
   if ((st = check_device())) return st;
-  unsigned char* ws = nullptr;
-  if ((st = get_workspace((hipStream_t)stream, 512 + (size_t)top_k * I * 2, &ws))) return st;
+  unsigned char* base = static_cast<unsigned char*>(ws) + kWsHeader;
   QgMoeArgs a{};
   a.x = x;
   a.logits = router_logits;
@@ -1127,9 +1439,9 @@ qg_status moe_expert_qgemv(const uint16_t* x, const float* router_logits, int to
   a.y = y;
   a.out_ids = out_ids;
   a.out_w = out_w;
-  a.route_ids = reinterpret_cast<int32_t*>(ws);      // 64 entries
-  a.route_w = reinterpret_cast<float*>(ws + 256);     // 64 entries
-  a.h = reinterpret_cast<uint16_t*>(ws + 512);
+  a.route_ids = reinterpret_cast<int32_t*>(base);   // 64 entries
+  a.route_w = reinterpret_cast<float*>(base + 256);  // 64 entries
+  a.h = reinterpret_cast<uint16_t*>(base + kMoeRouteBytes);
   a.E = E;
   a.D = D;
   a.I = I;

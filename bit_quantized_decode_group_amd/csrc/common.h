@@ -204,11 +204,13 @@ int qg_launch_moe(const QgMoeArgs& a, hipStream_t stream);
 int qg_launch_tile_pack(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, uint32_t* codes_t,
                         uint16_t* sb_t, int N, int K, hipStream_t stream);
 // The persistent MLP block (mlp.hip): pa = gate/up plan (y = h), pc = down
-// plan (x = h); state: qg_mlp_state_bytes(...) zeroed bytes (the grid
-// barrier's counters; failure flag at byte 16); grid a multiple of 32.
-size_t qg_mlp_state_bytes(int D, int I, int S_down, int* off_h, int* off_y, int* off_r);
-int qg_launch_mlp(const QgAffineArgs& pa, const QgAffineArgs& pc, unsigned char* state, int off_h, int off_y,
-                  int off_r, int spin_limit, int grid, size_t lds, hipStream_t stream);
+// plan (x = h); state: qg_mlp_state_bytes() bytes, zero when the launch starts
+// and left zero by it (the grid barrier's counters; failure flag of the launch
+// at byte 16, count of failed launches at byte 20); grid a multiple of 32,
+// every workgroup resident (cooperative launch).
+size_t qg_mlp_state_bytes();
+int qg_launch_mlp(const QgAffineArgs& pa, const QgAffineArgs& pc, unsigned char* state, int spin_limit, int grid,
+                  size_t lds, hipStream_t stream);
 const void* qg_mlp_kernel(int M);  // the kernel instance for M rows (occupancy queries)
 // Input randomised Hadamard transform: x [M][K] bf16 and signs [K] to the hi
 // and lo bf16 planes of (1/sqrt(had)) H_had diag(s) x, blockwise along K.

@@ -39,21 +39,22 @@ __device__ __forceinline__ float ld_coh(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Two-level grid barrier on counters that only grow.  The grid is split into
-// kBarGroups groups of equal size; a workgroup adds one to its group's
-// counter, the last arrival of a group adds one to the top counter, and the
-// last group to arrive writes the barrier's sequence number into every
-// group's release word.  Each workgroup then polls its own group's release
-// word, so no single address is polled by the whole grid (a hot address
-// slows every load that maps to its memory channel).  Counters are multiples
-// of their group count whenever no launch is running, so they need no reset.
-// Arrival and wait are separate so that a workgroup can issue loads that do
-// not depend on the other workgroups in between (waiting for the stores to
-// complete, vmcnt(0), would also wait for such loads).  The wait is bounded:
-// after spin_limit polls the workgroup records the failure in *err and goes on.
+// Two-level grid barrier.  The grid is split into kBarGroups groups of equal
+// size; a workgroup adds one to its group's counter, the last arrival of a
+// group adds one to the top counter, and the last group to arrive writes the
+// barrier's sequence number into every group's release word.  Each workgroup
+// then polls its own group's release word, so no single address is polled by
+// the whole grid (a hot address slows every load that maps to its memory
+// channel).  Arrival and wait are separate so that a workgroup can issue
+// loads that do not depend on the other workgroups in between (waiting for
+// the stores to complete, vmcnt(0), would also wait for such loads).  The wait
+// is bounded: after spin_limit polls the workgroup records the failure and
+// goes on.  The state lives in the caller's workspace, is zero when a launch
+// starts, and the last workgroup to leave the launch sets it back to zero.
 //
-// Barrier state (bytes): [0, 8) top counter, [16, 20) failure flag; group
-// g at 256 * (g + 1): [0, 8) arrival counter, [8, 16) release word.
+// Barrier state (bytes): [0, 8) top counter, [16, 20) failure flag of this
+// launch, [20, 24) failed launches not yet reported, [32, 40) exit counter;
+// group g at 256 * (g + 1): [0, 8) arrival counter, [8, 16) release word.
 constexpr int kBarGroups = 32;
 
 __device__ __forceinline__ void barrier_arrive(unsigned char* bar, unsigned long long* target_lds) {
@@ -354,23 +355,66 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   for (int job = blockIdx.x; job < jc; job += P) run_job<M, QG_MODE_PLAIN, R>(pc, job, smem, pre, job == (int)blockIdx.x);
   barrier_arrive(bar, &target);
   barrier_wait(bar, &target, spin_limit);
-  // phase D (the same arithmetic as k_split_reduce for a plain projection)
+  // phase D (the same arithmetic as k_split_reduce for a plain projection);
+  // agent-scope stores, so that a failed launch's NaN fill below is ordered
+  // after them
   {
     const int n_out = pc.M * pc.N;
     const size_t stride = (size_t)pc.M * pc.N;
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_out; i += P * blockDim.x)
-      pc.y[i] = f32_to_bf16_bits(sum_slices(pc.part, stride, (size_t)i, pc.S));
+      __hip_atomic_store(pc.y + i, f32_to_bf16_bits(sum_slices(pc.part, stride, (size_t)i, pc.S)), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // exit: the last workgroup to leave (every other one has passed its last
+  // wait and its stores have completed) fills h and y with NaN if a wait of
+  // this launch gave up, counts the failure, and sets the barrier state back
+  // to zero for the next launch on this workspace
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  __shared__ int last_out;
+  if (threadIdx.x == 0) {
+    const unsigned long long a = __hip_atomic_fetch_add(reinterpret_cast<unsigned long long*>(bar + 32), 1ull,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_out = (a == (unsigned long long)gridDim.x - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!last_out) return;
+  const unsigned failed = __hip_atomic_load(reinterpret_cast<unsigned*>(bar + 16), __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+  if (failed) {
+    const uint16_t qnan = 0x7FC0;
+    for (int i = threadIdx.x; i < pc.M * pc.N; i += blockDim.x)
+      __hip_atomic_store(pc.y + i, qnan, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = threadIdx.x; i < pa.M * (pa.N / 2); i += blockDim.x)
+      __hip_atomic_store(pa.y + i, qnan, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (threadIdx.x < kBarGroups) {
+    unsigned long long* g = reinterpret_cast<unsigned long long*>(bar + 256 * (threadIdx.x + 1));
+    __hip_atomic_store(g, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(g + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (threadIdx.x == 0) {
+    if (failed) __hip_atomic_fetch_add(reinterpret_cast<unsigned*>(bar + 20), 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(reinterpret_cast<unsigned*>(bar + 16), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(bar), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(bar + 32), 0ull, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 }  // namespace qg
 
 namespace {
+// A cooperative launch: the runtime refuses a grid whose workgroups cannot
+// all be resident at once, instead of letting the grid barrier wait for
+// workgroups that are not running.
 template <int M>
-int launch_mlp_m(const QgAffineArgs& pa, const QgAffineArgs& pc, unsigned char* bar, int spin_limit, int grid,
-                 size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL(qg::k_mlp_block<M>, dim3((unsigned)grid), dim3(256), lds, st, pa, pc, bar, spin_limit);
-  return (int)hipGetLastError();
+int launch_mlp_m(QgAffineArgs pa, QgAffineArgs pc, unsigned char* bar, int spin_limit, int grid, size_t lds,
+                 hipStream_t st) {
+  void* args[] = {&pa, &pc, &bar, &spin_limit};
+  return (int)hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&qg::k_mlp_block<M>), dim3((unsigned)grid),
+                                         dim3(256), args, (unsigned)lds, st);
 }
 }  // namespace
 
@@ -388,13 +432,10 @@ const void* qg_mlp_kernel(int M) {
   }
 }
 
-size_t qg_mlp_state_bytes(int, int, int, int* off_h, int* off_y, int* off_r) {
-  *off_h = *off_y = *off_r = 0;
-  return (size_t)256 * (qg::kBarGroups + 1);
-}
+size_t qg_mlp_state_bytes() { return (size_t)256 * (qg::kBarGroups + 1); }
 
-int qg_launch_mlp(const QgAffineArgs& pa, const QgAffineArgs& pc, unsigned char* bar, int, int, int, int spin_limit,
-                  int grid, size_t lds, hipStream_t st) {
+int qg_launch_mlp(const QgAffineArgs& pa, const QgAffineArgs& pc, unsigned char* bar, int spin_limit, int grid,
+                  size_t lds, hipStream_t st) {
   if (grid % qg::kBarGroups != 0) return (int)hipErrorInvalidValue;
   switch (pa.M) {
     case 1: return launch_mlp_m<1>(pa, pc, bar, spin_limit, grid, lds, st);

@@ -29,7 +29,8 @@
  * Common conventions
  *   * bf16 and fp16 values are passed as uint16_t bit patterns.
  *   * Every pointer is caller-owned device memory (hipMalloc / torch CUDA
- *     tensors).  X, codes and Q4_K blocks must be 16-byte aligned; float and
+ *     tensors), except the workspace, which is also caller-owned device
+ *     memory (see below).  X, codes and Q4_K blocks must be 16-byte aligned; float and
  *     int32 buffers 4-byte aligned; other bf16 buffers 2-byte aligned.
  *   * `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *     work and return; results are ready when the stream is synchronised.
@@ -37,15 +38,26 @@
  *     its checks writes nothing (the refuse-before-touching-weights and
  *     explicit-error conventions of the TensorFold and runNburn pages).
  *     Outputs may not overlap any input or each other (QG_EALIAS).
- *   * The library keeps one scratch workspace per (device, stream), allocated
- *     on first use (split-K partial sums, per-workgroup argmax keys, MoE expert
- *     activations).  Two calls on the same stream are ordered by the stream;
- *     calls on different streams use different workspaces.  A call that must
- *     grow the workspace synchronises that stream once.  A call may enqueue
- *     more than one kernel (a split-K or argmax reduction follows its main
- *     kernel on the same stream), so calls that share a stream must be issued
- *     by one host thread at a time: interleaved launches of two calls on one
- *     stream would share the workspace between their kernels.
+ *   * Workspace.  Entry points that need device scratch (split-K partial
+ *     sums, per-workgroup argmax keys, top-k candidates, the RHT's transformed
+ *     rows, MoE routing and expert activations, a grid barrier's counters)
+ *     take it from the caller as (ws, ws_bytes): the library never allocates,
+ *     frees or synchronises on a call.  <entry>_workspace(...) returns the
+ *     bytes a call of that shape needs (host-only, no GPU access); 0 means
+ *     none, and ws may then be NULL.  The size is the same on every gfx950
+ *     device.  ws must be 256-byte aligned, at least that large, and may not
+ *     overlap any input or output (QG_EALIAS).  A workspace must be zeroed
+ *     once (e.g. hipMemset) before its first use: its first
+ *     qg_workspace_header_bytes() bytes hold state that some entry points
+ *     need to find at zero and always leave at zero, so one workspace can
+ *     serve every entry point and every shape, one call at a time.  The
+ *     contents carry no results between calls.  Calls that may run at the
+ *     same time (different streams, or graphs replayed concurrently) need
+ *     different workspaces.  With that, calls are stateless: any number of
+ *     host threads may issue calls, and the calls can be captured into a HIP
+ *     graph on any stream, also as the stream's first work.
+ *   * A call may enqueue more than one kernel (a split-K or argmax reduction
+ *     follows its main kernel on the same stream).
  *   * Floating point: fp32 accumulation; bf16 outputs rounded to nearest even.
  *     Results are deterministic: the same inputs give the same bytes on every
  *     call (fixed reduction order, no atomics).
@@ -66,12 +78,13 @@ typedef int32_t qg_status;
 #define QG_EALIAS (-2)        /* an output overlaps an input or another output  */
 #define QG_EUNSUPPORTED (-3)  /* valid request with no kernel instance          */
 #define QG_EHIP (-4)          /* HIP runtime or launch error                    */
-#define QG_ENOMEM (-5)        /* workspace allocation failed                    */
 
 /* Static description of a status code. */
 const char* qg_status_string(qg_status status);
 /* Detail of the most recent failure on the calling thread ("" if none). */
 const char* qg_last_error(void);
+/* Bytes at the start of every workspace that hold zero-initialised state. */
+size_t qg_workspace_header_bytes(void);
 
 /*
  * qgemv_affine4 -- Y = X . dequant(W)^T for affine4 weights.
@@ -79,10 +92,14 @@ const char* qg_last_error(void);
  *   codes  uint32 [N][K/8]; scales, biases bf16 [N][K/64]
  *   y      bf16 [M][N]           output
  *   1 <= M <= 8; N >= 0 (N = 0 does nothing); K > 0, K % 64 == 0.
+ *   ws: split-K partial sums when K is long enough to be split:
+ *   qgemv_affine4_workspace(M, N, K) bytes (0 when it is not split).
  */
 qg_status qgemv_affine4(const uint16_t* x, const uint32_t* codes,
                         const uint16_t* scales, const uint16_t* biases,
-                        uint16_t* y, int M, int N, int K, void* stream);
+                        uint16_t* y, int M, int N, int K, void* ws, size_t ws_bytes,
+                        void* stream);
+size_t qgemv_affine4_workspace(int M, int N, int K);
 
 /*
  * qgemv_affine4_rht -- the projection of an input-side randomised Hadamard
@@ -102,7 +119,9 @@ qg_status qgemv_affine4(const uint16_t* x, const uint32_t* codes,
 qg_status qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had,
                             const uint32_t* codes, const uint16_t* scales,
                             const uint16_t* biases, uint16_t* y, int M, int N,
-                            int K, void* stream);
+                            int K, void* ws, size_t ws_bytes,
+                            void* stream);
+size_t qgemv_affine4_rht_workspace(int M, int N, int K);
 
 /*
  * qgemv_affine8 -- Y = X . dequant8(W)^T for MLX-style affine 8-bit weights
@@ -118,7 +137,9 @@ qg_status qgemv_affine4_rht(const uint16_t* x, const int8_t* signs, int had,
  */
 qg_status qgemv_affine8(const uint16_t* x, const uint32_t* codes,
                         const uint16_t* scales, const uint16_t* biases,
-                        uint16_t* y, int M, int N, int K, void* stream);
+                        uint16_t* y, int M, int N, int K, void* ws, size_t ws_bytes,
+                        void* stream);
+size_t qgemv_affine8_workspace(int M, int N, int K);
 
 /*
  * mlp_block_affine4_tiled -- the whole MLP block in one persistent launch
@@ -132,15 +153,15 @@ qg_status qgemv_affine8(const uint16_t* x, const uint32_t* codes,
  *   h       bf16 [M][I] output (16-byte aligned); y bf16 [M][D] output
  *   1 <= M <= 8; D % 512 == 0; I % 512 == 0.
  * h and y are bit-identical to rmsnorm_gateup_swiglu_tiled followed by
- * qgemv_affine4_tiled (same K splits, same summation order).  The launch
- * keeps one workgroup per resident slot and separates its phases (gate/up,
- * h, down, y) with grid barriers whose state is kept per (stream, M, D, I).
- * Waits are bounded: if the workgroups cannot all be resident (other work
- * holding the device for long), a wait gives up, the output is undefined and
- * qg_mlp_failures reports it; that state then stays unusable until the
- * process ends.  The first call for a (stream, M, D, I) allocates and clears
- * its state (do not make it under graph capture).  Calls on one stream are
- * ordered; calls on different streams use separate states.
+ * qgemv_affine4_tiled (same K splits, same summation order).  The launch is
+ * cooperative (the runtime refuses it, QG_EHIP, rather than start more
+ * workgroups than can be resident at once); it keeps one workgroup per
+ * resident slot and separates its phases (gate/up, h, down, y) with grid
+ * barriers whose counters live in the workspace header (zero when the call
+ * starts; the last workgroup to leave sets them back to zero).  Waits are
+ * bounded: should one give up, the call still ends, h and y are filled with
+ * NaN, and mlp_block_affine4_tiled_failures counts the call; the workspace is
+ * reusable as it is.  The workspace also holds the split-K partial sums.
  */
 qg_status mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma,
                                   float eps, const uint32_t* gu_codes_t,
@@ -148,10 +169,13 @@ qg_status mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma,
                                   const uint32_t* dn_codes_t,
                                   const uint16_t* dn_sb_t, uint16_t* h,
                                   uint16_t* y, int M, int D, int I,
+                                  void* ws, size_t ws_bytes,
                                   void* stream);
-/* Synchronises the stream and returns how many of its MLP-block states saw a
- * wait give up (0: none; -1: HIP error). */
-int32_t qg_mlp_failures(void* stream);
+size_t mlp_block_affine4_tiled_workspace(int M, int D, int I);
+/* Diagnostic, not for the decode path: synchronises `stream`, returns how many
+ * mlp_block_affine4_tiled calls on workspace `ws` had a barrier wait give up
+ * since the last query (0: none; -1: HIP error) and resets that count. */
+int32_t mlp_block_affine4_tiled_failures(void* ws, void* stream);
 
 /*
  * qgemv_q6k -- Y = X . dequant(W)^T for GGUF Q6_K weights as stored (runNburn
@@ -168,7 +192,9 @@ int32_t qg_mlp_failures(void* stream);
  *   1 <= M <= 8; N >= 0 (N = 0 does nothing); K > 0, K % 256 == 0.
  */
 qg_status qgemv_q6k(const uint16_t* x, const uint8_t* blocks, uint16_t* y,
-                    int M, int N, int K, void* stream);
+                    int M, int N, int K, void* ws, size_t ws_bytes,
+                    void* stream);
+size_t qgemv_q6k_workspace(int M, int N, int K);
 
 /*
  * Tile-order layout of affine4 weights (Husky page, section "MSI의 네 가지 구현
@@ -201,16 +227,22 @@ qg_status affine4_tile_pack(const uint32_t* codes, const uint16_t* scales,
                             uint16_t* sb_t, int N, int K, void* stream);
 qg_status qgemv_affine4_tiled(const uint16_t* x, const uint32_t* codes_t,
                               const uint16_t* sb_t, uint16_t* y, int M, int N,
-                              int K, void* stream);
+                              int K, void* ws, size_t ws_bytes,
+                              void* stream);
+size_t qgemv_affine4_tiled_workspace(int M, int N, int K);
 qg_status lmhead_argmax_tiled(const uint16_t* x, const uint32_t* codes_t,
                               const uint16_t* sb_t, float* logits,
                               int32_t* ids, const int32_t* draft,
                               int32_t* accepted, int M, int V, int K,
+                              void* ws, size_t ws_bytes,
                               void* stream);
+size_t lmhead_argmax_tiled_workspace(int M, int V, int K);
 qg_status rmsnorm_gateup_swiglu_tiled(const uint16_t* x, const uint16_t* gamma,
                                       float eps, const uint32_t* codes_t,
                                       const uint16_t* sb_t, uint16_t* h, int M,
-                                      int I, int K, void* stream);
+                                      int I, int K, void* ws, size_t ws_bytes,
+                                      void* stream);
+size_t rmsnorm_gateup_swiglu_tiled_workspace(int M, int I, int K);
 
 /*
  * qgemv_q4k -- Y = X . dequant(W)^T for Q4_K weights.
@@ -218,7 +250,9 @@ qg_status rmsnorm_gateup_swiglu_tiled(const uint16_t* x, const uint16_t* gamma,
  *   1 <= M <= 8; N >= 0; K > 0, K % 256 == 0.
  */
 qg_status qgemv_q4k(const uint16_t* x, const uint8_t* blocks, uint16_t* y,
-                    int M, int N, int K, void* stream);
+                    int M, int N, int K, void* ws, size_t ws_bytes,
+                    void* stream);
+size_t qgemv_q4k_workspace(int M, int N, int K);
 
 /*
  * rmsnorm_gateup_swiglu -- the front half of a dense SwiGLU MLP with the norm
@@ -235,7 +269,9 @@ qg_status rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma,
                                 float eps, const uint32_t* codes_gu,
                                 const uint16_t* scales_gu,
                                 const uint16_t* biases_gu, uint16_t* h, int M,
-                                int I, int K, void* stream);
+                                int I, int K, void* ws, size_t ws_bytes,
+                                void* stream);
+size_t rmsnorm_gateup_swiglu_workspace(int M, int I, int K);
 
 /*
  * moe_expert_qgemv -- one decode token through a routed-expert SwiGLU MLP
@@ -251,12 +287,17 @@ qg_status rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma,
  *   logit first); out_w fp32 [top_k] (nullable; their weights, same order).
  *   1 <= top_k <= E <= 1024, top_k <= 64; D, I > 0 and multiples of 256.
  *   NaN router logits are not supported.
+ *   ws: the routing (selected experts and weights) and the expert
+ *   activations h [top_k][I] (bf16) pass from the gate/up kernel to the down
+ *   kernel through it: moe_expert_qgemv_workspace(top_k, E, D, I) bytes.
  */
 qg_status moe_expert_qgemv(const uint16_t* x, const float* router_logits,
                            int top_k, const uint8_t* w_gu,
                            const uint8_t* w_down, uint16_t* y,
                            int32_t* out_ids, float* out_w, int E, int D, int I,
+                           void* ws, size_t ws_bytes,
                            void* stream);
+size_t moe_expert_qgemv_workspace(int top_k, int E, int D, int I);
 
 /*
  * lmhead_argmax -- untied LM-head readout with greedy verify (uzu page,
@@ -273,11 +314,15 @@ qg_status moe_expert_qgemv(const uint16_t* x, const float* router_logits,
  *   accepted int32 [1] (nullable).   1 <= M <= 8; V >= 1; K % 64 == 0.  All
  *   of x is staged on chip: ceil(K/128) * (264*M + 64) + 1024*M + 256 <= 163840
  *   bytes (M = 8: K <= 9088; M = 1: K <= 63360), else QG_EUNSUPPORTED.
+ *   ws: one (logit, index) key per row and workgroup, reduced by a second
+ *   kernel: lmhead_argmax_workspace(M, V, K) bytes.
  */
 qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes,
                         const uint16_t* scales, const uint16_t* biases,
                         float* logits, int32_t* ids, const int32_t* draft,
-                        int32_t* accepted, int M, int V, int K, void* stream);
+                        int32_t* accepted, int M, int V, int K, void* ws, size_t ws_bytes,
+                        void* stream);
+size_t lmhead_argmax_workspace(int M, int V, int K);
 
 /*
  * lmhead_topk -- top-k readout of the untied LM head (uzu page, section
@@ -289,8 +334,9 @@ qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes,
  *                    every number (NaNs by lower index)
  *   vals[m][j]     = logits[m][ids[m][j]]           (written only if non-null)
  *   x bf16 [M][K]; codes uint32 [V][K/8]; scales, biases bf16 [V][K/64];
- *   logits fp32 [M][V] (nullable: if null the library keeps them in its
- *   workspace); ids int32 [M][k]; vals fp32 [M][k] (nullable).
+ *   logits fp32 [M][V] (nullable: if null they are kept in the workspace,
+ *   which then needs 4*M*V more bytes: pass logits_kept = 0 to the size
+ *   query); ids int32 [M][k]; vals fp32 [M][k] (nullable).
  *   1 <= M <= 8; 1 <= k <= min(64, V); ceil(V/2048)*k <= 16384; K as for
  *   lmhead_argmax (all of x staged on chip).
  *   A call enqueues the projection and two selection kernels.
@@ -298,7 +344,9 @@ qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes,
 qg_status lmhead_topk(const uint16_t* x, const uint32_t* codes,
                       const uint16_t* scales, const uint16_t* biases,
                       float* logits, int32_t* ids, float* vals, int M, int V,
-                      int K, int k, void* stream);
+                      int K, int k, void* ws, size_t ws_bytes,
+                      void* stream);
+size_t lmhead_topk_workspace(int M, int V, int K, int k, int logits_kept);
 
 /*
  * qg_stream_read -- measurement aid, not part of the decode path: one plain
@@ -324,7 +372,9 @@ qg_status qg_stream_read(const void* buf, size_t bytes, uint32_t* sink,
  */
 qg_status qg_affine4_valu(const uint16_t* x, const uint32_t* codes,
                           const uint16_t* scales, const uint16_t* biases,
-                          uint16_t* y, int M, int N, int K, void* stream);
+                          uint16_t* y, int M, int N, int K, void* ws, size_t ws_bytes,
+                          void* stream);
+size_t qg_affine4_valu_workspace(int M, int N, int K);
 
 /*
  * Host-only twins of the entry points above: the same argument checks, no
@@ -333,22 +383,22 @@ qg_status qg_affine4_valu(const uint16_t* x, const uint32_t* codes,
  */
 qg_status qg_check_qgemv_affine4(const uint16_t* x, const uint32_t* codes,
                                  const uint16_t* scales, const uint16_t* biases,
-                                 uint16_t* y, int M, int N, int K);
+                                 uint16_t* y, int M, int N, int K, const void* ws, size_t ws_bytes);
 qg_status qg_check_mlp_block_affine4_tiled(
     const uint16_t* x, const uint16_t* gamma, float eps,
     const uint32_t* gu_codes_t, const uint16_t* gu_sb_t,
     const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
-    uint16_t* y, int M, int D, int I);
+    uint16_t* y, int M, int D, int I, const void* ws, size_t ws_bytes);
 qg_status qg_check_qgemv_q6k(const uint16_t* x, const uint8_t* blocks,
-                             uint16_t* y, int M, int N, int K);
+                             uint16_t* y, int M, int N, int K, const void* ws, size_t ws_bytes);
 qg_status qg_check_qgemv_affine8(const uint16_t* x, const uint32_t* codes,
                                  const uint16_t* scales, const uint16_t* biases,
-                                 uint16_t* y, int M, int N, int K);
+                                 uint16_t* y, int M, int N, int K, const void* ws, size_t ws_bytes);
 qg_status qg_check_qgemv_affine4_rht(const uint16_t* x, const int8_t* signs,
                                      int had, const uint32_t* codes,
                                      const uint16_t* scales,
                                      const uint16_t* biases, uint16_t* y, int M,
-                                     int N, int K);
+                                     int N, int K, const void* ws, size_t ws_bytes);
 qg_status qg_check_affine4_tile_pack(const uint32_t* codes,
                                      const uint16_t* scales,
                                      const uint16_t* biases, uint32_t* codes_t,
@@ -356,40 +406,40 @@ qg_status qg_check_affine4_tile_pack(const uint32_t* codes,
 qg_status qg_check_qgemv_affine4_tiled(const uint16_t* x,
                                        const uint32_t* codes_t,
                                        const uint16_t* sb_t, uint16_t* y, int M,
-                                       int N, int K);
+                                       int N, int K, const void* ws, size_t ws_bytes);
 qg_status qg_check_lmhead_argmax_tiled(const uint16_t* x,
                                        const uint32_t* codes_t,
                                        const uint16_t* sb_t, float* logits,
                                        int32_t* ids, const int32_t* draft,
-                                       int32_t* accepted, int M, int V, int K);
+                                       int32_t* accepted, int M, int V, int K, const void* ws, size_t ws_bytes);
 qg_status qg_check_rmsnorm_gateup_swiglu_tiled(const uint16_t* x,
                                                const uint16_t* gamma, float eps,
                                                const uint32_t* codes_t,
                                                const uint16_t* sb_t,
                                                uint16_t* h, int M, int I,
-                                               int K);
+                                               int K, const void* ws, size_t ws_bytes);
 qg_status qg_check_qgemv_q4k(const uint16_t* x, const uint8_t* blocks,
-                             uint16_t* y, int M, int N, int K);
+                             uint16_t* y, int M, int N, int K, const void* ws, size_t ws_bytes);
 qg_status qg_check_rmsnorm_gateup_swiglu(const uint16_t* x,
                                          const uint16_t* gamma, float eps,
                                          const uint32_t* codes_gu,
                                          const uint16_t* scales_gu,
                                          const uint16_t* biases_gu, uint16_t* h,
-                                         int M, int I, int K);
+                                         int M, int I, int K, const void* ws, size_t ws_bytes);
 qg_status qg_check_moe_expert_qgemv(const uint16_t* x,
                                     const float* router_logits, int top_k,
                                     const uint8_t* w_gu, const uint8_t* w_down,
                                     uint16_t* y, int32_t* out_ids, float* out_w,
-                                    int E, int D, int I);
+                                    int E, int D, int I, const void* ws, size_t ws_bytes);
 qg_status qg_check_lmhead_argmax(const uint16_t* x, const uint32_t* codes,
                                  const uint16_t* scales, const uint16_t* biases,
                                  float* logits, int32_t* ids,
                                  const int32_t* draft, int32_t* accepted, int M,
-                                 int V, int K);
+                                 int V, int K, const void* ws, size_t ws_bytes);
 qg_status qg_check_lmhead_topk(const uint16_t* x, const uint32_t* codes,
                                const uint16_t* scales, const uint16_t* biases,
                                float* logits, int32_t* ids, float* vals, int M,
-                               int V, int K, int k);
+                               int V, int K, int k, const void* ws, size_t ws_bytes);
 
 #ifdef __cplusplus
 }

@@ -12,7 +12,7 @@ import torch
 import oracle
 from bit_quantized_decode_group_amd import ops, synth
 from tests import packers
-from tests.gpu_util import (assert_close, assert_close_f32, assert_ids, bits_to_f64, dev_bf16, dev_f32, dev_i32, dev_u8, dev_u32,
+from tests.gpu_util import (assert_close, assert_close_f32, assert_ids, rows_identical, bits_to_f64, dev_bf16, dev_f32, dev_i32, dev_u8, dev_u32,
                             host_bf16_f64, host_bits)
 from tests.test_oracle_pins import HAND_BIASES, HAND_CODES, HAND_SCALES, HAND_VALUES, Q4K_HAND, Q4K_HAND_VALUES
 
@@ -662,9 +662,12 @@ def test_mlp_block_persistent_equals_separate(M, D, I):
     gu, dn = _mlp_dev(d)
     x, gam = dev_bf16(d["x"]), dev_bf16(d["gamma"])
     h_ref, y_ref = _mlp_separate(x, gam, d["eps"], gu, dn, D, I)
-    for rep in range(3):  # the barrier state carries over between launches
-        h, y = ops.mlp_block_affine4_tiled(x, gam, d["eps"], gu, dn, D, I)
-        assert ops.mlp_failures() == 0
+    ws = ops.workspace(ops.workspace_bytes("mlp_block_affine4_tiled", M, D, I))
+    for rep in range(3):  # the barrier state is left at zero for the next launch on the workspace
+        h, y = ops.mlp_block_affine4_tiled(x, gam, d["eps"], gu, dn, D, I, ws=ws)
+        assert ops.mlp_failures(ws) == 0
+        hdr = ws[:ops.lib().qg_workspace_header_bytes()]
+        assert int(torch.count_nonzero(hdr)) == 0, "barrier state not reset"
         assert torch.equal(h, h_ref), f"h differs (call {rep})"
         assert torch.equal(y, y_ref), f"y differs (call {rep})"
     h_or = oracle.rmsnorm_gateup_swiglu(d["x"], d["gamma"], d["eps"], d["codes_gu"], d["scales_gu"], d["biases_gu"])
@@ -674,19 +677,18 @@ def test_mlp_block_persistent_equals_separate(M, D, I):
 
 
 def test_mlp_block_persistent_alternating_rows():
-    """Launches with different M on one stream (separate barrier state per M) interleaved."""
-    D, I = 1024, 3072
-    outs = {}
-    for M in (8, 1, 5, 8, 1):
-        d = synth.mlp_block(M=M, D=D, I=I, seed=9900 + M)
+    """Launches with different M and shapes, and other entry points, interleaved on one
+    workspace (every call leaves the barrier state at zero)."""
+    ws = ops.workspace(64 << 20)
+    for M, D, I in ((8, 1024, 3072), (1, 1024, 3072), (5, 512, 1024), (8, 1024, 3072), (1, 512, 512)):
+        d = synth.mlp_block(M=M, D=D, I=I, seed=9900 + M + D)
         gu, dn = _mlp_dev(d)
         x, gam = dev_bf16(d["x"]), dev_bf16(d["gamma"])
-        h, y = ops.mlp_block_affine4_tiled(x, gam, d["eps"], gu, dn, D, I)
-        h_ref, y_ref = _mlp_separate(x, gam, d["eps"], gu, dn, D, I)
-        assert torch.equal(h, h_ref) and torch.equal(y, y_ref), f"M{M}"
-        outs[M] = y
-    for M in (8, 1, 5):
-        assert ops.mlp_failures() == 0
+        h, y = ops.mlp_block_affine4_tiled(x, gam, d["eps"], gu, dn, D, I, ws=ws)
+        h_ref = ops.rmsnorm_gateup_swiglu_tiled(x, gam, d["eps"], *gu, I, ws=ws)
+        y_ref = ops.qgemv_affine4_tiled(h_ref, *dn, D, ws=ws)
+        assert torch.equal(h, h_ref) and torch.equal(y, y_ref), f"M{M} D{D} I{I}"
+    assert ops.mlp_failures(ws) == 0
 
 
 # ---------------------------------------------------------------- qgemv_q6k --
@@ -785,3 +787,54 @@ def test_affine4_valu_full_size_sampled(M, N, K):
     rms = float(np.sqrt(np.mean(ym ** 2)))
     bad = np.abs(yv - ym) > 2.0 ** -7 * np.abs(ym) + 2e-3 * rms
     assert not bad.any(), f"valu vs mfma M{M} N{N} K{K}: {int(bad.sum())} outputs differ by more than one ulp"
+
+
+# ------------------------------------------------------------ batch invariance --
+# TensorFold page, section "핵심 메커니즘 2 — 정확 디코딩": a row's result must not
+# depend on the other rows of the batch.  The K split is sized for 8 rows
+# whatever M is, and a row's products and sums never mix with another row's, so
+# row i of an M = 8 call equals the 1-row call on row i alone, bit for bit.
+
+def _rows_check(call8, call1, X, what):
+    y8 = host_bits(call8(dev_bf16(X)))
+    rows = [host_bits(call1(dev_bf16(X[i:i + 1].copy()))) for i in range(X.shape[0])]
+    bad = rows_identical(y8, rows)
+    assert not bad, f"{what}: rows {bad} differ between the 8-row and the 1-row call"
+
+
+@pytest.mark.parametrize("N,K", [(3072, 1024), (2560, 12800), (40, 4096)])
+def test_batch_invariance_affine4(N, K):
+    d = synth.single_projection(M=8, N=N, K=K, seed=12000 + K)
+    w = _affine_dev(d)
+    f = lambda x: ops.qgemv_affine4(x, *w)
+    _rows_check(f, f, d["x"], f"affine4 {N}x{K}")
+    if K % 512 == 0:
+        t = ops.tile_pack(*w)
+        g = lambda x: ops.qgemv_affine4_tiled(x, *t, N)
+        _rows_check(g, g, d["x"], f"affine4 tiled {N}x{K}")
+
+
+@pytest.mark.parametrize("N,K", [(3072, 1024), (2560, 12800)])
+def test_batch_invariance_q4k_q6k(N, K):
+    g = synth.rng(12100 + K)
+    x = synth.normal_bf16(g, (8, K))
+    b4 = dev_u8(synth.q4k_matrix(g, N, K))
+    b6 = dev_u8(synth.q6k_matrix(g, N, K))
+    f4 = lambda xx: ops.qgemv_q4k(xx, b4)
+    f6 = lambda xx: ops.qgemv_q6k(xx, b6)
+    _rows_check(f4, f4, x, f"q4k {N}x{K}")
+    _rows_check(f6, f6, x, f"q6k {N}x{K}")
+
+
+def test_batch_invariance_gateup_and_lm_head():
+    d = synth.verify_block()
+    gu = (dev_u32(d["codes_gu"]), dev_bf16(d["scales_gu"]), dev_bf16(d["biases_gu"]))
+    gam = dev_bf16(d["gamma"])
+    f = lambda x: ops.rmsnorm_gateup_swiglu(x, gam, d["eps"], *gu)
+    _rows_check(f, f, d["x"], "gate/up 2560 -> 2x12800")
+    lm = synth.lm_head(M=8, V=20000, K=1024, seed=12200)
+    w = _affine_dev(lm)
+    lg8 = ops.lmhead_argmax(dev_bf16(lm["x"]), *w, want_logits=True)[2].cpu().numpy().view(np.uint32)
+    rows = [ops.lmhead_argmax(dev_bf16(lm["x"][i:i + 1].copy()), *w, want_logits=True)[2].cpu().numpy()
+            .view(np.uint32) for i in range(8)]
+    assert not rows_identical(lg8, rows), "lm head logits differ between the 8-row and the 1-row call"
