@@ -79,6 +79,16 @@ void collect(BufList* all, const Buf* outs, int nout, const Buf* ins, int nin) {
 constexpr size_t kLdsBudget = 163840;      // bytes of LDS one workgroup may use (all of a gfx950 CU's)
 constexpr size_t kQ4kLdsBudget = 65536;    // staged-slice bound of the Q4_K projection (keeps 2+ workgroups per CU)
 constexpr int kWaves = 4;                  // waves per workgroup of the projection kernels
+// Share (percent) of the resident workgroup slots an affine projection fills, per mode.
+#ifndef QG_FILL_GATEUP
+#define QG_FILL_GATEUP 100
+#endif
+#ifndef QG_FILL_PLAIN
+#define QG_FILL_PLAIN 75
+#endif
+#ifndef QG_FILL_OTHER
+#define QG_FILL_OTHER 50
+#endif
 constexpr int kTargetWaves = 2048;         // enough (tile, slice) pieces to cover HBM latency on 256 CUs
 constexpr int kMaxWavesInFlight = 4096;    // beyond this, waves stream several tiles
 constexpr int kMaxUnsplitSteps = 4;        // batches of loads per tile a plain projection takes unsplit
@@ -123,15 +133,16 @@ Plan plan_split(int ntiles, int nchunks, int cps_max, bool allow_split, int targ
 // ---------------------------------------------------------- workspace --
 // Scratch memory comes from the caller (ws, ws_bytes): the library never
 // allocates, frees or synchronises.  Layout of a workspace:
-//   [0, kWsHeader)  state words (barrier counters, failure flags) that must be
-//                   zero before the first call; every call that uses them
-//                   leaves them zero again (so one workspace can serve every
-//                   entry point and every shape, one call at a time);
-//   [kWsHeader, ...) per-call scratch (split-K partial sums, argmax keys,
-//                   top-k candidates, RHT planes, MoE routing and expert
+//   [0, kWsHeader)  state words (the LM head's running maxima and arrival
+//                   counter, the persistent block's barrier counters and
+//                   failure flags) that must be zero before the first call;
+//                   every call that uses them leaves them zero again (so one
+//                   workspace can serve every entry point and every shape,
+//                   one call at a time);
+//   [kWsHeader, ...) per-call scratch (split-K partial sums, top-k
+//                   candidates, RHT planes, MoE routing and expert
 //                   activations); written before it is read within a call.
 // A call that needs neither returns 0 from its size query and accepts ws = NULL.
-constexpr size_t kWsHeader = 16384;
 constexpr size_t kWsAlign = 256;
 constexpr int kMaxCus = 256;  // workspace sizes are computed for this many compute units (gfx950)
 
@@ -530,7 +541,7 @@ qg_status plan_affine(int mode, QgAffineArgs& a, const char* fn, size_t* lds_out
   // best on three quarters of the slots, the LM head and the other modes on
   // half, with two or more tiles per wave.
   const int target = (mode == QG_MODE_GATEUP) ? 4 * kTargetWaves : 2 * kTargetWaves;
-  const int fill_pct = (mode == QG_MODE_GATEUP) ? 100 : (mode == QG_MODE_PLAIN ? 75 : 50);
+  const int fill_pct = (mode == QG_MODE_GATEUP) ? QG_FILL_GATEUP : (mode == QG_MODE_PLAIN ? QG_FILL_PLAIN : QG_FILL_OTHER);
   Plan pl = plan_split(a.ntiles, a.nchunks, std::max(cps_max, 1), allow_split, target);
   // slices start on a batch boundary (4 chunks) when that keeps them within LDS
   const int batch = 4;
@@ -562,8 +573,13 @@ struct AffineCall {
   QgAffineArgs a{};
   size_t lds = 0;
   size_t reserve = 0;  // leading scratch of the entry point (the RHT planes)
-  size_t off_part = 0, off_ssq = 0, off_keys = 0, off_cand = 0, off_lg = 0, scratch = 0;
+  size_t off_part = 0, off_ssq = 0, off_cand = 0, off_lg = 0, scratch = 0;
 };
+
+// The greedy LM head merges its workgroups' maxima in the workspace header
+// and finishes in its last workgroup (no second kernel); the top-k readout
+// keeps per-block candidates instead.
+bool lm_fused(const AffineCall& c) { return c.mode == QG_MODE_LMHEAD && c.a.topk == 0; }
 
 qg_status affine_layout(AffineCall& c, const char* fn, int cus) {
   qg_status st = plan_affine(c.mode, c.a, fn, &c.lds, cus);
@@ -575,8 +591,6 @@ qg_status affine_layout(AffineCall& c, const char* fn, int cus) {
   off += partials ? align_up((size_t)a.S * a.M * a.N * 4, kWsAlign) : 0;
   c.off_ssq = off;
   off += (c.mode == QG_MODE_GATEUP) ? align_up((size_t)a.S * 8 * 4, kWsAlign) : 0;
-  c.off_keys = off;
-  off += (c.mode == QG_MODE_LMHEAD) ? align_up((size_t)a.S * a.rgroups * 8 * 8, kWsAlign) : 0;
   // top-k: the blocks' candidates, and the logits when the caller keeps none
   c.off_cand = off;
   off += a.topk > 0 ? align_up((size_t)a.M * ((a.N + kTopkBlock - 1) / kTopkBlock) * a.topk * 8, kWsAlign) : 0;
@@ -591,7 +605,7 @@ qg_status affine_layout(AffineCall& c, const char* fn, int cus) {
 qg_status affine_prepare(AffineCall& c, const char* fn, const void* ws, size_t ws_bytes, const BufList& bl) {
   qg_status st = affine_layout(c, fn, kMaxCus);
   if (st) return st;
-  return check_ws(fn, ws, ws_bytes, ws_total(c.scratch), bl.b, bl.n);
+  return check_ws(fn, ws, ws_bytes, ws_total(c.scratch, lm_fused(c)), bl.b, bl.n);
 }
 
 // Workspace bytes of an affine call of this shape (0 if it needs none or the
@@ -599,12 +613,12 @@ qg_status affine_prepare(AffineCall& c, const char* fn, const void* ws, size_t w
 size_t affine_query(AffineCall c, const char* fn) {
   if (c.a.M < 1 || c.a.M > 8 || c.a.N < 1 || c.a.K < 64 || c.a.K % 64) return 0;
   if (affine_layout(c, fn, kMaxCus)) return 0;
-  return ws_total(c.scratch);
+  return ws_total(c.scratch, lm_fused(c));
 }
 
 // After the checks: the plan's workgroup count for this device (the K split
-// and so the scratch needed are unchanged; the per-workgroup keys need no
-// more than was checked), the scratch pointers, and the launch.  `pre` (if
+// and so the scratch needed are unchanged), the scratch pointers, and the
+// launch.  `pre` (if
 // set) enqueues work that the projection reads (the RHT planes) and may
 // change the arguments.
 qg_status affine_launch(AffineCall c, const char* fn, void* ws, hipStream_t stream,
@@ -616,10 +630,10 @@ qg_status affine_launch(AffineCall c, const char* fn, void* ws, hipStream_t stre
     const int err = pre(base, c.a);
     if (err) return fail(QG_EHIP, "%s: launch failed: %s", fn, hipGetErrorString((hipError_t)err));
   }
+  if (lm_fused(c)) c.a.state = static_cast<unsigned char*>(ws);
   if (base) {
     c.a.part = reinterpret_cast<float*>(base + c.off_part);
     c.a.ssq_part = reinterpret_cast<float*>(base + c.off_ssq);
-    c.a.keys = reinterpret_cast<unsigned long long*>(base + c.off_keys);
     c.a.cand = reinterpret_cast<unsigned long long*>(base + c.off_cand);
     if (c.a.topk > 0 && !c.a.logits) c.a.logits = reinterpret_cast<float*>(base + c.off_lg);
   }

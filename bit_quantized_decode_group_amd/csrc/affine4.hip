@@ -28,9 +28,9 @@
 //     k_split_reduce, launched next on the same stream, adds them in slice
 //     order and applies the epilogue: no atomics, no cross-workgroup fences,
 //     and the result does not depend on timing.
-//   * The LM head stores one (logit, index) key per row and workgroup;
-//     k_lmhead_finalize takes the maximum over workgroups and writes the ids
-//     and the accepted count.
+//   * The LM head merges each workgroup's best (logit, index) key per row into
+//     a running maximum in the workspace header; the last workgroup writes the
+//     ids and the accepted count (lmhead_merge_finish).
 //   * Weight bytes are read exactly once; X is read once per workgroup.
 //
 // Per chunk and lane: codes word t (t = 0..3) of lane l covers
@@ -56,6 +56,40 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
+// Greedy verify fused into the LM-head projection.  Every workgroup has
+// merged its best key of each row into the row's slot in the workspace header
+// (an agent-scope maximum, applied at the device's coherence point); once those
+// atomics have completed it counts itself in.  The workgroup that arrives last
+// finds every row's maximum in the slots, writes the ids and the number of
+// leading rows that match the draft, and sets the slots and the counter back
+// to zero for the next call.
+template <int M>
+__device__ __forceinline__ void lmhead_merge_finish(const QgAffineArgs& p) {
+  __shared__ int last;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's maximum has been applied
+  __syncthreads();
+  unsigned* cnt = reinterpret_cast<unsigned*>(p.state + kHdrLmCount);
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+  __syncthreads();
+  if (!last || threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  unsigned long long* slot =
+      reinterpret_cast<unsigned long long*>(p.state + kHdrLmSlots + (size_t)min(lane, 7) * kHdrLmSlotStride);
+  const unsigned long long key = lane < M ? __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+  const int id = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
+  const int draft = (p.draft && lane < M) ? p.draft[lane] : -1;
+  if (lane < M) {
+    p.ids[lane] = id;
+    __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const unsigned long long match = __ballot(lane < M && p.draft && id == draft);
+  if (lane == 0) {
+    if (p.accepted) *p.accepted = (int)__builtin_ctzll(~match);
+    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // WIDE: every batch of every slice lies inside the row and the scale/bias rows
 // are aligned for one vector load per batch (the host checks G, the slice
 // length and the pointers); the loop body then has no data-dependent branch
@@ -74,8 +108,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   constexpr int BATCH = 4;                              // chunks whose loads are issued together
   constexpr int R = (MODE == QG_MODE_LMHEAD) ? 2 : 1;   // steps of weight loads in flight per wave
   constexpr int CW = (MODE == QG_MODE_PLAIN8) ? 2 : 1;  // 16-byte code loads per lane and chunk
+  constexpr bool NTL = (MODE == QG_MODE_LMHEAD);        // non-temporal weight loads (the long LM-head stream)
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int W = blockDim.x >> 6;
   const int slice = blockIdx.x % p.S;
   const int rg = blockIdx.x / p.S;
@@ -132,10 +167,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
       const size_t tile = (size_t)min(gw + ti * nw, p.ntiles - 1);  // a wave without work reloads a real tile
       const uint4* cbase = reinterpret_cast<const uint4*>(p.codes) + (tile * p.nchunks + c0 + cb) * 64 + lane;
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) bf.q[u] = cbase[u * 64];  // one base address, 1-KB immediate offsets
+      for (int u = 0; u < BATCH; ++u) bf.q[u] = ld_weights<NTL>(cbase + u * 64);  // one base address, 1-KB immediate offsets
       // one 16-byte record per (row, group parity): dword u = (scale, bias) of group 2(c0+cb+u) + half
       const uint16_t* rec = p.scales + ((tile * (p.nchunks / BATCH) + (c0 + cb) / BATCH) * 2 + half) * 128 + nl * 8;
-      const uint4 sv = *reinterpret_cast<const uint4*>(rec);
+      const uint4 sv = ld_weights<NTL>(rec);
       bf.sw[0] = sv.x; bf.sw[1] = sv.y; bf.sw[2] = sv.z; bf.sw[3] = sv.w;
       return;
     }
@@ -145,17 +180,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
       if constexpr (CW == 2) {
         // 8-bit: lane kb's 32 codes of chunk cg are bytes 32kb..32kb+31 of the chunk's 128
         const uint32_t wo = min((uint32_t)(cg * 32 + kb * 8), wmax);
-        bf.q[2 * u] = *reinterpret_cast<const uint4*>(p.codes + row_c * wrow_words + wo);
-        bf.q[2 * u + 1] = *reinterpret_cast<const uint4*>(p.codes + row_c * wrow_words + wo + 4);
+        bf.q[2 * u] = ld_weights<NTL>(p.codes + row_c * wrow_words + wo);
+        bf.q[2 * u + 1] = ld_weights<NTL>(p.codes + row_c * wrow_words + wo + 4);
       } else {
         const uint32_t wo = min((uint32_t)(cg * 16 + kb * 4), wmax);
-        bf.q[u] = *reinterpret_cast<const uint4*>(p.codes + row_c * wrow_words + wo);
+        bf.q[u] = ld_weights<NTL>(p.codes + row_c * wrow_words + wo);
       }
     }
     if constexpr (WIDE) {
       const size_t off = row_c * p.G + gb;
-      const uint4 sv = *reinterpret_cast<const uint4*>(p.scales + off);
-      const uint4 bv = *reinterpret_cast<const uint4*>(p.biases + off);
+      const uint4 sv = ld_weights<NTL>(p.scales + off);
+      const uint4 bv = ld_weights<NTL>(p.biases + off);
       bf.sw[0] = sv.x; bf.sw[1] = sv.y; bf.sw[2] = sv.z; bf.sw[3] = sv.w;
       bf.bw[0] = bv.x; bf.bw[1] = bv.y; bf.bw[2] = bv.z; bf.bw[3] = bv.w;
     } else {
@@ -174,7 +209,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   // ---- end of a tile: add the two group halves, then store / publish
   auto finish_tile = [&](int tile) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] += __shfl_xor(acc[r], 32);
+    for (int r = 0; r < 4; ++r) acc[r] = add_upper_half(acc[r]);
     const int row = tile * 16 + nl;
     if ((lane < 32) && row < p.N) {
       if (MODE == QG_MODE_GATEUP || p.S > 1) {
@@ -186,7 +221,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = mbase + r;
-          if (m < M) {
+          if (M == 8 || m < M) {  // lanes < 32 hold rows 0..7
             if (p.logits) p.logits[(size_t)m * p.N + row] = acc[r];
             const unsigned long long key = argmax_key(acc[r], (uint32_t)row);
             best[r] = key > best[r] ? key : best[r];
@@ -318,8 +353,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     if (threadIdx.x < M) {
       unsigned long long v = 0ull;
       for (int w = 0; w < W; ++w) v = wkeys[w * 8 + threadIdx.x] > v ? wkeys[w * 8 + threadIdx.x] : v;
-      p.keys[(size_t)blockIdx.x * 8 + threadIdx.x] = v;  // this workgroup's best (logit, index) of row m
+      // merged into the row's running maximum (order-independent)
+      __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(p.state + kHdrLmSlots +
+                                                                   threadIdx.x * kHdrLmSlotStride),
+                             v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    lmhead_merge_finish<M>(p);
   }
 }
 
@@ -372,52 +411,6 @@ __global__ void __launch_bounds__(256) k_split_reduce(QgAffineArgs p) {
   }
 }
 
-// Greedy verify: maximum key over all workgroups per row (order-independent),
-// then the ids and the number of leading rows that match the draft.  One
-// wave: lane l loads the 64-byte key records of workgroups l, l+64, ... (all
-// of its loads issued together), then a butterfly maximum per row.
-__global__ void __launch_bounds__(64) k_lmhead_finalize(QgAffineArgs p, int nwg) {
-  const int lane = threadIdx.x;
-  const int draft = (p.draft && lane < p.M) ? p.draft[lane] : -1;
-  unsigned long long v[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) v[m] = 0ull;
-  for (int w0 = 0; w0 < nwg; w0 += 64 * 8) {
-    ulonglong2 k[8][4];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int w = min(w0 + lane + 64 * q, nwg - 1);  // clamped: a repeated record does not change a maximum
-      const ulonglong2* kp = reinterpret_cast<const ulonglong2*>(p.keys + (size_t)w * 8);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) k[q][j] = kp[j];
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[2 * j] = k[q][j].x > v[2 * j] ? k[q][j].x : v[2 * j];
-        v[2 * j + 1] = k[q][j].y > v[2 * j + 1] ? k[q][j].y : v[2 * j + 1];
-      }
-  }
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const unsigned long long o = shfl_xor_u64(v[m], off);
-      v[m] = o > v[m] ? o : v[m];
-    }
-  }
-  // every lane now holds the row maxima; lane m writes row m's id
-  int id = 0;
-#pragma unroll
-  for (int m = 0; m < 8; ++m)
-    if (lane == m) id = (int)(0xFFFFFFFFu - (uint32_t)(v[m] & 0xFFFFFFFFull));
-  if (lane < p.M) p.ids[lane] = id;
-  // accepted = leading rows whose id equals the draft's
-  const unsigned long long match = __ballot(lane < p.M && p.draft && id == draft);
-  if (lane == 0 && p.accepted) *p.accepted = (int)__builtin_ctzll(~match);
-}
-
 template <int M, bool WIDE>
 static void launch_main(int mode, const QgAffineArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
   if (a.tiled) {  // tile-order weights: plain projection, gate/up and LM head
@@ -459,8 +452,6 @@ static int launch_affine_m(int mode, const QgAffineArgs& a, size_t lds, hipStrea
   if (err) return err;
   if (mode == QG_MODE_LMHEAD && a.topk > 0) {
     return qg_launch_topk(a, st);
-  } else if (mode == QG_MODE_LMHEAD) {
-    hipLaunchKernelGGL(k_lmhead_finalize, dim3(1), dim3(64), 0, st, a, (int)grid.x);
   } else if (a.S > 1 || mode == QG_MODE_GATEUP) {
     const size_t outs = (size_t)a.M * (mode == QG_MODE_GATEUP ? a.N / 2 : a.N);
     const unsigned nblk = (unsigned)((outs + 255) / 256);

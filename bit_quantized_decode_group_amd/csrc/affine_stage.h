@@ -47,7 +47,7 @@ __device__ __forceinline__ uint4 load_u4_coherent(const uint16_t* ptr) {
 
 template <int M, int MODE, bool COH = false>
 __device__ __forceinline__ void stage_load(const QgAffineArgs& p, int c0, int nc, int round, StageIn<MODE>& in) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id(), W = blockDim.x >> 6;
   const int m = min(lane & 7, M - 1), h = (lane >> 3) & 1, t = lane >> 4;
   const int glmax = 2 * nc - 1;
   constexpr int SG = stage_groups(MODE);
@@ -70,7 +70,7 @@ template <int M, int MODE>
 __device__ __forceinline__ void stage_store(const QgAffineArgs& p, uint4* xs, float* sx, float* ssq, int c0, int nc,
                                             int round, const StageIn<MODE>& in) {
   constexpr int PL = planes(MODE);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id(), W = blockDim.x >> 6;
   const int m = lane & 7, h = (lane >> 3) & 1, t = lane >> 4;
   const int ngl = 2 * nc;
   constexpr int SG = stage_groups(MODE);

@@ -39,6 +39,38 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
+// 16-byte load of weight bytes, each read exactly once.  NT: a non-temporal
+// (streaming) load, which does not keep the line in the caches it passes
+// through.  Measured on MI355X: a plain streaming read reaches 6.8-6.9 TB/s
+// with non-temporal loads against 6.0-6.1 TB/s with ordinary ones, and the
+// long LM-head stream gains from them; kernels whose waves live for a few
+// steps only (the split projections, the MoE) lose (their first loads wait
+// longer), so they use ordinary loads.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ uint4 ld_weights(const void* ptr) {
+  u32x4_t v;
+  if constexpr (NT)
+    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(ptr));
+  else
+    v = *reinterpret_cast<const u32x4_t*>(ptr);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// v + (the value of lane l ^ 32) for lanes 0..31, on the VALU (gfx950's
+// v_permlane32_swap exchanges the wave's two 32-lane halves) instead of an
+// LDS permute.  Each result is one addition of the same two values, so it
+// equals v + __shfl_xor(v, 32) bit for bit.
+__device__ __forceinline__ float add_upper_half(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The index of the calling wave in its workgroup, as a scalar (wave-uniform
+// values derived from it, such as tile and step counters and the address
+// arithmetic built on them, then stay on the scalar unit).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN, overflow -> inf.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
@@ -121,6 +153,16 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) 
 
 }  // namespace qg
 
+// ------------------------------------------------------ workspace header ---
+// The first kWsHeader bytes of a caller's workspace hold state that is zero
+// before a call and that the call leaves at zero (its last workgroup resets
+// it); the per-call scratch follows.  Offsets within the header:
+constexpr size_t kWsHeader = 16384;
+constexpr size_t kHdrMlpBarrier = 0;      // persistent MLP block: grid barrier (qg_mlp_state_bytes())
+constexpr size_t kHdrLmSlots = 8704;      // LM head: per row, the largest (logit, index) key so far,
+constexpr size_t kHdrLmSlotStride = 256;  //   one row per 256 bytes (rows in separate memory channels)
+constexpr size_t kHdrLmCount = 10752;     // LM head: workgroups that have merged their keys
+
 // ----------------------------------------------------------- host side ---
 // Launch descriptors filled by the ABI layer (abi.hip) and consumed by the
 // launchers in affine4.hip / q4k.hip.
@@ -146,7 +188,8 @@ struct QgAffineArgs {
   int32_t* accepted;
   float* part;                // [S][NB][M][N] split-K partials (NB = 2 for gate and up)
   float* ssq_part;            // [S][8] per-slice sums of x^2 (GATEUP with S > 1)
-  unsigned long long* keys;   // [workgroups][8] per-workgroup argmax keys (LM head)
+  unsigned char* state;       // workspace header (zero between calls): the LM head's running maxima
+                              // and arrival counter when its finalize is fused into the projection
   int M, N, K, G;
   int nchunks, S, cps, ntiles;
   int rgroups;  // workgroups per K slice; workgroup r owns tiles [r*ntiles/rgroups, (r+1)*ntiles/rgroups)

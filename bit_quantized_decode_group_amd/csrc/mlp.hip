@@ -114,7 +114,7 @@ struct Job {
 
 __device__ __forceinline__ Job job_of(const QgAffineArgs& p, int job) {
   Job j;
-  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6, wave = wave_id();
   j.slice = job % p.S;
   j.rg = job / p.S;
   j.c0 = j.slice * p.cps;
@@ -136,9 +136,9 @@ __device__ __forceinline__ void load_tstep(const QgAffineArgs& p, const Job& j, 
   const size_t tile = (size_t)min(j.gw + ti * j.nw, p.ntiles - 1);
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    b.q[u] = *reinterpret_cast<const uint4*>(p.codes + ((tile * p.nchunks + j.c0 + cb + u) * 64 + lane) * 4);
+    b.q[u] = ld_weights<false>(p.codes + ((tile * p.nchunks + j.c0 + cb + u) * 64 + lane) * 4);
   const uint16_t* rec = p.scales + ((tile * (p.nchunks / 4) + (j.c0 + cb) / 4) * 2 + half) * 128 + nl * 8;
-  b.sb = *reinterpret_cast<const uint4*>(rec);
+  b.sb = ld_weights<false>(rec);
 }
 
 // Stage the job's slice of X, run its steps (the first R from `pre` when
@@ -152,7 +152,7 @@ __device__ void run_job(const QgAffineArgs& p, int job, unsigned char* smem, TBu
   constexpr bool COH_X = (MODE == QG_MODE_PLAIN);
   const Job j = job_of(p, job);
   const int nc = j.nc;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id(), W = blockDim.x >> 6;
   constexpr int ZR = 64 * PL * M;
   uint4* zr = reinterpret_cast<uint4*>(smem);
   uint4* xs = zr + ZR;

@@ -122,9 +122,9 @@ __device__ __forceinline__ void q4k_load(Q4kBuf<NB, SB>& bf, const uint8_t* cons
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const uint8_t* bp = blk[b] + (size_t)min(sb + u, nsb - 1) * 144;
-      bf.hdr[b][u] = *reinterpret_cast<const uint4*>(bp);
+      bf.hdr[b][u] = ld_weights<false>(bp);
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) bf.cq[b][u][hh] = *reinterpret_cast<const uint4*>(bp + 16 + 64 * hh + 16 * kb);
+      for (int hh = 0; hh < 2; ++hh) bf.cq[b][u][hh] = ld_weights<false>(bp + 16 + 64 * hh + 16 * kb);
     }
   }
 }
@@ -205,7 +205,7 @@ __device__ __forceinline__ void q4k_tile(f32x4_t (&acc)[NB], const uint8_t* cons
 template <int M>
 __global__ void __launch_bounds__(256) k_q4k(QgQ4kArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id(), W = blockDim.x >> 6;
   const int slice = blockIdx.x % p.S, rg = blockIdx.x / p.S;
   const int sb0 = slice * p.cps;
   const int nsb = min(p.cps, p.nchunks - sb0);  // here a "chunk" of the split is one superblock
@@ -381,7 +381,7 @@ __global__ void __launch_bounds__(256) k_moe_gateup(QgMoeArgs p) {
   __shared__ float lg[1024];
   __shared__ __align__(16) unsigned long long keys[1026];
   __shared__ f32x4_t red[kMoeWaves][2][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int tiles = (p.I + 15) / 16;
   const int slot = blockIdx.x / tiles, tile = blockIdx.x % tiles;
   const int nsb = p.D / 256;
@@ -445,7 +445,7 @@ constexpr int kMoeDownBatch = 3;  // superblocks per load batch (I = 768: one ba
 __global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ f32x4_t red[kMoeDownWaves][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int W = blockDim.x >> 6;
   const int tile = blockIdx.x;
   const int nsb = p.I / 256;

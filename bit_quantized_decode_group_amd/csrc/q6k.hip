@@ -78,7 +78,7 @@ __device__ __forceinline__ void stage_q6k_x(const uint16_t* x, int K, uint4* xs,
 template <int M>
 __global__ void __launch_bounds__(256) k_q6k(QgQ4kArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id(), W = blockDim.x >> 6;
   const int slice = blockIdx.x % p.S, rg = blockIdx.x / p.S;
   const int sb0 = slice * p.cps;
   const int nsb = min(p.cps, p.nchunks - sb0);

@@ -35,7 +35,7 @@ struct ValuBuf {
 template <int M>
 __global__ void __launch_bounds__(256) k_affine_valu(QgAffineArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id(), W = blockDim.x >> 6;
   const int slice = blockIdx.x % p.S, rg = blockIdx.x / p.S;
   const int c0 = slice * p.cps;
   const int nc = min(p.cps, p.nchunks - c0);

@@ -15,6 +15,7 @@ Tensor conventions (bit patterns are what the ABI sees):
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -139,9 +140,14 @@ def workspace(nbytes, device=None):
     return t[off:off + n]
 
 
+@functools.lru_cache(maxsize=4096)
+def _ws_query(entry: str, shape: tuple) -> int:
+    return int(getattr(lib(), entry + "_workspace")(*shape))
+
+
 def workspace_bytes(entry: str, *shape) -> int:
     """Bytes of workspace `entry` (e.g. "lmhead_argmax") needs for this shape (0: none)."""
-    return int(getattr(lib(), entry + "_workspace")(*[int(v) for v in shape]))
+    return _ws_query(entry, tuple(int(v) for v in shape))
 
 
 _ws_cache = {}

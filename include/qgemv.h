@@ -56,8 +56,8 @@
  *     different workspaces.  With that, calls are stateless: any number of
  *     host threads may issue calls, and the calls can be captured into a HIP
  *     graph on any stream, also as the stream's first work.
- *   * A call may enqueue more than one kernel (a split-K or argmax reduction
- *     follows its main kernel on the same stream).
+ *   * A call may enqueue more than one kernel (a split-K reduction follows
+ *     its main kernel on the same stream).
  *   * Floating point: fp32 accumulation; bf16 outputs rounded to nearest even.
  *     Results are deterministic: the same inputs give the same bytes on every
  *     call (fixed reduction order, no atomics).
@@ -314,8 +314,10 @@ size_t moe_expert_qgemv_workspace(int top_k, int E, int D, int I);
  *   accepted int32 [1] (nullable).   1 <= M <= 8; V >= 1; K % 64 == 0.  All
  *   of x is staged on chip: ceil(K/128) * (264*M + 64) + 1024*M + 256 <= 163840
  *   bytes (M = 8: K <= 9088; M = 1: K <= 63360), else QG_EUNSUPPORTED.
- *   ws: one (logit, index) key per row and workgroup, reduced by a second
- *   kernel: lmhead_argmax_workspace(M, V, K) bytes.
+ *   ws: the header only (lmhead_argmax_workspace(M, V, K) bytes): every
+ *   workgroup merges its best (logit, index) of each row into a running
+ *   maximum there, and the last one to finish writes ids and accepted and
+ *   sets the maximum back to zero -- one kernel per call.
  */
 qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes,
                         const uint16_t* scales, const uint16_t* biases,
