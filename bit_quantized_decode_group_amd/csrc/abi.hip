@@ -630,7 +630,10 @@ qg_status affine_launch(AffineCall c, const char* fn, void* ws, hipStream_t stre
     const int err = pre(base, c.a);
     if (err) return fail(QG_EHIP, "%s: launch failed: %s", fn, hipGetErrorString((hipError_t)err));
   }
-  if (lm_fused(c)) c.a.state = static_cast<unsigned char*>(ws);
+  if (lm_fused(c)) {
+    if (!ws) return fail(QG_EINVAL, "%s: the greedy readout needs its workspace header", fn);
+    c.a.state = static_cast<unsigned char*>(ws);
+  }
   if (base) {
     c.a.part = reinterpret_cast<float*>(base + c.off_part);
     c.a.ssq_part = reinterpret_cast<float*>(base + c.off_ssq);

@@ -333,7 +333,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     }
   }
 
-  if (MODE == QG_MODE_LMHEAD) {
+  // greedy readout only: the top-k readout (no workspace state; p.state is
+  // null) selects from the stored logits in its own kernels
+  if (MODE == QG_MODE_LMHEAD && p.state) {
     // wave: lanes 0..15 share rows m = 0..3, lanes 16..31 rows 4..7
 #pragma unroll
     for (int r = 0; r < 4; ++r)
