@@ -1289,6 +1289,55 @@ qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes, const uint16_t
   return affine_launch(c, "lmhead_argmax", ws, (hipStream_t)stream);
 }
 
+// ----------------------------------------------------- lmhead_argmax_static --
+// lmhead_argmax for callers that cannot allocate device memory: the scratch
+// it needs (the workspace header: every row's running (logit, index) maximum
+// and the workgroups' arrival counter) is this file-scope device array, one
+// copy per GPU, zero when the library is loaded and left at zero by every
+// call.  Its device address is looked up once per device (hipGetSymbolAddress
+// with that device current) and only that address is passed to kernels.
+constexpr size_t kStaticScratchBytes = kWsHeader;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64] = {nullptr};
+
+static qg_status static_scratch(const char* fn, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QG_EHIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(QG_EUNSUPPORTED, "%s: device index %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(QG_EHIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QG_OK;
+}
+
+qg_status lmhead_argmax_static(const uint16_t* x, const uint32_t* codes, const uint16_t* scales,
+                               const uint16_t* biases, float* logits, int32_t* ids, const int32_t* draft,
+                               int32_t* accepted, int M, int V, int K, void* stream) {
+  const char* fn = "lmhead_argmax_static";
+  clear_err();
+  const size_t need = lmhead_argmax_workspace(M, V, K);
+  if (need > kStaticScratchBytes)
+    return fail(QG_EUNSUPPORTED, "%s: M=%d V=%d K=%d needs %zu bytes of scratch, the static array holds %zu", fn, M,
+                V, K, need, kStaticScratchBytes);
+  qg_status st;
+  if ((st = check_device())) return st;
+  void* ptr = nullptr;
+  if ((st = static_scratch(fn, &ptr))) return st;
+  AffineCall c;
+  st = prep_lmhead(x, codes, scales, biases, logits, ids, draft, accepted, M, V, K, ptr, kStaticScratchBytes, c);
+  if (st) return st;
+  return affine_launch(c, fn, ptr, (hipStream_t)stream);
+}
+
 qg_status qg_check_lmhead_argmax_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t,
                                        float* logits, int32_t* ids, const int32_t* draft, int32_t* accepted, int M,
                                        int V, int K, const void* ws, size_t ws_bytes) {

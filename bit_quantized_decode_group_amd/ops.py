@@ -64,6 +64,7 @@ _SIGS = {
     "qg_check_lmhead_argmax": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I] + _WS,
     "qg_check_lmhead_topk": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I] + _WS,
     "mlp_block_affine4_tiled_failures": [_P, _P],
+    "lmhead_argmax_static": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
 }
 # size queries: name -> shape arguments (all int); they return size_t
 _QUERIES = {
@@ -454,6 +455,30 @@ def lmhead_argmax(x, codes, scales, biases, draft=None, logits=None, want_logits
     with torch.cuda.device(x.device):
         _raise_on(lib().lmhead_argmax(_ptr(x), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(logits), _ptr(ids),
                                       _ptr(draft), _ptr(accepted), M, V, K, wsp, wsn, _stream()), "lmhead_argmax")
+    return ids, accepted, logits
+
+
+def lmhead_argmax_static(x, codes, scales, biases, draft=None, logits=None, want_logits=False, ids=None,
+                         accepted=None):
+    """lmhead_argmax with the library's static scratch (no workspace; the call allocates nothing on the device).
+    Returns (ids int32 [M], accepted int32 [1], logits fp32 [M,V] or None)."""
+    M, K = _dims2(x, "x")
+    V = codes.shape[0]
+    if logits is None and want_logits:
+        logits = torch.empty((M, V), dtype=torch.float32, device=x.device)
+    if ids is None:
+        ids = torch.empty(M, dtype=torch.int32, device=x.device)
+    if accepted is None:
+        accepted = torch.empty(1, dtype=torch.int32, device=x.device)
+    for t, n, e in ((x, "x", 2), (codes, "codes", 4), (scales, "scales", 2), (biases, "biases", 2),
+                    (logits, "logits", 4), (ids, "ids", 4), (draft, "draft", 4), (accepted, "accepted", 4)):
+        _need(t, n, e, x.device)
+    if draft is not None and draft.numel() < M:
+        raise ValueError("draft must hold at least M ids")
+    with torch.cuda.device(x.device):
+        _raise_on(lib().lmhead_argmax_static(_ptr(x), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(logits),
+                                             _ptr(ids), _ptr(draft), _ptr(accepted), M, V, K, _stream()),
+                  "lmhead_argmax_static")
     return ids, accepted, logits
 
 

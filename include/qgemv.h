@@ -327,6 +327,24 @@ qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes,
 size_t lmhead_argmax_workspace(int M, int V, int K);
 
 /*
+ * lmhead_argmax_static -- lmhead_argmax for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments, checks, kernel and results, minus the
+ * workspace.  Its scratch (the 16 KB workspace header: the running maxima and
+ * the arrival counter) is a static device array of the library, one per GPU,
+ * holding at most 16384 bytes (larger needs are refused with
+ * QG_EUNSUPPORTED); the call allocates nothing.  The array is zero when the
+ * library is loaded and every call leaves it at zero.  All calls on one GPU
+ * share it: calls that may overlap in time on one GPU (different streams,
+ * graphs replayed concurrently) race on it and give undefined ids.
+ */
+qg_status lmhead_argmax_static(const uint16_t* x, const uint32_t* codes,
+                               const uint16_t* scales, const uint16_t* biases,
+                               float* logits, int32_t* ids, const int32_t* draft,
+                               int32_t* accepted, int M, int V, int K,
+                               void* stream);
+
+/*
  * lmhead_topk -- top-k readout of the untied LM head (uzu page, section
  * "내부 동작 3: DFlash + Weaver": the target's readout of each draft position
  * yields a pool of its best candidate tokens):
