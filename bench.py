@@ -37,14 +37,18 @@ KERNEL_SOURCES = ["bit_quantized_decode_group_amd/csrc/common.h", "bit_quantized
                   "bit_quantized_decode_group_amd/csrc/mlp.hip", "bit_quantized_decode_group_amd/csrc/affine_stage.h",
                   "bit_quantized_decode_group_amd/csrc/q6k.hip", "bit_quantized_decode_group_amd/csrc/valu.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# rocprofv3 kernel-only averages of the step's kernels (written by --kernel-times from a kernel trace)
+KERNEL_TIMES_FILE_REL = "profiles/kernel_times.json"
+KERNEL_TIMES_FILE = os.path.join(ROOT, KERNEL_TIMES_FILE_REL)
 GRAPH_STEPS = 10  # at most this many consecutive steps (rotating weights, MoE stacks, router logits) per graph
 CALIB_BYTES = 384 << 20  # bytes read and written by the kernel that calibrates the HBM byte counters
 # kernels launched by each entry point (once per call) at M = 8
+# (the bench's default tile-order layout: k_affine<M, mode, WIDE = true, TILED = true>)
 ENTRY_KERNELS = {
-    "rmsnorm_gateup_swiglu": ["qg::k_affine<8, 1,", "qg::k_split_reduce<1>"],
-    "qgemv_affine4": ["qg::k_affine<8, 0,", "qg::k_split_reduce<0>"],
+    "rmsnorm_gateup_swiglu": ["qg::k_affine<8, 1, true, true>", "qg::k_split_reduce<1>"],
+    "qgemv_affine4": ["qg::k_affine<8, 0, true, true>", "qg::k_split_reduce<0>"],
     "moe_expert_qgemv": ["qg::k_moe_gateup", "qg::k_moe_down"],
-    "lmhead_argmax": ["qg::k_affine<8, 2,", "qg::k_lmhead_finalize"],
+    "lmhead_argmax": ["qg::k_affine<8, 2, true, true>"],
     "mlp_block": ["qg::k_mlp_block<8>"],
 }
 
@@ -70,8 +74,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m1", action="store_true", help="skip the M=1 step (verify ratio)")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration context timings")
-    ap.add_argument("--submission", choices=["graph", "eager"], default="eager",
-                    help="timed steps replayed from a HIP graph of GRAPH_STEPS captured steps, or launched eagerly")
+    ap.add_argument("--submission", choices=["graph", "eager"], default="graph",
+                    help="timed steps replayed from a HIP graph of GRAPH_STEPS captured steps (default), or "
+                         "launched eagerly from Python")
     ap.add_argument("--mlp", choices=["persistent", "separate"], default="separate",
                     help="MLP block as one persistent launch (mlp_block_affine4_tiled; tile-order layout only) or "
                          "as the two entry points rmsnorm_gateup_swiglu + qgemv_affine4")
@@ -81,6 +86,10 @@ def parse():
     ap.add_argument("--pmc-pass", action="store_true",
                     help="short run for a rocprofv3 --pmc pass: a copy of CALIB_BYTES (counter calibration), "
                          "then --steps M=8 steps; prints one JSON line")
+    ap.add_argument("--pmc-m1", action="store_true", help="with --pmc-pass: also run the M=1 steps")
+    ap.add_argument("--kernel-times", metavar="STATS_CSV",
+                    help="turn a rocprofv3 --kernel-trace --stats kernel_stats.csv of a bench run into "
+                         "profiles/kernel_times.json (no GPU needed)")
     ap.add_argument("--compare-valu", metavar="NxK",
                     help="only time the affine-4 projection W[N,K] with the products on the matrix cores and on "
                          "the vector ALU (M = 1 and 8), print one JSON line; for a rocprofv3 run of that pair")
@@ -136,10 +145,36 @@ def traffic_from_counters(fetch_csv, write_csv):
     print(json.dumps(out))
 
 
+def kernel_times_from_stats(stats_csv):
+    """Average kernel-only duration (rocprofv3 kernel_stats.csv, AverageNs) of the
+    kernels of each entry point at M = 8, summed per entry point."""
+    import csv
+    avg = {}
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            avg[r["Name"]] = float(r["AverageNs"]) / 1e3
+    out = {"source_hash": kernel_source_hash(), "stats": os.path.basename(stats_csv), "entries": {}}
+    for entry, kernels in ENTRY_KERNELS.items():
+        ks = {}
+        for pat in kernels:
+            hit = [n for n in avg if pat in n]
+            if hit:
+                ks[hit[0]] = round(avg[hit[0]], 3)
+        if ks:
+            out["entries"][entry] = {"kernels_us": ks, "kernel_us_m8": round(sum(ks.values()), 3)}
+    with open(KERNEL_TIMES_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.traffic:
         traffic_from_counters(*args.traffic)
+        return
+    if args.kernel_times:
+        kernel_times_from_stats(args.kernel_times)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus N with N > 1 is not supported "
@@ -262,70 +297,62 @@ def main():
     names = (["mlp_block"] if persistent else ["rmsnorm_gateup_swiglu", "qgemv_affine4"]) + \
         ["moe_expert_qgemv", "lmhead_argmax"]
 
-    def run_step(i, M, b, ev=None):
+    def run_step(i, M, b):
         c = copies[i % C]
         ms = moe_stacks[i % 2]
         lg = logits[i % n_logit_sets]
-        e = iter(ev) if ev is not None else None
-        if e is not None:
-            next(e).record()
-        if persistent:
+        dr = draft[:M]
+        for name in names:
+            entry_call(name, c, ms, lg, dr, b)
+
+    def entry_call(name, c, ms, lg, dr, b):
+        if name == "mlp_block":
             ops.mlp_block_affine4_tiled(b["x"], gamma, vb["eps"], c["t_gu"], c["t_d"], D, I, h=b["h"], y=b["y"],
                                         ws=b["ws"])
-        elif tiled:
-            ops.rmsnorm_gateup_swiglu_tiled(b["x"], gamma, vb["eps"], *c["t_gu"], I, h=b["h"], ws=b["ws"])
-        else:
-            ops.rmsnorm_gateup_swiglu(b["x"], gamma, vb["eps"], c["codes_gu"], c["scales_gu"], c["biases_gu"],
-                                      h=b["h"], ws=b["ws"])
-        if e is not None:
-            next(e).record()
-        if persistent:
-            pass
-        elif tiled:
-            ops.qgemv_affine4_tiled(b["h"], *c["t_d"], D, y=b["y"], ws=b["ws"])
-            if e is not None:
-                next(e).record()
-        else:
-            ops.qgemv_affine4(b["h"], c["codes_d"], c["scales_d"], c["biases_d"], y=b["y"], ws=b["ws"])
-            if e is not None:
-                next(e).record()
-        ops.moe_expert_qgemv(xm, lg, top_k, ms["w_gu"], ms["w_down"], y=b["ym"], out_ids=b["mids"], out_w=b["mw"],
-                             ws=b["ws"])
-        if e is not None:
-            next(e).record()
-        dr = draft[:M].contiguous() if M < 8 else draft
-        if tiled:
-            ops.lmhead_argmax_tiled(b["xl"], *c["t_lm"], V, draft=dr, ids=b["ids"], accepted=b["acc"], ws=b["ws"])
-        else:
-            ops.lmhead_argmax(b["xl"], c["codes_lm"], c["scales_lm"], c["biases_lm"], draft=dr, ids=b["ids"],
-                              accepted=b["acc"], ws=b["ws"])
-        if e is not None:
-            next(e).record()
-
-    spread = {}
+        elif name == "rmsnorm_gateup_swiglu":
+            if tiled:
+                ops.rmsnorm_gateup_swiglu_tiled(b["x"], gamma, vb["eps"], *c["t_gu"], I, h=b["h"], ws=b["ws"])
+            else:
+                ops.rmsnorm_gateup_swiglu(b["x"], gamma, vb["eps"], c["codes_gu"], c["scales_gu"], c["biases_gu"],
+                                          h=b["h"], ws=b["ws"])
+        elif name == "qgemv_affine4":
+            if tiled:
+                ops.qgemv_affine4_tiled(b["h"], *c["t_d"], D, y=b["y"], ws=b["ws"])
+            else:
+                ops.qgemv_affine4(b["h"], c["codes_d"], c["scales_d"], c["biases_d"], y=b["y"], ws=b["ws"])
+        elif name == "moe_expert_qgemv":
+            ops.moe_expert_qgemv(xm, lg, top_k, ms["w_gu"], ms["w_down"], y=b["ym"], out_ids=b["mids"],
+                                 out_w=b["mw"], ws=b["ws"])
+        elif name == "lmhead_argmax":
+            if tiled:
+                ops.lmhead_argmax_tiled(b["xl"], *c["t_lm"], V, draft=dr, ids=b["ids"], accepted=b["acc"],
+                                        ws=b["ws"])
+            else:
+                ops.lmhead_argmax(b["xl"], c["codes_lm"], c["scales_lm"], c["biases_lm"], draft=dr, ids=b["ids"],
+                                  accepted=b["acc"], ws=b["ws"])
 
     graph_checks = {}
+    spread = {}
+    use_graph = args.submission == "graph"
 
-    def timed(M, steps, warmup):
+    def timed_steps(M, steps, warmup):
+        """K whole steps: HIP-graph replays of GRAPH_STEPS captured consecutive steps (or eager
+        launches); events on the launch stream around all of them, and at five sub-batch
+        boundaries for the spread."""
         b = bufs(M)
-        use_graph = args.submission == "graph"
-        s = torch.cuda.Stream() if use_graph else torch.cuda.current_stream()
+        s = torch.cuda.Stream()
         with torch.cuda.stream(s):
             for i in range(warmup):
                 run_step(i, M, b)
         torch.cuda.synchronize()
-        # graph length: the largest divisor of the step count up to GRAPH_STEPS, so
-        # that exactly `steps` steps are timed
         glen = max(d for d in range(1, GRAPH_STEPS + 1) if steps % d == 0) if use_graph else 1
+        g = None
         if use_graph:
-            # the graph holds glen consecutive steps and every replay repeats them
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=s):
                 for i in range(glen):
                     run_step(i, M, b)
             torch.cuda.synchronize()
-        # K steps timed start to end; events at five sub-batch boundaries (no
-        # synchronisation between them) give the spread of the per-step time
         units = steps // glen
         nsub = 5 if units >= 5 else 1
         cut = [round(units * j / nsub) for j in range(nsub + 1)]
@@ -342,7 +369,6 @@ def main():
                 evb[j + 1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
-        per_unit = glen
         ms_step = evb[0].elapsed_time(evb[nsub]) / steps
         if use_graph:
             # the replayed outputs (those of captured step glen - 1) against the same step run eagerly
@@ -355,19 +381,21 @@ def main():
                 raise SystemExit(f"bench.py: graph replay at M={M} differs from the eager step")
             graph_checks[f"M{M}"] = f"{glen}-step graph: replay == eager (bit-identical)"
             del g
-        sub = [evb[j].elapsed_time(evb[j + 1]) / ((cut[j + 1] - cut[j]) * per_unit) for j in range(nsub)]
+        sub = [evb[j].elapsed_time(evb[j + 1]) / ((cut[j + 1] - cut[j]) * glen) for j in range(nsub)]
         spread[M] = {"median_ms": round(float(np.median(sub)), 5), "p10_ms": round(float(np.percentile(sub, 10)), 5),
                      "p90_ms": round(float(np.percentile(sub, 90)), 5), "sub_batches": nsub}
-        # per-kernel durations: the same steps again with events around each launch
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
-        with torch.cuda.stream(s):
-            for i in range(steps):
-                run_step(warmup + steps + i, M, b, evs[i])
-        torch.cuda.synchronize()
-        per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)])) * 1e3
-               for j, n in enumerate(names)}
-        inst = float(np.mean([evs[i][0].elapsed_time(evs[i][len(names)]) for i in range(steps)]))
-        return ms_step, wall, per, inst, b
+        return ms_step, wall, b
+
+    def entry_times(M):
+        """Per-call time of each entry point of the step: a HIP graph of 2*C back-to-back calls
+        (rotating weight copies, MoE stacks and router logits) replayed, events on its stream."""
+        b = bufs(M)
+        per = {}
+        for name in names:
+            fn = lambda i, nm=name: entry_call(nm, copies[i % C], moe_stacks[i % 2], logits[i % n_logit_sets],
+                                               draft[:M], b)
+            per[name] = graph_us(torch, fn, 2 * C)
+        return per
 
     if args.pmc_pass:
         # an elementwise kernel that reads and writes CALIB_BYTES (a plain
@@ -378,28 +406,33 @@ def main():
             torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-        b = bufs(8)
-        for i in range(args.warmup + args.steps):
-            run_step(i, 8, b)
+        for M in (8, 1) if args.pmc_m1 else (8,):
+            b = bufs(M)
+            for i in range(args.warmup + args.steps):
+                run_step(i, M, b)
         torch.cuda.synchronize()
         print(json.dumps({"pmc_pass": True, "calib_bytes": CALIB_BYTES, "steps": args.warmup + args.steps}), flush=True)
         return
 
-    log(f"[bench] timing M=8: warmup {args.warmup}, steps {args.steps}")
-    ms8, wall8, per8, inst8, b8 = timed(8, args.steps, args.warmup)
+    log(f"[bench] timing M=8: warmup {args.warmup}, steps {args.steps}, "
+        + ("graph replays" if use_graph else "eager launches"))
+    ms8, wall8, b8 = timed_steps(8, args.steps, args.warmup)
     bytes8, wbytes = step_bytes(8)
     total8 = sum(bytes8.values())
     value = total8 / (ms8 * 1e-3) / 1e9
-    log(f"[bench] M=8: {ms8 * 1e3:.1f} us/step -> {value:.0f} GB/s; per kernel (us): "
-        + ", ".join(f"{n}={per8[n]:.1f}" for n in names))
     accepted = int(b8["acc"].cpu()[0])
+    per8 = entry_times(8)
+    log(f"[bench] M=8: {ms8 * 1e3:.1f} us/step -> {value:.0f} GB/s; per call (us): "
+        + ", ".join(f"{n}={per8[n]:.1f}" for n in names))
 
     ms1 = per1 = None
     if not args.no_m1:
         s1 = max(20, args.steps // 2)
         log(f"[bench] timing M=1: steps {s1}")
-        ms1, _, per1, _, _ = timed(1, s1, max(5, args.warmup // 2))
-        log(f"[bench] M=1: {ms1 * 1e3:.1f} us/step; ratio {ms8 / ms1:.3f}")
+        ms1, _, _ = timed_steps(1, s1, max(5, args.warmup // 2))
+        per1 = entry_times(1)
+        log(f"[bench] M=1: {ms1 * 1e3:.1f} us/step; ratio {ms8 / ms1:.3f}; per call (us): "
+            + ", ".join(f"{n}={per1[n]:.1f}" for n in names))
 
     # context: the runtime's device-to-device copy of 1 GiB (bytes read + written)
     src = torch.empty(2 ** 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -429,6 +462,8 @@ def main():
     del src
 
     cfg = None if args.no_configs else config_timings(torch, ops, synth, to_dev, dev)
+    if cfg is not None:
+        cfg["mlp_stack_28x1024x3072"] = stack_timings(torch, ops, synth, to_dev, dev)
 
     kernels = {}
     for n in names:
@@ -441,10 +476,11 @@ def main():
                       "verify_ratio": round(per8[n] / per1[n], 3)})
         kernels[n] = k
 
-    # dominant kernel = largest share of the step's time
+    # dominant kernel = the entry point with the largest share of the step's time
     dom = max(names, key=lambda n: per8[n])
     dom_gbs = bytes8[dom] / (per8[dom] * 1e-6) / 1e9
     traffic = None
+    prof = {}
     if os.path.exists(TRAFFIC_FILE):
         try:
             tf = json.load(open(TRAFFIC_FILE))
@@ -453,11 +489,24 @@ def main():
                 traffic = ent.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
+    if os.path.exists(KERNEL_TIMES_FILE):
+        try:
+            kt = json.load(open(KERNEL_TIMES_FILE))
+            if kt.get("source_hash") == kernel_source_hash():
+                prof = kt.get("entries", {}).get(dom, {})
+        except (OSError, ValueError):
+            prof = {}
     entry = {"mlp_block": "mlp_block_affine4_tiled", "moe_expert_qgemv": "moe_expert_qgemv"}.get(
         dom, dom + ("_tiled" if tiled else ""))
     roofline = {"kernel": entry, "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes_per_launch": bytes8[dom], "avg_launch_us": round(per8[dom], 2)}
+                "algorithmic_bytes_per_launch": bytes8[dom], "avg_launch_us": round(per8[dom], 2),
+                "timing": "HIP events around a graph of back-to-back calls on its stream, per call"}
+    if prof.get("kernel_us_m8"):
+        ku = prof["kernel_us_m8"]
+        roofline.update({"kernel_only_us": ku, "frac_kernel_only": round(bytes8[dom] / (ku * 1e-6) / 1e9 /
+                                                                         PEAK_HBM_GBS, 4),
+                         "kernel_only_source": "rocprofv3 --kernel-trace average, " + KERNEL_TIMES_FILE_REL})
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -474,9 +523,9 @@ def main():
                    "M": 8, "weight_copies": C,
                    "mlp": ("one persistent launch (mlp_block_affine4_tiled)" if persistent
                            else "rmsnorm_gateup_swiglu + qgemv_affine4"),
-                   "submission": ("HIP graph replays of captured steps" if args.submission == "graph"
-                                  else "eager launches"),
-                   "layout": "tile-order (same bytes as canonical, packed at set-up)" if tiled else "canonical", "algorithmic_bytes_per_step": total8,
+                   "submission": ("HIP graph replays of captured steps" if use_graph else "eager launches"),
+                   "layout": "tile-order (same bytes as canonical, packed at set-up)" if tiled else "canonical",
+                   "algorithmic_bytes_per_step": total8,
                    "weight_bytes_per_step": sum(wbytes.values()), "accum": "fp32", "weights": "4-bit"},
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "ms_per_step_m1": round(ms1, 5) if ms1 else None,
@@ -492,7 +541,6 @@ def main():
         "roofline_frac_of_stream_read": round(dom_gbs / read_gbs, 4),
         "step_spread": {f"M{m}": v for m, v in spread.items()},
         "configs_context": cfg,
-        "instrumented_ms_per_step": round(inst8, 5),
         "graph_check": graph_checks or None,
         "wall_s_timed": round(wall8, 4),
         "kernel_source_hash": kernel_source_hash(),
@@ -500,18 +548,38 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def per_call_us(torch, fn, reps):
-    """Microseconds per call of fn(i): a short warm-up, then HIP events around reps back-to-back calls."""
-    for i in range(min(reps, 20)):
-        fn(i)
+def graph_us(torch, fn, ncalls, reps=10):
+    """Microseconds per call of fn(i): ncalls back-to-back calls (i = 0..ncalls-1) captured in a
+    HIP graph on a side stream, replayed reps times after a warm-up, HIP events on that stream.
+    The host's launch cost is out of the timed region, as it is for a caller that replays graphs."""
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for i in range(ncalls):
+            fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(ncalls):
+            fn(i)
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(reps):
-        fn(i)
-    e1.record()
+    with torch.cuda.stream(s):
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps * 1e3
+    us = e0.elapsed_time(e1) * 1e3 / (reps * ncalls)
+    del g
+    return us
+
+
+def per_call_us(torch, fn, reps):
+    """Microseconds per call of fn(i), graph-replayed (see graph_us)."""
+    return graph_us(torch, fn, reps)
 
 
 def compare_valu(torch, ops, synth, to_dev, dev, N, K, per_call):
@@ -536,6 +604,101 @@ def compare_valu(torch, ops, synth, to_dev, dev, N, K, per_call):
             r[f"M{M}_{name}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
         r[f"M{M}_valu_over_mfma"] = round(r[f"M{M}_valu"]["us"] / r[f"M{M}_mfma"]["us"], 3)
     return r
+
+
+def stack_timings(torch, ops, synth, to_dev, dev, L=28, D=1024, I=3072):
+    """Context: a stack of L distinct 0.6B-shaped MLP blocks (the 28 MLPs of a
+    decode step), block l + 1 taking block l's output, timed per pass at M = 1
+    and 8 in five ways: the separate entry points launched from the host one by
+    one (eager) and captured in one graph; one persistent launch per block,
+    eager and in one graph; and one persistent launch for the whole stack.
+    Enough stack copies rotate (>= 512 MB) that no pass finds its weights in
+    the Infinity Cache."""
+    gus, dns, gams = [], [], []
+    for l in range(L):
+        d = synth.mlp_block(M=8, D=D, I=I, seed=21000 + l)
+        if l == 0:
+            x8 = to_dev(d["x"], "bf16")
+        gus.append(ops.tile_pack(to_dev(d["codes_gu"], "u32"), to_dev(d["scales_gu"], "bf16"),
+                                 to_dev(d["biases_gu"], "bf16")))
+        dns.append(ops.tile_pack(to_dev(d["codes_d"], "u32"), to_dev(d["scales_d"], "bf16"),
+                                 to_dev(d["biases_d"], "bf16")))
+        gams.append(to_dev(d["gamma"], "bf16"))
+    nb_layer = 2 * I * D // 2 + 2 * I * (D // 64) * 4 + D * I // 2 + D * (I // 64) * 4
+    one = {"gamma": torch.stack(gams).contiguous(), "gu_c": torch.cat([g[0] for g in gus]),
+           "gu_s": torch.cat([g[1] for g in gus]), "dn_c": torch.cat([g[0] for g in dns]),
+           "dn_s": torch.cat([g[1] for g in dns])}
+    del gus, dns
+    n = max(2, (512 << 20) // (L * nb_layer) + 1)
+    stacks = [one] + [{k: v.clone() for k, v in one.items()} for _ in range(n - 1)]
+    gcb, gsb = ops.tiled_bytes(2 * I, D)
+    dcb, dsb = ops.tiled_bytes(D, I)
+
+    def layer(c, l):  # views of layer l of stack c
+        return ((c["gu_c"][l * gcb // 4:(l + 1) * gcb // 4], c["gu_s"][l * gsb // 2:(l + 1) * gsb // 2]),
+                (c["dn_c"][l * dcb // 4:(l + 1) * dcb // 4], c["dn_s"][l * dsb // 2:(l + 1) * dsb // 2]),
+                c["gamma"][l])
+    views = [[layer(c, l) for l in range(L)] for c in stacks]
+    out = {"layers": L, "D": D, "I": I, "stack_copies": n, "weight_bytes_per_pass": L * nb_layer}
+    for M in (1, 8):
+        xm = x8[:M].contiguous()
+        h = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+        ys = torch.empty((L, M, D), dtype=torch.bfloat16, device=dev)
+        ws = ops.workspace(max(ops.workspace_bytes("mlp_stack_affine4_tiled", M, D, I),
+                               ops.workspace_bytes("rmsnorm_gateup_swiglu_tiled", M, I, D),
+                               ops.workspace_bytes("qgemv_affine4_tiled", M, D, I)), dev)
+        b = L * (nb_layer + M * D * 2 * 2 + 2 * M * I * 2 + D * 2)
+
+        def separate(i):
+            v = views[i % n]
+            xin = xm
+            for l in range(L):
+                gu, dn, gam = v[l]
+                ops.rmsnorm_gateup_swiglu_tiled(xin, gam, 1e-6, *gu, I, h=h, ws=ws)
+                ops.qgemv_affine4_tiled(h, *dn, D, y=ys[l], ws=ws)
+                xin = ys[l]
+
+        def blocks(i):
+            v = views[i % n]
+            xin = xm
+            for l in range(L):
+                gu, dn, gam = v[l]
+                ops.mlp_block_affine4_tiled(xin, gam, 1e-6, gu, dn, D, I, h=h, y=ys[l], ws=ws)
+                xin = ys[l]
+
+        def stack(i):
+            c = stacks[i % n]
+            ops.mlp_stack_affine4_tiled(xm, c["gamma"], 1e-6, c["gu_c"], c["gu_s"], c["dn_c"], c["dn_s"], L, D, I,
+                                        h=h, ys=ys, ws=ws)
+
+        def eager_us(fn, reps):
+            for i in range(n):
+                fn(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / reps
+
+        res = {}
+        for name, fn, graphed in (("separate_eager", separate, False), ("separate_graph", separate, True),
+                                  ("block_per_layer_eager", blocks, False), ("block_per_layer_graph", blocks, True),
+                                  ("stack_one_launch", stack, False), ("stack_one_launch_graph", stack, True)):
+            try:
+                us = graph_us(torch, fn, 2 * n, reps=5) if graphed else eager_us(fn, 4 * n)
+            except Exception as e:  # a launch kind the graph capture refuses is reported, not fatal
+                res[name] = {"error": str(e)[:160]}
+                torch.cuda.synchronize()
+                continue
+            res[name] = {"us": round(us, 1), "us_per_layer": round(us / L, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
+        assert ops.mlp_failures(ws) == 0, "a grid barrier wait gave up during the stack timings"
+        out[f"M{M}"] = res
+    del stacks, views
+    log("[bench] stack: " + json.dumps(out))
+    return out
 
 
 def config_timings(torch, ops, synth, to_dev, dev):
@@ -692,29 +855,52 @@ def config_timings(torch, ops, synth, to_dev, dev):
     return out
 
 
-def cpu_baseline(vb, lm, moe, step_bytes, min_seconds=10.0, max_steps=12):
-    """The CPU oracle (plain single-threaded C, fp64) on the same step: the
-    full MLP block at M=8, the MoE token, and the LM head at M=8 with its draft
-    ids.  Whole steps are repeated (the MoE router logits rotating as in the
-    GPU run) until min_seconds of CPU work have been timed (at most
-    max_steps); reported in the same unit as the GPU value."""
+def _host_threads():
+    """Threads the oracle may use on this host: the process's affinity set, capped by
+    OMP_NUM_THREADS when that is set (the GPU machine grants 16 CPUs per GPU)."""
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS")
+    n = min(aff, int(env)) if env and env.isdigit() and int(env) > 0 else aff
+    return max(1, n), aff
+
+
+def cpu_baseline(vb, lm, moe, step_bytes, min_seconds=10.0, max_steps=64):
+    """The CPU oracle (plain C, fp64) on the same step: the full MLP block at M=8,
+    the MoE token, and the LM head at M=8 with its draft ids.  Whole steps are
+    repeated (the MoE router logits rotating as in the GPU run) until about
+    min_seconds of work have been timed.  Run twice: on all the host threads
+    the process may use (the OpenMP build: output rows split over threads, the
+    same bits) -- the reported value -- and on one thread.  Same unit as the GPU
+    value."""
     import oracle
-    n, t = 0, time.perf_counter()
-    while True:
-        oracle.mlp_block(vb["x"], vb["gamma"], vb["eps"], vb["codes_gu"], vb["scales_gu"], vb["biases_gu"],
-                         vb["codes_d"], vb["scales_d"], vb["biases_d"])
-        oracle.moe(moe["x"], moe["logits"][n % len(moe["logits"])], moe["top_k"], moe["w_gu"], moe["w_down"],
-                   moe["E"], moe["D"], moe["I"])
-        oracle.lmhead(lm["x"], lm["codes"], lm["scales"], lm["biases"], draft=lm["draft"], want_logits=False)
-        n += 1
-        dt = time.perf_counter() - t
-        if dt >= min_seconds or n >= max_steps:
-            break
-    log(f"[bench] cpu oracle: {n} full steps in {dt:.1f}s")
-    return {"value": round(n * step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+
+    def run(threads, seconds):
+        used = oracle.use_threads(threads)
+        n, t = 0, time.perf_counter()
+        while True:
+            oracle.mlp_block(vb["x"], vb["gamma"], vb["eps"], vb["codes_gu"], vb["scales_gu"], vb["biases_gu"],
+                             vb["codes_d"], vb["scales_d"], vb["biases_d"])
+            oracle.moe(moe["x"], moe["logits"][n % len(moe["logits"])], moe["top_k"], moe["w_gu"], moe["w_down"],
+                       moe["E"], moe["D"], moe["I"])
+            oracle.lmhead(lm["x"], lm["codes"], lm["scales"], lm["biases"], draft=lm["draft"], want_logits=False)
+            n += 1
+            dt = time.perf_counter() - t
+            if dt >= seconds or n >= max_steps:
+                break
+        return n, dt, used
+
+    threads, aff = _host_threads()
+    n, dt, used = run(threads, min_seconds)
+    n1, dt1, _ = run(1, min_seconds)
+    oracle.use_threads(1)
+    log(f"[bench] cpu oracle: {n} full steps in {dt:.1f}s on {used} threads; {n1} in {dt1:.1f}s on 1 thread")
+    return {"value": round(n * step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
             "sample": f"{n} full steps (MLP block M=8, MoE token with rotating router logits, LM head M=8), "
-                      "same seeded inputs as the GPU run",
-            "steps": n, "seconds": round(dt, 2)}
+                      "same seeded inputs as the GPU run; output rows split over the threads (OpenMP build of "
+                      "the same C, same bits)",
+            "steps": n, "seconds": round(dt, 2), "cpu_count": os.cpu_count(), "affinity_cpus": aff,
+            "single_thread": {"value": round(n1 * step_bytes / dt1 / 1e9, 4), "cores": 1, "steps": n1,
+                              "seconds": round(dt1, 2)}}
 
 
 if __name__ == "__main__":

@@ -540,7 +540,13 @@ qg_status plan_affine(int mode, QgAffineArgs& a, const char* fn, size_t* lds_out
   // costliest, prefers many short slices on every slot; plain projections run
   // best on three quarters of the slots, the LM head and the other modes on
   // half, with two or more tiles per wave.
-  const int target = (mode == QG_MODE_GATEUP) ? 4 * kTargetWaves : 2 * kTargetWaves;
+#ifndef QG_TARGET_GATEUP
+#define QG_TARGET_GATEUP (4 * kTargetWaves)
+#endif
+#ifndef QG_TARGET_OTHER
+#define QG_TARGET_OTHER (2 * kTargetWaves)
+#endif
+  const int target = (mode == QG_MODE_GATEUP) ? QG_TARGET_GATEUP : QG_TARGET_OTHER;
   const int fill_pct = (mode == QG_MODE_GATEUP) ? QG_FILL_GATEUP : (mode == QG_MODE_PLAIN ? QG_FILL_PLAIN : QG_FILL_OTHER);
   Plan pl = plan_split(a.ntiles, a.nchunks, std::max(cps_max, 1), allow_split, target);
   // slices start on a batch boundary (4 chunks) when that keeps them within LDS
@@ -697,23 +703,30 @@ __global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ p
 // ------------------------------------------------ persistent MLP block --
 constexpr int kMlpSpinLimit = 200000;  // polls of one wait before a workgroup gives up (tens of ms)
 
-qg_status do_check_mlp(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* gu_codes_t,
-                       const uint16_t* gu_sb_t, const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
-                       uint16_t* y, int M, int D, int I, BufList* all = nullptr) {
-  const char* fn = "mlp_block_affine4_tiled";
+// The persistent MLP stack: L layers of stacked tile-order weights; gamma
+// [L][D]; h [M][I] (scratch output, the last layer's h); ys [L][M][D] (layer
+// l's output, layer l + 1's input).  L = 1 is mlp_block_affine4_tiled.
+constexpr int kMaxLayers = 4096;
+
+qg_status do_check_mlp(const char* fn, const uint16_t* x, const uint16_t* gamma, float eps,
+                       const uint32_t* gu_codes_t, const uint16_t* gu_sb_t, const uint32_t* dn_codes_t,
+                       const uint16_t* dn_sb_t, uint16_t* h, uint16_t* ys, int L, int M, int D, int I,
+                       BufList* all = nullptr) {
+  if (L < 1 || L > kMaxLayers) return fail(QG_EINVAL, "%s: L=%d must be in 1..%d", fn, L, kMaxLayers);
   if (M < 1 || M > 8) return fail(QG_EINVAL, "%s: M=%d must be in 1..8", fn, M);
   if (D <= 0 || D % 512 != 0) return fail(QG_EINVAL, "%s: D=%d must be a positive multiple of 512", fn, D);
   if (I <= 0 || I % 512 != 0) return fail(QG_EINVAL, "%s: I=%d must be a positive multiple of 512", fn, I);
   if ((long long)I * 2 * 16 > 0x7FFFFFFFLL || (long long)D * 16 > 0x7FFFFFFFLL)
     return fail(QG_EINVAL, "%s: D=%d or I=%d too large", fn, D, I);
   if (!(eps > 0.0f) || eps != eps || eps > 3.0e38f) return fail(QG_EINVAL, "%s: eps must be positive and finite", fn);
+  const size_t l = (size_t)L;
   const Buf in[] = {{x, (size_t)M * D * 2, "x"},
-                    {gamma, (size_t)D * 2, "gamma"},
-                    {gu_codes_t, tiled_codes_bytes(2 * I, D), "gu_codes_t"},
-                    {gu_sb_t, tiled_sb_bytes(2 * I, D), "gu_sb_t"},
-                    {dn_codes_t, tiled_codes_bytes(D, I), "dn_codes_t"},
-                    {dn_sb_t, tiled_sb_bytes(D, I), "dn_sb_t"}};
-  const Buf out[] = {{h, (size_t)M * I * 2, "h"}, {y, (size_t)M * D * 2, "y"}};
+                    {gamma, l * D * 2, "gamma"},
+                    {gu_codes_t, l * tiled_codes_bytes(2 * I, D), "gu_codes_t"},
+                    {gu_sb_t, l * tiled_sb_bytes(2 * I, D), "gu_sb_t"},
+                    {dn_codes_t, l * tiled_codes_bytes(D, I), "dn_codes_t"},
+                    {dn_sb_t, l * tiled_sb_bytes(D, I), "dn_sb_t"}};
+  const Buf out[] = {{h, (size_t)M * I * 2, "h"}, {ys, l * M * D * 2, L > 1 ? "ys" : "y"}};
   qg_status st;
   for (const Buf& b : in)
     if ((st = check_ptr(b, 16, fn))) return st;
@@ -819,44 +832,35 @@ const char* qg_last_error(void) { return g_err; }
 
 size_t qg_workspace_header_bytes(void) { return kWsHeader; }
 
-// ------------------------------------------------------ mlp_block_affine4 --
-static qg_status prep_mlp(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* gu_codes_t,
-                          const uint16_t* gu_sb_t, const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
-                          uint16_t* y, int M, int D, int I, const void* ws, size_t ws_bytes, MlpCall& c) {
-  const char* fn = "mlp_block_affine4_tiled";
+// ------------------------------------------- mlp_block / mlp_stack_affine4 --
+static qg_status prep_mlp(const char* fn, const uint16_t* x, const uint16_t* gamma, float eps,
+                          const uint32_t* gu_codes_t, const uint16_t* gu_sb_t, const uint32_t* dn_codes_t,
+                          const uint16_t* dn_sb_t, uint16_t* h, uint16_t* ys, int L, int M, int D, int I,
+                          const void* ws, size_t ws_bytes, MlpCall& c) {
   BufList bl;
-  qg_status st = do_check_mlp(x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, y, M, D, I, &bl);
+  qg_status st = do_check_mlp(fn, x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, ys, L, M, D, I, &bl);
   if (st) return st;
-  mlp_fill(c, x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, y, M, D, I);
+  mlp_fill(c, x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, ys, M, D, I);
   if ((st = mlp_layout(c, fn, kMaxCus))) return st;
   return check_ws(fn, ws, ws_bytes, ws_total(c.scratch, true), bl.b, bl.n);
 }
 
-size_t mlp_block_affine4_tiled_workspace(int M, int D, int I) {
+static size_t mlp_query(int M, int D, int I) {
   if (M < 1 || M > 8 || D <= 0 || D % 512 || I <= 0 || I % 512) return 0;
   MlpCall c;
   mlp_fill(c, nullptr, nullptr, 1e-6f, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M, D, I);
-  if (mlp_layout(c, "mlp_block_affine4_tiled", kMaxCus)) return 0;
+  if (mlp_layout(c, "mlp_stack_affine4_tiled", kMaxCus)) return 0;
   return ws_total(c.scratch, true);
 }
 
-qg_status qg_check_mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma, float eps,
-                                           const uint32_t* gu_codes_t, const uint16_t* gu_sb_t,
-                                           const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
-                                           uint16_t* y, int M, int D, int I, const void* ws, size_t ws_bytes) {
+static qg_status run_mlp(const char* fn, const uint16_t* x, const uint16_t* gamma, float eps,
+                         const uint32_t* gu_codes_t, const uint16_t* gu_sb_t, const uint32_t* dn_codes_t,
+                         const uint16_t* dn_sb_t, uint16_t* h, uint16_t* ys, int L, int M, int D, int I, void* ws,
+                         size_t ws_bytes, void* stream) {
   clear_err();
   MlpCall c;
-  return prep_mlp(x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, y, M, D, I, ws, ws_bytes, c);
-}
-
-qg_status mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* gu_codes_t,
-                                  const uint16_t* gu_sb_t, const uint32_t* dn_codes_t, const uint16_t* dn_sb_t,
-                                  uint16_t* h, uint16_t* y, int M, int D, int I, void* ws, size_t ws_bytes,
-                                  void* stream) {
-  const char* fn = "mlp_block_affine4_tiled";
-  clear_err();
-  MlpCall c;
-  qg_status st = prep_mlp(x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, y, M, D, I, ws, ws_bytes, c);
+  qg_status st = prep_mlp(fn, x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, ys, L, M, D, I, ws, ws_bytes,
+                          c);
   if (st) return st;
   if ((st = check_device())) return st;
   if ((st = mlp_layout(c, fn, device_cus()))) return st;
@@ -870,9 +874,57 @@ qg_status mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma, floa
   pa.part = reinterpret_cast<float*>(base + c.off_part_a);
   pa.ssq_part = reinterpret_cast<float*>(base + c.off_ssq_a);
   pc.part = reinterpret_cast<float*>(base + c.off_part_c);
-  return launched(qg_launch_mlp(pa, pc, static_cast<unsigned char*>(ws), kMlpSpinLimit, P, c.lds,
+  QgMlpStack stk{};
+  stk.L = L;
+  stk.gu_codes = tiled_codes_bytes(2 * I, D) / 4;
+  stk.gu_sb = tiled_sb_bytes(2 * I, D) / 2;
+  stk.dn_codes = tiled_codes_bytes(D, I) / 4;
+  stk.dn_sb = tiled_sb_bytes(D, I) / 2;
+  stk.gamma = (size_t)D;
+  stk.y = (size_t)M * D;
+  return launched(qg_launch_mlp(pa, pc, stk, static_cast<unsigned char*>(ws), kMlpSpinLimit, P, c.lds,
                                 (hipStream_t)stream),
                   fn);
+}
+
+size_t mlp_block_affine4_tiled_workspace(int M, int D, int I) { return mlp_query(M, D, I); }
+size_t mlp_stack_affine4_tiled_workspace(int M, int D, int I) { return mlp_query(M, D, I); }
+
+qg_status qg_check_mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma, float eps,
+                                           const uint32_t* gu_codes_t, const uint16_t* gu_sb_t,
+                                           const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
+                                           uint16_t* y, int M, int D, int I, const void* ws, size_t ws_bytes) {
+  clear_err();
+  MlpCall c;
+  return prep_mlp("mlp_block_affine4_tiled", x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, y, 1, M, D,
+                  I, ws, ws_bytes, c);
+}
+
+qg_status mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* gu_codes_t,
+                                  const uint16_t* gu_sb_t, const uint32_t* dn_codes_t, const uint16_t* dn_sb_t,
+                                  uint16_t* h, uint16_t* y, int M, int D, int I, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  return run_mlp("mlp_block_affine4_tiled", x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, y, 1, M, D, I,
+                 ws, ws_bytes, stream);
+}
+
+qg_status qg_check_mlp_stack_affine4_tiled(const uint16_t* x, const uint16_t* gamma, float eps,
+                                           const uint32_t* gu_codes_t, const uint16_t* gu_sb_t,
+                                           const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
+                                           uint16_t* ys, int L, int M, int D, int I, const void* ws,
+                                           size_t ws_bytes) {
+  clear_err();
+  MlpCall c;
+  return prep_mlp("mlp_stack_affine4_tiled", x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, ys, L, M, D,
+                  I, ws, ws_bytes, c);
+}
+
+qg_status mlp_stack_affine4_tiled(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* gu_codes_t,
+                                  const uint16_t* gu_sb_t, const uint32_t* dn_codes_t, const uint16_t* dn_sb_t,
+                                  uint16_t* h, uint16_t* ys, int L, int M, int D, int I, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  return run_mlp("mlp_stack_affine4_tiled", x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, h, ys, L, M, D,
+                 I, ws, ws_bytes, stream);
 }
 
 int32_t mlp_block_affine4_tiled_failures(void* ws, void* stream) {

@@ -106,7 +106,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int PL = planes(MODE);  // activation planes (hi, lo)
   constexpr int BATCH = 4;                              // chunks whose loads are issued together
-  constexpr int R = (MODE == QG_MODE_LMHEAD) ? 2 : 1;   // steps of weight loads in flight per wave
+#ifndef QG_R_SPLIT
+#define QG_R_SPLIT 1
+#endif
+  constexpr int R = (MODE == QG_MODE_LMHEAD) ? 2 : QG_R_SPLIT;  // steps of weight loads in flight per wave
   constexpr int CW = (MODE == QG_MODE_PLAIN8) ? 2 : 1;  // 16-byte code loads per lane and chunk
   constexpr bool NTL = (MODE == QG_MODE_LMHEAD);        // non-temporal weight loads (the long LM-head stream)
   const int lane = threadIdx.x & 63;

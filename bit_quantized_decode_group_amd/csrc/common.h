@@ -252,8 +252,14 @@ int qg_launch_tile_pack(const uint32_t* codes, const uint16_t* scales, const uin
 // at byte 16, count of failed launches at byte 20); grid a multiple of 32,
 // every workgroup resident (cooperative launch).
 size_t qg_mlp_state_bytes();
-int qg_launch_mlp(const QgAffineArgs& pa, const QgAffineArgs& pc, unsigned char* state, int spin_limit, int grid,
-                  size_t lds, hipStream_t stream);
+// A stack of L MLP blocks in one launch: strides (in elements) from one
+// layer's tile-order weights, gamma and output to the next layer's.
+struct QgMlpStack {
+  int L;
+  size_t gu_codes, gu_sb, dn_codes, dn_sb, gamma, y;
+};
+int qg_launch_mlp(const QgAffineArgs& pa, const QgAffineArgs& pc, const QgMlpStack& stack, unsigned char* state,
+                  int spin_limit, int grid, size_t lds, hipStream_t stream);
 const void* qg_mlp_kernel(int M);  // the kernel instance for M rows (occupancy queries)
 // Input randomised Hadamard transform: x [M][K] bf16 and signs [K] to the hi
 // and lo bf16 planes of (1/sqrt(had)) H_had diag(s) x, blockwise along K.

@@ -15,6 +15,12 @@
 // job, so that the down projection's weights stream in while phase B and the
 // barriers run.
 //
+// The same kernel runs a stack of L blocks, block l + 1 taking block l's
+// output as its input (the page's next step: one dispatch spanning layers).
+// A fifth barrier separates the blocks; before waiting on it each workgroup
+// issues the loads of its first gate/up step of the next block, whose
+// weights do not depend on the block that is finishing.
+//
 // Data handed from one workgroup to another within the launch (partial sums,
 // sums of squares, h) is written with agent-scope stores and read with
 // agent-scope loads; the barrier waits for each thread's stores to complete
@@ -149,7 +155,9 @@ __device__ __forceinline__ void load_tstep(const QgAffineArgs& p, const Job& j, 
 template <int M, int MODE, int R>
 __device__ void run_job(const QgAffineArgs& p, int job, unsigned char* smem, TBuf (&ring)[R], bool preloaded) {
   constexpr int PL = planes(MODE);
-  constexpr bool COH_X = (MODE == QG_MODE_PLAIN);
+  // X was written earlier in this launch (h by phase B; a layer's input by the
+  // previous layer's phase D), so it is read with agent-scope loads
+  constexpr bool COH_X = true;
   const Job j = job_of(p, job);
   const int nc = j.nc;
   const int lane = threadIdx.x & 63, wave = wave_id(), W = blockDim.x >> 6;
@@ -315,55 +323,86 @@ __device__ __forceinline__ void gateup_pair(const QgAffineArgs& p, int m, int n,
 }  // namespace
 
 // grid: one workgroup per resident slot (a multiple of kBarGroups); pa
-// (gate/up) and pc (down) carry their split plans; pc.x is h; bar: the
-// barrier state (kBarGroups + 1 slots of 256 bytes).
+// (gate/up) and pc (down) carry the split plans and layer 0's pointers; st
+// gives the number of layers and the strides from one layer's weights,
+// gamma and output to the next's; pc.x is h; bar: the barrier state
+// (kBarGroups + 1 slots of 256 bytes).  Layer l reads its input from layer
+// l - 1's output (layer 0: pa.x) and writes its output to pc.y + l * y_stride.
 template <int M>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
-    k_mlp_block(QgAffineArgs pa, QgAffineArgs pc, unsigned char* bar, int spin_limit) {
+    k_mlp_block(QgAffineArgs pa0, QgAffineArgs pc0, QgMlpStack st, unsigned char* bar, int spin_limit) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int R = 2;  // down-projection steps in flight per wave (prefetched before the barriers)
   const int P = gridDim.x;
-  // phase A (one step in flight, as the separate gate/up kernel)
-  {
-    TBuf ring[1];
-    for (int job = blockIdx.x; job < pa.S * pa.rgroups; job += P) run_job<M, QG_MODE_GATEUP, 1>(pa, job, smem, ring, false);
-  }
   __shared__ unsigned long long target;
-  barrier_arrive(bar, &target);
-  // the first phase-C job's weights go out while the barriers and phase B run
-  TBuf pre[R];
-  const int jc = pc.S * pc.rgroups;
-  if ((int)blockIdx.x < jc) {
-    const Job j = job_of(pc, blockIdx.x);
-#pragma unroll
-    for (int r = 0; r < R; ++r) load_tstep(pc, j, min(r, max(j.nsteps - 1, 0)), pre[r]);
-  }
-  barrier_wait(bar, &target, spin_limit);
-  // phase B
-  {
-    const int I = pa.N / 2;
-    const int npairs = pa.M * (I / 2);
-    uint32_t* h = reinterpret_cast<uint32_t*>(pa.y);
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < npairs; i += P * blockDim.x) {
-      const int m = i / (I / 2);
-      gateup_pair(pa, m, 2 * (i - m * (I / 2)), h);
+  const int ja = pa0.S * pa0.rgroups, jc = pc0.S * pc0.rgroups;
+  // the first gate/up job's weights of the next layer go out before the barrier
+  // that precedes its phase A (layer 0: at the start)
+  TBuf ring_a[1];
+  bool a_pre = false;
+  for (int l = 0; l < st.L; ++l) {
+    QgAffineArgs pa = pa0, pc = pc0;
+    pa.codes += (size_t)l * st.gu_codes;
+    pa.scales += (size_t)l * st.gu_sb;
+    pa.biases = pa.scales;
+    pa.gamma += (size_t)l * st.gamma;
+    if (l > 0) pa.x = pc0.y + (size_t)(l - 1) * st.y;
+    pc.codes += (size_t)l * st.dn_codes;
+    pc.scales += (size_t)l * st.dn_sb;
+    pc.biases = pc.scales;
+    pc.y += (size_t)l * st.y;
+    // phase A (one step in flight, as the separate gate/up kernel)
+    for (int job = blockIdx.x; job < ja; job += P) {
+      run_job<M, QG_MODE_GATEUP, 1>(pa, job, smem, ring_a, a_pre && job == (int)blockIdx.x);
     }
-  }
-  barrier_arrive(bar, &target);
-  barrier_wait(bar, &target, spin_limit);
-  // phase C
-  for (int job = blockIdx.x; job < jc; job += P) run_job<M, QG_MODE_PLAIN, R>(pc, job, smem, pre, job == (int)blockIdx.x);
-  barrier_arrive(bar, &target);
-  barrier_wait(bar, &target, spin_limit);
-  // phase D (the same arithmetic as k_split_reduce for a plain projection);
-  // agent-scope stores, so that a failed launch's NaN fill below is ordered
-  // after them
-  {
-    const int n_out = pc.M * pc.N;
-    const size_t stride = (size_t)pc.M * pc.N;
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_out; i += P * blockDim.x)
-      __hip_atomic_store(pc.y + i, f32_to_bf16_bits(sum_slices(pc.part, stride, (size_t)i, pc.S)), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    a_pre = false;
+    barrier_arrive(bar, &target);
+    // the first phase-C job's weights go out while the barriers and phase B run
+    TBuf pre[R];
+    if ((int)blockIdx.x < jc) {
+      const Job j = job_of(pc, blockIdx.x);
+#pragma unroll
+      for (int r = 0; r < R; ++r) load_tstep(pc, j, min(r, max(j.nsteps - 1, 0)), pre[r]);
+    }
+    barrier_wait(bar, &target, spin_limit);
+    // phase B
+    {
+      const int I = pa.N / 2;
+      const int npairs = pa.M * (I / 2);
+      uint32_t* h = reinterpret_cast<uint32_t*>(pa.y);
+      for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < npairs; i += P * blockDim.x) {
+        const int m = i / (I / 2);
+        gateup_pair(pa, m, 2 * (i - m * (I / 2)), h);
+      }
+    }
+    barrier_arrive(bar, &target);
+    barrier_wait(bar, &target, spin_limit);
+    // phase C
+    for (int job = blockIdx.x; job < jc; job += P) run_job<M, QG_MODE_PLAIN, R>(pc, job, smem, pre, job == (int)blockIdx.x);
+    barrier_arrive(bar, &target);
+    barrier_wait(bar, &target, spin_limit);
+    // phase D (the same arithmetic as k_split_reduce for a plain projection);
+    // agent-scope stores: the next layer's phase A and a failed launch's NaN
+    // fill below read or overwrite them from other workgroups
+    {
+      const int n_out = pc.M * pc.N;
+      const size_t stride = (size_t)pc.M * pc.N;
+      for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_out; i += P * blockDim.x)
+        __hip_atomic_store(pc.y + i, f32_to_bf16_bits(sum_slices(pc.part, stride, (size_t)i, pc.S)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (l + 1 < st.L) {
+      barrier_arrive(bar, &target);
+      // the next layer's first gate/up weights (they do not depend on this layer's output)
+      if ((int)blockIdx.x < ja) {
+        QgAffineArgs pn = pa0;
+        pn.codes += (size_t)(l + 1) * st.gu_codes;
+        pn.scales += (size_t)(l + 1) * st.gu_sb;
+        load_tstep(pn, job_of(pn, blockIdx.x), 0, ring_a[0]);
+        a_pre = true;
+      }
+      barrier_wait(bar, &target, spin_limit);
+    }
   }
   // exit: the last workgroup to leave (every other one has passed its last
   // wait and its stores have completed) fills h and y with NaN if a wait of
@@ -383,10 +422,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
                                             __HIP_MEMORY_SCOPE_AGENT);
   if (failed) {
     const uint16_t qnan = 0x7FC0;
-    for (int i = threadIdx.x; i < pc.M * pc.N; i += blockDim.x)
-      __hip_atomic_store(pc.y + i, qnan, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int i = threadIdx.x; i < pa.M * (pa.N / 2); i += blockDim.x)
-      __hip_atomic_store(pa.y + i, qnan, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (size_t i = threadIdx.x; i < (size_t)st.L * st.y; i += blockDim.x)
+      __hip_atomic_store(pc0.y + i, qnan, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = threadIdx.x; i < pa0.M * (pa0.N / 2); i += blockDim.x)
+      __hip_atomic_store(pa0.y + i, qnan, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (threadIdx.x < kBarGroups) {
     unsigned long long* g = reinterpret_cast<unsigned long long*>(bar + 256 * (threadIdx.x + 1));
@@ -410,9 +449,9 @@ namespace {
 // all be resident at once, instead of letting the grid barrier wait for
 // workgroups that are not running.
 template <int M>
-int launch_mlp_m(QgAffineArgs pa, QgAffineArgs pc, unsigned char* bar, int spin_limit, int grid, size_t lds,
-                 hipStream_t st) {
-  void* args[] = {&pa, &pc, &bar, &spin_limit};
+int launch_mlp_m(QgAffineArgs pa, QgAffineArgs pc, QgMlpStack stk, unsigned char* bar, int spin_limit, int grid,
+                 size_t lds, hipStream_t st) {
+  void* args[] = {&pa, &pc, &stk, &bar, &spin_limit};
   return (int)hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&qg::k_mlp_block<M>), dim3((unsigned)grid),
                                          dim3(256), args, (unsigned)lds, st);
 }
@@ -434,18 +473,18 @@ const void* qg_mlp_kernel(int M) {
 
 size_t qg_mlp_state_bytes() { return (size_t)256 * (qg::kBarGroups + 1); }
 
-int qg_launch_mlp(const QgAffineArgs& pa, const QgAffineArgs& pc, unsigned char* bar, int spin_limit, int grid,
-                  size_t lds, hipStream_t st) {
+int qg_launch_mlp(const QgAffineArgs& pa, const QgAffineArgs& pc, const QgMlpStack& stk, unsigned char* bar,
+                  int spin_limit, int grid, size_t lds, hipStream_t st) {
   if (grid % qg::kBarGroups != 0) return (int)hipErrorInvalidValue;
   switch (pa.M) {
-    case 1: return launch_mlp_m<1>(pa, pc, bar, spin_limit, grid, lds, st);
-    case 2: return launch_mlp_m<2>(pa, pc, bar, spin_limit, grid, lds, st);
-    case 3: return launch_mlp_m<3>(pa, pc, bar, spin_limit, grid, lds, st);
-    case 4: return launch_mlp_m<4>(pa, pc, bar, spin_limit, grid, lds, st);
-    case 5: return launch_mlp_m<5>(pa, pc, bar, spin_limit, grid, lds, st);
-    case 6: return launch_mlp_m<6>(pa, pc, bar, spin_limit, grid, lds, st);
-    case 7: return launch_mlp_m<7>(pa, pc, bar, spin_limit, grid, lds, st);
-    case 8: return launch_mlp_m<8>(pa, pc, bar, spin_limit, grid, lds, st);
+    case 1: return launch_mlp_m<1>(pa, pc, stk, bar, spin_limit, grid, lds, st);
+    case 2: return launch_mlp_m<2>(pa, pc, stk, bar, spin_limit, grid, lds, st);
+    case 3: return launch_mlp_m<3>(pa, pc, stk, bar, spin_limit, grid, lds, st);
+    case 4: return launch_mlp_m<4>(pa, pc, stk, bar, spin_limit, grid, lds, st);
+    case 5: return launch_mlp_m<5>(pa, pc, stk, bar, spin_limit, grid, lds, st);
+    case 6: return launch_mlp_m<6>(pa, pc, stk, bar, spin_limit, grid, lds, st);
+    case 7: return launch_mlp_m<7>(pa, pc, stk, bar, spin_limit, grid, lds, st);
+    case 8: return launch_mlp_m<8>(pa, pc, stk, bar, spin_limit, grid, lds, st);
     default: return (int)hipErrorInvalidValue;
   }
 }

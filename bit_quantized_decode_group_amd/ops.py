@@ -65,6 +65,8 @@ _SIGS = {
     "qg_check_lmhead_topk": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I] + _WS,
     "mlp_block_affine4_tiled_failures": [_P, _P],
     "lmhead_argmax_static": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "mlp_stack_affine4_tiled": [_P, _P, _F, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I] + _WS + [_P],
+    "qg_check_mlp_stack_affine4_tiled": [_P, _P, _F, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I] + _WS,
 }
 # size queries: name -> shape arguments (all int); they return size_t
 _QUERIES = {
@@ -73,6 +75,7 @@ _QUERIES = {
     "qgemv_q6k_workspace": 3, "rmsnorm_gateup_swiglu_workspace": 3, "rmsnorm_gateup_swiglu_tiled_workspace": 3,
     "lmhead_argmax_workspace": 3, "lmhead_argmax_tiled_workspace": 3, "lmhead_topk_workspace": 5,
     "moe_expert_qgemv_workspace": 4, "mlp_block_affine4_tiled_workspace": 3,
+    "mlp_stack_affine4_tiled_workspace": 3,
 }
 
 
@@ -249,17 +252,25 @@ def qgemv_affine4_rht(x, signs, had, codes, scales, biases, y=None, ws=None):
     return y
 
 
+def tiled_bytes(N, K):
+    """(codes bytes, scale/bias bytes) of the tile-order copy of an [N, K] affine-4 matrix."""
+    l = lib()
+    l.qg_tiled_bytes.argtypes = [_I, _I, ctypes.POINTER(ctypes.c_size_t)]
+    l.qg_tiled_bytes.restype = ctypes.c_size_t
+    sbb = ctypes.c_size_t(0)
+    cb = int(l.qg_tiled_bytes(int(N), int(K), ctypes.byref(sbb)))
+    if cb == 0:
+        raise ValueError("tile order needs N >= 1 and K % 512 == 0")
+    return cb, int(sbb.value)
+
+
 def tile_pack(codes, scales, biases):
     """Tile-order copies (codes_t int32, sb_t bf16) of canonical affine-4 weights [N, K] (K % 512 == 0)."""
     N = codes.shape[0]
     K = codes.shape[1] * 8
     l = lib()
-    l.qg_tiled_bytes.argtypes = [_I, _I, ctypes.POINTER(ctypes.c_size_t)]
-    l.qg_tiled_bytes.restype = ctypes.c_size_t
-    sbb = ctypes.c_size_t(0)
-    cb = int(l.qg_tiled_bytes(N, K, ctypes.byref(sbb)))
-    if cb == 0:
-        raise ValueError("tile order needs N >= 1 and K % 512 == 0")
+    cb, sbb = tiled_bytes(N, K)
+    sbb = ctypes.c_size_t(sbb)
     codes_t = torch.empty(cb // 4, dtype=torch.int32, device=codes.device)
     sb_t = torch.empty(sbb.value // 2, dtype=torch.bfloat16, device=codes.device)
     for t, n, e in ((codes, "codes", 4), (scales, "scales", 2), (biases, "biases", 2)):
@@ -307,6 +318,36 @@ def mlp_block_affine4_tiled(x, gamma, eps, gu_t, dn_t, D, I, h=None, y=None, ws=
                                                 _ptr(dn_t[0]), _ptr(dn_t[1]), _ptr(h), _ptr(y), M, D, I, wsp, wsn, _stream()),
                   "mlp_block_affine4_tiled")
     return h, y
+
+
+def mlp_stack_affine4_tiled(x, gamma, eps, gu_codes_t, gu_sb_t, dn_codes_t, dn_sb_t, L, D, I, h=None, ys=None,
+                            ws=None):
+    """L MLP blocks in one persistent launch on stacked tile-order weights: gamma [L, D];
+    gu_codes_t / gu_sb_t and dn_codes_t / dn_sb_t hold the L layers' tile_pack outputs one after
+    the other.  Returns (h [M, I] of the last layer, ys [L, M, D] = every layer's output)."""
+    M, K = _dims2(x, "x")
+    if K != D:
+        raise ValueError(f"x has {K} columns, D = {D}")
+    if h is None:
+        h = torch.empty((M, I), dtype=torch.bfloat16, device=x.device)
+    if ys is None:
+        ys = torch.empty((L, M, D), dtype=torch.bfloat16, device=x.device)
+    for t, n, e in ((x, "x", 2), (gamma, "gamma", 2), (gu_codes_t, "gu_codes_t", 4), (gu_sb_t, "gu_sb_t", 2),
+                    (dn_codes_t, "dn_codes_t", 4), (dn_sb_t, "dn_sb_t", 2), (h, "h", 2), (ys, "ys", 2)):
+        _need(t, n, e, x.device)
+    gcb, gsb = tiled_bytes(2 * I, D)
+    dcb, dsb = tiled_bytes(D, I)
+    for t, n, b in ((gamma, "gamma", L * D * 2), (gu_codes_t, "gu_codes_t", L * gcb), (gu_sb_t, "gu_sb_t", L * gsb),
+                    (dn_codes_t, "dn_codes_t", L * dcb), (dn_sb_t, "dn_sb_t", L * dsb), (h, "h", M * I * 2),
+                    (ys, "ys", L * M * D * 2)):
+        if t.numel() * t.element_size() != b:
+            raise ValueError(f"{n} holds {t.numel() * t.element_size()} bytes, L={L} layers need {b}")
+    wsp, wsn = _ws_args("mlp_stack_affine4_tiled", (M, D, I), ws, x.device)
+    with torch.cuda.device(x.device):
+        _raise_on(lib().mlp_stack_affine4_tiled(_ptr(x), _ptr(gamma), float(eps), _ptr(gu_codes_t), _ptr(gu_sb_t),
+                                                _ptr(dn_codes_t), _ptr(dn_sb_t), _ptr(h), _ptr(ys), int(L), M, D, I,
+                                                wsp, wsn, _stream()), "mlp_stack_affine4_tiled")
+    return h, ys
 
 
 def mlp_failures(ws):

@@ -172,6 +172,39 @@ qg_status mlp_block_affine4_tiled(const uint16_t* x, const uint16_t* gamma,
                                   void* ws, size_t ws_bytes,
                                   void* stream);
 size_t mlp_block_affine4_tiled_workspace(int M, int D, int I);
+/*
+ * mlp_stack_affine4_tiled -- L MLP blocks in a row in one persistent launch,
+ * layer l's output being layer l + 1's input (Husky page, section "전체 단계
+ * 메가커널의 실험과 다음 과제": one dispatch for several layers pays off when
+ * the weight reads of the next layer overlap the tail of the previous one):
+ *   x_0 = x;  x_{l+1} = y_l = MLP_l(x_l) (as mlp_block_affine4_tiled)
+ *   x       bf16 [M][D]; gamma bf16 [L][D]; eps > 0
+ *   gu_codes_t, gu_sb_t  L stacked tile-order copies of the [2I][D]
+ *                        gate-then-up matrices (qg_tiled_bytes(2I, D) and its
+ *                        sb_bytes per layer)
+ *   dn_codes_t, dn_sb_t  L stacked tile-order copies of the [D][I] down matrices
+ *   h       bf16 [M][I] (16-byte aligned): the last layer's SwiGLU output
+ *   ys      bf16 [L][M][D]: every layer's output (ys[L-1] is the stack's)
+ *   1 <= L <= 4096; other rules as mlp_block_affine4_tiled, whose results each
+ *   layer reproduces bit for bit.  Before the barrier that precedes a layer's
+ *   gate/up phase, every workgroup issues the loads of its first gate/up
+ *   weights (they do not depend on the previous layer's output).
+ *   ws: mlp_stack_affine4_tiled_workspace(M, D, I) bytes (the same as one block).
+ */
+qg_status mlp_stack_affine4_tiled(const uint16_t* x, const uint16_t* gamma,
+                                  float eps, const uint32_t* gu_codes_t,
+                                  const uint16_t* gu_sb_t,
+                                  const uint32_t* dn_codes_t,
+                                  const uint16_t* dn_sb_t, uint16_t* h,
+                                  uint16_t* ys, int L, int M, int D, int I,
+                                  void* ws, size_t ws_bytes, void* stream);
+size_t mlp_stack_affine4_tiled_workspace(int M, int D, int I);
+qg_status qg_check_mlp_stack_affine4_tiled(
+    const uint16_t* x, const uint16_t* gamma, float eps,
+    const uint32_t* gu_codes_t, const uint16_t* gu_sb_t,
+    const uint32_t* dn_codes_t, const uint16_t* dn_sb_t, uint16_t* h,
+    uint16_t* ys, int L, int M, int D, int I, const void* ws, size_t ws_bytes);
+
 /* Diagnostic, not for the decode path: synchronises `stream`, returns how many
  * mlp_block_affine4_tiled calls on workspace `ws` had a barrier wait give up
  * since the last query (0: none; -1: HIP error) and resets that count. */

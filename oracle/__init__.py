@@ -19,31 +19,50 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_MT_PATH = os.path.join(_HERE, "liboracle_mt.so")
 _lib = None
+_mt = False  # which build _lib is
 
 
 def build(force: bool = False) -> str:
-    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (-O2, no fast-math,
-    no FMA contraction).  Returns the library path."""
+    """Compile ``oracle.c`` with gcc (-O2, no fast-math, no FMA contraction)
+    into ``liboracle.so`` (single-threaded, what the tests use) and
+    ``liboracle_mt.so`` (the same code with OpenMP: output rows split over
+    threads, every row's sum unchanged; only for timing the oracle on all host
+    cores).  Returns the path of the single-threaded library."""
     src = os.path.join(_HERE, "oracle.c")
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
-        os.path.getmtime(src), os.path.getmtime(os.path.join(_HERE, "oracle.h"))
-    ):
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(
-            ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
-             "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, src, "-lm"],
-            cwd=_HERE,
-        )
-        os.replace(tmp, _LIB_PATH)
+    for path, extra in ((_LIB_PATH, []), (_MT_PATH, ["-fopenmp"])):
+        if force or not os.path.exists(path) or os.path.getmtime(path) < max(
+            os.path.getmtime(src), os.path.getmtime(os.path.join(_HERE, "oracle.h"))
+        ):
+            tmp = path + ".tmp%d" % os.getpid()
+            subprocess.check_call(
+                ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
+                 "-fno-fast-math", "-Wall", "-Wextra", "-Wno-unknown-pragmas", *extra, "-o", tmp, src, "-lm"],
+                cwd=_HERE,
+            )
+            os.replace(tmp, path)
     return _LIB_PATH
+
+
+def use_threads(n: int) -> int:
+    """Run the following oracle calls on n host threads (n > 1: the OpenMP
+    build; n <= 1: the single-threaded build).  Returns the threads in use."""
+    global _lib, _mt
+    want_mt = n > 1
+    if _lib is not None and _mt != want_mt:
+        _lib = None
+    _mt = want_mt
+    return int(_load().oracle_set_threads(int(n)))
 
 
 def _load():
     global _lib
     if _lib is None:
         build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        lib = ctypes.CDLL(_MT_PATH if _mt else _LIB_PATH)
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = ctypes.c_int
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         I = ctypes.c_int

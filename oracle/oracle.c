@@ -9,6 +9,9 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* ---------------------------------------------------------------- O0 ---- */
 
@@ -147,21 +150,37 @@ static double dot_asc(const double* a, const double* b, int64_t K) {
   return s;
 }
 
+int oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
+}
+
 int oracle_qgemv_affine4_f64x(const double* x, const uint32_t* codes,
                               const uint16_t* scales, const uint16_t* biases,
                               int M, int64_t N, int64_t K, double* y) {
   if (!x || !y || M < 1 || N < 0) return -1;
-  double* wrow = (double*)malloc(sizeof(double) * (size_t)K);
-  if (!wrow) return -1;
-  for (int64_t n = 0; n < N; ++n) {
-    if (oracle_dequant_affine4(codes, scales, biases, N, K, n, 1, wrow)) {
-      free(wrow);
-      return -1;
+  int rc = 0;
+#pragma omp parallel reduction(| : rc)
+  {
+    double* wrow = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!wrow) rc = -1;
+#pragma omp for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+      if (rc) continue;
+      if (oracle_dequant_affine4(codes, scales, biases, N, K, n, 1, wrow)) {
+        rc = -1;
+        continue;
+      }
+      for (int m = 0; m < M; ++m) y[(int64_t)m * N + n] = dot_asc(x + (int64_t)m * K, wrow, K);
     }
-    for (int m = 0; m < M; ++m) y[(int64_t)m * N + n] = dot_asc(x + (int64_t)m * K, wrow, K);
+    free(wrow);
   }
-  free(wrow);
-  return 0;
+  return rc;
 }
 
 int oracle_qgemv_affine4(const uint16_t* x, const uint32_t* codes,
@@ -178,17 +197,23 @@ int oracle_qgemv_affine4(const uint16_t* x, const uint32_t* codes,
 static int qgemv_q4k_f64x(const double* x, const uint8_t* blocks, int M,
                           int64_t N, int64_t K, double* y) {
   if (!x || !y || M < 1 || N < 0) return -1;
-  double* wrow = (double*)malloc(sizeof(double) * (size_t)K);
-  if (!wrow) return -1;
-  for (int64_t n = 0; n < N; ++n) {
-    if (oracle_dequant_q4k(blocks, N, K, n, 1, wrow)) {
-      free(wrow);
-      return -1;
+  int rc = 0;
+#pragma omp parallel reduction(| : rc)
+  {
+    double* wrow = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!wrow) rc = -1;
+#pragma omp for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+      if (rc) continue;
+      if (oracle_dequant_q4k(blocks, N, K, n, 1, wrow)) {
+        rc = -1;
+        continue;
+      }
+      for (int m = 0; m < M; ++m) y[(int64_t)m * N + n] = dot_asc(x + (int64_t)m * K, wrow, K);
     }
-    for (int m = 0; m < M; ++m) y[(int64_t)m * N + n] = dot_asc(x + (int64_t)m * K, wrow, K);
+    free(wrow);
   }
-  free(wrow);
-  return 0;
+  return rc;
 }
 
 int oracle_qgemv_q4k(const uint16_t* x, const uint8_t* blocks, int M, int64_t N,
@@ -351,23 +376,24 @@ int oracle_lmhead(const uint16_t* x, const uint32_t* codes,
   if (!x || !codes || !scales || !biases || !ids || M < 1 || V < 1 || K <= 0)
     return -1;
   double* xd = decode_bf16_rows(x, M, K);
-  double* wrow = (double*)malloc(sizeof(double) * (size_t)K);
+  /* every logit (O3's dot product over ascending k), then the selection in
+   * ascending v */
+  double* L_all = logits ? logits : (double*)malloc(sizeof(double) * (size_t)M * (size_t)V);
   double* bestv = (double*)malloc(sizeof(double) * (size_t)M);
   double* second = (double*)malloc(sizeof(double) * (size_t)M);
   int64_t* best = (int64_t*)malloc(sizeof(int64_t) * (size_t)M);
   char* isnan_best = (char*)calloc((size_t)M, 1);
-  int rc = (xd && wrow && bestv && second && best && isnan_best) ? 0 : -1;
+  int rc = (xd && L_all && bestv && second && best && isnan_best) ? 0 : -1;
+  /* L_all[m][v]: the projection O3 with N = V */
+  if (rc == 0) rc = oracle_qgemv_affine4_f64x(xd, codes, scales, biases, M, V, K, L_all);
   for (int m = 0; m < M && rc == 0; ++m) {
     best[m] = -1;
     bestv[m] = -INFINITY;
     second[m] = -INFINITY;
   }
   for (int64_t v = 0; v < V && rc == 0; ++v) {
-    rc = oracle_dequant_affine4(codes, scales, biases, V, K, v, 1, wrow);
-    if (rc) break;
     for (int m = 0; m < M; ++m) {
-      double L = dot_asc(xd + (int64_t)m * K, wrow, K);
-      if (logits) logits[(int64_t)m * V + v] = L;
+      double L = L_all[(int64_t)m * V + v];
       if (isnan_best[m]) continue;
       if (isnan(L)) {
         best[m] = v;
@@ -397,7 +423,7 @@ int oracle_lmhead(const uint16_t* x, const uint32_t* codes,
     }
   }
   free(xd);
-  free(wrow);
+  if (L_all != logits) free(L_all);
   free(bestv);
   free(second);
   free(best);

@@ -59,6 +59,10 @@ extern "C" {
 #endif
 
 /* O0: exact decoders and the round-to-nearest-even encoder used by tests. */
+/* Threads of the all-cores build (liboracle_mt.so) for the calls that follow;
+ * returns the count in effect (always 1 in the single-threaded build). */
+int oracle_set_threads(int n);
+
 double o_bf16_to_f64(uint16_t h);
 double o_f16_to_f64(uint16_t h);
 uint16_t o_f64_to_bf16_rne(double v);

@@ -295,6 +295,27 @@ def test_mlp_block_checks(lib):
     assert c(*bad) == ops.QG_EINVAL          # h alignment
 
 
+def test_mlp_stack_checks(lib):
+    c = lambda *a: ops.check("mlp_stack_affine4_tiled", *a, *WS)
+    ok = [A[0], A[1], 1e-6, A[2], A[3], A[4], A[5], A[6], A[7], 28, 8, 1024, 3072]
+    assert c(*ok) == ops.QG_OK
+    for i, v in ((9, 0), (9, 4097), (10, 0), (10, 9), (11, 1000), (12, 3000)):
+        bad = list(ok); bad[i] = v
+        assert c(*bad) == ops.QG_EINVAL, (i, v)
+    one = list(ok); one[9] = 1
+    assert c(*one) == ops.QG_OK
+    # ys spans all L layers: the second layer's output would overlap h placed just past the first's
+    bad = list(ok); bad[7] = A[7] + 8 * 1024 * 2
+    assert c(*bad) == ops.QG_EALIAS
+    assert c(*one[:7], A[7] + 8 * 1024 * 2, *one[8:]) == ops.QG_OK
+    # gamma holds L rows: ys just past the first row of gamma overlaps the second
+    bad = list(ok); bad[8] = A[1] + 1024 * 2
+    assert c(*bad) == ops.QG_EALIAS
+    assert c(*one[:8], A[1] + 1024 * 2, *one[9:]) == ops.QG_OK
+    assert ops.workspace_bytes("mlp_stack_affine4_tiled", 8, 1024, 3072) == ops.workspace_bytes(
+        "mlp_block_affine4_tiled", 8, 1024, 3072)
+
+
 def test_qgemv_q6k_checks(lib):
     c = lambda *a: ops.check("qgemv_q6k", *a, *WS)
     assert c(A[0], A[1], A[2], 8, 3072, 1024) == ops.QG_OK
