@@ -93,11 +93,10 @@ __device__ __forceinline__ void stage_store(const QgAffineArgs& p, uint4* xs, fl
         sq = fmaf(x1, x1, sq);
         const float p0 = x0 * bf16_bits_to_f32(gg[d] & 0xFFFFu);  // exact in fp32
         const float p1 = x1 * bf16_bits_to_f32(gg[d] >> 16);
-        const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
-        const uint32_t l0 = f32_to_bf16_bits(p0 - bf16_bits_to_f32(h0));  // exact remainder
-        const uint32_t l1 = f32_to_bf16_bits(p1 - bf16_bits_to_f32(h1));
-        v[0][d] = h0 | (h1 << 16);
-        v[PL - 1][d] = l0 | (l1 << 16);
+        const uint32_t hh = pack_bf16x2(p0, p1);
+        v[0][d] = hh;
+        // the remainders are exact bf16 values
+        v[PL - 1][d] = pack_bf16x2(p0 - __uint_as_float(hh << 16), p1 - __uint_as_float(hh & 0xFFFF0000u));
       }
     } else if constexpr (MODE == QG_MODE_PLANES) {
       const uint32_t lo[4] = {live ? in.gm[j].x : 0u, live ? in.gm[j].y : 0u, live ? in.gm[j].z : 0u,
@@ -121,12 +120,10 @@ __device__ __forceinline__ void stage_store(const QgAffineArgs& p, uint4* xs, fl
                                  (v[pl][1] & 0xFFFFu) | (v[pl][3] << 16), (v[pl][1] >> 16) | (v[pl][3] & 0xFFFF0000u));
       if (m < M) xs[(((c * 4 + t) * 4 + kb) * PL + pl) * M + m] = e;
     }
-    // sum over the eight lanes of row m (every lane ends with the same value)
-#pragma unroll
-    for (int off = 8; off <= 32; off <<= 1) {
-      sum += __shfl_xor(sum, off);
-      if constexpr (MODE == QG_MODE_GATEUP) sq += __shfl_xor(sq, off);
-    }
+    // sum over the eight lanes of row m, lanes l ^ 8, l ^ 16, l ^ 32 in turn
+    // (every lane ends with the same value), on the VALU
+    sum = add_upper_half(add_xor16(add_xor8(sum)));
+    if constexpr (MODE == QG_MODE_GATEUP) sq = add_upper_half(add_xor16(add_xor8(sq)));
     if (lane < 8) {
       sx[gl * 8 + m] = sum;
       if (MODE == QG_MODE_GATEUP && m < M) ssq[m * ngl + gl] = sq;

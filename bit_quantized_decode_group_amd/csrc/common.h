@@ -66,6 +66,35 @@ __device__ __forceinline__ float add_upper_half(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// v + (the value of lane l ^ 16), on the VALU (v_permlane16_swap exchanges
+// the odd and even 16-lane rows); equal to v + __shfl_xor(v, 16) bit for bit.
+__device__ __forceinline__ float add_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// v + (the value of lane l ^ 8): a rotation by 8 inside each 16-lane row (DPP
+// row_ror:8) is the lane l ^ 8; equal to v + __shfl_xor(v, 8) bit for bit.
+__device__ __forceinline__ float add_xor8(float v) {
+  const int r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false);
+  return v + __int_as_float(r);
+}
+
+// Two fp32 values as bf16, round to nearest even (gfx950's v_cvt_pk_bf16_f32),
+// `lo` in the low half; the same bits as f32_to_bf16_bits for every non-NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// a.lo*b.lo + a.hi*b.hi + c for two packed bf16 pairs (v_dot2_f32_bf16): the
+// products are exact in fp32.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 // The index of the calling wave in its workgroup, as a scalar (wave-uniform
 // values derived from it, such as tile and step counters and the address
 // arithmetic built on them, then stay on the scalar unit).

@@ -19,12 +19,6 @@
 
 namespace qg {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
 constexpr int kValuBatch = 4;  // chunks whose loads are issued together
 
 struct ValuBuf {
