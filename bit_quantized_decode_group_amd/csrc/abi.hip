@@ -847,6 +847,7 @@ static qg_status prep_mlp(const char* fn, const uint16_t* x, const uint16_t* gam
 
 static size_t mlp_query(int M, int D, int I) {
   if (M < 1 || M > 8 || D <= 0 || D % 512 || I <= 0 || I % 512) return 0;
+  if ((long long)I * 2 * 16 > 0x7FFFFFFFLL || (long long)D * 16 > 0x7FFFFFFFLL) return 0;
   MlpCall c;
   mlp_fill(c, nullptr, nullptr, 1e-6f, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M, D, I);
   if (mlp_layout(c, "mlp_stack_affine4_tiled", kMaxCus)) return 0;
@@ -1217,17 +1218,21 @@ static qg_status prep_gateup_tiled(const uint16_t* x, const uint16_t* gamma, flo
   return affine_prepare(c, "rmsnorm_gateup_swiglu_tiled", ws, ws_bytes, bl);
 }
 
+// I in range for the fused [2I][K] matrix (2I rows of 16-row tiles in an int)
+static bool gateup_rows_ok(int I) { return I >= 1 && (long long)I * 2 * 16 <= 0x7FFFFFFFLL; }
+
 size_t rmsnorm_gateup_swiglu_workspace(int M, int I, int K) {
+  if (!gateup_rows_ok(I)) return 0;
   AffineCall c;
   fill_gateup(c, nullptr, nullptr, 1e-6f, nullptr, nullptr, nullptr, nullptr, M, I, K, 0);
-  return I < 1 ? 0 : affine_query(c, "rmsnorm_gateup_swiglu");
+  return affine_query(c, "rmsnorm_gateup_swiglu");
 }
 
 size_t rmsnorm_gateup_swiglu_tiled_workspace(int M, int I, int K) {
-  if (K % 512) return 0;
+  if (K % 512 || !gateup_rows_ok(I)) return 0;
   AffineCall c;
   fill_gateup(c, nullptr, nullptr, 1e-6f, nullptr, nullptr, nullptr, nullptr, M, I, K, 1);
-  return I < 1 ? 0 : affine_query(c, "rmsnorm_gateup_swiglu_tiled");
+  return affine_query(c, "rmsnorm_gateup_swiglu_tiled");
 }
 
 qg_status qg_check_rmsnorm_gateup_swiglu(const uint16_t* x, const uint16_t* gamma, float eps,
