@@ -849,6 +849,15 @@ def config_timings(torch, ops, synth, to_dev, dev):
                       n, 6 * n)
         b = nb + M * lm["K"] * 2 + M * 8
         res[f"M{M}_tiled"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
+    # top-k readout on tile-order weights (selection fused into the projection)
+    for M, k in ((1, 8), (8, 8), (8, 64)):
+        xm = x8[:M].contiguous()
+        ti, tv = tids[:M, :k].contiguous(), tvals[:M, :k].contiguous()
+        us = per_call(lambda i: ops.lmhead_topk_tiled(xm, tcs[i % n][0], tcs[i % n][1], lm["V"], k, ids=ti, vals=tv),
+                      n, 6 * n)
+        b = nb + M * lm["K"] * 2 + M * k * 8
+        res[f"M{M}_top{k}_tiled"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1),
+                                     "over_argmax_tiled": round(us / res[f"M{M}_tiled"]["us"], 3)}
     out["lm_head_151936x1024"] = res
     del tcs
     log("[bench] context: " + json.dumps(out))

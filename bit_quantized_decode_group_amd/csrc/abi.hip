@@ -78,7 +78,6 @@ void collect(BufList* all, const Buf* outs, int nout, const Buf* ins, int nin) {
 
 constexpr size_t kLdsBudget = 163840;      // bytes of LDS one workgroup may use (all of a gfx950 CU's)
 constexpr size_t kQ4kLdsBudget = 65536;    // staged-slice bound of the Q4_K projection (keeps 2+ workgroups per CU)
-constexpr int kWaves = 4;                  // waves per workgroup of the projection kernels
 // Share (percent) of the resident workgroup slots an affine projection fills, per mode.
 #ifndef QG_FILL_GATEUP
 #define QG_FILL_GATEUP 100
@@ -380,9 +379,6 @@ qg_status do_check_lmhead_topk(const uint16_t* x, const uint32_t* codes, const u
   if (V < 1) return fail(QG_EINVAL, "%s: V=%d must be >= 1", fn, V);
   if (k < 1 || k > V) return fail(QG_EINVAL, "%s: k=%d must be in 1..V", fn, k);
   if (k > kTopkMax) return fail(QG_EUNSUPPORTED, "%s: k=%d above %d", fn, k, kTopkMax);
-  if ((long long)((V + kTopkBlock - 1) / kTopkBlock) * k > kTopkMergeMax)
-    return fail(QG_EUNSUPPORTED, "%s: V=%d with k=%d exceeds the on-chip merge (%d candidates)", fn, V, k,
-                kTopkMergeMax);
   if (!fits_lds_unsplit(M, K))
     return fail(QG_EUNSUPPORTED, "%s: M=%d rows of K=%d do not fit the staged-activation LDS budget", fn, M, K);
   const size_t v = (size_t)V, kk = (size_t)K;
@@ -489,6 +485,26 @@ qg_status do_check_lmhead_tiled(const uint16_t* x, const uint32_t* codes_t, cons
   return check_alias(out, 3, &dr, 1, fn);
 }
 
+qg_status do_check_lmhead_topk_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t,
+                                     float* logits, int32_t* ids, float* vals, int M, int V, int K, int k,
+                                     BufList* all) {
+  const char* fn = "lmhead_topk_tiled";
+  if (V < 1) return fail(QG_EINVAL, "%s: V=%d must be >= 1", fn, V);
+  if (k < 1 || k > V) return fail(QG_EINVAL, "%s: k=%d must be in 1..V", fn, k);
+  if (k > kTopkMax) return fail(QG_EUNSUPPORTED, "%s: k=%d above %d", fn, k, kTopkMax);
+  if (!fits_lds_unsplit(M, K) && M >= 1 && M <= 8)
+    return fail(QG_EUNSUPPORTED, "%s: M=%d rows of K=%d do not fit the staged-activation LDS budget", fn, M, K);
+  const Buf out[] = {{logits, logits ? (size_t)M * V * 4 : 0, "logits"},
+                     {ids, (size_t)M * k * 4, "ids"},
+                     {vals, vals ? (size_t)M * k * 4 : (size_t)0, "vals"}};
+  qg_status st = do_check_tiled(fn, x, codes_t, sb_t, M, V, K, out, 3, all);
+  if (st) return st;
+  if ((st = check_ptr(out[1], 4, fn))) return st;
+  if (logits && (st = check_ptr(out[0], 4, fn))) return st;
+  if (vals && (st = check_ptr(out[2], 4, fn))) return st;
+  return QG_OK;
+}
+
 qg_status do_check_gateup_tiled(const uint16_t* x, const uint16_t* gamma, float eps, const uint32_t* codes_t,
                                 const uint16_t* sb_t, uint16_t* h, int M, int I, int K, BufList* all) {
   const char* fn = "rmsnorm_gateup_swiglu_tiled";
@@ -579,29 +595,44 @@ struct AffineCall {
   QgAffineArgs a{};
   size_t lds = 0;
   size_t reserve = 0;  // leading scratch of the entry point (the RHT planes)
-  size_t off_part = 0, off_ssq = 0, off_cand = 0, off_lg = 0, scratch = 0;
+  size_t off_part = 0, off_ssq = 0, off_cand = 0, off_surv = 0, off_lg = 0, scratch = 0;
 };
 
 // The greedy LM head merges its workgroups' maxima in the workspace header
 // and finishes in its last workgroup (no second kernel); the top-k readout
-// keeps per-block candidates instead.
+// stores them in its scratch for the selection kernel instead.
 bool lm_fused(const AffineCall& c) { return c.mode == QG_MODE_LMHEAD && c.a.topk == 0; }
 
 qg_status affine_layout(AffineCall& c, const char* fn, int cus) {
-  qg_status st = plan_affine(c.mode, c.a, fn, &c.lds, cus);
+  // the top-k readout is planned for kMaxCus compute units whatever the device:
+  // its scratch (one key per workgroup and row, the kept keys) depends on the plan
+  const bool topk = c.mode == QG_MODE_LMHEAD && c.a.topk > 0;
+  qg_status st = plan_affine(c.mode, c.a, fn, &c.lds, topk ? kMaxCus : cus);
   if (st) return st;
-  const QgAffineArgs& a = c.a;
+  QgAffineArgs& a = c.a;
   size_t off = align_up(c.reserve, kWsAlign);
   const bool partials = a.S > 1 || c.mode == QG_MODE_GATEUP;
   c.off_part = off;
   off += partials ? align_up((size_t)a.S * a.M * a.N * 4, kWsAlign) : 0;
   c.off_ssq = off;
   off += (c.mode == QG_MODE_GATEUP) ? align_up((size_t)a.S * 8 * 4, kWsAlign) : 0;
-  // top-k: the blocks' candidates, and the logits when the caller keeps none
-  c.off_cand = off;
-  off += a.topk > 0 ? align_up((size_t)a.M * ((a.N + kTopkBlock - 1) / kTopkBlock) * a.topk * 8, kWsAlign) : 0;
-  c.off_lg = off;
-  off += (a.topk > 0 && !a.logits) ? align_up((size_t)a.M * a.N * 4, kWsAlign) : 0;
+  c.off_cand = c.off_surv = c.off_lg = off;
+  if (topk) {
+    // each workgroup's largest key per row; the kept keys past the LDS list
+    // (at most min(k, workgroups) workgroups' keys); the logits when the
+    // caller keeps none
+    const int nwg = a.S * a.rgroups;
+    if (a.S != 1 || nwg > kTopkMaxWg)
+      return fail(QG_EUNSUPPORTED, "%s: %d workgroups exceed the top-k selection's %d", fn, nwg, kTopkMaxWg);
+    a.topk_tpw = (a.ntiles + a.rgroups * a.waves - 1) / (a.rgroups * a.waves);
+    const long long keep = (long long)std::min(a.topk, nwg) * 16 * a.waves * a.topk_tpw;
+    if (keep > 0x7FFFFFFFLL) return fail(QG_EUNSUPPORTED, "%s: V=%d too large for the top-k selection", fn, a.N);
+    off += align_up((size_t)a.M * nwg * 8, kWsAlign);
+    c.off_surv = off;
+    off += align_up((size_t)a.M * (size_t)keep * 8, kWsAlign);
+    c.off_lg = off;
+    off += a.logits ? 0 : align_up((size_t)a.M * a.N * 4, kWsAlign);
+  }
   c.scratch = off;
   return QG_OK;
 }
@@ -644,6 +675,8 @@ qg_status affine_launch(AffineCall c, const char* fn, void* ws, hipStream_t stre
     c.a.part = reinterpret_cast<float*>(base + c.off_part);
     c.a.ssq_part = reinterpret_cast<float*>(base + c.off_ssq);
     c.a.cand = reinterpret_cast<unsigned long long*>(base + c.off_cand);
+    c.a.surv = reinterpret_cast<unsigned long long*>(base + c.off_surv);
+    // the top-k readout reads the logits back (from the scratch when the caller keeps none)
     if (c.a.topk > 0 && !c.a.logits) c.a.logits = reinterpret_cast<float*>(base + c.off_lg);
   }
   return launched(qg_launch_affine(c.mode, c.a, c.lds, stream), fn);
@@ -1453,6 +1486,46 @@ qg_status lmhead_topk(const uint16_t* x, const uint32_t* codes, const uint16_t* 
   if (st) return st;
   if ((st = check_device())) return st;
   return affine_launch(c, "lmhead_topk", ws, (hipStream_t)stream);
+}
+
+static qg_status prep_topk_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, float* logits,
+                                 int32_t* ids, float* vals, int M, int V, int K, int k, const void* ws,
+                                 size_t ws_bytes, AffineCall& c) {
+  BufList bl;
+  qg_status st = do_check_lmhead_topk_tiled(x, codes_t, sb_t, logits, ids, vals, M, V, K, k, &bl);
+  if (st) return st;
+  fill_lmhead(c, x, codes_t, sb_t, sb_t, logits, ids, nullptr, nullptr, M, V, K, 1);
+  c.a.topk = k;
+  c.a.topk_vals = vals;
+  return affine_prepare(c, "lmhead_topk_tiled", ws, ws_bytes, bl);
+}
+
+size_t lmhead_topk_tiled_workspace(int M, int V, int K, int k, int logits_kept) {
+  if (k < 1 || k > kTopkMax || K % 512) return 0;
+  AffineCall c;
+  fill_lmhead(c, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M, V, K, 1);
+  c.a.topk = k;
+  c.a.logits = logits_kept ? reinterpret_cast<float*>(kWsAlign) : nullptr;  // only its presence matters here
+  return affine_query(c, "lmhead_topk_tiled");
+}
+
+qg_status qg_check_lmhead_topk_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t,
+                                     float* logits, int32_t* ids, float* vals, int M, int V, int K, int k,
+                                     const void* ws, size_t ws_bytes) {
+  clear_err();
+  AffineCall c;
+  return prep_topk_tiled(x, codes_t, sb_t, logits, ids, vals, M, V, K, k, ws, ws_bytes, c);
+}
+
+qg_status lmhead_topk_tiled(const uint16_t* x, const uint32_t* codes_t, const uint16_t* sb_t, float* logits,
+                            int32_t* ids, float* vals, int M, int V, int K, int k, void* ws, size_t ws_bytes,
+                            void* stream) {
+  clear_err();
+  AffineCall c;
+  qg_status st = prep_topk_tiled(x, codes_t, sb_t, logits, ids, vals, M, V, K, k, ws, ws_bytes, c);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  return affine_launch(c, "lmhead_topk_tiled", ws, (hipStream_t)stream);
 }
 
 // ------------------------------------------------------- qgemv_q4k / q6k --

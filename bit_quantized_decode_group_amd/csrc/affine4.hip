@@ -30,7 +30,9 @@
 //     and the result does not depend on timing.
 //   * The LM head merges each workgroup's best (logit, index) key per row into
 //     a running maximum in the workspace header; the last workgroup writes the
-//     ids and the accepted count (lmhead_merge_finish).
+//     ids and the accepted count (lmhead_merge_finish).  For the top-k
+//     readout it stores the logits and each workgroup's best key per row
+//     instead, and k_topk_select (topk.hip) follows.
 //   * Weight bytes are read exactly once; X is read once per workgroup.
 //
 // Per chunk and lane: codes word t (t = 0..3) of lane l covers
@@ -101,7 +103,9 @@ __device__ __forceinline__ void lmhead_merge_finish(const QgAffineArgs& p) {
 // projections' waves live for a few steps and run best with one (measured:
 // the extra registers and waits cost more than the overlap gains there).
 // Every mode keeps within 128 registers per lane (4 waves per SIMD).
-template <int M, int MODE, bool WIDE, bool TILED = false>
+// TK (LM head only): the top-k readout's projection, which stores each
+// workgroup's largest key of every row instead of the greedy finish.
+template <int M, int MODE, bool WIDE, bool TILED = false, bool TK = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) k_affine(QgAffineArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int PL = planes(MODE);  // activation planes (hi, lo)
@@ -336,9 +340,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     }
   }
 
-  // greedy readout only: the top-k readout (no workspace state; p.state is
-  // null) selects from the stored logits in its own kernels
-  if (MODE == QG_MODE_LMHEAD && p.state) {
+  // the workgroup's largest key of each row: merged into the greedy readout's
+  // running maxima (then its finish), or stored for the top-k selection
+  if (MODE == QG_MODE_LMHEAD && (TK || p.state)) {
     // wave: lanes 0..15 share rows m = 0..3, lanes 16..31 rows 4..7
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -358,12 +362,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     if (threadIdx.x < M) {
       unsigned long long v = 0ull;
       for (int w = 0; w < W; ++w) v = wkeys[w * 8 + threadIdx.x] > v ? wkeys[w * 8 + threadIdx.x] : v;
-      // merged into the row's running maximum (order-independent)
-      __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(p.state + kHdrLmSlots +
-                                                                   threadIdx.x * kHdrLmSlotStride),
-                             v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if constexpr (TK) {
+        p.cand[(size_t)threadIdx.x * gridDim.x + blockIdx.x] = v;  // 0: the workgroup had no tile
+      } else {
+        // merged into the row's running maximum (order-independent)
+        __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(p.state + kHdrLmSlots +
+                                                                     threadIdx.x * kHdrLmSlotStride),
+                               v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
-    lmhead_merge_finish<M>(p);
+    if constexpr (!TK) lmhead_merge_finish<M>(p);
   }
 }
 
@@ -419,7 +427,9 @@ __global__ void __launch_bounds__(256) k_split_reduce(QgAffineArgs p) {
 template <int M, bool WIDE>
 static void launch_main(int mode, const QgAffineArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
   if (a.tiled) {  // tile-order weights: plain projection, gate/up and LM head
-    if (mode == QG_MODE_LMHEAD)
+    if (mode == QG_MODE_LMHEAD && a.topk > 0)
+      hipLaunchKernelGGL((k_affine<M, QG_MODE_LMHEAD, true, true, true>), grid, block, lds, st, a);
+    else if (mode == QG_MODE_LMHEAD)
       hipLaunchKernelGGL((k_affine<M, QG_MODE_LMHEAD, true, true>), grid, block, lds, st, a);
     else if (mode == QG_MODE_GATEUP)
       hipLaunchKernelGGL((k_affine<M, QG_MODE_GATEUP, true, true>), grid, block, lds, st, a);
@@ -441,7 +451,10 @@ static void launch_main(int mode, const QgAffineArgs& a, dim3 grid, dim3 block, 
       hipLaunchKernelGGL((k_affine<M, QG_MODE_PLAIN8, WIDE>), grid, block, lds, st, a);
       break;
     default:
-      hipLaunchKernelGGL((k_affine<M, QG_MODE_LMHEAD, WIDE>), grid, block, lds, st, a);
+      if (a.topk > 0)
+        hipLaunchKernelGGL((k_affine<M, QG_MODE_LMHEAD, WIDE, false, true>), grid, block, lds, st, a);
+      else
+        hipLaunchKernelGGL((k_affine<M, QG_MODE_LMHEAD, WIDE>), grid, block, lds, st, a);
       break;
   }
 }
@@ -456,7 +469,7 @@ static int launch_affine_m(int mode, const QgAffineArgs& a, size_t lds, hipStrea
   int err = (int)hipGetLastError();
   if (err) return err;
   if (mode == QG_MODE_LMHEAD && a.topk > 0) {
-    return qg_launch_topk(a, st);
+    return qg_launch_topk(a, (int)grid.x, st);
   } else if (a.S > 1 || mode == QG_MODE_GATEUP) {
     const size_t outs = (size_t)a.M * (mode == QG_MODE_GATEUP ? a.N / 2 : a.N);
     const unsigned nblk = (unsigned)((outs + 255) / 256);

@@ -180,6 +180,14 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) 
   return ((unsigned long long)fk << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
 }
 
+// The logit of an argmax_key: the exact value for every number (-0 comes back
+// as +0), a quiet NaN for a NaN.
+__device__ __forceinline__ float key_logit(unsigned long long key) {
+  const uint32_t fk = (uint32_t)(key >> 32);
+  if (fk == 0xFFFFFFFFu) return __uint_as_float(0x7FC00000u);
+  return __uint_as_float((fk & 0x80000000u) ? (fk & 0x7FFFFFFFu) : ~fk);
+}
+
 }  // namespace qg
 
 // ------------------------------------------------------ workspace header ---
@@ -225,11 +233,14 @@ struct QgAffineArgs {
   int waves;    // waves per workgroup
   int wide;     // scales/biases of a whole batch can be loaded as one aligned vector per row
   int tiled;    // codes / scales hold the tile-order layout (see affine4.hip); biases unused
-  // top-k readout (LM head mode with topk > 0): logits must be set; ids is
-  // [M][topk]; the selection runs after the projection instead of the argmax
+  // top-k readout (LM head mode with topk > 0): the projection stores the
+  // logits and each workgroup's largest key of every row; k_topk_select
+  // (topk.hip) then finds the k largest keys of each row
   int topk;
-  float* topk_vals;              // [M][topk] (nullable)
-  unsigned long long* cand;      // [M][topk_blocks][topk] per-block candidates
+  float* topk_vals;          // [M][topk] (nullable)
+  unsigned long long* cand;  // [M][workgroups] each workgroup's largest key of the row
+  unsigned long long* surv;  // [M][min(topk, workgroups) * 16 * waves * topk_tpw] selected keys past the LDS list
+  int topk_tpw;              // tiles per wave of the projection's plan
 };
 
 struct QgQ4kArgs {
@@ -295,8 +306,9 @@ const void* qg_mlp_kernel(int M);  // the kernel instance for M rows (occupancy 
 constexpr int kRhtMax = 4096;  // largest transform block
 int qg_launch_rht(const uint16_t* x, const int8_t* signs, int had, int M, int K, uint16_t* hi, uint16_t* lo,
                   hipStream_t stream);
-// Top-k selection over stored fp32 logits [M][V] (after the LM-head projection).
-constexpr int kTopkBlock = 2048;     // logits per first-stage selection block
+constexpr int kWaves = 4;  // waves per workgroup of the projection kernels
+// Top-k selection after the LM-head projection (topk.hip).
 constexpr int kTopkMax = 64;         // largest k
-constexpr int kTopkMergeMax = 16384; // candidates one row's merge can sort on chip
-int qg_launch_topk(const QgAffineArgs& a, hipStream_t stream);
+constexpr int kTopkMaxWg = 512;      // projection workgroups whose row maxima one wave ranks (8 per lane)
+constexpr int kTopkSurvLds = 2048;   // selected keys a row keeps in LDS (the rest go to QgAffineArgs::surv)
+int qg_launch_topk(const QgAffineArgs& a, int nwg, hipStream_t stream);

@@ -63,6 +63,8 @@ _SIGS = {
     "qg_check_moe_expert_qgemv": [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I] + _WS,
     "qg_check_lmhead_argmax": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I] + _WS,
     "qg_check_lmhead_topk": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I] + _WS,
+    "lmhead_topk_tiled": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I] + _WS + [_P],
+    "qg_check_lmhead_topk_tiled": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I] + _WS,
     "mlp_block_affine4_tiled_failures": [_P, _P],
     "lmhead_argmax_static": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "mlp_stack_affine4_tiled": [_P, _P, _F, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I] + _WS + [_P],
@@ -74,6 +76,7 @@ _QUERIES = {
     "qgemv_affine4_rht_workspace": 3, "qgemv_affine4_tiled_workspace": 3, "qgemv_q4k_workspace": 3,
     "qgemv_q6k_workspace": 3, "rmsnorm_gateup_swiglu_workspace": 3, "rmsnorm_gateup_swiglu_tiled_workspace": 3,
     "lmhead_argmax_workspace": 3, "lmhead_argmax_tiled_workspace": 3, "lmhead_topk_workspace": 5,
+    "lmhead_topk_tiled_workspace": 5,
     "moe_expert_qgemv_workspace": 4, "mlp_block_affine4_tiled_workspace": 3,
     "mlp_stack_affine4_tiled_workspace": 3,
 }
@@ -541,6 +544,26 @@ def lmhead_topk(x, codes, scales, biases, k, logits=None, want_logits=False, ids
     with torch.cuda.device(x.device):
         _raise_on(lib().lmhead_topk(_ptr(x), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(logits), _ptr(ids),
                                     _ptr(vals), M, V, K, int(k), wsp, wsn, _stream()), "lmhead_topk")
+    return ids, vals, logits
+
+
+def lmhead_topk_tiled(x, codes_t, sb_t, V, k, logits=None, want_logits=False, ids=None, vals=None, want_vals=True,
+                      ws=None):
+    """lmhead_topk on tile-order weights.  Returns (ids [M,k], vals [M,k] or None, logits [M,V] or None)."""
+    M, K = _dims2(x, "x")
+    if logits is None and want_logits:
+        logits = torch.empty((M, V), dtype=torch.float32, device=x.device)
+    if ids is None:
+        ids = torch.empty((M, k), dtype=torch.int32, device=x.device)
+    if vals is None and want_vals:
+        vals = torch.empty((M, k), dtype=torch.float32, device=x.device)
+    for t, n, e in ((x, "x", 2), (codes_t, "codes_t", 4), (sb_t, "sb_t", 2), (logits, "logits", 4),
+                    (ids, "ids", 4), (vals, "vals", 4)):
+        _need(t, n, e, x.device)
+    wsp, wsn = _ws_args("lmhead_topk_tiled", (M, V, K, k, logits is not None), ws, x.device)
+    with torch.cuda.device(x.device):
+        _raise_on(lib().lmhead_topk_tiled(_ptr(x), _ptr(codes_t), _ptr(sb_t), _ptr(logits), _ptr(ids), _ptr(vals),
+                                          M, V, K, int(k), wsp, wsn, _stream()), "lmhead_topk_tiled")
     return ids, vals, logits
 
 

@@ -390,9 +390,15 @@ qg_status lmhead_argmax_static(const uint16_t* x, const uint32_t* codes,
  *   logits fp32 [M][V] (nullable: if null they are kept in the workspace,
  *   which then needs 4*M*V more bytes: pass logits_kept = 0 to the size
  *   query); ids int32 [M][k]; vals fp32 [M][k] (nullable).
- *   1 <= M <= 8; 1 <= k <= min(64, V); ceil(V/2048)*k <= 16384; K as for
- *   lmhead_argmax (all of x staged on chip).
- *   A call enqueues the projection and two selection kernels.
+ *   1 <= M <= 8; 1 <= k <= min(64, V); K as for lmhead_argmax (all of x
+ *   staged on chip).
+ *   A call enqueues two kernels: the projection, which stores the logits and
+ *   each of its workgroups' largest logit per row, and a selection kernel,
+ *   one workgroup per row.  The k-th largest of those maxima bounds the
+ *   row's k-th largest logit from below, so only the k workgroups ranked
+ *   first can hold the top k; the selection reads their logits alone and
+ *   sorts the ones at or above the bound.  vals come from the selection
+ *   keys: a -0 logit is returned as +0, a NaN as a quiet NaN.
  */
 qg_status lmhead_topk(const uint16_t* x, const uint32_t* codes,
                       const uint16_t* scales, const uint16_t* biases,
@@ -400,6 +406,16 @@ qg_status lmhead_topk(const uint16_t* x, const uint32_t* codes,
                       int K, int k, void* ws, size_t ws_bytes,
                       void* stream);
 size_t lmhead_topk_workspace(int M, int V, int K, int k, int logits_kept);
+
+/*
+ * lmhead_topk_tiled -- lmhead_topk on the tile-order copy of W (codes_t, sb_t
+ * from affine4_tile_pack, K % 512 == 0); the same results.
+ */
+qg_status lmhead_topk_tiled(const uint16_t* x, const uint32_t* codes_t,
+                            const uint16_t* sb_t, float* logits, int32_t* ids,
+                            float* vals, int M, int V, int K, int k, void* ws,
+                            size_t ws_bytes, void* stream);
+size_t lmhead_topk_tiled_workspace(int M, int V, int K, int k, int logits_kept);
 
 /*
  * qg_stream_read -- measurement aid, not part of the decode path: one plain
@@ -493,6 +509,10 @@ qg_status qg_check_lmhead_topk(const uint16_t* x, const uint32_t* codes,
                                const uint16_t* scales, const uint16_t* biases,
                                float* logits, int32_t* ids, float* vals, int M,
                                int V, int K, int k, const void* ws, size_t ws_bytes);
+qg_status qg_check_lmhead_topk_tiled(const uint16_t* x, const uint32_t* codes_t,
+                                     const uint16_t* sb_t, float* logits,
+                                     int32_t* ids, float* vals, int M, int V,
+                                     int K, int k, const void* ws, size_t ws_bytes);
 
 #ifdef __cplusplus
 }

@@ -67,6 +67,10 @@ void checks() {
           note(qg_check_lmhead_topk(fake<uint16_t>(0), fake<uint32_t>(1), fake<uint16_t>(2), fake<uint16_t>(3),
                                     (k & 1) ? fake<float>(4) : nullptr, fake<int32_t>(5), fake<float>(6), M, N, K,
                                     k, kWs, kWsBytes));
+        for (int k : {0, 1, 8, 64, 65})
+          note(qg_check_lmhead_topk_tiled(fake<uint16_t>(0), fake<uint32_t>(1), fake<uint16_t>(2),
+                                          (k & 1) ? fake<float>(4) : nullptr, fake<int32_t>(5), fake<float>(6), M,
+                                          N, K, k, kWs, kWsBytes));
         note(qg_check_mlp_block_affine4_tiled(fake<uint16_t>(0), fake<uint16_t>(1), 1e-6f, fake<uint32_t>(2),
                                               fake<uint16_t>(3), fake<uint32_t>(4), fake<uint16_t>(5),
                                               fake<uint16_t>(6), fake<uint16_t>(7), M, K, N, kWs, kWsBytes));
@@ -81,7 +85,8 @@ void checks() {
              qgemv_affine4_rht_workspace(M, N, K) + rmsnorm_gateup_swiglu_workspace(M, N, K) +
              rmsnorm_gateup_swiglu_tiled_workspace(M, N, K) + lmhead_argmax_workspace(M, N, K) +
              lmhead_argmax_tiled_workspace(M, N, K) + lmhead_topk_workspace(M, N, K, 8, 0) +
-             lmhead_topk_workspace(M, N, K, 64, 1) + mlp_block_affine4_tiled_workspace(M, K, N) +
+             lmhead_topk_workspace(M, N, K, 64, 1) + lmhead_topk_tiled_workspace(M, N, K, 8, 0) +
+             lmhead_topk_tiled_workspace(M, N, K, 64, 1) + mlp_block_affine4_tiled_workspace(M, K, N) +
              mlp_stack_affine4_tiled_workspace(M, K, N) + qg_affine4_valu_workspace(M, N, K);
         size_t sb = 0;
         q += qg_tiled_bytes(N, K, &sb) + sb;

@@ -189,9 +189,7 @@ def test_lmhead_topk_checks(lib):
     small[10] = 5
     assert c(*small) == ops.QG_OK
     big = list(ok)
-    big[8] = 2048 * 256 + 1  # 257 blocks x 64 candidates exceed the on-chip merge
-    assert c(*big) == ops.QG_EUNSUPPORTED
-    big[10] = 32
+    big[8] = 2048 * 512 + 1  # a long vocabulary: more tiles per workgroup, the same selection
     assert c(*big) == ops.QG_OK
     bad = list(ok)
     bad[5] = 0  # ids required
@@ -205,6 +203,37 @@ def test_lmhead_topk_checks(lib):
     P = ops._P
     assert lib.lmhead_topk(P(A[0]), P(A[1]), P(A[2]), P(A[3]), None, P(A[5]), None, 1, 16, 64, 0,
                            P(WS[0]), WS[1], None) == ops.QG_EINVAL
+
+
+def test_lmhead_topk_tiled_checks(lib):
+    c = lambda *a: ops.check("lmhead_topk_tiled", *a, *WS)
+    ok = [A[0], A[1], A[2], A[4], A[5], A[6], 8, 151936, 1024, 64]
+    assert c(*ok) == ops.QG_OK
+    opt = list(ok)
+    opt[3] = 0  # logits and vals are optional
+    opt[5] = 0
+    assert c(*opt) == ops.QG_OK
+    for idx, val, st in [(9, 0, ops.QG_EINVAL), (9, 65, ops.QG_EUNSUPPORTED), (6, 9, ops.QG_EINVAL),
+                         (7, 0, ops.QG_EINVAL), (8, 1088, ops.QG_EINVAL), (8, 100, ops.QG_EINVAL)]:
+        bad = list(ok)
+        bad[idx] = val
+        assert c(*bad) == st, (idx, val)
+    small = list(ok)
+    small[7], small[9] = 5, 6  # k > V
+    assert c(*small) == ops.QG_EINVAL
+    big = list(ok)
+    big[7] = 2048 * 512 + 1
+    assert c(*big) == ops.QG_OK
+    bad = list(ok)
+    bad[4] = 0  # ids required
+    assert c(*bad) == ops.QG_EINVAL
+    bad = list(ok)
+    bad[5] = A[4]  # vals over ids
+    assert c(*bad) == ops.QG_EALIAS
+    bad = list(ok)
+    bad[3] = A[1]  # logits over codes
+    assert c(*bad) == ops.QG_EALIAS
+    assert ops.workspace_bytes("lmhead_topk_tiled", 8, 151936, 1000, 64, 0) == 0  # K not whole 512-k batches
 
 
 def test_stream_read_checks(lib):
@@ -344,7 +373,10 @@ def test_workspace_queries(lib):
     assert q("rmsnorm_gateup_swiglu", 8, 12800, 2560) > hdr
     assert q("rmsnorm_gateup_swiglu_tiled", 8, 12800, 2560) == q("rmsnorm_gateup_swiglu", 8, 12800, 2560)
     assert q("lmhead_argmax", 8, 151936, 1024) == hdr  # header state only (the fused finalize)
+    # top-k: the logits (unless the caller keeps them), one key per workgroup and row, the kept keys
     assert q("lmhead_topk", 8, 151936, 1024, 64, 0) - q("lmhead_topk", 8, 151936, 1024, 64, 1) >= 8 * 151936 * 4
+    assert q("lmhead_topk", 8, 151936, 1024, 64, 1) > hdr
+    assert q("lmhead_topk_tiled", 8, 151936, 1024, 64, 0) == q("lmhead_topk", 8, 151936, 1024, 64, 0)
     assert q("qgemv_affine4_rht", 8, 3072, 1024) >= hdr + 2 * 8 * 1024 * 2
     assert q("moe_expert_qgemv", 8, 128, 2048, 768) >= hdr + 8 * 768 * 2
     assert q("qgemv_q4k", 8, 3072, 1024) > hdr and q("qgemv_q4k", 8, 2560, 12800) > hdr  # split for parallelism

@@ -438,6 +438,25 @@ def test_lmhead_topk_order_ties_nan_and_signed_zero():
     assert ids.cpu().numpy()[0].tolist() == [7, 2100, 0]
 
 
+@pytest.mark.parametrize("tiled", [False, True])
+def test_lmhead_topk_all_logits_equal(tiled):
+    """Every logit of a 151,936-row head equal: the keys differ by index alone,
+    so the k largest are ids 0..k-1.  The kept keys far outnumber k here
+    (thousands tie with the bound), which takes the radix selection and the
+    spill of kept keys past LDS."""
+    V, K = 151936, 512
+    x = dev_bf16(np.full((3, K), 0x3F80, np.uint16))  # ones: logit = K * bias = 256
+    args = _bias_rows(V, K, np.full(V, 0x3F00, np.uint16))
+    for k in (1, 8, 64):
+        if tiled:
+            ct, sb = ops.tile_pack(*args)
+            ids, vals, _ = ops.lmhead_topk_tiled(x, ct, sb, V, k)
+        else:
+            ids, vals, _ = ops.lmhead_topk(x, *args, k)
+        assert ids.cpu().numpy().tolist() == [list(range(k))] * 3, (k, tiled)
+        assert np.all(vals.cpu().numpy() == 256.0)
+
+
 def test_lmhead_topk_k1_is_argmax_and_deterministic():
     d = synth.lm_head(M=8, V=20000, K=1024, seed=8101)
     x, args = dev_bf16(d["x"]), _affine_dev(d)
@@ -451,6 +470,30 @@ def test_lmhead_topk_k1_is_argmax_and_deterministic():
     _, _, lg = ops.lmhead_topk(x, *args, 8, want_logits=True)
     _, _, lg2 = ops.lmhead_argmax(x, *args, want_logits=True)
     assert torch.equal(lg, lg2)
+
+
+@pytest.mark.parametrize("M,V,K,k", [(8, 2000, 9088, 8), (8, 4000, 9088, 64), (4, 3000, 18176, 5)])
+def test_lmhead_topk_longest_k(M, V, K, k):
+    """The longest K the projection stages for M rows, against the oracle."""
+    d = synth.lm_head(M=M, V=V, K=K, seed=8200 + M + V + k)
+    ids, vals, _ = ops.lmhead_topk(dev_bf16(d["x"]), *_affine_dev(d), k)
+    _assert_topk(ids.cpu().numpy(), vals.cpu().numpy().astype(np.float64), d, k, f"topk M{M} V{V} K{K}")
+
+
+@pytest.mark.parametrize("M,V,K,k", [(1, 151936, 1024, 8), (8, 151936, 1024, 64), (3, 5000, 512, 5),
+                                     (8, 2000, 8704, 8)])
+def test_lmhead_topk_tiled_equals_canonical(M, V, K, k):
+    """Tile order gives the canonical call's ids and values bit for bit."""
+    d = synth.lm_head(M=M, V=V, K=K, seed=8300 + M + k)
+    x, args = dev_bf16(d["x"]), _affine_dev(d)
+    ct, sb = ops.tile_pack(*args)
+    ids, vals, lg = ops.lmhead_topk(x, *args, k, want_logits=True)
+    ids_t, vals_t, lg_t = ops.lmhead_topk_tiled(x, ct, sb, V, k, want_logits=True)
+    assert torch.equal(ids_t, ids) and torch.equal(vals_t, vals) and torch.equal(lg_t, lg)
+    ids_t2, _, _ = ops.lmhead_topk_tiled(x, ct, sb, V, k, want_vals=False)  # no logits, no vals kept
+    assert torch.equal(ids_t2, ids)
+    if V <= 5000:
+        _assert_topk(ids_t.cpu().numpy(), vals_t.cpu().numpy().astype(np.float64), d, k, f"tiled topk M{M} V{V}")
 
 
 @pytest.mark.parametrize("k", [8, 64])
