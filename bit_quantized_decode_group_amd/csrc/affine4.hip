@@ -59,36 +59,59 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 // Greedy verify fused into the LM-head projection.  Every workgroup has
-// merged its best key of each row into the row's slot in the workspace header
-// (an agent-scope maximum, applied at the device's coherence point); once those
-// atomics have completed it counts itself in.  The workgroup that arrives last
-// finds every row's maximum in the slots, writes the ids and the number of
-// leading rows that match the draft, and sets the slots and the counter back
-// to zero for the next call.
+// merged its best key of each row into its group's slot for the row in the
+// workspace header (an agent-scope maximum, applied at the device's coherence
+// point; blockIdx.x mod kLmGroups picks the group, so each slot takes a
+// group's share of the atomics instead of every workgroup's); once those
+// atomics have completed it counts itself into its group, and the group's
+// last workgroup counts the group in.  The workgroup that completes the last
+// group finds every row's maximum across the group slots, writes the ids and
+// the number of leading rows that match the draft, and sets the slots and
+// counters back to zero for the next call.
 template <int M>
 __device__ __forceinline__ void lmhead_merge_finish(const QgAffineArgs& p) {
+  static_assert(kLmGroups == 8, "one lane per (group, row) below");
   __shared__ int last;
   __builtin_amdgcn_s_waitcnt(0);  // this thread's maximum has been applied
   __syncthreads();
-  unsigned* cnt = reinterpret_cast<unsigned*>(p.state + kHdrLmCount);
-  if (threadIdx.x == 0)
-    last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+  const unsigned g = blockIdx.x & (kLmGroups - 1);
+  const unsigned ngroups = min((unsigned)kLmGroups, gridDim.x);
+  if (threadIdx.x == 0) {
+    unsigned* gcnt = reinterpret_cast<unsigned*>(p.state + kHdrLmGroupCount + (size_t)g * 64);
+    unsigned* cnt = reinterpret_cast<unsigned*>(p.state + kHdrLmCount);
+    const unsigned in_group = (gridDim.x - g + kLmGroups - 1) / kLmGroups;
+    int l = 0;
+    if (__hip_atomic_fetch_add(gcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_group - 1)
+      l = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ngroups - 1;
+    last = l;
+  }
   __syncthreads();
   if (!last || threadIdx.x >= 64) return;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x, gl = lane >> 3, m = lane & 7;  // lane = group * 8 + row
   unsigned long long* slot =
-      reinterpret_cast<unsigned long long*>(p.state + kHdrLmSlots + (size_t)min(lane, 7) * kHdrLmSlotStride);
-  const unsigned long long key = lane < M ? __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
-  const int id = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
-  const int draft = (p.draft && lane < M) ? p.draft[lane] : -1;
-  if (lane < M) {
-    p.ids[lane] = id;
+      reinterpret_cast<unsigned long long*>(p.state + kHdrLmSlots + (size_t)lane * kHdrLmSlotStride);
+  unsigned long long key = 0ull;
+  if (m < M && (unsigned)gl < ngroups) {
+    key = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  const unsigned long long match = __ballot(lane < M && p.draft && id == draft);
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1) {  // the maximum over the groups, in every lane of the row
+    const unsigned long long o = shfl_xor_u64(key, off);
+    key = o > key ? o : key;
+  }
+  const int id = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
+  const bool row = lane < M;  // lanes 0..M-1: group 0's lanes carry the rows' results
+  const int draft = (p.draft && row) ? p.draft[lane] : -1;
+  if (row) p.ids[lane] = id;
+  if (lane < kLmGroups)
+    __hip_atomic_store(reinterpret_cast<unsigned*>(p.state + kHdrLmGroupCount + (size_t)lane * 64), 0u,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long match = __ballot(row && p.draft && id == draft);
   if (lane == 0) {
     if (p.accepted) *p.accepted = (int)__builtin_ctzll(~match);
-    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(reinterpret_cast<unsigned*>(p.state + kHdrLmCount), 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -365,10 +388,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
       if constexpr (TK) {
         p.cand[(size_t)threadIdx.x * gridDim.x + blockIdx.x] = v;  // 0: the workgroup had no tile
       } else {
-        // merged into the row's running maximum (order-independent)
-        __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(p.state + kHdrLmSlots +
-                                                                     threadIdx.x * kHdrLmSlotStride),
-                               v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // merged into the group's running maximum of the row (order-independent)
+        const size_t slot = ((size_t)(blockIdx.x & (kLmGroups - 1)) * 8 + threadIdx.x) * kHdrLmSlotStride;
+        __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(p.state + kHdrLmSlots + slot), v,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     if constexpr (!TK) lmhead_merge_finish<M>(p);

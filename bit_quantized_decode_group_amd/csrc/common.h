@@ -196,9 +196,13 @@ __device__ __forceinline__ float key_logit(unsigned long long key) {
 // it); the per-call scratch follows.  Offsets within the header:
 constexpr size_t kWsHeader = 16384;
 constexpr size_t kHdrMlpBarrier = 0;      // persistent MLP block: grid barrier (qg_mlp_state_bytes())
-constexpr size_t kHdrLmSlots = 8704;      // LM head: per row, the largest (logit, index) key so far,
-constexpr size_t kHdrLmSlotStride = 256;  //   one row per 256 bytes (rows in separate memory channels)
-constexpr size_t kHdrLmCount = 10752;     // LM head: workgroups that have merged their keys
+// LM head, greedy finish: the workgroups form kLmGroups groups (blockIdx.x mod
+// kLmGroups) so that no address takes more than a group's share of the atomics.
+constexpr int kLmGroups = 8;
+constexpr size_t kHdrLmSlots = 8704;       // per group g and row m, at (g * 8 + m) * kHdrLmSlotStride: the
+constexpr size_t kHdrLmSlotStride = 64;    //   largest (logit, index) key of the group's workgroups so far
+constexpr size_t kHdrLmGroupCount = 12800; // per group, at g * 64: its workgroups that have merged their keys
+constexpr size_t kHdrLmCount = 13312;      // groups whose workgroups have all merged
 
 // ----------------------------------------------------------- host side ---
 // Launch descriptors filled by the ABI layer (abi.hip) and consumed by the
