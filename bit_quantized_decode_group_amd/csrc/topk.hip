@@ -27,38 +27,6 @@
 
 namespace qg {
 
-// The value of lane lane ^ S (S = 1, 2, 8: DPP quad permutes and a rotation
-// by 8 in each row of 16; S = 4: a swizzle).
-template <int S>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
-  if constexpr (S == 4) {
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (4 << 10) | 0x1F);
-  } else {
-    static_assert(S == 1 || S == 2 || S == 8, "lane distance");
-    constexpr int ctrl = S == 1 ? 0xB1 : S == 2 ? 0x4E : 0x128;  // quad_perm [1,0,3,2], [2,3,0,1]; row_ror:8
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xF, 0xF, false);
-  }
-}
-
-// v summed over the P neighbouring lanes of its group (P a power of two <= 64,
-// uniform); distances 16 and 32 go through the permlane swaps, which return
-// this lane's value and its partner's in either order.
-__device__ __forceinline__ uint32_t group_sum(uint32_t v, unsigned P) {
-  if (P > 1) v += lane_xor<1>(v);
-  if (P > 2) v += lane_xor<2>(v);
-  if (P > 4) v += lane_xor<4>(v);
-  if (P > 8) v += lane_xor<8>(v);
-  if (P > 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    v = r[0] + r[1];
-  }
-  if (P > 32) {
-    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    v = r[0] + r[1];
-  }
-  return v;
-}
-
 __device__ __forceinline__ unsigned long long max_u64(unsigned long long a, unsigned long long b) {
   return a > b ? a : b;
 }
