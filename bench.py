@@ -42,15 +42,20 @@ KERNEL_TIMES_FILE_REL = "profiles/kernel_times.json"
 KERNEL_TIMES_FILE = os.path.join(ROOT, KERNEL_TIMES_FILE_REL)
 GRAPH_STEPS = 10  # at most this many consecutive steps (rotating weights, MoE stacks, router logits) per graph
 CALIB_BYTES = 384 << 20  # bytes read and written by the kernel that calibrates the HBM byte counters
-# kernels launched by each entry point (once per call) at M = 8
-# (the bench's default tile-order layout: k_affine<M, mode, WIDE = true, TILED = true>)
-ENTRY_KERNELS = {
-    "rmsnorm_gateup_swiglu": ["qg::k_affine<8, 1, true, true>", "qg::k_split_reduce<1>"],
-    "qgemv_affine4": ["qg::k_affine<8, 0, true, true>", "qg::k_split_reduce<0>"],
-    "moe_expert_qgemv": ["qg::k_moe_gateup", "qg::k_moe_down"],
-    "lmhead_argmax": ["qg::k_affine<8, 2, true, true>"],
-    "mlp_block": ["qg::k_mlp_block<8>"],
-}
+# kernels launched by each entry point (once per call) with M rows (the
+# bench's default tile-order layout: k_affine<M, mode, WIDE = true, TILED =
+# true, top-k = false>; the MoE token is one row at every M)
+def entry_kernels(M=8):
+    return {
+        "rmsnorm_gateup_swiglu": [f"qg::k_affine<{M}, 1, true, true, false>", "qg::k_split_reduce<1>"],
+        "qgemv_affine4": [f"qg::k_affine<{M}, 0, true, true, false>", "qg::k_split_reduce<0>"],
+        "moe_expert_qgemv": ["qg::k_moe_gateup", "qg::k_moe_down"],
+        "lmhead_argmax": [f"qg::k_affine<{M}, 2, true, true, false>"],
+        "mlp_block": [f"qg::k_mlp_block<{M}>"],
+    }
+
+
+ENTRY_KERNELS = entry_kernels(8)
 
 
 def log(*a):
@@ -86,7 +91,8 @@ def parse():
     ap.add_argument("--pmc-pass", action="store_true",
                     help="short run for a rocprofv3 --pmc pass: a copy of CALIB_BYTES (counter calibration), "
                          "then --steps M=8 steps; prints one JSON line")
-    ap.add_argument("--pmc-m1", action="store_true", help="with --pmc-pass: also run the M=1 steps")
+    ap.add_argument("--pmc-m", type=int, choices=[1, 8], default=8,
+                    help="with --pmc-pass: the rows of the steps run (8 or 1); with --traffic: the table filled")
     ap.add_argument("--kernel-times", metavar="STATS_CSV",
                     help="turn a rocprofv3 --kernel-trace --stats kernel_stats.csv of a bench run into "
                          "profiles/kernel_times.json (no GPU needed)")
@@ -99,10 +105,12 @@ def parse():
     return ap.parse_args()
 
 
-def traffic_from_counters(fetch_csv, write_csv):
+def traffic_from_counters(fetch_csv, write_csv, M=8):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every kernel, each
     scaled by the factor that makes the calibration copy read and write
-    CALIB_BYTES, summed over the kernels of each entry point."""
+    CALIB_BYTES, summed over the kernels of each entry point.  M = 8 fills
+    "kernels", M = 1 (a pass of M = 1 steps only) "kernels_m1"; an existing
+    file of the same kernel sources keeps the other table."""
     import csv
 
     def per_kernel(path, counter):
@@ -114,7 +122,16 @@ def traffic_from_counters(fetch_csv, write_csv):
                 vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return vals
 
-    out = {"source_hash": kernel_source_hash(), "calib_bytes": CALIB_BYTES, "kernels": {}}
+    key = "kernels" if M == 8 else f"kernels_m{M}"
+    out = {"source_hash": kernel_source_hash(), "calib_bytes": CALIB_BYTES}
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            old = json.load(open(TRAFFIC_FILE))
+            if old.get("source_hash") == out["source_hash"]:
+                out.update({k: v for k, v in old.items() if k.startswith("kernels") or k.endswith("_factor")})
+        except (OSError, ValueError):
+            pass
+    out[key] = {}
     avgs = {}
     for which, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         vals = per_kernel(path, counter)
@@ -122,9 +139,9 @@ def traffic_from_counters(fetch_csv, write_csv):
         if not copies:
             raise SystemExit(f"bench.py --traffic: no calibration copy found in {path}")
         factor = CALIB_BYTES / float(np.mean(copies))
-        out[f"{which}_factor"] = round(factor, 4)
+        out[f"{which}_factor" + ("" if M == 8 else f"_m{M}")] = round(factor, 4)
         avgs[which] = {n: float(np.mean(l)) * 1024 * factor for n, l in vals.items()}
-    for entry, kernels in ENTRY_KERNELS.items():
+    for entry, kernels in entry_kernels(M).items():
         ent = {"kernels": {}}
         total = 0.0
         for pat in kernels:
@@ -138,7 +155,7 @@ def traffic_from_counters(fetch_csv, write_csv):
         if not ent["kernels"]:
             continue  # entry point not in this run (e.g. the persistent MLP block when --mlp separate)
         ent["bytes_per_launch"] = round(total)
-        out["kernels"][entry] = ent
+        out[key][entry] = ent
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
@@ -171,7 +188,7 @@ def kernel_times_from_stats(stats_csv):
 def main():
     args = parse()
     if args.traffic:
-        traffic_from_counters(*args.traffic)
+        traffic_from_counters(*args.traffic, M=args.pmc_m)
         return
     if args.kernel_times:
         kernel_times_from_stats(args.kernel_times)
@@ -406,7 +423,7 @@ def main():
             torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-        for M in (8, 1) if args.pmc_m1 else (8,):
+        for M in (args.pmc_m,):
             b = bufs(M)
             for i in range(args.warmup + args.steps):
                 run_step(i, M, b)
@@ -465,10 +482,22 @@ def main():
     if cfg is not None:
         cfg["mlp_stack_28x1024x3072"] = stack_timings(torch, ops, synth, to_dev, dev)
 
+    tf_tab = {}  # counted HBM bytes per call (profiles/traffic.json, when it matches these kernel sources)
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tf_all = json.load(open(TRAFFIC_FILE))
+            if tf_all.get("source_hash") == kernel_source_hash():
+                tf_tab = {"m8": tf_all.get("kernels", {}), "m1": tf_all.get("kernels_m1", {})}
+        except (OSError, ValueError):
+            tf_tab = {}
     kernels = {}
     for n in names:
         k = {"us_m8": round(per8[n], 2), "bytes_m8": bytes8[n], "gb_s_m8": round(bytes8[n] / (per8[n] * 1e-6) / 1e9, 1),
              "frac_m8": round(bytes8[n] / (per8[n] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        for tag in ("m8", "m1"):
+            t = tf_tab.get(tag, {}).get(n)
+            if t:
+                k[f"traffic_{tag}"] = t["bytes_per_launch"]
         if per1 is not None:
             b1 = step_bytes(1)[0][n]
             k.update({"us_m1": round(per1[n], 2), "gb_s_m1": round(b1 / (per1[n] * 1e-6) / 1e9, 1),

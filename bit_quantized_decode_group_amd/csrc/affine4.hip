@@ -323,16 +323,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   };
 
   // ---- prologue: the activation loads go out first and the first R weight
-  // steps right after them, so staging waits only for the former.  Every
-  // load_step takes a step index clamped to [0, last]: a wave without work,
-  // or the steps past its last one, reload an in-bounds step.
-  const int last = max(nsteps - 1, 0);
+  // steps right after them, so staging waits only for the former.  A wave
+  // loads only its own steps (a ring slot past the last step stays unused).
   Buf ring[R];
   StageIn<MODE> sin;
   stage_load<M, MODE>(p, c0, nc, 0, sin);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int r = 0; r < R; ++r) load_step(ring[r], min(r, last));
+  for (int r = 0; r < R; ++r)
+    if (r < nsteps) load_step(ring[r], r);
   __builtin_amdgcn_sched_barrier(0);
   for (int i = threadIdx.x; i < ZR; i += blockDim.x) zr[i] = make_uint4(0u, 0u, 0u, 0u);
   if (MODE == QG_MODE_LMHEAD) {
@@ -352,13 +351,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   }
 
   // ---- main loop: compute step st from ring slot st % R, then refill the
-  // slot with step st + R (the scheduling barriers keep the compiler from
-  // moving loads across the computation that waits for older ones)
+  // slot with step st + R if there is one (the scheduling barriers keep the
+  // compiler from moving loads across the computation that waits for older
+  // ones).  Reloading an in-bounds step instead of skipping costs HBM bytes:
+  // the weight loads are non-temporal (LM head), so the repeat misses L2.
   for (int st = 0; st < nsteps; st += R) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (st + r < nsteps) compute_step(ring[r], st + r);
-      load_step(ring[r], min(st + r + R, last));
+      if (st + r + R < nsteps) load_step(ring[r], st + r + R);  // uniform; nothing is reloaded past the last step
       __builtin_amdgcn_sched_barrier(0);
     }
   }

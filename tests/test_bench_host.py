@@ -36,11 +36,12 @@ def test_traffic_from_counters(tmp_path, monkeypatch):
     out = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
     calib_kib = bench.CALIB_BYTES / 1024
-    lm = "void qg::k_affine<8, 2, true, true>(QgAffineArgs)"
+    lm = "void qg::k_affine<8, 2, true, true, false>(QgAffineArgs)"
+    lm_topk = "void qg::k_affine<8, 2, true, true, true>(QgAffineArgs)"  # the top-k projection: not the greedy entry
     fin = "qg::k_lmhead_finalize(QgAffineArgs, int)"
     moe_gu, moe_dn = "qg::k_moe_gateup(QgMoeArgs)", "qg::k_moe_down(QgMoeArgs)"
     fetch = [("void at::native::elementwise_kernel<bitwise_not>", calib_kib / 2)] * 2 + [
-        (lm, 40000.0), (lm, 42000.0), (fin, 20.0), (moe_gu, 7000.0), (moe_dn, 3500.0)]
+        (lm_topk, 99000.0), (lm, 40000.0), (lm, 42000.0), (fin, 20.0), (moe_gu, 7000.0), (moe_dn, 3500.0)]
     write = [("void at::native::elementwise_kernel<bitwise_not>", calib_kib)] + [
         (lm, 16.0), (fin, 0.0), (moe_gu, 6.0), (moe_dn, 2.0)]
     _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", fetch)
@@ -55,6 +56,16 @@ def test_traffic_from_counters(tmp_path, monkeypatch):
     assert fin not in lmh["kernels"]
     assert t["kernels"]["moe_expert_qgemv"]["bytes_per_launch"] == round((7000 * 2 + 6 + 3500 * 2 + 2) * 1024)
     assert "mlp_block" not in t["kernels"] and "qgemv_affine4" not in t["kernels"]
+    # an M = 1 pass fills its own table and keeps the M = 8 one
+    lm1 = "void qg::k_affine<1, 2, true, true, false>(QgAffineArgs)"
+    _counter_csv(tmp_path / "f1.csv", "FETCH_SIZE",
+                 [("void at::native::elementwise_kernel<bitwise_not>", calib_kib / 2), (lm1, 40500.0)])
+    _counter_csv(tmp_path / "w1.csv", "WRITE_SIZE",
+                 [("void at::native::elementwise_kernel<bitwise_not>", calib_kib), (lm1, 2.0)])
+    bench.traffic_from_counters(str(tmp_path / "f1.csv"), str(tmp_path / "w1.csv"), M=1)
+    t = json.loads(out.read_text())
+    assert t["kernels_m1"]["lmhead_argmax"]["bytes_per_launch"] == round((40500.0 * 2 + 2) * 1024)
+    assert t["kernels"]["lmhead_argmax"]["bytes_per_launch"] == round((41000.0 * 2 + 16) * 1024)
 
 
 def test_traffic_needs_the_calibration_copy(tmp_path, monkeypatch):
@@ -84,9 +95,9 @@ def test_kernel_times_from_stats(tmp_path, monkeypatch):
     with open(stats, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs"])
         w.writeheader()
-        w.writerow({"Name": "void qg::k_affine<8, 2, true, true>(QgAffineArgs)", "Calls": 10,
+        w.writerow({"Name": "void qg::k_affine<8, 2, true, true, false>(QgAffineArgs)", "Calls": 10,
                     "TotalDurationNs": 210000, "AverageNs": 21000.0})
-        w.writerow({"Name": "void qg::k_affine<8, 0, true, true>(QgAffineArgs)", "Calls": 10,
+        w.writerow({"Name": "void qg::k_affine<8, 0, true, true, false>(QgAffineArgs)", "Calls": 10,
                     "TotalDurationNs": 80000, "AverageNs": 8000.0})
         w.writerow({"Name": "void qg::k_split_reduce<0>(QgAffineArgs)", "Calls": 10,
                     "TotalDurationNs": 33000, "AverageNs": 3300.0})
