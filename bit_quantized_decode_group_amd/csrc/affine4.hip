@@ -193,14 +193,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     const int gb = 2 * (c0 + cb);  // first scale group of the batch
     if constexpr (TILED) {
       // tile order: every load of the wave reads 1 KB (codes) or 256 bytes
-      // (scales, biases) of consecutive memory
-      const size_t tile = (size_t)min(gw + ti * nw, p.ntiles - 1);  // a wave without work reloads a real tile
-      const uint4* cbase = reinterpret_cast<const uint4*>(p.codes) + (tile * p.nchunks + c0 + cb) * 64 + lane;
+      // (scales, biases) of consecutive memory, through a resource based at
+      // the step's own bytes.  A step past the wave's last (ring refills at
+      // the end, a wave without work) gets resources of zero bytes: the loads
+      // are issued, so every wait of the loop leaves the next step's loads in
+      // flight, but they read nothing.
+      const bool real = st < nsteps;  // uniform
+      const size_t tile = (size_t)min(gw + ti * nw, p.ntiles - 1);
+      const char* cbase = reinterpret_cast<const char*>(p.codes) + (tile * p.nchunks + c0 + cb) * 1024;
+      const auto rc = weight_rsrc(cbase, real ? BATCH * 1024 : 0);
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) bf.q[u] = ld_weights<NTL>(cbase + u * 64);  // one base address, 1-KB immediate offsets
+      for (int u = 0; u < BATCH; ++u) bf.q[u] = ld_weights<NTL>(rc, lane * 16 + u * 1024);  // 1-KB immediate offsets
       // one 16-byte record per (row, group parity): dword u = (scale, bias) of group 2(c0+cb+u) + half
-      const uint16_t* rec = p.scales + ((tile * (p.nchunks / BATCH) + (c0 + cb) / BATCH) * 2 + half) * 128 + nl * 8;
-      const uint4 sv = ld_weights<NTL>(rec);
+      const char* rec = reinterpret_cast<const char*>(p.scales) + (tile * (p.nchunks / BATCH) + (c0 + cb) / BATCH) * 512;
+      const uint4 sv = ld_weights<NTL>(weight_rsrc(rec, real ? 512 : 0), half * 256 + nl * 16);
       bf.sw[0] = sv.x; bf.sw[1] = sv.y; bf.sw[2] = sv.z; bf.sw[3] = sv.w;
       return;
     }
@@ -323,15 +329,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   };
 
   // ---- prologue: the activation loads go out first and the first R weight
-  // steps right after them, so staging waits only for the former.  A wave
-  // loads only its own steps (a ring slot past the last step stays unused).
+  // steps right after them, so staging waits only for the former.  A ring
+  // slot past the wave's last step reads nothing (see load_step).
   Buf ring[R];
   StageIn<MODE> sin;
   stage_load<M, MODE>(p, c0, nc, 0, sin);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int r = 0; r < R; ++r)
-    if (r < nsteps) load_step(ring[r], r);
+    if (TILED || r < nsteps) load_step(ring[r], r);
   __builtin_amdgcn_sched_barrier(0);
   for (int i = threadIdx.x; i < ZR; i += blockDim.x) zr[i] = make_uint4(0u, 0u, 0u, 0u);
   if (MODE == QG_MODE_LMHEAD) {
@@ -339,9 +345,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   }
   stage_store<M, MODE>(p, xs, sx, ssq, c0, nc, 0, sin);
   const int rounds = (2 * nc + stage_groups(MODE) * W - 1) / (stage_groups(MODE) * W);
-  for (int r = 1; r < rounds; ++r) {
-    stage_load<M, MODE>(p, c0, nc, r, sin);
-    stage_store<M, MODE>(p, xs, sx, ssq, c0, nc, r, sin);
+  if (rounds > 1) {
+    for (int r = 1; r < rounds; ++r) {
+      stage_load<M, MODE>(p, c0, nc, r, sin);
+      stage_store<M, MODE>(p, xs, sx, ssq, c0, nc, r, sin);
+    }
+    // the last round's loads past the slice's last group are never read; wait
+    // for them here (the reads above have already waited for the weight
+    // loads), or the main loop would wait for every load in flight each step
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
   __syncthreads();
   if (MODE == QG_MODE_GATEUP && rg == 0 && threadIdx.x < M) {
@@ -359,7 +371,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (st + r < nsteps) compute_step(ring[r], st + r);
-      if (st + r + R < nsteps) load_step(ring[r], st + r + R);  // uniform; nothing is reloaded past the last step
+      // nothing is reloaded past the last step: the tiled loads read zero
+      // bytes there, the row-major ones are skipped (a uniform branch)
+      if (TILED || st + r + R < nsteps) load_step(ring[r], st + r + R);
       __builtin_amdgcn_sched_barrier(0);
     }
   }

@@ -57,6 +57,21 @@ __device__ __forceinline__ uint4 ld_weights(const void* ptr) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// The same 16-byte weight load through a buffer resource (raw, untyped:
+// stride 0, gfx9's third descriptor word) over `bytes` bytes from `base`.  A
+// buffer load whose offset lies past the resource's size reads no memory and
+// returns zero, so a resource of zero bytes turns the load into one that is
+// still issued (the compiler's count of loads in flight stays exact) but moves
+// nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <bool NT>
+__device__ __forceinline__ uint4 ld_weights(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // v + (the value of lane l ^ 32) for lanes 0..31, on the VALU (gfx950's
 // v_permlane32_swap exchanges the wave's two 32-lane halves) instead of an
 // LDS permute.  Each result is one addition of the same two values, so it
