@@ -90,7 +90,7 @@ def parse():
                          "arrays; same bytes, reordered) or the canonical [N][K/8] layout")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="short run for a rocprofv3 --pmc pass: a copy of CALIB_BYTES (counter calibration), "
-                         "then --steps M=8 steps; prints one JSON line")
+                         "then --steps M=8 steps, then six streaming reads of 88 MiB; prints one JSON line")
     ap.add_argument("--pmc-m", type=int, choices=[1, 8], default=8,
                     help="with --pmc-pass: the rows of the steps run (8 or 1); with --traffic: the table filled")
     ap.add_argument("--kernel-times", metavar="STATS_CSV",
@@ -427,7 +427,14 @@ def main():
             b = bufs(M)
             for i in range(args.warmup + args.steps):
                 run_step(i, M, b)
+        # the library's plain streaming read of 88 MiB (about the LM head's
+        # bytes), six buffers in turn (more than the on-package cache holds),
+        # so that the read ceiling's counters sit beside the kernels'
+        reads = [torch.empty(88 << 20, dtype=torch.uint8, device=dev).fill_(3) for _ in range(6)]
+        for r in reads:
+            ops.stream_read(r)
         torch.cuda.synchronize()
+        del reads
         print(json.dumps({"pmc_pass": True, "calib_bytes": CALIB_BYTES, "steps": args.warmup + args.steps}), flush=True)
         return
 
