@@ -101,7 +101,10 @@ size_t affine_lds_fixed(int M, int PL) { return (size_t)1024 * PL * M + (size_t)
 size_t q4k_lds_per_sb(int M) { return (size_t)512 * M + 256; }
 size_t q6k_lds_per_sb(int M) { return (size_t)512 * M + 512; }  // operands + 16 scale-block sums x 8 rows
 
-// The LM-head mode stages all of K (no split): ceil(K/128) chunks must fit.
+// The greedy LM head splits K when M staged rows of it exceed the LDS budget
+// (partial sums then go through the workspace); this bounds K all the same.
+constexpr int kLmMaxK = 1 << 18;
+// The top-k readout stages all of K (no split): ceil(K/128) chunks must fit.
 bool fits_lds_unsplit(int M, int K) {
   const size_t nchunks = ((size_t)K / 64 + 1) / 2;
   return nchunks * affine_lds_per_chunk(M, 1) + affine_lds_fixed(M, 1) <= kLdsBudget;
@@ -349,8 +352,7 @@ qg_status do_check_lmhead(const uint16_t* x, const uint32_t* codes, const uint16
   qg_status st = check_affine_common(fn, M, V, K);
   if (st) return st;
   if (V < 1) return fail(QG_EINVAL, "%s: V=%d must be >= 1", fn, V);
-  if (!fits_lds_unsplit(M, K))
-    return fail(QG_EUNSUPPORTED, "%s: M=%d rows of K=%d do not fit the staged-activation LDS budget", fn, M, K);
+  if (K > kLmMaxK) return fail(QG_EUNSUPPORTED, "%s: K=%d above %d", fn, K, kLmMaxK);
   const size_t v = (size_t)V, k = (size_t)K;
   const Buf in[] = {{x, (size_t)M * k * 2, "x"},
                     {codes, v * k / 2, "codes"},
@@ -469,8 +471,7 @@ qg_status do_check_lmhead_tiled(const uint16_t* x, const uint32_t* codes_t, cons
                                 BufList* all) {
   const char* fn = "lmhead_argmax_tiled";
   if (V < 1) return fail(QG_EINVAL, "%s: V=%d must be >= 1", fn, V);
-  if (!fits_lds_unsplit(M, K) && M >= 1 && M <= 8)
-    return fail(QG_EUNSUPPORTED, "%s: M=%d rows of K=%d do not fit the staged-activation LDS budget", fn, M, K);
+  if (K > kLmMaxK) return fail(QG_EUNSUPPORTED, "%s: K=%d above %d", fn, K, kLmMaxK);
   const Buf out[] = {{logits, logits ? (size_t)M * V * 4 : 0, "logits"},
                      {ids, (size_t)M * 4, "ids"},
                      {accepted, accepted ? (size_t)4 : (size_t)0, "accepted"}};
@@ -542,7 +543,12 @@ qg_status plan_affine(int mode, QgAffineArgs& a, const char* fn, size_t* lds_out
   const int Ms = split_ok ? 8 : a.M;  // rows the slice length is sized for
   const int cps_max = (int)std::min<size_t>(
       (size_t)a.nchunks, (kLdsBudget - affine_lds_fixed(Ms, PL)) / affine_lds_per_chunk(Ms, PL));
-  if (!split_ok && a.nchunks > cps_max)
+  // the LM head keeps K in one slice whenever its M staged rows fit; the
+  // greedy readout splits K beyond that (in as few slices as fit), the top-k
+  // readout does not
+  if (mode == QG_MODE_LMHEAD && a.K > kLmMaxK) return fail(QG_EUNSUPPORTED, "%s: K=%d above %d", fn, a.K, kLmMaxK);
+  const bool lm_split = (mode == QG_MODE_LMHEAD) && a.nchunks > cps_max;
+  if (lm_split && a.topk > 0)
     return fail(QG_EUNSUPPORTED, "%s: K=%d needs a split of K this mode or size lacks", fn, a.K);
   // A split costs a follow-up kernel (a few microseconds); a plain projection
   // is split only when a tile has more than kMaxUnsplitSteps batches of
@@ -564,7 +570,8 @@ qg_status plan_affine(int mode, QgAffineArgs& a, const char* fn, size_t* lds_out
 #endif
   const int target = (mode == QG_MODE_GATEUP) ? QG_TARGET_GATEUP : QG_TARGET_OTHER;
   const int fill_pct = (mode == QG_MODE_GATEUP) ? QG_FILL_GATEUP : (mode == QG_MODE_PLAIN ? QG_FILL_PLAIN : QG_FILL_OTHER);
-  Plan pl = plan_split(a.ntiles, a.nchunks, std::max(cps_max, 1), allow_split, target);
+  Plan pl = lm_split ? plan_split(a.ntiles, a.nchunks, std::max(cps_max, 1), true, 0)
+                     : plan_split(a.ntiles, a.nchunks, std::max(cps_max, 1), allow_split, target);
   // slices start on a batch boundary (4 chunks) when that keeps them within LDS
   const int batch = 4;
   if (pl.S > 1) {

@@ -379,8 +379,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   }
 
   // the workgroup's largest key of each row: merged into the greedy readout's
-  // running maxima (then its finish), or stored for the top-k selection
-  if (MODE == QG_MODE_LMHEAD && (TK || p.state)) {
+  // running maxima (then its finish), or stored for the top-k selection.  With
+  // K split (S > 1) the slices store partial sums and k_lmhead_reduce does this.
+  if (MODE == QG_MODE_LMHEAD && (TK || p.state) && p.S == 1) {
     // wave: lanes 0..15 share rows m = 0..3, lanes 16..31 rows 4..7
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -462,6 +463,58 @@ __global__ void __launch_bounds__(256) k_split_reduce(QgAffineArgs p) {
   }
 }
 
+// Greedy LM head with K split over S slices (K beyond what one slice's M
+// staged rows hold in LDS): thread n adds the slices' partial sums of output
+// n of every row in slice order (the same additions as k_split_reduce), stores
+// the logits if asked, and takes each row's (logit, index) key; the
+// workgroup's largest key of each row is merged into the greedy readout's
+// running maxima, then the greedy finish runs as in the unsplit projection.
+template <int M>
+__global__ void __launch_bounds__(256) k_lmhead_reduce(QgAffineArgs p) {
+  __shared__ unsigned long long wk[4][8];  // per wave and row
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)p.M * p.N;  // one slice
+  unsigned long long best[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) best[m] = 0ull;
+  if (n < p.N) {
+    float t[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) t[m] = 0.f;
+    for (int s = 0; s < p.S; ++s) {
+      float v[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) v[m] = p.part[(size_t)s * stride + (size_t)m * p.N + n];
+#pragma unroll
+      for (int m = 0; m < M; ++m) t[m] += v[m];
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      if (p.logits) p.logits[(size_t)m * p.N + n] = t[m];
+      best[m] = argmax_key(t[m], (uint32_t)n);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const unsigned long long o = shfl_xor_u64(best[m], off);
+      best[m] = o > best[m] ? o : best[m];
+    }
+    if (lane == 0) wk[wave][m] = best[m];
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < M) {
+    unsigned long long v = 0ull;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) v = wk[w][threadIdx.x] > v ? wk[w][threadIdx.x] : v;
+    const size_t slot = ((size_t)(blockIdx.x & (kLmGroups - 1)) * 8 + threadIdx.x) * kHdrLmSlotStride;
+    __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(p.state + kHdrLmSlots + slot), v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
+  lmhead_merge_finish<M>(p);
+}
+
 template <int M, bool WIDE>
 static void launch_main(int mode, const QgAffineArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
   if (a.tiled) {  // tile-order weights: plain projection, gate/up and LM head
@@ -508,6 +561,8 @@ static int launch_affine_m(int mode, const QgAffineArgs& a, size_t lds, hipStrea
   if (err) return err;
   if (mode == QG_MODE_LMHEAD && a.topk > 0) {
     return qg_launch_topk(a, (int)grid.x, st);
+  } else if (mode == QG_MODE_LMHEAD && a.S > 1) {
+    hipLaunchKernelGGL(k_lmhead_reduce<M>, dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, st, a);
   } else if (a.S > 1 || mode == QG_MODE_GATEUP) {
     const size_t outs = (size_t)a.M * (mode == QG_MODE_GATEUP ? a.N / 2 : a.N);
     const unsigned nblk = (unsigned)((outs + 255) / 256);

@@ -344,13 +344,18 @@ size_t moe_expert_qgemv_workspace(int top_k, int E, int D, int I);
  *                  (written only if non-null; 0 if draft is null)
  *   x bf16 [M][K]; codes uint32 [V][K/8]; scales, biases bf16 [V][K/64];
  *   logits fp32 [M][V] (nullable); ids int32 [M]; draft int32 [M] (nullable);
- *   accepted int32 [1] (nullable).   1 <= M <= 8; V >= 1; K % 64 == 0.  All
- *   of x is staged on chip: ceil(K/128) * (264*M + 64) + 1024*M + 256 <= 163840
- *   bytes (M = 8: K <= 9088; M = 1: K <= 63360), else QG_EUNSUPPORTED.
- *   ws: the header only (lmhead_argmax_workspace(M, V, K) bytes): every
- *   workgroup merges its best (logit, index) of each row into a running
- *   maximum there, and the last one to finish writes ids and accepted and
- *   sets the maximum back to zero -- one kernel per call.
+ *   accepted int32 [1] (nullable).   1 <= M <= 8; V >= 1; K % 64 == 0;
+ *   K <= 262144 (else QG_EUNSUPPORTED).
+ *   ws (lmhead_argmax_workspace(M, V, K) bytes): when all of x fits on chip,
+ *   ceil(K/128) * (264*M + 64) + 1024*M + 256 <= 163840 bytes (M = 8:
+ *   K <= 9088; M = 1: K <= 63360), the header only: every workgroup merges
+ *   its best (logit, index) of each row into a running maximum there, and
+ *   the last one to finish writes ids and accepted and sets the maximum back
+ *   to zero -- one kernel per call.  Beyond that K is split into the fewest
+ *   slices that fit, each slice's fp32 partial sums [S][M][V] go to the
+ *   workspace after the header, and a second kernel adds them in slice order
+ *   and then merges and finishes as above (the summation order then differs
+ *   from a call with fewer rows whose x still fits in one slice).
  */
 qg_status lmhead_argmax(const uint16_t* x, const uint32_t* codes,
                         const uint16_t* scales, const uint16_t* biases,

@@ -2,6 +2,7 @@
 function include/qgemv.h declares, and every entry point checks its arguments
 before touching the GPU (the host-only qg_check_* twins and the entry points
 themselves return the same status for rejected arguments)."""
+import ctypes
 import os
 import re
 import subprocess
@@ -164,10 +165,25 @@ def test_lmhead_checks(lib):
     bad[7] = A[5]  # accepted over ids
     assert c(*bad) == ops.QG_EALIAS
     bad = list(ok)
-    bad[10] = 9088  # largest K whose 8 staged rows fit in 160 KB of LDS
+    bad[10] = 9088  # largest K whose 8 staged rows fit in 160 KB of LDS: one slice
     assert c(*bad) == ops.QG_OK
-    bad[10] = 9152
+    bad[10] = 9152  # beyond it the greedy readout splits K
+    assert c(*bad) == ops.QG_OK
+    bad[10] = (1 << 18) + 64
     assert c(*bad) == ops.QG_EUNSUPPORTED
+
+
+def test_lmhead_split_k_workspace_and_static_limit(lib):
+    """A K split needs the slices' partial sums in the workspace; the entry point that allocates
+    nothing has only the header, so it refuses such a shape before touching the GPU."""
+    one = ops.workspace_bytes("lmhead_argmax", 8, 151936, 9088)
+    two = ops.workspace_bytes("lmhead_argmax", 8, 151936, 9152)
+    assert one == lib.qg_workspace_header_bytes()
+    assert two >= one + 2 * 8 * 151936 * 4
+    P = ctypes.c_void_p
+    st = lib.lmhead_argmax_static(P(A[0]), P(A[1]), P(A[2]), P(A[3]), None, P(A[5]), None, None,
+                                  ctypes.c_int(8), ctypes.c_int(151936), ctypes.c_int(9152), None)
+    assert st == ops.QG_EUNSUPPORTED
 
 
 def test_lmhead_topk_checks(lib):
@@ -280,7 +296,8 @@ def test_tiled_layout_checks(lib):
     assert h(A[0], A[1], A[2], 0, A[4], 0, 0, 8, 151936, 1024) == ops.QG_OK
     assert h(A[0], A[1], A[2], A[3], 0, A[5], A[6], 8, 151936, 1024) == ops.QG_EINVAL  # ids required
     assert h(A[0], A[1], A[2], A[3], A[4], A[5], A[4], 8, 151936, 1024) == ops.QG_EALIAS  # accepted over ids
-    assert h(A[0], A[1], A[2], A[3], A[4], A[5], A[6], 8, 151936, 9216) == ops.QG_EUNSUPPORTED
+    assert h(A[0], A[1], A[2], A[3], A[4], A[5], A[6], 8, 151936, 9216) == ops.QG_OK  # K split in two
+    assert h(A[0], A[1], A[2], A[3], A[4], A[5], A[6], 8, 151936, (1 << 18) + 512) == ops.QG_EUNSUPPORTED
 
 
 def test_gateup_tiled_checks(lib):
@@ -383,7 +400,8 @@ def test_workspace_queries(lib):
     assert q("qgemv_q6k", 8, 2560, 12800) > hdr
     assert q("mlp_block_affine4_tiled", 8, 1024, 3072) > hdr
     # shapes with no plan
-    assert q("qgemv_affine4", 9, 16, 64) == 0 and q("lmhead_argmax", 8, 1000, 9216) == 0
+    assert q("qgemv_affine4", 9, 16, 64) == 0 and q("lmhead_argmax", 8, 1000, (1 << 18) + 64) == 0
+    assert q("lmhead_argmax", 8, 1000, 9216) == hdr + 2 * 8 * 1000 * 4  # K split in two: the slices' partial sums
 
 
 def test_workspace_checks(lib):

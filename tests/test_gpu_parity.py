@@ -227,6 +227,39 @@ def test_lmhead_tiled_longest_k():
     assert torch.equal(lg_t, lg) and torch.equal(ids_t, ids)
 
 
+@pytest.mark.parametrize("M,K", [(8, 9152), (8, 20480), (4, 18240), (1, 65536)])
+def test_lmhead_split_k(M, K):
+    """K past what M staged rows hold in LDS: the greedy readout splits K into slices (partial
+    sums in the workspace, added in slice order by the reduce kernel, which then merges the rows'
+    keys and runs the greedy finish).  Logits, ids and the accepted prefix against the oracle,
+    twice in a row (the workspace header is left at zero)."""
+    d = synth.lm_head(M=M, V=700, K=K, seed=6300 + M + K)
+    logits, ids, gap, _ = oracle.lmhead(d["x"], d["codes"], d["scales"], d["biases"])
+    draft = ids.copy()
+    draft[M // 2] = (draft[M // 2] + 1) % 700
+    x, args = dev_bf16(d["x"]), _affine_dev(d)
+    ws = ops.workspace(ops.workspace_bytes("lmhead_argmax", M, 700, K))
+    assert ops.workspace_bytes("lmhead_argmax", M, 700, K) > ops.workspace_bytes("lmhead_argmax", M, 700, 1024)
+    for _ in range(2):
+        gi, acc, gl = ops.lmhead_argmax(x, *args, draft=dev_i32(draft), want_logits=True, ws=ws)
+        assert_close_f32(gl.cpu().numpy(), logits, what=f"split K logits M{M} K{K}")
+        assert_ids(gi.cpu().numpy(), ids, gap, logits, what=f"split K ids M{M} K{K}")
+        if (gap > 1e-2).all():
+            assert int(acc.cpu()[0]) == M // 2
+
+
+def test_lmhead_tiled_split_k():
+    """Tile order with K split (8 rows, K = 10,240: two slices of 40 chunks in both layouts):
+    equal to the canonical call, bit for bit."""
+    d = synth.lm_head(M=8, V=900, K=10240, seed=6400)
+    args = _affine_dev(d)
+    ct, sb = ops.tile_pack(*args)
+    x = dev_bf16(d["x"])
+    ids, acc, lg = ops.lmhead_argmax(x, *args, want_logits=True)
+    ids_t, acc_t, lg_t = ops.lmhead_argmax_tiled(x, ct, sb, d["V"], want_logits=True)
+    assert torch.equal(lg_t, lg) and torch.equal(ids_t, ids)
+
+
 def test_lmhead_ties_nan_and_planted():
     V, K = 3000, 128
     x = dev_bf16(np.full((2, K), 0x3F80, np.uint16))
