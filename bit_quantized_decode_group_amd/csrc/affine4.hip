@@ -185,9 +185,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     uint4 q[BATCH * CW];
     uint32_t sw[BATCH], bw[BATCH];
   };
-  auto load_step = [&](Buf& bf, int st) {
-    const int ti = st / nbt;
-    const int cb = (st - ti * nbt) * BATCH;
+  // a step st = ti * nbt + bi (tile ti of the wave's, batch bi of the tile)
+  auto load_step = [&](Buf& bf, int st, int ti, int bi) {
+    const int cb = bi * BATCH;
     const int row = (gw + ti * nw) * 16 + nl;
     const size_t row_c = (size_t)min(row, p.N - 1);
     const int gb = 2 * (c0 + cb);  // first scale group of the batch
@@ -275,9 +275,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   };
 
   // ---- compute one (tile, batch) step: independent MFMA chains per chunk, then the group epilogues
-  auto compute_step = [&](const Buf& bf, int st) {
-    const int ti = st / nbt;
-    const int bi = st - ti * nbt;
+  auto compute_step = [&](const Buf& bf, int ti, int bi) {
     const int cb = bi * BATCH;
     const uint32_t a_base = a_act ? a_lane + (uint32_t)(cb * 16 * PL * M) : 0u;  // entry in zr[]
     f32x4_t C[BATCH];
@@ -337,7 +335,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int r = 0; r < R; ++r)
-    if (TILED || r < nsteps) load_step(ring[r], r);
+    if (TILED || r < nsteps) load_step(ring[r], r, r / nbt, r % nbt);
   __builtin_amdgcn_sched_barrier(0);
   for (int i = threadIdx.x; i < ZR; i += blockDim.x) zr[i] = make_uint4(0u, 0u, 0u, 0u);
   if (MODE == QG_MODE_LMHEAD) {
@@ -367,13 +365,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   // compiler from moving loads across the computation that waits for older
   // ones).  Reloading an in-bounds step instead of skipping costs HBM bytes:
   // the weight loads are non-temporal (LM head), so the repeat misses L2.
+  // (tile, batch) of the step computed next and of the step loaded next,
+  // advanced one step at a time instead of divided out of st
+  int cti = 0, cbi = 0, lti = R / nbt, lbi = R % nbt;
   for (int st = 0; st < nsteps; st += R) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (st + r < nsteps) compute_step(ring[r], st + r);
+      if (st + r < nsteps) compute_step(ring[r], cti, cbi);
+      if (++cbi == nbt) {  // uniform: the next step computed starts a tile
+        cbi = 0;
+        ++cti;
+      }
       // nothing is reloaded past the last step: the tiled loads read zero
       // bytes there, the row-major ones are skipped (a uniform branch)
-      if (TILED || st + r + R < nsteps) load_step(ring[r], st + r + R);
+      if (TILED || st + r + R < nsteps) load_step(ring[r], st + r + R, lti, lbi);
+      if (++lbi == nbt) {
+        lbi = 0;
+        ++lti;
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
