@@ -260,6 +260,36 @@ def test_lmhead_tiled_split_k():
     assert torch.equal(lg_t, lg) and torch.equal(ids_t, ids)
 
 
+def test_lmhead_split_k_rows_independent():
+    """K split (8 rows, K = 9152): row i of the call does not depend on the other rows (same
+    logits and id as in a call with the other rows in another order)."""
+    d = synth.lm_head(M=8, V=1500, K=9152, seed=6500)
+    args = _affine_dev(d)
+    perm = np.array([3, 0, 7, 1, 6, 2, 5, 4])
+    ids, _, lg = ops.lmhead_argmax(dev_bf16(d["x"]), *args, want_logits=True)
+    ids_p, _, lg_p = ops.lmhead_argmax(dev_bf16(np.ascontiguousarray(d["x"][perm])), *args, want_logits=True)
+    assert torch.equal(lg_p, lg[torch.from_numpy(perm).to(lg.device)])
+    assert torch.equal(ids_p, ids[torch.from_numpy(perm).to(ids.device)])
+
+
+def test_lmhead_split_k_ties_and_nan():
+    """The split path's argmax (reduce kernel) keeps the readout's rules: an equal maximum goes
+    to the lower index, and a NaN logit wins over every number (the first NaN)."""
+    V, K = 3000, 9152
+    x = dev_bf16(np.full((8, K), 0x3F80, np.uint16))
+    bias = np.full(V, 0x3F00, np.uint16)
+    bias[2222] = 0x3F80
+    ids, _, _ = ops.lmhead_argmax(x, *_bias_rows(V, K, bias))
+    assert list(ids.cpu().numpy()) == [2222] * 8
+    bias[17] = 0x3F80
+    ids, _, _ = ops.lmhead_argmax(x, *_bias_rows(V, K, bias))
+    assert list(ids.cpu().numpy()) == [17] * 8
+    bias[2500] = 0x7FC0
+    bias[2900] = 0x7FC0
+    ids, _, _ = ops.lmhead_argmax(x, *_bias_rows(V, K, bias))
+    assert list(ids.cpu().numpy()) == [2500] * 8
+
+
 def test_lmhead_ties_nan_and_planted():
     V, K = 3000, 128
     x = dev_bf16(np.full((2, K), 0x3F80, np.uint16))
