@@ -101,14 +101,9 @@ size_t affine_lds_fixed(int M, int PL) { return (size_t)1024 * PL * M + (size_t)
 size_t q4k_lds_per_sb(int M) { return (size_t)512 * M + 256; }
 size_t q6k_lds_per_sb(int M) { return (size_t)512 * M + 512; }  // operands + 16 scale-block sums x 8 rows
 
-// The greedy LM head splits K when M staged rows of it exceed the LDS budget
+// The LM head splits K when M staged rows of it exceed the LDS budget
 // (partial sums then go through the workspace); this bounds K all the same.
 constexpr int kLmMaxK = 1 << 18;
-// The top-k readout stages all of K (no split): ceil(K/128) chunks must fit.
-bool fits_lds_unsplit(int M, int K) {
-  const size_t nchunks = ((size_t)K / 64 + 1) / 2;
-  return nchunks * affine_lds_per_chunk(M, 1) + affine_lds_fixed(M, 1) <= kLdsBudget;
-}
 
 struct Plan {
   int S, cps, tpw, rgroups;
@@ -381,8 +376,7 @@ qg_status do_check_lmhead_topk(const uint16_t* x, const uint32_t* codes, const u
   if (V < 1) return fail(QG_EINVAL, "%s: V=%d must be >= 1", fn, V);
   if (k < 1 || k > V) return fail(QG_EINVAL, "%s: k=%d must be in 1..V", fn, k);
   if (k > kTopkMax) return fail(QG_EUNSUPPORTED, "%s: k=%d above %d", fn, k, kTopkMax);
-  if (!fits_lds_unsplit(M, K))
-    return fail(QG_EUNSUPPORTED, "%s: M=%d rows of K=%d do not fit the staged-activation LDS budget", fn, M, K);
+  if (K > kLmMaxK) return fail(QG_EUNSUPPORTED, "%s: K=%d above %d", fn, K, kLmMaxK);
   const size_t v = (size_t)V, kk = (size_t)K;
   const Buf in[] = {{x, (size_t)M * kk * 2, "x"},
                     {codes, v * kk / 2, "codes"},
@@ -493,8 +487,7 @@ qg_status do_check_lmhead_topk_tiled(const uint16_t* x, const uint32_t* codes_t,
   if (V < 1) return fail(QG_EINVAL, "%s: V=%d must be >= 1", fn, V);
   if (k < 1 || k > V) return fail(QG_EINVAL, "%s: k=%d must be in 1..V", fn, k);
   if (k > kTopkMax) return fail(QG_EUNSUPPORTED, "%s: k=%d above %d", fn, k, kTopkMax);
-  if (!fits_lds_unsplit(M, K) && M >= 1 && M <= 8)
-    return fail(QG_EUNSUPPORTED, "%s: M=%d rows of K=%d do not fit the staged-activation LDS budget", fn, M, K);
+  if (K > kLmMaxK) return fail(QG_EUNSUPPORTED, "%s: K=%d above %d", fn, K, kLmMaxK);
   const Buf out[] = {{logits, logits ? (size_t)M * V * 4 : 0, "logits"},
                      {ids, (size_t)M * k * 4, "ids"},
                      {vals, vals ? (size_t)M * k * 4 : (size_t)0, "vals"}};
@@ -543,13 +536,10 @@ qg_status plan_affine(int mode, QgAffineArgs& a, const char* fn, size_t* lds_out
   const int Ms = split_ok ? 8 : a.M;  // rows the slice length is sized for
   const int cps_max = (int)std::min<size_t>(
       (size_t)a.nchunks, (kLdsBudget - affine_lds_fixed(Ms, PL)) / affine_lds_per_chunk(Ms, PL));
-  // the LM head keeps K in one slice whenever its M staged rows fit; the
-  // greedy readout splits K beyond that (in as few slices as fit), the top-k
-  // readout does not
+  // the LM head keeps K in one slice whenever its M staged rows fit, and
+  // splits K beyond that (in as few slices as fit)
   if (mode == QG_MODE_LMHEAD && a.K > kLmMaxK) return fail(QG_EUNSUPPORTED, "%s: K=%d above %d", fn, a.K, kLmMaxK);
   const bool lm_split = (mode == QG_MODE_LMHEAD) && a.nchunks > cps_max;
-  if (lm_split && a.topk > 0)
-    return fail(QG_EUNSUPPORTED, "%s: K=%d needs a split of K this mode or size lacks", fn, a.K);
   // A split costs a follow-up kernel (a few microseconds); a plain projection
   // is split only when a tile has more than kMaxUnsplitSteps batches of
   // loads (or the slice would not fit on chip).  Gate/up always ends in the
@@ -628,8 +618,10 @@ qg_status affine_layout(AffineCall& c, const char* fn, int cus) {
     // each workgroup's largest key per row; the kept keys past the LDS list
     // (at most min(k, workgroups) workgroups' keys); the logits when the
     // caller keeps none
-    const int nwg = a.S * a.rgroups;
-    if (a.S != 1 || nwg > kTopkMaxWg)
+    // one candidate row per workgroup of a slice (with K split, k_topk_reduce
+    // forms them over the same tiles after adding the slices)
+    const int nwg = a.rgroups;
+    if (nwg > kTopkMaxWg)
       return fail(QG_EUNSUPPORTED, "%s: %d workgroups exceed the top-k selection's %d", fn, nwg, kTopkMaxWg);
     a.topk_tpw = (a.ntiles + a.rgroups * a.waves - 1) / (a.rgroups * a.waves);
     const long long keep = (long long)std::min(a.topk, nwg) * 16 * a.waves * a.topk_tpw;

@@ -524,6 +524,57 @@ __global__ void __launch_bounds__(256) k_lmhead_reduce(QgAffineArgs p) {
   lmhead_merge_finish<M>(p);
 }
 
+// Top-k readout with K split over S slices: workgroup g covers the tiles the
+// projection's workgroup g streams when K is not split (tiles 4g + w + t*nw
+// for wave w, t < topk_tpw).  Lane (mg, n) of a wave adds the slices' partial
+// sums of output n of rows mg and mg + 4 in slice order, stores the logits
+// (the selection reads them back) and keeps each row's largest (logit, index)
+// key; cand[m][g] gets the workgroup's largest key of row m, as the unsplit
+// projection leaves it for k_topk_select.
+template <int M>
+__global__ void __launch_bounds__(256) k_topk_reduce(QgAffineArgs p) {
+  static_assert(kWaves == 4, "the selection reads the tiles of four waves per workgroup");
+  __shared__ unsigned long long wk[kWaves][8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = p.rgroups * kWaves, gw = blockIdx.x * kWaves + wave;
+  const size_t stride = (size_t)p.M * p.N;  // one slice
+  const int nl = lane & 15, mg = lane >> 4;   // output of the tile; rows mg and mg + 4
+  unsigned long long best[2] = {0ull, 0ull};
+  for (int t = 0; t < p.topk_tpw; ++t) {
+    const int tile = gw + t * nw;
+    const int n = tile * 16 + nl;
+    if (tile < p.ntiles && n < p.N) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int m = mg + 4 * j;
+        if (m < M) {
+          float v = 0.f;
+          for (int s = 0; s < p.S; ++s) v += p.part[(size_t)s * stride + (size_t)m * p.N + n];
+          p.logits[(size_t)m * p.N + n] = v;
+          const unsigned long long key = argmax_key(v, (uint32_t)n);
+          best[j] = key > best[j] ? key : best[j];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {  // within the 16 lanes of one row group
+      const unsigned long long o = shfl_xor_u64(best[j], off);
+      best[j] = o > best[j] ? o : best[j];
+    }
+    if (nl == 0 && mg + 4 * j < M) wk[wave][mg + 4 * j] = best[j];
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < M) {
+    unsigned long long v = 0ull;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v = wk[w][threadIdx.x] > v ? wk[w][threadIdx.x] : v;
+    p.cand[(size_t)threadIdx.x * gridDim.x + blockIdx.x] = v;  // 0: the workgroup had no output
+  }
+}
+
 template <int M, bool WIDE>
 static void launch_main(int mode, const QgAffineArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
   if (a.tiled) {  // tile-order weights: plain projection, gate/up and LM head
@@ -569,6 +620,11 @@ static int launch_affine_m(int mode, const QgAffineArgs& a, size_t lds, hipStrea
   int err = (int)hipGetLastError();
   if (err) return err;
   if (mode == QG_MODE_LMHEAD && a.topk > 0) {
+    if (a.S > 1) {  // K split: add the slices and form the candidate rows first
+      hipLaunchKernelGGL(k_topk_reduce<M>, dim3((unsigned)a.rgroups), dim3(64 * kWaves), 0, st, a);
+      if ((err = (int)hipGetLastError())) return err;
+      return qg_launch_topk(a, a.rgroups, st);
+    }
     return qg_launch_topk(a, (int)grid.x, st);
   } else if (mode == QG_MODE_LMHEAD && a.S > 1) {
     hipLaunchKernelGGL(k_lmhead_reduce<M>, dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, st, a);

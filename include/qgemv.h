@@ -395,11 +395,12 @@ qg_status lmhead_argmax_static(const uint16_t* x, const uint32_t* codes,
  *   logits fp32 [M][V] (nullable: if null they are kept in the workspace,
  *   which then needs 4*M*V more bytes: pass logits_kept = 0 to the size
  *   query); ids int32 [M][k]; vals fp32 [M][k] (nullable).
- *   1 <= M <= 8; 1 <= k <= min(64, V); K as for lmhead_argmax (all of x
- *   staged on chip).
+ *   1 <= M <= 8; 1 <= k <= min(64, V); K as for lmhead_argmax.
  *   A call enqueues two kernels: the projection, which stores the logits and
  *   each of its workgroups' largest logit per row, and a selection kernel,
- *   one workgroup per row.  The k-th largest of those maxima bounds the
+ *   one workgroup per row.  (With K split as for lmhead_argmax, a third
+ *   kernel between them adds the slices' partial sums, stores the logits and
+ *   forms the same per-workgroup maxima over the same tiles.)  The k-th largest of those maxima bounds the
  *   row's k-th largest logit from below, so only the k workgroups ranked
  *   first can hold the top k; the selection reads their logits alone and
  *   sorts the ones at or above the bound.  vals come from the selection

@@ -535,16 +535,18 @@ def test_lmhead_topk_k1_is_argmax_and_deterministic():
     assert torch.equal(lg, lg2)
 
 
-@pytest.mark.parametrize("M,V,K,k", [(8, 2000, 9088, 8), (8, 4000, 9088, 64), (4, 3000, 18176, 5)])
+@pytest.mark.parametrize("M,V,K,k", [(8, 2000, 9088, 8), (8, 4000, 9088, 64), (4, 3000, 18176, 5),
+                                     (8, 2000, 9152, 8), (8, 3000, 20480, 64), (4, 3000, 18240, 5)])
 def test_lmhead_topk_longest_k(M, V, K, k):
-    """The longest K the projection stages for M rows, against the oracle."""
+    """The longest K the projection stages for M rows, and K past it (split into slices whose
+    partial sums k_topk_reduce adds before the selection), against the oracle."""
     d = synth.lm_head(M=M, V=V, K=K, seed=8200 + M + V + k)
     ids, vals, _ = ops.lmhead_topk(dev_bf16(d["x"]), *_affine_dev(d), k)
     _assert_topk(ids.cpu().numpy(), vals.cpu().numpy().astype(np.float64), d, k, f"topk M{M} V{V} K{K}")
 
 
 @pytest.mark.parametrize("M,V,K,k", [(1, 151936, 1024, 8), (8, 151936, 1024, 64), (3, 5000, 512, 5),
-                                     (8, 2000, 8704, 8)])
+                                     (8, 2000, 8704, 8), (8, 2000, 10240, 8)])
 def test_lmhead_topk_tiled_equals_canonical(M, V, K, k):
     """Tile order gives the canonical call's ids and values bit for bit."""
     d = synth.lm_head(M=M, V=V, K=K, seed=8300 + M + k)
