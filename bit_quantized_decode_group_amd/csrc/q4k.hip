@@ -38,6 +38,39 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
 // operand of MFMA (p, t, n) for lane kb); sx[jl*8 + m] is the fp32 sum of
 // sub-block jl's 32 staged values.  Source rows are bf16 (T = uint16_t) or
 // fp32 rounded to bf16 (T = float).
+// One staged piece: the 32 bf16 values (as 16 dword pairs in v) of sub-block
+// jl of row m of a region, into that region's operand entries and sub-block sums.
+template <int M>
+__device__ __forceinline__ void stage_q4k_piece(const uint4 (&hv)[4], uint4* rxs, float* rsx, int jl, int m) {
+  uint32_t v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[4 * i] = hv[i].x; v[4 * i + 1] = hv[i].y; v[4 * i + 2] = hv[i].z; v[4 * i + 3] = hv[i].w;
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    sum += bf16_bits_to_f32(v[i] & 0xFFFFu);
+    sum += bf16_bits_to_f32(v[i] >> 16);
+  }
+  const int sbl = jl >> 3, c = (jl >> 1) & 3, nb = jl & 1, pp = c >> 1;
+  constexpr int kByte[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int kbn = 2 * (c & 1) + (g >> 1), t = g & 1;
+    uint32_t e[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int klo = 8 * g + kByte[2 * j], khi = 8 * g + kByte[2 * j + 1];
+      const uint32_t lo = (klo & 1) ? (v[klo >> 1] >> 16) : (v[klo >> 1] & 0xFFFFu);
+      const uint32_t hi = (khi & 1) ? (v[khi >> 1] >> 16) : (v[khi >> 1] & 0xFFFFu);
+      e[j] = lo | (hi << 16);
+    }
+    rxs[((((sbl * 2 + pp) * 2 + t) * 2 + nb) * 4 + kbn) * M + m] = make_uint4(e[0], e[1], e[2], e[3]);
+  }
+  rsx[jl * 8 + m] = sum;
+}
+
 template <int M, typename T>
 __device__ __forceinline__ void stage_q4k_x(const T* src, size_t ld, int K, uint4* xs, float* sx, int sb0,
                                             int nsb, int tid, int nthr, int regions = 1) {
@@ -50,54 +83,26 @@ __device__ __forceinline__ void stage_q4k_x(const T* src, size_t ld, int K, uint
     const int jl = pi - reg * M * nj - m * nj;
     const size_t k0 = (size_t)(sb0 * 8 + jl) * 32;
     const size_t srow = (size_t)reg * M + m;
-    uint4* rxs = xs + (size_t)reg * nsb * 32 * M;
-    float* rsx = sx + (size_t)reg * nsb * 64;
-    uint32_t v[16];  // 32 bf16 values, pairs
-    float sum = 0.f;
+    uint4 hv[4] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u),
+                   make_uint4(0u, 0u, 0u, 0u)};  // 32 bf16 values, pairs
     if (k0 < (size_t)K) {
       if constexpr (sizeof(T) == 2) {
         const uint4* s4 = reinterpret_cast<const uint4*>(src + srow * ld + k0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 t = s4[i];
-          v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
-        }
+        for (int i = 0; i < 4; ++i) hv[i] = s4[i];
       } else {
         const float4* s4 = reinterpret_cast<const float4*>(src + srow * ld + k0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float4 t = s4[i];
-          v[2 * i] = (uint32_t)f32_to_bf16_bits(t.x) | ((uint32_t)f32_to_bf16_bits(t.y) << 16);
-          v[2 * i + 1] = (uint32_t)f32_to_bf16_bits(t.z) | ((uint32_t)f32_to_bf16_bits(t.w) << 16);
+        for (int i = 0; i < 4; ++i) {
+          const float4 a = s4[2 * i], b = s4[2 * i + 1];
+          hv[i] = make_uint4((uint32_t)f32_to_bf16_bits(a.x) | ((uint32_t)f32_to_bf16_bits(a.y) << 16),
+                             (uint32_t)f32_to_bf16_bits(a.z) | ((uint32_t)f32_to_bf16_bits(a.w) << 16),
+                             (uint32_t)f32_to_bf16_bits(b.x) | ((uint32_t)f32_to_bf16_bits(b.y) << 16),
+                             (uint32_t)f32_to_bf16_bits(b.z) | ((uint32_t)f32_to_bf16_bits(b.w) << 16));
         }
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sum += bf16_bits_to_f32(v[i] & 0xFFFFu);
-        sum += bf16_bits_to_f32(v[i] >> 16);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = 0u;
     }
-    // sub-block jl = 8*sbl + 2c + n; its values 8g .. 8g+7 (g = 0..3) go to lane
-    // kb = 2(c%2) + g/2 of MFMA (p = c/2, t = g%2, n)
-    const int sbl = jl >> 3, c = (jl >> 1) & 3, nb = jl & 1, pp = c >> 1;
-    constexpr int kByte[8] = {0, 2, 1, 3, 4, 6, 5, 7};
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int kbn = 2 * (c & 1) + (g >> 1), t = g & 1;
-      uint32_t e[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int klo = 8 * g + kByte[2 * j], khi = 8 * g + kByte[2 * j + 1];
-        const uint32_t lo = (klo & 1) ? (v[klo >> 1] >> 16) : (v[klo >> 1] & 0xFFFFu);
-        const uint32_t hi = (khi & 1) ? (v[khi >> 1] >> 16) : (v[khi >> 1] & 0xFFFFu);
-        e[j] = lo | (hi << 16);
-      }
-      rxs[((((sbl * 2 + pp) * 2 + t) * 2 + nb) * 4 + kbn) * M + m] = make_uint4(e[0], e[1], e[2], e[3]);
-    }
-    rsx[jl * 8 + m] = sum;
+    stage_q4k_piece<M>(hv, xs + (size_t)reg * nsb * 32 * M, sx + (size_t)reg * nsb * 64, jl, m);
   }
   if (M < 8) {
     for (int pi = tid; pi < regions * nj * (8 - M); pi += nthr)
@@ -464,13 +469,34 @@ __global__ void __launch_bounds__(512) k_moe_down(QgMoeArgs p) {
   const int s0 = min(wave, p.top_k - 1);
   const uint8_t* blk0[1] = {expert_blocks(s0)};
   Q4kBuf<1, kMoeDownBatch> first;
-  q4k_load<1>(first, blk0, 0, nsb, lane >> 4);
-  const float pe0 = p.route_w[s0];  // in flight with the weights, used after the MFMAs
-  __builtin_amdgcn_sched_barrier(0);
-
   if (threadIdx.x == 0) lds[0] = make_uint4(0u, 0u, 0u, 0u);
-  // the selected experts' activations, one row per expert slot, staged in one pass
-  stage_q4k_x<1, uint16_t>(p.h, (size_t)p.I, p.I, lds + 1, sx, 0, nsb, threadIdx.x, blockDim.x, p.top_k);
+  // the selected experts' activations, one row per expert slot.  When each
+  // thread stages at most one piece, its loads go out before the first weight
+  // batch (loads complete in order per wave, so staging then waits for h
+  // alone, while the weights are still in flight)
+  const int pieces = p.top_k * 8 * nsb;
+  if (pieces <= (int)blockDim.x) {  // uniform
+    const int pi = threadIdx.x;
+    uint4 hv[4];
+    const int reg = pi / (8 * nsb), jl = pi - reg * 8 * nsb;
+    const bool live = pi < pieces;
+    const uint4* src = reinterpret_cast<const uint4*>(p.h + (size_t)min(reg, p.top_k - 1) * p.I + (size_t)jl * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hv[i] = src[i];
+    q4k_load<1>(first, blk0, 0, nsb, lane >> 4);
+    __builtin_amdgcn_sched_barrier(0);
+    if (live) {
+      float* rsx = sx + (size_t)reg * nsb * 64;
+      stage_q4k_piece<1>(hv, lds + 1 + xs_per * reg, rsx, jl, 0);
+#pragma unroll
+      for (int r = 1; r < 8; ++r) rsx[jl * 8 + r] = 0.f;  // rows past M = 1, as stage_q4k_x leaves them
+    }
+  } else {
+    q4k_load<1>(first, blk0, 0, nsb, lane >> 4);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_q4k_x<1, uint16_t>(p.h, (size_t)p.I, p.I, lds + 1, sx, 0, nsb, threadIdx.x, blockDim.x, p.top_k);
+  }
+  const float pe0 = p.route_w[s0];  // used after the MFMAs
   __syncthreads();
 
   f32x4_t tot = {0.f, 0.f, 0.f, 0.f};
