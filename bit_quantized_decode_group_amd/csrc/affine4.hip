@@ -126,10 +126,13 @@ __device__ __forceinline__ void lmhead_merge_finish(const QgAffineArgs& p) {
 // projections' waves live for a few steps and run best with one (measured:
 // the extra registers and waits cost more than the overlap gains there).
 // Every mode keeps within 128 registers per lane (4 waves per SIMD).
+// Workgroups have p.waves waves: four, except gate/up at M < 5, which runs
+// 8 or 16 (one staged copy of the slice shared by more waves).
 // TK (LM head only): the top-k readout's projection, which stores each
 // workgroup's largest key of every row instead of the greedy finish.
 template <int M, int MODE, bool WIDE, bool TILED = false, bool TK = false>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) k_affine(QgAffineArgs p) {
+__global__ void __launch_bounds__(MODE == QG_MODE_GATEUP ? 1024 : 256) __attribute__((amdgpu_waves_per_eu(4, 8)))
+k_affine(QgAffineArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int PL = planes(MODE);  // activation planes (hi, lo)
   constexpr int BATCH = 4;                              // chunks whose loads are issued together
