@@ -194,8 +194,8 @@ def main():
         kernel_times_from_stats(args.kernel_times)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus N with N > 1 is not supported "
-              "(the projection has no multi-GPU path here)", file=sys.stderr)
+        print("bench.py: the library runs on exactly one GPU; --gpus N with N > 1 is not supported "
+              "(the projection has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -902,7 +902,7 @@ def config_timings(torch, ops, synth, to_dev, dev):
 
 def _host_threads():
     """Threads the oracle may use on this host: the process's affinity set, capped by
-    OMP_NUM_THREADS when that is set (the GPU machine grants 16 CPUs per GPU)."""
+    OMP_NUM_THREADS when that is set (a host may grant a GPU's process fewer CPUs than it has)."""
     aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     env = os.environ.get("OMP_NUM_THREADS")
     n = min(aff, int(env)) if env and env.isdigit() and int(env) > 0 else aff
