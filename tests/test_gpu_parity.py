@@ -934,6 +934,27 @@ def test_batch_invariance_q4k_q6k(N, K):
     _rows_check(f6, f6, x, f"q6k {N}x{K}")
 
 
+@pytest.mark.parametrize("tiled", [False, True])
+def test_gateup_rows_equal_across_m(tiled):
+    """Gate/up at M = 2..5 (workgroups of 8 waves up to M = 4, of 4 from M = 5; 16 at
+    M = 1, checked above) equals the first M rows of the 8-row call bit for bit: the
+    workgroup width changes which waves compute a tile, never a row's arithmetic."""
+    d = synth.verify_block()
+    gu = (dev_u32(d["codes_gu"]), dev_bf16(d["scales_gu"]), dev_bf16(d["biases_gu"]))
+    gam = dev_bf16(d["gamma"])
+    if tiled:
+        t = ops.tile_pack(*gu)
+        f = lambda x: ops.rmsnorm_gateup_swiglu_tiled(x, gam, d["eps"], *t, gu[0].shape[0] // 2)
+    else:
+        f = lambda x: ops.rmsnorm_gateup_swiglu(x, gam, d["eps"], *gu)
+    h8 = host_bits(f(dev_bf16(d["x"])))
+    for M in (2, 3, 4, 5):
+        print(f"[gate/up rows across M] tiled={tiled} M={M}", flush=True)
+        hm = host_bits(f(dev_bf16(d["x"][:M].copy())))
+        bad = [i for i in range(M) if not np.array_equal(h8[i], hm[i])]
+        assert not bad, f"gate/up tiled={tiled}: rows {bad} of the {M}-row call differ from the 8-row call"
+
+
 def test_batch_invariance_gateup_and_lm_head():
     d = synth.verify_block()
     gu = (dev_u32(d["codes_gu"]), dev_bf16(d["scales_gu"]), dev_bf16(d["biases_gu"]))
