@@ -79,8 +79,16 @@ void collect(BufList* all, const Buf* outs, int nout, const Buf* ins, int nin) {
 constexpr size_t kLdsBudget = 163840;      // bytes of LDS one workgroup may use (all of a gfx950 CU's)
 constexpr size_t kQ4kLdsBudget = 65536;    // staged-slice bound of the Q4_K projection (keeps 2+ workgroups per CU)
 // Share (percent) of the resident workgroup slots an affine projection fills, per mode.
+// Gate/up with 4-wave workgroups (M >= 5) fills three of a CU's four slots: on
+// the 2560 -> 2 x 12,800 block 13.6-13.7 us at M = 8 against 14.3 at 100%, and
+// 14.6-14.9 / 14.8-14.9 / 14.6-14.7 at 50 / 60 / 85% (the same number of
+// workgroups on every CU matters more than the count); its 8- and 16-wave
+// workgroups fill every slot (one or two per CU).
 #ifndef QG_FILL_GATEUP
 #define QG_FILL_GATEUP 100
+#endif
+#ifndef QG_FILL_GATEUP4
+#define QG_FILL_GATEUP4 75
 #endif
 #ifndef QG_FILL_PLAIN
 #define QG_FILL_PLAIN 75
@@ -562,7 +570,8 @@ qg_status plan_affine(int mode, QgAffineArgs& a, const char* fn, size_t* lds_out
                                         a.nchunks > cps_max);
   // Pieces to aim for and share of the resident workgroup slots to fill, per
   // mode (measured on the decode shapes): gate/up, whose staging is the
-  // costliest, prefers many short slices on every slot; plain projections run
+  // costliest, prefers many short slices, on three quarters of the slots with
+  // 4-wave workgroups and on every slot with wider ones; plain projections run
   // best on three quarters of the slots, the LM head and the other modes on
   // half, with two or more tiles per wave.
 #ifndef QG_TARGET_GATEUP
@@ -572,7 +581,8 @@ qg_status plan_affine(int mode, QgAffineArgs& a, const char* fn, size_t* lds_out
 #define QG_TARGET_OTHER (2 * kTargetWaves)
 #endif
   const int target = (mode == QG_MODE_GATEUP) ? QG_TARGET_GATEUP : QG_TARGET_OTHER;
-  const int fill_pct = (mode == QG_MODE_GATEUP) ? QG_FILL_GATEUP : (mode == QG_MODE_PLAIN ? QG_FILL_PLAIN : QG_FILL_OTHER);
+  const int fill_pct = (mode == QG_MODE_GATEUP) ? (a.waves == kWaves ? QG_FILL_GATEUP4 : QG_FILL_GATEUP)
+                                                : (mode == QG_MODE_PLAIN ? QG_FILL_PLAIN : QG_FILL_OTHER);
   Plan pl = lm_split ? plan_split(a.ntiles, a.nchunks, std::max(cps_max, 1), true, 0)
                      : plan_split(a.ntiles, a.nchunks, std::max(cps_max, 1), allow_split, target);
   // slices start on a batch boundary (4 chunks) when that keeps them within LDS
