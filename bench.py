@@ -820,6 +820,24 @@ def config_timings(torch, ops, synth, to_dev, dev):
             res[f"{N6}x{K6}_M{M}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
         del cps
     out["projection_q6k"] = res
+    # GGUF Q4_K projections, the same two shapes (144-byte superblocks as stored)
+    res = {}
+    for (N4, K4) in ((3072, 1024), (2560, 12800)):
+        g4 = synth.rng(1008 + K4)
+        x4 = to_dev(synth.normal_bf16(g4, (8, K4)), "bf16")
+        blocks4 = synth.q4k_matrix(g4, N4, K4)
+        wb = to_dev(blocks4, "u8")
+        nb = int(blocks4.nbytes)
+        n = max(2, (512 << 20) // nb + 1)
+        cps = [wb] + [wb.clone() for _ in range(n - 1)]
+        for M in (1, 8):
+            xm = x4[:M].contiguous()
+            ym = torch.empty((M, N4), dtype=torch.bfloat16, device=dev)
+            us = per_call(lambda i: ops.qgemv_q4k(xm, cps[i % n], y=ym), n, 3 * n)
+            b = nb + M * K4 * 2 + M * N4 * 2
+            res[f"{N4}x{K4}_M{M}"] = {"us": round(us, 2), "gb_s": round(b / (us * 1e-6) / 1e9, 1)}
+        del cps
+    out["projection_q4k"] = res
     # the M-row products on the matrix cores or on the vector ALU, same work
     out["products_mfma_vs_valu"] = {f"{N}x{K}": compare_valu(torch, ops, synth, to_dev, dev, N, K, per_call)
                                     for (N, K) in ((3072, 1024), (2560, 12800), (151936, 1024))}
