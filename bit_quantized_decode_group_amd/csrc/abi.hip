@@ -720,10 +720,11 @@ void q4k_layout(Q4kCall& c, int bpb) {
   const size_t per8 = bpb == 144 ? q4k_lds_per_sb(8) : q6k_lds_per_sb(8);
   const size_t per = bpb == 144 ? q4k_lds_per_sb(a.M) : q6k_lds_per_sb(a.M);
   const int cps_max = (int)std::max<size_t>(1, std::min<size_t>((size_t)a.nchunks, (kQ4kLdsBudget - 16) / per8));
-  // Q4_K splits for 4096 (tile, slice) pieces: on 2560 x 12,800, 25 slices of
-  // two superblocks took 10.7-10.8 / 12.45 us at M = 1 / 8 against
-  // 11.5 / 12.9 with 13 slices of four (2048 pieces; 50 slices: the same as 25)
-  Plan pl = plan_split(a.ntiles, a.nchunks, cps_max, true, bpb == 144 ? 2 * kTargetWaves : kTargetWaves);
+  // Both formats split for 4096 (tile, slice) pieces.  On 2560 x 12,800, 25
+  // slices of two superblocks took 10.7-10.8 / 12.45 us (Q4_K) and 20.4 / 21.3
+  // us (Q6_K) at M = 1 / 8, against 11.5 / 12.9 and 22.5 / 23.15 us with 13
+  // slices of four (2048 pieces); 50 slices measured the same as 25 (Q4_K).
+  Plan pl = plan_split(a.ntiles, a.nchunks, cps_max, true, 2 * kTargetWaves);
   a.S = pl.S;
   a.cps = pl.cps;
   a.tpw = pl.tpw;
